@@ -1,0 +1,363 @@
+/*
+ * fp64 CPU oracle for the Flint-style small-batch MoE decode layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: it is used by the tests, by the smoke check and by the
+ * benchmark's CPU-baseline leg, and by nothing else.  It shares no code,
+ * header, table or helper with the HIP library; it reads the same packed
+ * input bytes and computes the layer from its definition, slowly, in fp64.
+ *
+ * What it follows (pages: "Day-0 Support for Flint on vLLM", the vLLM blog on
+ * Recursive's Flint, in its zh / ja / fr / ko renderings; and the AREX article
+ * on vLLM's Day-0 support for Inkling-2-Small, cited only where marked):
+ *  - Model architecture section: 256 experts chosen by a sigmoid top-6, plus
+ *    one shared expert that every token uses.
+ *  - Model architecture section: the NVFP4 checkpoint runs weight-only
+ *    (W4A16) with BF16 activations.
+ *  - Optimization section, Fig. 2 change list: the router and the expert
+ *    GEMVs read only the selected experts' weights, i.e. the layer is the
+ *    sparse evaluation of the dense masked sum (pinned by or_forward_dense).
+ *  - Optimization section: the SiLU kernels (SiLU-gated expert FFN).
+ *  - Optimization section, low-latency path: routing and the expert combine.
+ *  - Inkling-2-Small article, 48-layer MoE section: NVFP4 blocks of 16 with
+ *    an FP4 maximum of 6; accuracy section: the router is kept in FP32 (the
+ *    oracle keeps it in fp64).
+ * Readings where the pages are silent (no router bias or scaling factor,
+ * ties to the lower expert index, renormalisation w = s / sum s, shared
+ * expert with weight 1, element 2j in the low nibble) are the plainest ones;
+ * the repository's design notes list each.
+ *
+ * Formats decoded from their published closed forms:
+ *  - E2M1 (OCP Microscaling Formats v1.0, FP4): bit 3 sign, bits 2..1
+ *    exponent with bias 1, bit 0 mantissa; exponent 0 is subnormal m * 0.5.
+ *  - E4M3FN (OCP 8-bit Floating Point v1.0): bit 7 sign, bits 6..3 exponent
+ *    with bias 7, bits 2..0 mantissa; exponent 0 is subnormal m/8 * 2^-6;
+ *    S.1111.111 is NaN (never produced by the input generator).
+ *  - bf16: the upper 16 bits of an IEEE binary32.
+ *
+ * Numerics: every weight is used at its exact fp64 value
+ * e2m1 * e4m3 * global (at most 30 significant bits, so exact in fp64);
+ * every sum runs sequentially in index order; OpenMP only splits independent
+ * rows or tokens, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#else
+static int omp_in_parallel(void) { return 0; }
+#endif
+
+/* ------------------------------------------------------------------ formats */
+
+double or_e2m1(uint8_t nib) {
+  int sign = (nib >> 3) & 1;
+  int ex = (nib >> 1) & 3;
+  int man = nib & 1;
+  double mag = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+  return sign ? -mag : mag;
+}
+
+double or_e4m3(uint8_t byte) {
+  int sign = (byte >> 7) & 1;
+  int ex = (byte >> 3) & 15;
+  int man = byte & 7;
+  double mag;
+  if (ex == 15 && man == 7) return NAN;
+  if (ex == 0) mag = ldexp(man / 8.0, -6);
+  else mag = ldexp(1.0 + man / 8.0, ex - 7);
+  return sign ? -mag : mag;
+}
+
+double or_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Lookup tables filled from the closed forms above on first use. */
+static double g_e2m1[16], g_e4m3[256];
+static int g_tables_ready = 0;
+static void or_tables(void) {
+  if (g_tables_ready) return;
+  #pragma omp critical(or_tables_init)
+  {
+    if (!g_tables_ready) {
+      for (int i = 0; i < 16; ++i) g_e2m1[i] = or_e2m1((uint8_t)i);
+      for (int i = 0; i < 256; ++i) g_e4m3[i] = or_e4m3((uint8_t)i);
+      g_tables_ready = 1;
+    }
+  }
+}
+
+/* ------------------------------------------------------------ weight access */
+
+enum { OR_NVFP4 = 0, OR_BF16 = 1 };
+
+/* One expert set (n experts).  NVFP4: w13 u8 [n][2][I][H/2], w13s u8
+ * [n][2][I][H/16], w2 u8 [n][H][I/2], w2s u8 [n][H][I/16], glob f32 [n][3].
+ * BF16: w13 u16 [n][2][I][H], w2 u16 [n][H][I]; w13s, w2s, glob unused. */
+typedef struct {
+  const void* w13;
+  const uint8_t* w13s;
+  const void* w2;
+  const uint8_t* w2s;
+  const float* glob;
+  int32_t fmt;
+} or_experts;
+
+typedef struct {
+  int32_t hidden, inter, n_experts, top_k, n_shared;
+} or_shape;
+
+/* Row r of matrix t (0 gate, 1 up, 2 down) of expert e, dequantised to fp64.
+ * gate/up rows have H columns; down rows have I columns. */
+static void or_row(const or_experts* X, int64_t e, int t, int64_t r, int64_t H, int64_t I,
+                   double* out) {
+  int64_t rows = t < 2 ? I : H;
+  int64_t cols = t < 2 ? H : I;
+  if (X->fmt == OR_BF16) {
+    const uint16_t* base = t < 2 ? (const uint16_t*)X->w13 + ((e * 2 + t) * rows) * cols
+                                 : (const uint16_t*)X->w2 + (e * rows) * cols;
+    for (int64_t c = 0; c < cols; ++c) out[c] = or_bf16(base[r * cols + c]);
+    return;
+  }
+  const uint8_t* codes = t < 2 ? (const uint8_t*)X->w13 + ((e * 2 + t) * rows) * (cols / 2)
+                               : (const uint8_t*)X->w2 + (e * rows) * (cols / 2);
+  const uint8_t* scales = t < 2 ? X->w13s + ((e * 2 + t) * rows) * (cols / 16)
+                                : X->w2s + (e * rows) * (cols / 16);
+  double global = (double)X->glob[e * 3 + t];
+  for (int64_t c = 0; c < cols; ++c) {
+    uint8_t byte = codes[r * (cols / 2) + c / 2];
+    uint8_t nib = (c & 1) ? (byte >> 4) : (byte & 15);
+    out[c] = g_e2m1[nib] * g_e4m3[scales[r * (cols / 16) + c / 16]] * global;
+  }
+}
+
+/* Dequantise one NVFP4 tensor [rows][cols] to fp32 with a single rounding:
+ * fp32(e2m1 * e4m3 * global), the product being exact in fp64. */
+void or_dequant_f32(const uint8_t* codes, const uint8_t* scales, float global, int64_t rows,
+                    int64_t cols, float* out) {
+  or_tables();
+  #pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      uint8_t byte = codes[r * (cols / 2) + c / 2];
+      uint8_t nib = (c & 1) ? (byte >> 4) : (byte & 15);
+      out[r * cols + c] = (float)(g_e2m1[nib] * g_e4m3[scales[r * (cols / 16) + c / 16]] *
+                                  (double)global);
+    }
+}
+
+/* The same tensor at its exact fp64 value. */
+void or_dequant_f64(const uint8_t* codes, const uint8_t* scales, float global, int64_t rows,
+                    int64_t cols, double* out) {
+  or_tables();
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      uint8_t byte = codes[r * (cols / 2) + c / 2];
+      uint8_t nib = (c & 1) ? (byte >> 4) : (byte & 15);
+      out[r * cols + c] = g_e2m1[nib] * g_e4m3[scales[r * (cols / 16) + c / 16]] * (double)global;
+    }
+}
+
+/* ------------------------------------------------------------------ routing */
+
+/* logits[e] = sum_k W_r[e][k] * x[k], fp64, k ascending. */
+void or_router_logits(const uint16_t* x, const uint16_t* router, int32_t E, int32_t H,
+                      double* logits) {
+  #pragma omp parallel for schedule(static) if (!omp_in_parallel())
+  for (int64_t e = 0; e < E; ++e) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < H; ++k) acc += or_bf16(router[e * H + k]) * or_bf16(x[k]);
+    logits[e] = acc;
+  }
+}
+
+double or_sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* The k largest scores, ordered by (score descending, expert index ascending).
+ * gap = s_(k) - s_(k+1), the distance between the last chosen and the first
+ * rejected score (+inf when every expert is chosen). */
+void or_topk(const double* scores, int32_t E, int32_t k, int32_t* ids, double* gap) {
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  for (int32_t i = 0; i < E; ++i) order[i] = i;
+  /* insertion sort on (score desc, index asc) */
+  for (int32_t i = 1; i < E; ++i) {
+    int32_t v = order[i];
+    int32_t j = i - 1;
+    while (j >= 0 && (scores[order[j]] < scores[v] ||
+                      (scores[order[j]] == scores[v] && order[j] > v))) {
+      order[j + 1] = order[j];
+      --j;
+    }
+    order[j + 1] = v;
+  }
+  for (int32_t i = 0; i < k; ++i) ids[i] = order[i];
+  *gap = k < E ? scores[order[k - 1]] - scores[order[k]] : INFINITY;
+  free(order);
+}
+
+/* Routing of one token: ids [k] (score descending), weights w [k] = s / sum s,
+ * gap as in or_topk; scores_out [E] (nullable) receives every sigmoid score.
+ * When forced is non-null its k ids are used instead of the top-k. */
+static void or_route_token(const or_shape* S, const uint16_t* x, const uint16_t* router,
+                           const int32_t* forced, int32_t* ids, double* w, double* gap,
+                           double* scores_out) {
+  int32_t E = S->n_experts, k = S->top_k;
+  double* logits = (double*)malloc(sizeof(double) * (size_t)E);
+  double* scores = (double*)malloc(sizeof(double) * (size_t)E);
+  or_router_logits(x, router, E, S->hidden, logits);
+  for (int32_t e = 0; e < E; ++e) scores[e] = or_sigmoid(logits[e]);
+  or_topk(scores, E, k, ids, gap);
+  if (forced) for (int32_t j = 0; j < k; ++j) ids[j] = forced[j];
+  double sum = 0.0;
+  for (int32_t j = 0; j < k; ++j) sum += scores[ids[j]];
+  for (int32_t j = 0; j < k; ++j) w[j] = scores[ids[j]] / sum;
+  if (scores_out) memcpy(scores_out, scores, sizeof(double) * (size_t)E);
+  free(logits);
+  free(scores);
+}
+
+void or_route(const or_shape* S, const uint16_t* x, int32_t B, const uint16_t* router,
+              int32_t* ids, double* w, double* gap, double* scores) {
+  for (int32_t t = 0; t < B; ++t)
+    or_route_token(S, x + (int64_t)t * S->hidden, router, NULL, ids + (int64_t)t * S->top_k,
+                   w + (int64_t)t * S->top_k, gap + t,
+                   scores ? scores + (int64_t)t * S->n_experts : NULL);
+}
+
+/* ------------------------------------------------------------------ experts */
+
+/* d = D_e (SiLU(G_e x) * (U_e x)) for one token x (fp64, length H). */
+void or_expert(const or_shape* S, const or_experts* X, int32_t e, const double* x, double* d) {
+  int64_t H = S->hidden, I = S->inter;
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  or_tables();
+  #pragma omp parallel if (!omp_in_parallel())
+  {
+    double* row = (double*)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+    #pragma omp for schedule(static)
+    for (int64_t i = 0; i < I; ++i) {
+      double g = 0.0, u = 0.0;
+      or_row(X, e, 0, i, H, I, row);
+      for (int64_t k = 0; k < H; ++k) g += row[k] * x[k];
+      or_row(X, e, 1, i, H, I, row);
+      for (int64_t k = 0; k < H; ++k) u += row[k] * x[k];
+      h[i] = g * or_sigmoid(g) * u;
+    }
+    #pragma omp for schedule(static)
+    for (int64_t j = 0; j < H; ++j) {
+      double acc = 0.0;
+      or_row(X, e, 2, j, H, I, row);
+      for (int64_t i = 0; i < I; ++i) acc += row[i] * h[i];
+      d[j] = acc;
+    }
+    free(row);
+  }
+  free(h);
+}
+
+static int or_cmp_i32(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* One token of the layer: y = sum_j w_j d_{e_j} (ascending expert id) + d_shared. */
+static void or_forward_token(const or_shape* S, const uint16_t* xb, const uint16_t* router,
+                             const or_experts* routed, const or_experts* shared,
+                             const int32_t* forced, double* y, int32_t* ids, double* w,
+                             double* gap) {
+  int64_t H = S->hidden;
+  int32_t k = S->top_k;
+  double* x = (double*)malloc(sizeof(double) * (size_t)H);
+  double* d = (double*)malloc(sizeof(double) * (size_t)H);
+  int32_t* sorted = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  for (int64_t c = 0; c < H; ++c) x[c] = or_bf16(xb[c]);
+  or_route_token(S, xb, router, forced, ids, w, gap, NULL);
+  memcpy(sorted, ids, sizeof(int32_t) * (size_t)k);
+  qsort(sorted, (size_t)k, sizeof(int32_t), or_cmp_i32);
+  for (int64_t c = 0; c < H; ++c) y[c] = 0.0;
+  for (int32_t s = 0; s < k; ++s) {
+    double wj = 0.0;
+    for (int32_t j = 0; j < k; ++j) if (ids[j] == sorted[s]) wj = w[j];
+    or_expert(S, routed, sorted[s], x, d);
+    for (int64_t c = 0; c < H; ++c) y[c] += wj * d[c];
+  }
+  if (shared && S->n_shared > 0) {
+    or_expert(S, shared, 0, x, d);
+    for (int64_t c = 0; c < H; ++c) y[c] += d[c];
+  }
+  free(x);
+  free(d);
+  free(sorted);
+}
+
+/* The layer for B tokens.  y [B][H] fp64; ids [B][k]; w [B][k]; gap [B].
+ * forced (nullable) [B][k]: use these expert ids instead of the top-k. */
+void or_forward(const or_shape* S, const uint16_t* x, int32_t B, const uint16_t* router,
+                const or_experts* routed, const or_experts* shared, const int32_t* forced,
+                double* y, int32_t* ids, double* w, double* gap) {
+  or_tables();
+  int64_t H = S->hidden, k = S->top_k;
+  #pragma omp parallel for schedule(dynamic, 1) if (B > 1)
+  for (int32_t t = 0; t < B; ++t)
+    or_forward_token(S, x + t * H, router, routed, shared, forced ? forced + t * k : NULL,
+                     y + t * H, ids + t * k, w + t * k, gap + t);
+}
+
+/* Dense evaluation with masked weights: every routed expert is computed and
+ * scaled by m_e = w_e if e was selected and 0 otherwise, summed in ascending
+ * expert id, then the shared expert is added.  Equal to or_forward bit for bit. */
+void or_forward_dense(const or_shape* S, const uint16_t* xb, int32_t B, const uint16_t* router,
+                      const or_experts* routed, const or_experts* shared, double* y) {
+  or_tables();
+  int64_t H = S->hidden;
+  int32_t E = S->n_experts, k = S->top_k;
+  double* x = (double*)malloc(sizeof(double) * (size_t)H);
+  double* d = (double*)malloc(sizeof(double) * (size_t)H);
+  double* m = (double*)malloc(sizeof(double) * (size_t)E);
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  double* w = (double*)malloc(sizeof(double) * (size_t)k);
+  for (int32_t t = 0; t < B; ++t) {
+    double gap;
+    for (int64_t c = 0; c < H; ++c) x[c] = or_bf16(xb[t * H + c]);
+    or_route_token(S, xb + t * H, router, NULL, ids, w, &gap, NULL);
+    for (int32_t e = 0; e < E; ++e) m[e] = 0.0;
+    for (int32_t j = 0; j < k; ++j) m[ids[j]] = w[j];
+    double* yt = y + t * H;
+    for (int64_t c = 0; c < H; ++c) yt[c] = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+      or_expert(S, routed, e, x, d);
+      for (int64_t c = 0; c < H; ++c) yt[c] += m[e] * d[c];
+    }
+    if (shared && S->n_shared > 0) {
+      or_expert(S, shared, 0, x, d);
+      for (int64_t c = 0; c < H; ++c) yt[c] += d[c];
+    }
+  }
+  free(x);
+  free(d);
+  free(m);
+  free(ids);
+  free(w);
+}
+
+int or_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void or_set_num_threads(int n) {
+#ifdef _OPENMP
+  omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

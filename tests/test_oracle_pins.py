@@ -1,0 +1,274 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Layer definition ("Day-0 Support for Flint on vLLM", Model architecture:
+256 experts chosen by a sigmoid top-6 plus one shared expert; Optimization,
+Fig. 2 list: only the selected experts' weights are read; SiLU kernels;
+low-latency path: routing and expert combine).  Each test below would fail for
+a plausible slip in the oracle: a dropped or extra term, a wrong sign, a
+swapped gate/up, a transposed matrix, a wrong tie order or expert index.
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+import testgen
+from tests.helpers import bf16_bits_to_f32, f32_to_bf16_bits_exact
+
+H, I, E, K = 32, 16, 8, 2
+
+
+def tiny_layer(seed=3, fmt="nvfp4", H=H, I=I, E=E, K=K, sigma=0.5):
+    return testgen.make_layer(seed, 0, fmt, H, I, E, K, sigma)
+
+
+def f64(u16):
+    return bf16_bits_to_f32(u16).astype(np.float64)
+
+
+# ----------------------------------------------------------------- routing
+def test_sigmoid_matches_library():
+    for z in [-40.0, -3.0, -1e-3, 0.0, 0.5, 2.0, 30.0]:
+        assert oracle.sigmoid(z) == pytest.approx(float(expit(z)), rel=1e-15, abs=1e-300)
+
+
+def test_router_logits_match_numpy_gemv():
+    x = testgen.make_x(5, 1, 2048)[0]
+    R = testgen.make_router(5, 0)
+    got = oracle.router_logits(x, R)
+    want = f64(R) @ f64(x)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_topk_is_the_max_sum_subset(seed):
+    """For distinct scores the top-k set is the unique k-subset of largest sum,
+    found here by brute force over all C(E, k) subsets."""
+    rng = np.random.default_rng(seed)
+    n, k = 12, 4
+    scores = expit(rng.normal(0, 1, n))
+    ids, gap = oracle.topk(scores, k)
+    best = max(itertools.combinations(range(n), k), key=lambda c: scores[list(c)].sum())
+    assert sorted(ids.tolist()) == sorted(best)
+    assert all(scores[ids[j]] > scores[ids[j + 1]] for j in range(k - 1))
+    rest = sorted(set(range(n)) - set(ids.tolist()), key=lambda e: -scores[e])
+    assert gap == scores[ids[-1]] - scores[rest[0]]
+
+
+def test_zero_input_ties_pick_lowest_indices():
+    """x = 0 -> every logit 0, every score 1/2 -> ids 0..5, w = 1/6."""
+    x = np.zeros((1, 2048), np.uint16)
+    R = testgen.make_router(1, 0)
+    ids, w, gap, _ = oracle.route(x, R, 6)
+    assert ids[0].tolist() == [0, 1, 2, 3, 4, 5]
+    np.testing.assert_array_equal(w[0], np.full(6, 1 / 6))
+    assert gap[0] == 0.0
+
+
+def test_duplicate_router_rows_tie_to_lower_index():
+    x = testgen.make_x(2, 1, 2048)
+    R = testgen.make_router(2, 0).copy()
+    logits = oracle.router_logits(x[0], R)
+    top = int(np.argmax(logits))
+    R[200] = R[top]                     # an exact duplicate of the best expert, higher index
+    R[top if top < 100 else 0] = R[top]
+    ids, _, _, _ = oracle.route(x, R, 6)
+    dup = sorted({top, 200, top if top < 100 else 0})
+    assert ids[0][:len(dup)].tolist() == dup
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_renormalised_weights(seed):
+    x = testgen.make_x(seed, 4, 2048)
+    R = testgen.make_router(seed, 0)
+    ids, w, gap, scores = oracle.route(x, R, 6)
+    logits = f64(x) @ f64(R).T
+    for t in range(4):
+        s = expit(logits[t])
+        np.testing.assert_allclose(scores[t], s, rtol=1e-12)
+        assert sorted(ids[t].tolist()) == sorted(np.argsort(-s, kind="stable")[:6].tolist())
+        assert abs(w[t].sum() - 1.0) < 1e-15
+        assert np.all((w[t] > 0) & (w[t] < 1))
+        np.testing.assert_allclose(w[t], s[ids[t]] / s[ids[t]].sum(), rtol=1e-14)
+        assert gap[t] > 0
+
+
+# ----------------------------------------------------------------- experts
+def _bf16_experts(w13, w2):
+    """An expert set in bf16 format from float arrays (values must be bf16-exact)."""
+    n = w13.shape[0]
+    return testgen.Experts("bf16", n, f32_to_bf16_bits_exact(w13), f32_to_bf16_bits_exact(w2))
+
+
+def _round_bf16(a):
+    return bf16_bits_to_f32(np.array([testgen.bf16_rne(float(v)) for v in a.ravel()],
+                                     np.uint16)).reshape(a.shape)
+
+
+def test_expert_is_silu_gated_ffn_when_gate_saturates():
+    """With every gate pre-activation g >= 60, SiLU(g) = g to 1e-26, so the
+    expert reduces to D ((G x) * (U x)) — a plain matrix product checked with
+    numpy.  A swapped gate/up, a transposed D or a dropped product fails."""
+    rng = np.random.default_rng(0)
+    x = np.abs(_round_bf16(rng.normal(0, 1, H))) + 0.25
+    x = _round_bf16(x)
+    G = _round_bf16(np.abs(rng.normal(0, 1, (I, H))) + 2.0)     # g = G x >> 0
+    U = _round_bf16(rng.normal(0, 1, (I, H)))
+    D = _round_bf16(rng.normal(0, 1, (H, I)))
+    X = _bf16_experts(np.stack([G, U])[None], D[None])
+    g = G.astype(np.float64) @ x
+    assert g.min() > 60
+    want = D.astype(np.float64) @ (g * (U.astype(np.float64) @ x))
+    got = oracle.expert(X, 0, x.astype(np.float64), H, I)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13 * np.abs(want).max())
+
+
+def test_expert_vanishes_when_gate_is_very_negative():
+    rng = np.random.default_rng(1)
+    x = _round_bf16(np.abs(rng.normal(0, 1, H)) + 0.25)
+    G = _round_bf16(-(np.abs(rng.normal(0, 1, (I, H))) + 2.0))  # g << 0 -> SiLU(g) ~ g e^g
+    U = _round_bf16(rng.normal(0, 1, (I, H)) * 50)
+    D = _round_bf16(rng.normal(0, 1, (H, I)))
+    X = _bf16_experts(np.stack([G, U])[None], D[None])
+    got = oracle.expert(X, 0, x.astype(np.float64), H, I)
+    assert np.abs(got).max() < 1e-20
+
+
+def test_expert_at_zero_gate_is_zero():
+    rng = np.random.default_rng(2)
+    x = _round_bf16(rng.normal(0, 1, H))
+    G = np.zeros((I, H), np.float32)
+    U = _round_bf16(rng.normal(0, 1, (I, H)))
+    D = _round_bf16(rng.normal(0, 1, (H, I)))
+    X = _bf16_experts(np.stack([G, U])[None], D[None])
+    got = oracle.expert(X, 0, x.astype(np.float64), H, I)
+    assert np.all(got == 0)
+
+
+def test_silu_value_at_ln3():
+    """sigmoid(ln 3) = 3/4, so an expert with a single active path computes
+    0.75 ln3 * u * d exactly up to rounding."""
+    x = np.zeros(H, np.float32)
+    x[0] = 1.0
+    G = np.zeros((I, H), np.float32)
+    U = np.zeros((I, H), np.float32)
+    D = np.zeros((H, I), np.float32)
+    ln3 = float(_round_bf16(np.array([np.log(3.0)]))[0])        # bf16(ln 3)
+    G[0, 0] = ln3
+    U[0, 0] = 2.0
+    D[5, 0] = -0.5
+    X = _bf16_experts(np.stack([G, U])[None], D[None])
+    got = oracle.expert(X, 0, x.astype(np.float64), H, I)
+    want = -0.5 * 2.0 * ln3 / (1 + 1 / np.exp(ln3))
+    assert got[5] == pytest.approx(want, rel=1e-15)
+    assert np.count_nonzero(got) == 1
+
+
+# ----------------------------------------------------------------- layer
+@pytest.mark.parametrize("fmt", ["nvfp4", "bf16"])
+def test_sparse_equals_dense_masked(fmt):
+    L = tiny_layer(fmt=fmt)
+    x = testgen.make_x(11, 3, H)
+    y, ids, w, gap = oracle.forward_layer(x, L)
+    yd = oracle.forward_dense(x, L.router, L.routed, L.shared, K, I)
+    np.testing.assert_array_equal(y, yd)
+
+
+def test_identical_routed_experts_make_routing_irrelevant():
+    """All routed experts equal -> y = f(x) + shared(x) whatever the routing,
+    since the renormalised weights sum to 1."""
+    L = tiny_layer(fmt="nvfp4")
+    R = L.routed
+    same = testgen.Experts("nvfp4", E, np.repeat(R.w13[:1], E, 0), np.repeat(R.w2[:1], E, 0),
+                           np.repeat(R.w13_scale[:1], E, 0), np.repeat(R.w2_scale[:1], E, 0),
+                           np.repeat(R.glob[:1], E, 0))
+    x = testgen.make_x(4, 2, H)
+    y, ids, w, _ = oracle.forward(x, L.router, same, L.shared, K, I)
+    for t in range(2):
+        xt = f64(x[t])
+        want = oracle.expert(same, 0, xt, H, I) + oracle.expert(L.shared, 0, xt, H, I)
+        np.testing.assert_allclose(y[t], want, rtol=1e-14, atol=1e-15)
+
+
+def test_expert_relabelling_is_invisible():
+    """Permuting router rows and routed experts together leaves y unchanged."""
+    L = tiny_layer(fmt="nvfp4")
+    perm = np.random.default_rng(5).permutation(E)
+    R = L.routed
+    P = testgen.Experts("nvfp4", E, R.w13[perm].copy(), R.w2[perm].copy(),
+                        R.w13_scale[perm].copy(), R.w2_scale[perm].copy(), R.glob[perm].copy())
+    x = testgen.make_x(8, 3, H)
+    y, ids, _, _ = oracle.forward(x, L.router, L.routed, L.shared, K, I)
+    y2, ids2, _, _ = oracle.forward(x, L.router[perm].copy(), P, L.shared, K, I)
+    np.testing.assert_allclose(y2, y, rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(perm[ids2], ids)
+
+
+def test_tokens_are_independent():
+    L = tiny_layer(fmt="nvfp4")
+    x = testgen.make_x(9, 4, H)
+    y, ids, w, gap = oracle.forward_layer(x, L)
+    for t in range(4):
+        y1, ids1, _, _ = oracle.forward_layer(x[t:t + 1], L)
+        np.testing.assert_array_equal(y1[0], y[t])
+        np.testing.assert_array_equal(ids1[0], ids[t])
+
+
+def test_shared_expert_is_added_with_weight_one():
+    L = tiny_layer(fmt="nvfp4")
+    x = testgen.make_x(10, 2, H)
+    y, _, _, _ = oracle.forward_layer(x, L)
+    y0, _, _, _ = oracle.forward(x, L.router, L.routed, None, K, I)
+    for t in range(2):
+        sh = oracle.expert(L.shared, 0, f64(x[t]), H, I)
+        np.testing.assert_allclose(y[t] - y0[t], sh, rtol=1e-12, atol=1e-14)
+
+
+def test_forced_ids_reproduce_routing_when_equal():
+    L = tiny_layer(fmt="nvfp4")
+    x = testgen.make_x(12, 2, H)
+    y, ids, w, _ = oracle.forward_layer(x, L)
+    y2, ids2, w2, _ = oracle.forward_layer(x, L, forced_ids=ids[:, ::-1].copy())
+    np.testing.assert_array_equal(y2, y)
+    np.testing.assert_array_equal(np.sort(w2, 1), np.sort(w, 1))
+
+
+def test_nvfp4_layer_equals_bf16_layer_on_grid_weights():
+    """NVFP4 weights whose global is a power of two dequantise to bf16-exact
+    values; a bf16 copy of those values (built from the OCP tables, not from
+    the oracle's decoder) must give the identical layer output."""
+    rng = np.random.default_rng(4)
+    e2 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6])
+    glob = 2.0 ** -10
+
+    def rand_tensor(n, rows, cols):
+        codes = rng.integers(0, 256, (n, rows, cols // 2), dtype=np.uint8)
+        scales = rng.integers(0x28, 0x48, (n, rows, cols // 16), dtype=np.uint8)
+        sval = np.array([2.0 ** (((b >> 3) & 15) - 7) * (1 + (b & 7) / 8) for b in range(256)])
+        lo, hi = codes & 15, codes >> 4
+        nib = np.stack([lo, hi], -1).reshape(n, rows, cols)
+        vals = e2[nib] * np.repeat(sval[scales], 16, -1) * glob
+        return codes, scales, vals
+
+    c13, s13, v13 = rand_tensor(E + 1, 2 * I, H)
+    c2, s2, v2 = rand_tensor(E + 1, H, I)
+    g = np.full((E + 1, 3), glob, np.float32)
+
+    def nv(sl):
+        return testgen.Experts("nvfp4", len(range(*sl.indices(E + 1))),
+                               c13[sl].reshape(-1, 2, I, H // 2).copy(), c2[sl].copy(),
+                               s13[sl].reshape(-1, 2, I, H // 16).copy(), s2[sl].copy(),
+                               g[sl].copy())
+
+    def bf(sl):
+        return _bf16_experts(v13[sl].reshape(-1, 2, I, H).astype(np.float32),
+                             v2[sl].astype(np.float32))
+
+    L = tiny_layer()
+    x = testgen.make_x(13, 3, H)
+    y_nv, ids_nv, _, _ = oracle.forward(x, L.router, nv(slice(0, E)), nv(slice(E, E + 1)), K, I)
+    y_bf, ids_bf, _, _ = oracle.forward(x, L.router, bf(slice(0, E)), bf(slice(E, E + 1)), K, I)
+    np.testing.assert_array_equal(ids_nv, ids_bf)
+    np.testing.assert_array_equal(y_nv, y_bf)
