@@ -1,0 +1,155 @@
+/*
+ * moe_decode.h — C ABI of the MI355X (gfx950) Flint-style MoE layer.
+ *
+ * The layer ("Day-0 Support for Flint on vLLM", Model architecture): a
+ * sigmoid router over 256 experts picks the top 6 for each token, and one
+ * shared expert that every token uses is added.  Each expert is a SiLU-gated
+ * FFN, y_e = D_e (SiLU(G_e x) * (U_e x)), with G_e, U_e [512 x 2048] and
+ * D_e [2048 x 512].  The layer output is
+ *     y = sum_j w_j y_{e_j} + y_shared,     w_j = s_j / sum_sel s,  s = sigmoid(W_r x).
+ * Weights are NVFP4, run weight-only with BF16 activations (W4A16), or BF16
+ * (Model architecture section); only the selected experts' weights are read
+ * (Optimization section, Fig. 2 list, small-batch MoE kernels); routing and
+ * the expert combine are fused into the neighbouring GEMV kernels on the
+ * low-latency path for up to 8 requests (Optimization section).
+ *
+ * Conventions for every entry point
+ *  - Every data pointer is a DEVICE pointer owned by the caller, 16-byte
+ *    aligned (workspace: 256-byte aligned).  The library allocates nothing,
+ *    keeps no state between calls, never synchronises and never reads
+ *    routing back to the host, so a call can be captured in a HIP graph.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it; device-side faults surface at the caller's
+ *    next synchronisation.
+ *  - Arguments are checked before anything is launched; on error nothing is
+ *    launched and the status says why.  MOE_ERR_UNSUPPORTED means a valid
+ *    request this library does not serve (another shape, B > 8, ...): the
+ *    caller should fall back to a generic implementation, the convention the
+ *    Flint pages describe for configurations outside their kernels
+ *    (Usage notes section).
+ *  - Calls on distinct workspaces may run concurrently; calls sharing a
+ *    workspace must be ordered (same stream, or events).
+ *  - No C++ exception crosses this boundary.
+ *
+ * Tensor layouts (E experts in a set; H = hidden = 2048, I = inter = 512)
+ *  x, out         bf16 [T][H], token-major.
+ *  router_w       bf16 [E_routed][H] (row e gives logit e).
+ *  NVFP4 expert set (16-element blocks along the input dimension):
+ *    w13          u8  [E][2][I][H/2]   codes of gate (index 0) and up (1);
+ *                                      byte j of a row holds element 2j in
+ *                                      bits 0-3 and element 2j+1 in bits 4-7;
+ *                                      a code is E2M1 (sign, 2-bit exponent
+ *                                      with bias 1, 1-bit mantissa).
+ *    w13_scale    u8  [E][2][I][H/16]  E4M3FN block scales.
+ *    w2           u8  [E][H][I/2]      codes of down.
+ *    w2_scale     u8  [E][H][I/16]     E4M3FN block scales.
+ *    global       f32 [E][3]           per-tensor scales (gate, up, down).
+ *    weight value = e2m1(code) * e4m3(block scale) * global.
+ *  BF16 expert set: w13 bf16 [E][2][I][H], w2 bf16 [E][H][I]; the scale and
+ *    global pointers must be NULL.
+ *  The shared expert is an expert set with E = 1 in the same format.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, aliasing output      */
+  MOE_ERR_UNSUPPORTED = -2, /* valid request outside what this library runs */
+  MOE_ERR_MISALIGNED = -3,  /* a pointer breaks the alignment rule above     */
+  MOE_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required    */
+  MOE_ERR_HIP = -5          /* a HIP launch failed                           */
+} moe_status;
+
+typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1 } moe_wformat;
+
+/* Layer shape.  This library serves {2048, 512, 256, 6, 1, NVFP4 | BF16}
+ * (Model architecture section: hidden 2048, 256 experts, sigmoid top-6, one
+ * shared expert); anything else returns MOE_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t hidden;    /* H */
+  int32_t inter;     /* I, per expert */
+  int32_t n_experts; /* routed experts */
+  int32_t top_k;
+  int32_t n_shared;
+  int32_t wfmt;      /* moe_wformat */
+} moe_shape;
+
+typedef struct {
+  const void* w13;
+  const void* w13_scale;
+  const void* w2;
+  const void* w2_scale;
+  const float* global;
+} moe_experts;
+
+/* Version of this ABI (incremented on any incompatible change). */
+int32_t moe_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status status);
+
+/* Workspace bytes needed for `tokens` tokens: prefill = 0 for the decode
+ * entry points (tokens 1..8), 1 for moe_prefill_forward.  Returns 0 when the
+ * shape or token count is not served.  The workspace must be zero-filled
+ * once before its first use (e.g. allocated with torch.zeros); every call
+ * leaves its internal counters at zero again when its kernels finish. */
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens, int32_t prefill);
+
+/* Router GEMV + sigmoid + top-k + renormalisation for B = 1..8 tokens
+ * (Model architecture: sigmoid top-6; Optimization: routing fused into the
+ * router GEMV).  logits_e = sum_k W_r[e][k] x[k] in fp32, s_e = sigmoid;
+ * the k largest are chosen (ties go to the lower expert index), returned in
+ * descending score order, with w_j = s_j / sum of the chosen s.
+ *   x        bf16 [B][H]          ids  int32 [B][top_k]   (written)
+ *   router_w bf16 [E][H]          w    f32   [B][top_k]   (written)
+ * B > 8 returns MOE_ERR_UNSUPPORTED. */
+moe_status moe_decode_route(const moe_shape* shape, const void* x, int32_t B,
+                            const void* router_w, int32_t* ids, float* w, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* The whole layer for B = 1..8 tokens (the low-latency decode path):
+ * route, then the SiLU-gated GEMVs of only the selected experts and of the
+ * shared expert, then the weighted combine, all in fp32 with the output
+ * rounded once to bf16.  At B > 1 each expert chosen by several tokens has
+ * its weights read once for all of them.
+ *   out      bf16 [B][H]   (written; must not overlap x)
+ *   ids_out  int32 [B][top_k], w_out f32 [B][top_k]: the routing used
+ *            (each nullable). */
+moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
+                              const void* router_w, const moe_experts* routed,
+                              const moe_experts* shared, void* out, int32_t* ids_out,
+                              float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/* The same layer for T >= 1 tokens at prefill sizes (Optimization section:
+ * the MoE kernels were also the largest prefill gain, measured on an
+ * 8,192-token prefill): tokens are grouped by expert and each expert runs as
+ * a dense bf16 matrix-core GEMM over its tokens.  Arguments as
+ * moe_decode_forward, with T tokens; the workspace comes from
+ * moe_workspace_bytes(shape, T, 1). */
+moe_status moe_prefill_forward(const moe_shape* shape, const void* x, int32_t T,
+                               const void* router_w, const moe_experts* routed,
+                               const moe_experts* shared, void* out, int32_t* ids_out,
+                               float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Parity probe of the in-register NVFP4 decode: writes tensor `tensor`
+ * (0 gate, 1 up, 2 down) of expert `expert` of an NVFP4 set as fp32,
+ * out[r][c] = fp32(e2m1 * e4m3) * global (the first product is exact, so this
+ * is one rounding of the exact weight).  out: f32 [I][H] for gate/up,
+ * [H][I] for down.  The set must hold more than `expert` experts (not
+ * checked: the caller knows its set size). */
+moe_status moe_nvfp4_dequant(const moe_shape* shape, const moe_experts* set, int32_t expert,
+                             int32_t tensor, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

@@ -1,0 +1,166 @@
+"""Python binding of the gfx950 MoE layer library (libmoe_decode.so).
+
+Thin ctypes marshalling over the C ABI declared in include/moe_decode.h:
+the same entry-point names, torch tensors in, device pointers and the
+current HIP stream out.  Every step of the layer runs in the library's HIP
+kernels; this module computes nothing.  If the library is not built, or the
+GPU is missing, calls fail loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+HERE = pathlib.Path(__file__).resolve().parent
+LIB_PATH = HERE / "libmoe_decode.so"
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED = 0, -1, -2
+MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = -3, -4, -5
+MOE_W_NVFP4, MOE_W_BF16 = 0, 1
+HIDDEN, INTER, N_EXPERTS, TOP_K, N_SHARED = 2048, 512, 256, 6, 1
+MAX_DECODE_BATCH = 8
+
+_LIB = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("wfmt", ctypes.c_int32)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("global_", ctypes.c_void_p)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it was not built)."""
+    global _LIB
+    if _LIB is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(str(LIB_PATH))
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.moe_abi_version.restype = i32
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_bytes.argtypes = [P(Shape), i32, i32]
+        L.moe_decode_route.restype = ctypes.c_int
+        L.moe_decode_route.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_decode_forward.restype = ctypes.c_int
+        L.moe_decode_forward.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp, vp,
+                                         vp, vp, sz, vp]
+        L.moe_prefill_forward.restype = ctypes.c_int
+        L.moe_prefill_forward.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp, vp,
+                                          vp, vp, sz, vp]
+        L.moe_nvfp4_dequant.restype = ctypes.c_int
+        L.moe_nvfp4_dequant.argtypes = [P(Shape), P(Experts), i32, i32, vp, vp]
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def shape(fmt: int = MOE_W_NVFP4, hidden=HIDDEN, inter=INTER, n_experts=N_EXPERTS, top_k=TOP_K,
+          n_shared=N_SHARED) -> Shape:
+    return Shape(hidden, inter, n_experts, top_k, n_shared, fmt)
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        return {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16}[fmt]
+    return int(fmt)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def experts_struct(ex) -> Experts:
+    """ex: object with w13, w2 and (NVFP4) w13_scale, w2_scale, glob device tensors."""
+    return Experts(_ptr(ex.w13), _ptr(getattr(ex, "w13_scale", None)), _ptr(ex.w2),
+                   _ptr(getattr(ex, "w2_scale", None)), _ptr(getattr(ex, "glob", None)))
+
+
+def abi_version() -> int:
+    return int(lib().moe_abi_version())
+
+
+def moe_workspace_bytes(tokens: int, prefill: bool = False, fmt=MOE_W_NVFP4) -> int:
+    S = shape(_fmt(fmt))
+    return int(lib().moe_workspace_bytes(ctypes.byref(S), tokens, 1 if prefill else 0))
+
+
+def moe_decode_route(x, router_w, ids, w, ws, fmt=MOE_W_NVFP4, stream=None, S: Shape | None = None):
+    """Router + top-k for x bf16 [B, H]; writes ids int32 [B, k] and w f32 [B, k]."""
+    S = S or shape(_fmt(fmt))
+    B = x.shape[0] if hasattr(x, "shape") else 1
+    st = lib().moe_decode_route(ctypes.byref(S), _ptr(x), B, _ptr(router_w), _ptr(ids), _ptr(w),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_decode_route")
+
+
+def moe_decode_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_out=None,
+                       fmt=MOE_W_NVFP4, stream=None, S: Shape | None = None, B: int | None = None):
+    """The layer for x bf16 [B, H] (B <= 8) into out bf16 [B, H]."""
+    S = S or shape(_fmt(fmt))
+    B = x.shape[0] if B is None else B
+    R, Sh = experts_struct(routed), experts_struct(shared)
+    st = lib().moe_decode_forward(ctypes.byref(S), _ptr(x), B, _ptr(router_w), ctypes.byref(R),
+                                  ctypes.byref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_decode_forward")
+
+
+def moe_prefill_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_out=None,
+                        fmt=MOE_W_NVFP4, stream=None, S: Shape | None = None, T: int | None = None):
+    """The layer for x bf16 [T, H] at prefill sizes into out bf16 [T, H]."""
+    S = S or shape(_fmt(fmt))
+    T = x.shape[0] if T is None else T
+    R, Sh = experts_struct(routed), experts_struct(shared)
+    st = lib().moe_prefill_forward(ctypes.byref(S), _ptr(x), T, _ptr(router_w), ctypes.byref(R),
+                                   ctypes.byref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_prefill_forward")
+
+
+def moe_nvfp4_dequant(expert_set, expert: int, tensor: int, out, stream=None):
+    """Decode tensor (0 gate, 1 up, 2 down) of one expert of an NVFP4 set into out f32."""
+    S = shape(MOE_W_NVFP4)
+    X = experts_struct(expert_set)
+    st = lib().moe_nvfp4_dequant(ctypes.byref(S), ctypes.byref(X), expert, tensor, _ptr(out),
+                                 _stream(stream))
+    _check(st, "moe_nvfp4_dequant")
+
+
+from .device import DeviceExperts, DeviceLayer, alloc_workspace  # noqa: E402,F401

@@ -1,0 +1,186 @@
+// C ABI of the gfx950 MoE layer library: argument checks, workspace sizing and
+// launches on the caller's stream.  Declarations and the contract of each
+// entry point are in include/moe_decode.h.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe_decode.h"
+#include "common.h"
+#include "launch.h"
+
+
+using moe::ExpertsDev;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->wfmt != MOE_W_NVFP4 && s->wfmt != MOE_W_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->hidden != moe::kH || s->inter != moe::kI || s->n_experts != moe::kE ||
+      s->top_k != moe::kK || s->n_shared != 1)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_ptr(const void* p, uintptr_t a = 16) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (!aligned(p, a)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+moe_status check_experts(const moe_experts* X, int fmt) {
+  if (!X) return MOE_ERR_INVALID_ARG;
+  moe_status st;
+  if ((st = check_ptr(X->w13)) != MOE_OK) return st;
+  if ((st = check_ptr(X->w2)) != MOE_OK) return st;
+  if (fmt == MOE_W_NVFP4) {
+    if ((st = check_ptr(X->w13_scale)) != MOE_OK) return st;
+    if ((st = check_ptr(X->w2_scale)) != MOE_OK) return st;
+    if ((st = check_ptr(X->global)) != MOE_OK) return st;
+  } else if (X->w13_scale || X->w2_scale || X->global) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+ExpertsDev to_dev(const moe_experts* X) {
+  return ExpertsDev{static_cast<const uint8_t*>(X->w13), static_cast<const uint8_t*>(X->w13_scale),
+                    static_cast<const uint8_t*>(X->w2), static_cast<const uint8_t*>(X->w2_scale),
+                    X->global};
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// Checks common to moe_decode_forward and moe_prefill_forward.
+moe_status check_forward(const moe_shape* shape, const void* x, int32_t T, const void* router_w,
+                         const moe_experts* routed, const moe_experts* shared, const void* out,
+                         const int32_t* ids_out, const float* w_out, const void* ws,
+                         size_t ws_bytes, size_t ws_need) {
+  moe_status st;
+  if ((st = check_shape(shape)) != MOE_OK) return st;
+  if (T < 1) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ptr(x)) != MOE_OK) return st;
+  if ((st = check_ptr(router_w)) != MOE_OK) return st;
+  if ((st = check_ptr(out)) != MOE_OK) return st;
+  if ((st = check_experts(routed, shape->wfmt)) != MOE_OK) return st;
+  if ((st = check_experts(shared, shape->wfmt)) != MOE_OK) return st;
+  if (ids_out && !aligned(ids_out, 4)) return MOE_ERR_MISALIGNED;
+  if (w_out && !aligned(w_out, 4)) return MOE_ERR_MISALIGNED;
+  if (!ws || ws_need == 0 || ws_bytes < ws_need) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_MISALIGNED;
+  const size_t xb = (size_t)T * moe::kH * 2;
+  if (overlap(out, xb, x, xb)) return MOE_ERR_INVALID_ARG;
+  if (overlap(out, xb, ws, ws_bytes)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens, int32_t prefill) {
+  if (check_shape(shape) != MOE_OK || tokens < 1) return 0;
+  if (!prefill) return tokens <= moe::kMaxB ? moe::kDecodeWsBytes : 0;
+  return moe::prefill_ws_bytes(tokens);
+}
+
+moe_status moe_decode_route(const moe_shape* shape, const void* x, int32_t B, const void* router_w,
+                            int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
+  if ((st = check_shape(shape)) != MOE_OK) return st;
+  if (B < 1) return MOE_ERR_INVALID_ARG;
+  if (B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_ptr(x)) != MOE_OK) return st;
+  if ((st = check_ptr(router_w)) != MOE_OK) return st;
+  if (!ids || !w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ids, 4) || !aligned(w, 4)) return MOE_ERR_MISALIGNED;
+  if (!ws || ws_bytes < moe::kDecodeWsBytes) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_MISALIGNED;
+  const ExpertsDev none{};
+  hipError_t e = moe::launch_decode(B, shape->wfmt, true, static_cast<const uint16_t*>(x),
+                                    static_cast<const uint16_t*>(router_w), none, none, nullptr,
+                                    ids, w, static_cast<uint8_t*>(ws),
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
+                              const void* router_w, const moe_experts* routed,
+                              const moe_experts* shared, void* out, int32_t* ids_out,
+                              float* w_out, void* ws, size_t ws_bytes, void* stream) {
+  if (shape && check_shape(shape) == MOE_OK && B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
+  moe_status st = check_forward(shape, x, B, router_w, routed, shared, out, ids_out, w_out, ws,
+                                ws_bytes, moe::kDecodeWsBytes);
+  if (st != MOE_OK) return st;
+  hipError_t e = moe::launch_decode(B, shape->wfmt, false, static_cast<const uint16_t*>(x),
+                                    static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                    to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                    static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_prefill_forward(const moe_shape* shape, const void* x, int32_t T,
+                               const void* router_w, const moe_experts* routed,
+                               const moe_experts* shared, void* out, int32_t* ids_out,
+                               float* w_out, void* ws, size_t ws_bytes, void* stream) {
+  const size_t need = (shape && check_shape(shape) == MOE_OK && T >= 1) ? moe::prefill_ws_bytes(T) : 0;
+  moe_status st = check_forward(shape, x, T, router_w, routed, shared, out, ids_out, w_out, ws,
+                                ws_bytes, need == 0 ? 1 : need);
+  if (st != MOE_OK) return st;
+  if (need == 0) return MOE_ERR_UNSUPPORTED;
+  hipError_t e = moe::launch_prefill(T, shape->wfmt, static_cast<const uint16_t*>(x),
+                                     static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                     to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                     static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_nvfp4_dequant(const moe_shape* shape, const moe_experts* set, int32_t expert,
+                             int32_t tensor, float* out, void* stream) {
+  moe_status st;
+  if ((st = check_shape(shape)) != MOE_OK) return st;
+  if (shape->wfmt != MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_experts(set, MOE_W_NVFP4)) != MOE_OK) return st;
+  if ((st = check_ptr(out)) != MOE_OK) return st;
+  if (expert < 0 || tensor < 0 || tensor > 2) return MOE_ERR_INVALID_ARG;
+  const ExpertsDev X = to_dev(set);
+  const size_t mat = (size_t)moe::kH * moe::kI;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int rows, cols;
+  if (tensor < 2) {
+    codes = X.w13 + ((size_t)expert * 2 + tensor) * (mat / 2);
+    scales = X.w13s + ((size_t)expert * 2 + tensor) * (mat / 16);
+    rows = moe::kI;
+    cols = moe::kH;
+  } else {
+    codes = X.w2 + (size_t)expert * (mat / 2);
+    scales = X.w2s + (size_t)expert * (mat / 16);
+    rows = moe::kH;
+    cols = moe::kI;
+  }
+  hipError_t e = moe::launch_dequant(codes, scales, X.glob + (size_t)expert * 3 + tensor, rows,
+                                     cols, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,470 @@
+// Low-latency decode path (B <= 8 tokens) of the Flint-style MoE layer on gfx950.
+//
+// Three kernels per call, enqueued back to back on the caller's stream:
+//   k_route   router GEMV (bf16 x bf16 -> fp32) over the 256 experts, one wave
+//             per expert row; the last workgroup to arrive (device-scope
+//             ticket) runs sigmoid + top-6 + renormalisation per token and
+//             builds the dispatch list: the distinct experts touched by the
+//             call, a token mask and a weight per token for each, shared
+//             expert last.  ("Day-0 Support for Flint on vLLM", Optimization:
+//             routing is fused into the neighbouring GEMV kernel.)
+//   k_gateup  gate and up GEMVs of the listed experts only, weights decoded in
+//             registers, SiLU(g) * u written to the workspace in fp32.
+//             (Optimization, Fig. 2 list: expert GEMVs read only the selected
+//             experts' weights; SiLU kernels.)
+//   k_down    down GEMV of the listed experts with the routing-weighted
+//             combine and the shared expert folded in; each output element is
+//             a fixed-order fp32 sum, rounded once to bf16.  (Optimization:
+//             expert combine fused into the adjacent GEMV.)
+// Each expert touched by several tokens of the call is read once for all of
+// them.  Nothing here uses atomics on data, so results are bitwise
+// reproducible run to run.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ helpers
+__device__ __forceinline__ void load_x_chunk(const uint16_t* __restrict__ x, int t, int lane,
+                                             uint32_t (&xw)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * kH + 32 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 v = p[i];
+    xw[4 * i + 0] = v.x;
+    xw[4 * i + 1] = v.y;
+    xw[4 * i + 2] = v.z;
+    xw[4 * i + 3] = v.w;
+  }
+}
+
+// 32 NVFP4 codes (one 16-byte chunk) decoded to 16 bf16 pairs; exact.
+__device__ __forceinline__ void fp4_chunk_to_bf16(uint4 c, bf16x2 (&q)[16]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    q[4 * d + 0] = fp4x2_to_bf16<0>(w[d]);
+    q[4 * d + 1] = fp4x2_to_bf16<1>(w[d]);
+    q[4 * d + 2] = fp4x2_to_bf16<2>(w[d]);
+    q[4 * d + 3] = fp4x2_to_bf16<3>(w[d]);
+  }
+}
+
+// sum over a lane's 32 elements: block 0 = pairs 0..7, block 1 = pairs 8..15
+__device__ __forceinline__ float dot_fp4_chunk(const bf16x2 (&q)[16], float s0, float s1,
+                                               const uint32_t (&xw)[16]) {
+  float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b0 = dot2_bf16(q[i], xw[i], b0);
+#pragma unroll
+  for (int i = 8; i < 16; ++i) b1 = dot2_bf16(q[i], xw[i], b1);
+  return b0 * s0 + b1 * s1;
+}
+
+__device__ __forceinline__ float dot_bf16_chunk(const uint32_t (&wq)[16], const uint32_t (&xw)[16]) {
+  float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b0 = dot2_bf16(wq[i], xw[i], b0);
+#pragma unroll
+  for (int i = 8; i < 16; ++i) b1 = dot2_bf16(wq[i], xw[i], b1);
+  return b0 + b1;
+}
+
+// ------------------------------------------------------------------ route
+// Selection inside one wave for one token: logits of experts lane + 64 q.
+// Six rounds of wave argmax under the total order (logit desc, index asc).
+template <int B>
+__device__ void route_select(DecodeCtl* __restrict__ ctl, const float* __restrict__ logits,
+                             int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  __shared__ int s_ids[kMaxB][kK];
+  __shared__ float s_w[kMaxB][kK];
+  __shared__ unsigned s_mask[kE];
+  __shared__ int s_slot[kE];
+  __shared__ int s_nrouted;
+
+  for (int t = wave; t < B; t += 4) {
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = logits[t * kE + lane + 64 * q];
+    float sel_l[kK];
+    int sel_i[kK];
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+      float bv = v[0];
+      int bi = lane;
+#pragma unroll
+      for (int q = 1; q < 4; ++q)
+        if (v[q] > bv) { bv = v[q]; bi = lane + 64 * q; }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        float ov = __shfl_xor(bv, o, kWave);
+        int oi = __shfl_xor(bi, o, kWave);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      sel_l[j] = bv;
+      sel_i[j] = bi;
+      if ((bi & 63) == lane) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if ((bi >> 6) == q) v[q] = -INFINITY;
+      }
+    }
+    if (lane == 0) {
+      float s[kK], sum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        s[j] = 1.0f / (1.0f + expf(-sel_l[j]));
+        sum += s[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        s_ids[t][j] = sel_i[j];
+        s_w[t][j] = s[j] / sum;
+      }
+    }
+  }
+  for (int e = tid; e < kE; e += blockDim.x) s_mask[e] = 0u;
+  __syncthreads();
+  if (tid < B * kK) {
+    const int t = tid / kK, j = tid % kK;
+    atomicOr(&s_mask[s_ids[t][j]], 1u << t);
+    ctl->ids[t][j] = s_ids[t][j];
+    ctl->w[t][j] = s_w[t][j];
+    if (ids_out) ids_out[t * kK + j] = s_ids[t][j];
+    if (w_out) w_out[t * kK + j] = s_w[t][j];
+  }
+  __syncthreads();
+  if (wave == 0) {   // compact the touched experts in ascending id order
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 64 * q + lane;
+      const unsigned m = s_mask[e];
+      const uint64_t bal = __ballot(m != 0u);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (m != 0u) {
+        ctl->active_expert[pos] = e;
+        ctl->active_mask[pos] = m;
+        s_slot[e] = pos;
+      }
+      base += __popcll(bal);
+    }
+    if (lane == 0) {
+      s_nrouted = base;
+      ctl->n_active = base + 1;
+      ctl->active_expert[base] = kE;
+      ctl->active_mask[base] = (1u << B) - 1u;
+    }
+  }
+  __syncthreads();
+  const int nr = s_nrouted;
+  for (int idx = tid; idx < (nr + 1) * B; idx += blockDim.x) {
+    const int a = idx / B, t = idx % B;
+    float wt = 0.0f;
+    if (a == nr) {
+      wt = 1.0f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kK; ++j)
+        if (s_slot[s_ids[t][j]] == a) wt = s_w[t][j];
+    }
+    ctl->wtab[a][t] = wt;
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x,
+                                               const uint16_t* __restrict__ rw,
+                                               uint8_t* __restrict__ ws,
+                                               int32_t* __restrict__ ids_out,
+                                               float* __restrict__ w_out) {
+  DecodeCtl* ctl = reinterpret_cast<DecodeCtl*>(ws);
+  float* logits = reinterpret_cast<float*>(ws + kLogitsOff);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 4 + wave;
+
+  uint32_t wv[16];
+  {
+    const uint4* p = reinterpret_cast<const uint4*>(rw + (size_t)e * kH + 32 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 v = p[i];
+      wv[4 * i + 0] = v.x;
+      wv[4 * i + 1] = v.y;
+      wv[4 * i + 2] = v.z;
+      wv[4 * i + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < B; ++t) {
+    uint32_t xw[16];
+    load_x_chunk(x, t, lane, xw);
+    float acc = dot_bf16_chunk(wv, xw);
+    acc = wave_sum(acc);
+    if (lane == 0) logits[t * kE + e] = acc;
+  }
+
+  __shared__ int s_last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();   // publish this workgroup's logits device-wide
+    const unsigned prev = atomicInc(&ctl->ticket, gridDim.x - 1);   // wraps to 0 on the last
+    s_last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();     // see every other workgroup's logits
+  route_select<B>(ctl, logits, ids_out, w_out);
+}
+
+// ------------------------------------------------------------------ gate/up
+// Workgroup = 4 waves; wave handles R consecutive rows i of gate and up for
+// one dispatch entry (blockIdx.y).  Lane l covers input columns [32l, 32l+32).
+template <int B, int FMT, int R>
+__global__ __launch_bounds__(256) void k_gateup(const uint16_t* __restrict__ x, ExpertsDev routed,
+                                                ExpertsDev shared, uint8_t* __restrict__ ws) {
+  const DecodeCtl* ctl = reinterpret_cast<const DecodeCtl*>(ws);
+  float* hbuf = reinterpret_cast<float*>(ws + kHOff);
+  const int a = blockIdx.y;
+  if (a >= ctl->n_active) return;
+  const int e = ctl->active_expert[a];
+  const unsigned mask = ctl->active_mask[a];
+  const bool sh = (e == kE);
+  const ExpertsDev X = sh ? shared : routed;
+  const size_t ee = sh ? 0 : (size_t)e;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * 4 + wave) * R;
+
+  if constexpr (FMT == FMT_NVFP4) {
+    uint4 cg[R], cu[R];
+    uint32_t sg[R], su[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const size_t rg = (ee * 2 + 0) * kI + row0 + r;
+      const size_t ru = (ee * 2 + 1) * kI + row0 + r;
+      cg[r] = *reinterpret_cast<const uint4*>(X.w13 + rg * (kH / 2) + 16 * lane);
+      cu[r] = *reinterpret_cast<const uint4*>(X.w13 + ru * (kH / 2) + 16 * lane);
+      sg[r] = *reinterpret_cast<const uint16_t*>(X.w13s + rg * (kH / 16) + 2 * lane);
+      su[r] = *reinterpret_cast<const uint16_t*>(X.w13s + ru * (kH / 16) + 2 * lane);
+    }
+    const float gg = X.glob[ee * 3 + 0];
+    const float gu = X.glob[ee * 3 + 1];
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      if (!((mask >> t) & 1u)) continue;
+      uint32_t xw[16];
+      load_x_chunk(x, t, lane, xw);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        bf16x2 q[16];
+        fp4_chunk_to_bf16(cg[r], q);
+        float g = dot_fp4_chunk(q, e4m3_to_f32<0>(sg[r]), e4m3_to_f32<1>(sg[r]), xw);
+        fp4_chunk_to_bf16(cu[r], q);
+        float u = dot_fp4_chunk(q, e4m3_to_f32<0>(su[r]), e4m3_to_f32<1>(su[r]), xw);
+        g = wave_sum(g) * gg;
+        u = wave_sum(u) * gu;
+        if (lane == 0) hbuf[((size_t)a * kMaxB + t) * kI + row0 + r] = silu_mul(g, u);
+      }
+    }
+  } else {
+    uint32_t wg[R][16], wu[R][16];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const size_t rg = (ee * 2 + 0) * kI + row0 + r;
+      const size_t ru = (ee * 2 + 1) * kI + row0 + r;
+      const uint4* pg = reinterpret_cast<const uint4*>(X.w13 + (rg * kH + 32 * lane) * 2);
+      const uint4* pu = reinterpret_cast<const uint4*>(X.w13 + (ru * kH + 32 * lane) * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint4 v = pg[i];
+        wg[r][4 * i] = v.x; wg[r][4 * i + 1] = v.y; wg[r][4 * i + 2] = v.z; wg[r][4 * i + 3] = v.w;
+        v = pu[i];
+        wu[r][4 * i] = v.x; wu[r][4 * i + 1] = v.y; wu[r][4 * i + 2] = v.z; wu[r][4 * i + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      if (!((mask >> t) & 1u)) continue;
+      uint32_t xw[16];
+      load_x_chunk(x, t, lane, xw);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float g = wave_sum(dot_bf16_chunk(wg[r], xw));
+        float u = wave_sum(dot_bf16_chunk(wu[r], xw));
+        if (lane == 0) hbuf[((size_t)a * kMaxB + t) * kI + row0 + r] = silu_mul(g, u);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ down
+// Workgroup = 4 waves over the same 4 output rows; 16 lanes per row, lane
+// (l & 15) covers intermediate columns [32c, 32c+32).  Wave w takes dispatch
+// entries w, w+4, ...; the four partial sums are added in wave order.
+template <int B, int FMT>
+__global__ __launch_bounds__(256) void k_down(ExpertsDev routed, ExpertsDev shared,
+                                              const uint8_t* __restrict__ ws,
+                                              uint16_t* __restrict__ out) {
+  const DecodeCtl* ctl = reinterpret_cast<const DecodeCtl*>(ws);
+  const float* hbuf = reinterpret_cast<const float*>(ws + kHOff);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15;
+  const int rs = lane >> 4;
+  const int row = blockIdx.x * 4 + rs;
+  const int n_active = ctl->n_active;
+
+  float acc[B];
+#pragma unroll
+  for (int t = 0; t < B; ++t) acc[t] = 0.0f;
+
+  for (int a = wave; a < n_active; a += 4) {
+    const int e = ctl->active_expert[a];
+    const unsigned mask = ctl->active_mask[a];
+    const bool sh = (e == kE);
+    const ExpertsDev X = sh ? shared : routed;
+    const size_t ee = sh ? 0 : (size_t)e;
+    float wf[32];
+    float s0, s1, gl;
+    if constexpr (FMT == FMT_NVFP4) {
+      const uint4 cw = *reinterpret_cast<const uint4*>(X.w2 + (ee * kH + row) * (kI / 2) + 16 * c);
+      const uint32_t sc = *reinterpret_cast<const uint16_t*>(X.w2s + (ee * kH + row) * (kI / 16) + 2 * c);
+      gl = X.glob[ee * 3 + 2];
+      s0 = e4m3_to_f32<0>(sc);
+      s1 = e4m3_to_f32<1>(sc);
+      const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        f32x2 p;
+        p = fp4x2_to_f32<0>(w4[d]); wf[8 * d + 0] = p.x; wf[8 * d + 1] = p.y;
+        p = fp4x2_to_f32<1>(w4[d]); wf[8 * d + 2] = p.x; wf[8 * d + 3] = p.y;
+        p = fp4x2_to_f32<2>(w4[d]); wf[8 * d + 4] = p.x; wf[8 * d + 5] = p.y;
+        p = fp4x2_to_f32<3>(w4[d]); wf[8 * d + 6] = p.x; wf[8 * d + 7] = p.y;
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(X.w2 + ((ee * kH + row) * kI + 32 * c) * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = p[i];
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          wf[8 * i + 2 * k] = bf16_lo(vv[k]);
+          wf[8 * i + 2 * k + 1] = bf16_hi(vv[k]);
+        }
+      }
+      s0 = 1.0f;
+      s1 = 1.0f;
+      gl = 1.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      if (!((mask >> t) & 1u)) continue;
+      const float4* hp = reinterpret_cast<const float4*>(hbuf + ((size_t)a * kMaxB + t) * kI + 32 * c);
+      float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 h = hp[i];
+        b0 += wf[4 * i + 0] * h.x;
+        b0 += wf[4 * i + 1] * h.y;
+        b0 += wf[4 * i + 2] * h.z;
+        b0 += wf[4 * i + 3] * h.w;
+      }
+#pragma unroll
+      for (int i = 4; i < 8; ++i) {
+        const float4 h = hp[i];
+        b1 += wf[4 * i + 0] * h.x;
+        b1 += wf[4 * i + 1] * h.y;
+        b1 += wf[4 * i + 2] * h.z;
+        b1 += wf[4 * i + 3] * h.w;
+      }
+      acc[t] += ctl->wtab[a][t] * gl * (b0 * s0 + b1 * s1);
+    }
+  }
+
+  __shared__ float part[4][4][kMaxB];
+#pragma unroll
+  for (int t = 0; t < B; ++t) {
+    const float v = group16_sum(acc[t]);
+    if (c == 0) part[wave][rs][t] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 4 * B) {
+    const int r = threadIdx.x / B, t = threadIdx.x % B;
+    const float s = part[0][r][t] + part[1][r][t] + part[2][r][t] + part[3][r][t];
+    out[(size_t)t * kH + blockIdx.x * 4 + r] = f32_to_bf16_rne(s);
+  }
+}
+
+// ------------------------------------------------------------------ dequant probe
+// out[r][c] = fp32(e2m1 * e4m3) * global; one thread per 8 codes.
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ scales,
+                                                 const float* __restrict__ glob, int rows,
+                                                 int cols, float* __restrict__ out) {
+  const int per_row = cols / 8;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * per_row) return;
+  const int r = idx / per_row, d = idx % per_row;
+  const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[idx];
+  const float s = e4m3_to_f32<0>(scales[(size_t)r * (cols / 16) + d / 2]);
+  const float g = *glob;
+  float* o = out + (size_t)r * cols + 8 * d;
+  f32x2 p;
+  p = fp4x2_to_f32<0>(w); o[0] = (p.x * s) * g; o[1] = (p.y * s) * g;
+  p = fp4x2_to_f32<1>(w); o[2] = (p.x * s) * g; o[3] = (p.y * s) * g;
+  p = fp4x2_to_f32<2>(w); o[4] = (p.x * s) * g; o[5] = (p.y * s) * g;
+  p = fp4x2_to_f32<3>(w); o[6] = (p.x * s) * g; o[7] = (p.y * s) * g;
+}
+
+// ------------------------------------------------------------------ launchers
+template <int B>
+static hipError_t launch_decode_b(int fmt, bool route_only, const uint16_t* x, const uint16_t* rw,
+                                  const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                                  int32_t* ids, float* w, uint8_t* ws, hipStream_t st) {
+  constexpr int R = 2;
+  hipLaunchKernelGGL(k_route<B>, dim3(kE / 4), dim3(256), 0, st, x, rw, ws, ids, w);
+  if (route_only) return hipGetLastError();
+  const dim3 g2(kI / (4 * R), B * kK + 1);
+  if (fmt == FMT_NVFP4) {
+    hipLaunchKernelGGL((k_gateup<B, FMT_NVFP4, R>), g2, dim3(256), 0, st, x, routed, shared, ws);
+    hipLaunchKernelGGL((k_down<B, FMT_NVFP4>), dim3(kH / 4), dim3(256), 0, st, routed, shared,
+                       (const uint8_t*)ws, out);
+  } else {
+    hipLaunchKernelGGL((k_gateup<B, FMT_BF16, R>), g2, dim3(256), 0, st, x, routed, shared, ws);
+    hipLaunchKernelGGL((k_down<B, FMT_BF16>), dim3(kH / 4), dim3(256), 0, st, routed, shared,
+                       (const uint8_t*)ws, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(int B, int fmt, bool route_only, const uint16_t* x, const uint16_t* rw,
+                         const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                         int32_t* ids, float* w, uint8_t* ws, hipStream_t st) {
+  switch (B) {
+    case 1: return launch_decode_b<1>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
+    case 2: return launch_decode_b<2>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
+    case 3: return launch_decode_b<3>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
+    case 4: return launch_decode_b<4>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
+    case 5: return launch_decode_b<5>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
+    case 6: return launch_decode_b<6>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
+    case 7: return launch_decode_b<7>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
+    case 8: return launch_decode_b<8>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob, int rows,
+                          int cols, float* out, hipStream_t st) {
+  const int n = rows * (cols / 8);
+  hipLaunchKernelGGL(k_dequant, dim3((n + 255) / 256), dim3(256), 0, st, codes, scales, glob, rows,
+                     cols, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

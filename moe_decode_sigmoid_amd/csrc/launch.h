@@ -1,0 +1,25 @@
+// Host-side launchers of the gfx950 MoE layer kernels (internal to the library).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Decode path, B = 1..8.  route_only: only the router + selection kernel.
+hipError_t launch_decode(int B, int fmt, bool route_only, const uint16_t* x, const uint16_t* rw,
+                         const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                         int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
+
+// Parity probe: one NVFP4 tensor [rows][cols] decoded to fp32.
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob, int rows,
+                          int cols, float* out, hipStream_t st);
+
+// Prefill path, T >= 1 tokens.
+hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
+                          const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                          int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
+
+// Workspace bytes of the prefill path for T tokens (0 = not served).
+size_t prefill_ws_bytes(int T);
+
+}  // namespace moe

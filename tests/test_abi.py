@@ -1,0 +1,135 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import re
+
+import pytest
+
+import moe_decode_sigmoid_amd as moe
+from tests.conftest import ROOT
+
+HEADER = ROOT / "include" / "moe_decode.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["moe_decode_route", "moe_decode_forward", "moe_prefill_forward",
+              "moe_nvfp4_dequant", "moe_workspace_bytes", "moe_status_string",
+              "moe_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+
+
+def test_status_strings_and_version():
+    assert moe.abi_version() == 1
+    assert moe.status_string(moe.MOE_OK) == "MOE_OK"
+    assert moe.status_string(moe.MOE_ERR_UNSUPPORTED) == "MOE_ERR_UNSUPPORTED"
+    assert moe.status_string(-99) == "MOE_ERR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    for B in range(1, 9):
+        assert moe.moe_workspace_bytes(B) > 0
+    assert moe.moe_workspace_bytes(9) == 0
+    assert moe.moe_workspace_bytes(0) == 0
+    S = moe.shape(moe.MOE_W_NVFP4, hidden=4096)
+    assert moe.lib().moe_workspace_bytes(ctypes.byref(S), 1, 0) == 0
+
+
+# Fake, never-dereferenced device addresses: every call below must be refused
+# by the argument checks, which run before any HIP call.
+A = 0x7F0000000000          # 256-byte aligned
+WS_BIG = 1 << 30
+
+
+class _FakeExperts:
+    def __init__(self, base, fmt="nvfp4"):
+        self.w13 = base
+        self.w2 = base + 0x100000
+        if fmt == "nvfp4":
+            self.w13_scale = base + 0x200000
+            self.w2_scale = base + 0x300000
+            self.glob = base + 0x400000
+
+
+def _forward(S=None, x=A, B=1, router=A + 0x1000000, routed=None, shared=None, out=A + 0x2000000,
+             ids=None, w=None, ws=A + 0x3000000, ws_bytes=WS_BIG, prefill=False):
+    S = S or moe.shape()
+    R = moe.experts_struct(routed or _FakeExperts(A + 0x4000000))
+    Sh = moe.experts_struct(shared or _FakeExperts(A + 0x5000000))
+    fn = moe.lib().moe_prefill_forward if prefill else moe.lib().moe_decode_forward
+    return fn(ctypes.byref(S), x, B, router, ctypes.byref(R), ctypes.byref(Sh), out, ids, w, ws,
+              ws_bytes, 0)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_forward_argument_errors(prefill):
+    E = moe
+    if prefill and moe.moe_workspace_bytes(8192, prefill=True) == 0:
+        pytest.skip("prefill path not built into this library")
+    assert _forward(x=None, prefill=prefill) == E.MOE_ERR_INVALID_ARG
+    assert _forward(router=None, prefill=prefill) == E.MOE_ERR_INVALID_ARG
+    assert _forward(out=None, prefill=prefill) == E.MOE_ERR_INVALID_ARG
+    assert _forward(B=0, prefill=prefill) == E.MOE_ERR_INVALID_ARG
+    assert _forward(x=A + 8, prefill=prefill) == E.MOE_ERR_MISALIGNED
+    assert _forward(out=A + 0x2000004, prefill=prefill) == E.MOE_ERR_MISALIGNED
+    assert _forward(ws=A + 0x3000010, prefill=prefill) == E.MOE_ERR_MISALIGNED
+    assert _forward(ws=None, prefill=prefill) == E.MOE_ERR_WORKSPACE
+    assert _forward(ws_bytes=1024, prefill=prefill) == E.MOE_ERR_WORKSPACE
+    assert _forward(out=A, prefill=prefill) == E.MOE_ERR_INVALID_ARG            # out aliases x
+    assert _forward(out=A + 0x3000000 + 4096, prefill=prefill) == E.MOE_ERR_INVALID_ARG  # in ws
+    bad = _FakeExperts(A + 0x4000000)
+    bad.w2_scale = None
+    assert _forward(routed=bad, prefill=prefill) == E.MOE_ERR_INVALID_ARG
+    bf = _FakeExperts(A + 0x4000000)                     # BF16 sets carry no scales
+    assert _forward(S=moe.shape(moe.MOE_W_BF16), routed=bf, prefill=prefill) == E.MOE_ERR_INVALID_ARG
+    assert _forward(ids=A + 2, prefill=prefill) == E.MOE_ERR_MISALIGNED
+    for kw in [dict(hidden=4096), dict(inter=1024), dict(n_experts=384), dict(top_k=8),
+               dict(n_shared=2)]:
+        assert _forward(S=moe.shape(**kw), prefill=prefill) == E.MOE_ERR_UNSUPPORTED
+    assert _forward(S=moe.shape(7), prefill=prefill) == E.MOE_ERR_UNSUPPORTED
+
+
+def test_decode_batch_limit_is_unsupported_not_invalid():
+    assert _forward(B=9) == moe.MOE_ERR_UNSUPPORTED
+    assert _forward(B=64) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_route_argument_errors():
+    L = moe.lib()
+    S = moe.shape()
+    call = lambda **k: L.moe_decode_route(  # noqa: E731
+        ctypes.byref(k.get("S", S)), k.get("x", A), k.get("B", 1), k.get("r", A + 0x1000000),
+        k.get("ids", A + 0x2000000), k.get("w", A + 0x2100000), k.get("ws", A + 0x3000000),
+        k.get("wsb", WS_BIG), 0)
+    assert call(B=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(B=9) == moe.MOE_ERR_UNSUPPORTED
+    assert call(ids=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(w=A + 0x2100001) == moe.MOE_ERR_MISALIGNED
+    assert call(wsb=64) == moe.MOE_ERR_WORKSPACE
+    assert call(x=A + 4) == moe.MOE_ERR_MISALIGNED
+
+
+def test_dequant_argument_errors():
+    L = moe.lib()
+    X = moe.experts_struct(_FakeExperts(A))
+    S = moe.shape()
+    assert L.moe_nvfp4_dequant(ctypes.byref(S), ctypes.byref(X), 0, 3, A + 0x1000000, 0) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_nvfp4_dequant(ctypes.byref(S), ctypes.byref(X), -1, 0, A + 0x1000000, 0) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_nvfp4_dequant(ctypes.byref(S), ctypes.byref(X), 0, 0, None, 0) == \
+        moe.MOE_ERR_INVALID_ARG
+    Sb = moe.shape(moe.MOE_W_BF16)
+    assert L.moe_nvfp4_dequant(ctypes.byref(Sb), ctypes.byref(X), 0, 0, A + 0x1000000, 0) == \
+        moe.MOE_ERR_UNSUPPORTED
