@@ -1,0 +1,202 @@
+"""Benchmark of the MI355X MoE decode layer: MoE-layer decode us/layer and
+achieved HBM GB/s, W4A16 (NVFP4 weights, bf16 activations), batch 1 and 8.
+
+Workload: a stack of 47 independent Flint-shaped MoE layers (hidden 2048,
+256 routed experts + 1 shared, sigmoid top-6, expert intermediate 512),
+distinct seeded NVFP4 weights per layer (21.4 GB resident in HBM), run back
+to back at batch 1 from one HIP graph.  One step = one pass over the 47
+layers.  A pass touches 631 MB, more than the 256 MiB last-level cache, so
+the weights stream from HBM every step.  The same stack at batch 8 is timed
+too and reported alongside.
+
+value = algorithmic bytes per pass / time per pass, in GB/s: the selected
+experts' packed weights (codes + block scales + tensor scales), the shared
+expert, the router, x and y; the untouched experts are not counted.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+H, I, E, K = 2048, 512, 256, 6
+NVFP4_EXPERT_BYTES = 3 * (H * I // 2 + H * I // 16 + 4)        # 1,769,484
+BF16_EXPERT_BYTES = 3 * H * I * 2                               # 6,291,456
+ROUTER_BYTES = E * H * 2                                        # 1,048,576
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def layer_bytes(n_experts_read: int, B: int, fmt: str) -> int:
+    per = NVFP4_EXPERT_BYTES if fmt == "nvfp4" else BF16_EXPERT_BYTES
+    return n_experts_read * per + ROUTER_BYTES + 2 * B * H * 2
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=47)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "bf16"])
+    ap.add_argument("--no-batch8", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate host time spent on the oracle baseline (0 = skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this MoE decode layer runs on one GPU (tensor/expert sharding is "
+              f"described in DESIGN.md but not built); --gpus {max(args.gpus, world)} is not "
+              f"supported", file=sys.stderr)
+        return 2
+
+    import torch
+    import moe_decode_sigmoid_amd as moe
+    import testgen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    fmt = args.fmt
+    L = args.layers
+
+    # ---------------------------------------------------------------- weights
+    t0 = time.time()
+    layers = []
+    host0 = None
+    for l in range(L):
+        hl = testgen.make_layer(args.seed, l, fmt)
+        layers.append(moe.DeviceLayer.from_host(hl, dev))
+        if l == 0:
+            host0 = hl
+        del hl
+        if l % 8 == 7 or l == L - 1:
+            log(f"layer {l + 1}/{L} generated and resident ({time.time() - t0:.1f} s)")
+    def nbytes(t):
+        return 0 if t is None else t.numel() * t.element_size()
+    resident = sum(nbytes(d.router) + sum(nbytes(getattr(s, f)) for s in (d.routed, d.shared)
+                                          for f in ("w13", "w2", "w13_scale", "w2_scale", "glob"))
+                   for d in layers)
+
+    def run_batch(B: int) -> dict:
+        x = testgen.make_x(args.seed, B)
+        xd = moe.device.to_device_bf16(x, dev)
+        outs = torch.empty((L, B, H), dtype=torch.bfloat16, device=dev)
+        ids = torch.empty((L, B, K), dtype=torch.int32, device=dev)
+        ws = moe.alloc_workspace(moe.moe_workspace_bytes(B, fmt=fmt), dev)
+        S = moe.shape(moe._fmt(fmt))
+
+        def one_pass(with_ids: bool):
+            for l, d in enumerate(layers):
+                moe.moe_decode_forward(xd, d.router, d.routed, d.shared, outs[l], ws,
+                                       ids[l] if with_ids else None, None, S=S, B=B)
+
+        one_pass(True)                                   # eager, records the routing
+        torch.cuda.synchronize()
+        ids_h = ids.cpu().numpy()
+        n_read = [len(set(ids_h[l].ravel().tolist())) + 1 for l in range(L)]
+        pass_bytes = sum(layer_bytes(n, B, fmt) for n in n_read)
+
+        # per-call timing of the eager layer call (events on the launch stream)
+        st = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+        for l, d in enumerate(layers):
+            ev[2 * l].record(st)
+            moe.moe_decode_forward(xd, d.router, d.routed, d.shared, outs[l], ws, None, None,
+                                   S=S, B=B)
+            ev[2 * l + 1].record(st)
+        torch.cuda.synchronize()
+        call_ms = [ev[2 * l].elapsed_time(ev[2 * l + 1]) for l in range(L)]
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_pass(False)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        # graph output must equal the eager output
+        ref = outs.clone()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(ref, outs))
+        return dict(B=B, ms_per_pass=ms, us_per_layer=ms * 1000 / L, pass_bytes=pass_bytes,
+                    gbps=pass_bytes / (ms * 1e-3) / 1e9, experts_read_mean=float(np.mean(n_read)),
+                    call_us_mean=float(np.mean(call_ms)) * 1000,
+                    call_gbps=float(np.mean([layer_bytes(n, B, fmt) / (c * 1e-3) / 1e9
+                                             for n, c in zip(n_read, call_ms)])),
+                    graph_matches_eager=same)
+
+    r1 = run_batch(1)
+    log(f"B=1: {r1['us_per_layer']:.2f} us/layer, {r1['gbps']:.0f} GB/s")
+    r8 = None
+    if not args.no_batch8:
+        r8 = run_batch(8)
+        log(f"B=8: {r8['us_per_layer']:.2f} us/layer, {r8['gbps']:.0f} GB/s")
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        x1 = testgen.make_x(args.seed, 1)
+        nthreads = oracle.num_threads()
+        reps, t_start = 0, time.time()
+        while True:
+            oracle.forward_layer(x1, host0)
+            reps += 1
+            if time.time() - t_start >= args.cpu_seconds:
+                break
+        per_layer = (time.time() - t_start) / reps
+        n_read0 = 7
+        cpu = {"value": layer_bytes(n_read0, 1, fmt) / per_layer / 1e9, "unit": "GB/s",
+               "cores": nthreads, "kind": "oracle",
+               "us_per_layer": per_layer * 1e6,
+               "sample": f"fp64 C oracle, batch-1 forward of layer 0 (from packed weights, "
+                         f"incl. its dequant of the 7 experts read), {reps} reps in "
+                         f"{time.time() - t_start:.1f} s on {nthreads} OpenMP threads"}
+        log(f"oracle: {per_layer * 1e6:.0f} us/layer on {nthreads} threads")
+
+    roof = {"bound": "hbm", "kernel": "moe_decode_forward (route + gate/up + down launches)",
+            "achieved": r1["call_gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": r1["call_gbps"] / PEAK_HBM_GBS, "traffic": None,
+            "per_launch_bytes": r1["pass_bytes"] / L, "launch_us": r1["call_us_mean"]}
+    res = {
+        "metric": "MoE-layer decode µs/layer + achieved HBM GB/s (W4A16, batch 1 and 8)",
+        "value": round(r1["gbps"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r1["ms_per_pass"], 4),
+        "us_per_layer": round(r1["us_per_layer"], 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4-w/bf16-a, fp32 accumulate" if fmt == "nvfp4" else "bf16, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights packed to NVFP4)",
+        "config": {"workload": f"{L}-layer Flint-shaped MoE decode stack, batch 1, {fmt}, "
+                               f"one HIP graph per pass, weights cold (pass > last-level cache)",
+                   "hidden": H, "inter": I, "experts": E, "top_k": K, "shared": 1,
+                   "layers": L, "batch": 1, "weight_format": fmt,
+                   "resident_weight_bytes": int(resident)},
+        "batch1": r1, "batch8": r8, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

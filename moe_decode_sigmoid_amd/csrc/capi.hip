@@ -2,6 +2,7 @@
 // launches on the caller's stream.  Declarations and the contract of each
 // entry point are in include/moe_decode.h.
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/moe_decode.h"
@@ -79,6 +80,14 @@ moe_status check_forward(const moe_shape* shape, const void* x, int32_t T, const
   return MOE_OK;
 }
 
+// MOE_DECODE_SPLIT=1 selects the three-launch decode path even where the
+// fused kernel can run (both compute the same layer; read on every call so a
+// test can compare the two in one process).
+bool split_path_forced() {
+  const char* v = getenv("MOE_DECODE_SPLIT");
+  return v && v[0] == '1';
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,10 +140,11 @@ moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
   moe_status st = check_forward(shape, x, B, router_w, routed, shared, out, ids_out, w_out, ws,
                                 ws_bytes, moe::kDecodeWsBytes);
   if (st != MOE_OK) return st;
-  hipError_t e = moe::launch_decode(B, shape->wfmt, false, static_cast<const uint16_t*>(x),
-                                    static_cast<const uint16_t*>(router_w), to_dev(routed),
-                                    to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
-                                    static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+  const bool fused = moe::fused_supported() && !split_path_forced();
+  hipError_t e = (fused ? moe::launch_decode_fused : moe::launch_decode_split)(
+      B, shape->wfmt, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w),
+      to_dev(routed), to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+      static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

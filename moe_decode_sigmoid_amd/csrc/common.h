@@ -35,9 +35,12 @@ enum { FMT_NVFP4 = 0, FMT_BF16 = 1 };
 // ---------------------------------------------------------------- workspace
 // Decode workspace, all offsets in bytes from a 256-byte-aligned base.
 struct DecodeCtl {
-  unsigned ticket;                       // route kernel arrival counter (self-resetting)
-  int n_active;                          // routed experts touched + 1 (shared last)
-  int pad0[62];
+  unsigned ticket;                       // 0: route kernel arrival counter (self-resetting)
+  int n_active;                          // 4: dispatch entries of the split path (shared last)
+  unsigned err;                          // 8: nonzero when a device-side wait timed out
+  unsigned pad0;                         // 12
+  unsigned long long arrive[2];          // 16: grid barrier counters of the fused kernel
+  int pad1[56];
   int active_expert[64];                 // expert id; kE marks the shared expert
   unsigned active_mask[64];              // bit t set when token t uses the entry
   float wtab[64][kMaxB];                 // routing weight of token t for the entry
@@ -47,7 +50,15 @@ struct DecodeCtl {
 constexpr size_t kCtlBytes = (sizeof(DecodeCtl) + 255) / 256 * 256;
 constexpr size_t kLogitsOff = kCtlBytes;                          // f32 [kMaxB][kE]
 constexpr size_t kHOff = kLogitsOff + sizeof(float) * kMaxB * kE; // f32 [kMaxActive][kMaxB][kI]
-constexpr size_t kDecodeWsBytes = kHOff + sizeof(float) * kMaxActive * kMaxB * kI;
+constexpr size_t kTraceOff = kHOff + sizeof(float) * kMaxActive * kMaxB * kI;  // u64 [256][8]
+// Fused kernel: tagged 8-byte logit slots {fp32 value, call epoch}; then
+// u32 words on 128-byte lines: per-workgroup epoch counters (and spare
+// per-workgroup words), then 64 h-ready counters.
+constexpr size_t kSlotLogitOff = kTraceOff + 256 * 8 * 8;                          // [kMaxB][kE]
+constexpr size_t kFlagOff = kSlotLogitOff + 8 * kMaxB * kE;
+constexpr size_t kFlagStride = 128;
+constexpr size_t kDecodeWsBytes = kFlagOff + (4 * 256 + 64) * kFlagStride;
+constexpr int kShSlot = kMaxActive - 1;  // h entry of the shared expert in the fused kernel
 
 // ---------------------------------------------------------------- numerics
 // Two E2M1 codes (one byte of `w`, selected by SEL) to two fp32 values; the
@@ -90,22 +101,93 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Device-coherent accesses for data one workgroup hands to others inside a
+// kernel: relaxed atomics at agent scope are issued with device-scope
+// coherence (they bypass the per-XCD L2 copies), so no cache write-back or
+// invalidation is needed; ordering comes from waiting for the stores before
+// counting in at a barrier.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Two consecutive floats (8-byte aligned) in one coherent load.
+__device__ __forceinline__ f32x2 load_coherent2(const float* p) {
+  const unsigned long long v = __hip_atomic_load(
+      reinterpret_cast<unsigned long long*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(f32x2, v);
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-// Butterfly sum over the 64 lanes of a wave; every lane ends with the sum.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// Cross-lane moves through DPP (no LDS round trip).  Controls (GFX9 DPP):
+// quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E; row_ror:4 = 0x124, row_ror:8 = 0x128.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, false));
+}
+
+// Sum over each aligned group of 16 lanes (a DPP row); every lane of the
+// group ends with the group's sum.
+__device__ __forceinline__ float group16_sum(float v) {
+  v += dpp_f32<0x128>(v);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0xB1>(v);
   return v;
 }
 
-// Sum over aligned groups of 16 lanes.
-__device__ __forceinline__ float group16_sum(float v) {
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes of a wave, returned uniformly (same value in every lane).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group16_sum(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+// Maximum over the 64 lanes of a wave, returned uniformly.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0x128>(v));
+  v = fmaxf(v, dpp_f32<0x124>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+               fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+// Top-k of 256 scores held 4 per lane (expert e = lane + 64 q in v[q]) under
+// the total order (value descending, index ascending).  Each round takes the
+// wave maximum, then the lowest index holding it (q-major ballots: indices of
+// v[0] are all below those of v[1], ...).  Every lane returns the same ids and
+// values; the chosen entries of v are set to -inf.
+template <int K>
+__device__ __forceinline__ void wave_topk256(float (&v)[4], int lane, int (&ids)[K],
+                                             float (&vals)[K]) {
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  for (int j = 0; j < K; ++j) {
+    const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    int idx = -1;
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+      const uint64_t bal = __ballot(v[q] == m);
+      if (bal) idx = 64 * q + __builtin_ctzll(bal);
+    }
+    if (idx < 0) idx = j;   // only when every value is NaN (outside the contract): stay in range
+    ids[j] = idx;
+    vals[j] = m;
+    if ((idx & 63) == lane) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((idx >> 6) == q) v[q] = -INFINITY;
+    }
+  }
 }
 
 }  // namespace moe

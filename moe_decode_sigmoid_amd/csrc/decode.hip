@@ -88,30 +88,10 @@ __device__ void route_select(DecodeCtl* __restrict__ ctl, const float* __restric
   for (int t = wave; t < B; t += 4) {
     float v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = logits[t * kE + lane + 64 * q];
+    for (int q = 0; q < 4; ++q) v[q] = load_coherent(logits + t * kE + lane + 64 * q);
     float sel_l[kK];
     int sel_i[kK];
-#pragma unroll
-    for (int j = 0; j < kK; ++j) {
-      float bv = v[0];
-      int bi = lane;
-#pragma unroll
-      for (int q = 1; q < 4; ++q)
-        if (v[q] > bv) { bv = v[q]; bi = lane + 64 * q; }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float ov = __shfl_xor(bv, o, kWave);
-        int oi = __shfl_xor(bi, o, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      sel_l[j] = bv;
-      sel_i[j] = bi;
-      if ((bi & 63) == lane) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if ((bi >> 6) == q) v[q] = -INFINITY;
-      }
-    }
+    wave_topk256<kK>(v, lane, sel_i, sel_l);
     if (lane == 0) {
       float s[kK], sum = 0.0f;
 #pragma unroll
@@ -205,19 +185,23 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x,
     load_x_chunk(x, t, lane, xw);
     float acc = dot_bf16_chunk(wv, xw);
     acc = wave_sum(acc);
-    if (lane == 0) logits[t * kE + e] = acc;
+    if (lane == 0) store_coherent(logits + t * kE + e, acc);
   }
 
+  // Logits travel through device-coherent stores and loads; the workgroup
+  // fence waits for this thread's stores before the ticket is taken.
   __shared__ int s_last;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);      // this thread's coherent stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();   // publish this workgroup's logits device-wide
-    const unsigned prev = atomicInc(&ctl->ticket, gridDim.x - 1);   // wraps to 0 on the last
-    s_last = (prev == gridDim.x - 1);
+    const unsigned prev = __builtin_amdgcn_atomic_inc32(&ctl->ticket, gridDim.x - 1u,
+                                                        __ATOMIC_RELAXED, "agent");
+    s_last = (prev == gridDim.x - 1);   // the counter wraps back to 0 on the last arrival
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();     // see every other workgroup's logits
   route_select<B>(ctl, logits, ids_out, w_out);
 }
 
@@ -457,6 +441,12 @@ hipError_t launch_decode(int B, int fmt, bool route_only, const uint16_t* x, con
     case 8: return launch_decode_b<8>(fmt, route_only, x, rw, routed, shared, out, ids, w, ws, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode_split(int B, int fmt, const uint16_t* x, const uint16_t* rw,
+                               const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                               int32_t* ids, float* w, uint8_t* ws, hipStream_t st) {
+  return launch_decode(B, fmt, false, x, rw, routed, shared, out, ids, w, ws, st);
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob, int rows,

@@ -10,6 +10,17 @@ hipError_t launch_decode(int B, int fmt, bool route_only, const uint16_t* x, con
                          const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
                          int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
 
+// The same path as three launches (route, gate/up, down).
+hipError_t launch_decode_split(int B, int fmt, const uint16_t* x, const uint16_t* rw,
+                               const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                               int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
+
+// Fused single-launch decode path, B = 1..8 (needs 256 co-resident workgroups).
+bool fused_supported();
+hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t* rw,
+                               const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                               int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
+
 // Parity probe: one NVFP4 tensor [rows][cols] decoded to fp32.
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob, int rows,
                           int cols, float* out, hipStream_t st);
