@@ -31,6 +31,13 @@ NVFP4_EXPERT_BYTES = 3 * (H * I // 2 + H * I // 16 + 4)        # 1,769,484
 BF16_EXPERT_BYTES = 3 * H * I * 2                               # 6,291,456
 ROUTER_BYTES = E * H * 2                                        # 1,048,576
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PREFILL_T = 8192
+
+
+def prefill_flop(T: int) -> float:
+    """Algorithmic prefill FLOP: 7 experts per token x (gate, up, down) + router."""
+    return 2.0 * T * 7 * 3 * I * H + 2.0 * T * E * H
 
 
 def log(msg: str) -> None:
@@ -53,6 +60,9 @@ def main() -> int:
     ap.add_argument("--no-batch8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate host time spent on the oracle baseline (0 = skip)")
+    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill"],
+                    help="decode = the 47-layer stack only; prefill = the 8192-token layer only")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -70,7 +80,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     dev = "cuda:0"
     fmt = args.fmt
-    L = args.layers
+    L = 1 if args.workload == "prefill" else args.layers
 
     # ---------------------------------------------------------------- weights
     t0 = time.time()
@@ -146,12 +156,41 @@ def main() -> int:
                                              for n, c in zip(n_read, call_ms)])),
                     graph_matches_eager=same)
 
-    r1 = run_batch(1)
-    log(f"B=1: {r1['us_per_layer']:.2f} us/layer, {r1['gbps']:.0f} GB/s")
-    r8 = None
-    if not args.no_batch8:
-        r8 = run_batch(8)
-        log(f"B=8: {r8['us_per_layer']:.2f} us/layer, {r8['gbps']:.0f} GB/s")
+    def run_prefill() -> dict:
+        T = PREFILL_T
+        d = layers[0]
+        x = moe.device.to_device_bf16(testgen.make_x(args.seed + 1000, T), dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ws = moe.alloc_workspace(moe.moe_workspace_bytes(T, prefill=True, fmt=fmt), dev)
+        S = moe.shape(moe._fmt(fmt))
+        for _ in range(2):
+            moe.moe_prefill_forward(x, d.router, d.routed, d.shared, out, ws, S=S, T=T)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.prefill_steps):
+            moe.moe_prefill_forward(x, d.router, d.routed, d.shared, out, ws, S=S, T=T)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.prefill_steps
+        tf = prefill_flop(T) / (ms * 1e-3) / 1e12
+        return dict(tokens=T, ms_per_layer=ms, tflops=tf, mfma_util=tf / PEAK_BF16_TFLOPS,
+                    flop=prefill_flop(T))
+
+    r1 = r8 = rp = None
+    if args.workload in ("all", "decode"):
+        r1 = run_batch(1)
+        log(f"B=1: {r1['us_per_layer']:.2f} us/layer, {r1['gbps']:.0f} GB/s")
+        if not args.no_batch8:
+            r8 = run_batch(8)
+            log(f"B=8: {r8['us_per_layer']:.2f} us/layer, {r8['gbps']:.0f} GB/s")
+    if args.workload in ("all", "prefill"):
+        rp = run_prefill()
+        log(f"prefill {rp['tokens']} tokens: {rp['ms_per_layer']:.3f} ms/layer, "
+            f"{rp['tflops']:.0f} TFLOP/s ({100 * rp['mfma_util']:.1f}% of bf16 peak)")
+    if r1 is None:
+        print(json.dumps({"prefill": rp}), flush=True)
+        return 0
 
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
@@ -175,7 +214,7 @@ def main() -> int:
                          f"{time.time() - t_start:.1f} s on {nthreads} OpenMP threads"}
         log(f"oracle: {per_layer * 1e6:.0f} us/layer on {nthreads} threads")
 
-    roof = {"bound": "hbm", "kernel": "moe_decode_forward (route + gate/up + down launches)",
+    roof = {"bound": "hbm", "kernel": "k_decode_fused<1, nvfp4> (one launch per layer)",
             "achieved": r1["call_gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": r1["call_gbps"] / PEAK_HBM_GBS, "traffic": None,
             "per_launch_bytes": r1["pass_bytes"] / L, "launch_us": r1["call_us_mean"]}
@@ -192,7 +231,7 @@ def main() -> int:
                    "hidden": H, "inter": I, "experts": E, "top_k": K, "shared": 1,
                    "layers": L, "batch": 1, "weight_format": fmt,
                    "resident_weight_bytes": int(resident)},
-        "batch1": r1, "batch8": r8, "roofline": roof, "cpu_baseline": cpu,
+        "batch1": r1, "batch8": r8, "prefill": rp, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -1,0 +1,127 @@
+"""GPU parity of the prefill path (grouped bf16 MFMA GEMMs) against the fp64
+oracle, through the C ABI.  Same synthetic Flint-shaped layer as the decode
+tests; token counts span several router tiles and work items with ragged
+tails, up to the 8,192-token prefill the pages measure ("Day-0 Support for
+Flint on vLLM", Optimization section, Fig. 2 caption)."""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import testgen
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+moe = pytest.importorskip("moe_decode_sigmoid_amd")
+
+
+@functools.lru_cache(maxsize=None)
+def host_layer(seed: int, fmt: str = "nvfp4"):
+    return testgen.make_layer(seed, 0, fmt)
+
+
+_DEV = {}
+
+
+def dev_layer(seed: int, fmt: str = "nvfp4"):
+    key = (seed, fmt)
+    if key not in _DEV:
+        if len(_DEV) >= 2:
+            _DEV.pop(next(iter(_DEV)))
+        _DEV[key] = moe.DeviceLayer.from_host(host_layer(seed, fmt))
+    return _DEV[key]
+
+
+def run_prefill(seed, x, fmt="nvfp4"):
+    L = dev_layer(seed, fmt)
+    T = x.shape[0]
+    xd = moe.device.to_device_bf16(x)
+    out = torch.empty((T, 2048), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, 6), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 6), dtype=torch.float32, device="cuda")
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(T, prefill=True, fmt=fmt))
+    moe.moe_prefill_forward(xd, L.router, L.routed, L.shared, out, ws, ids, w, fmt=fmt)
+    torch.cuda.synchronize()
+    return parity.bf16_out_to_f64(out), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def check_tokens(seed, x, y, ids, w, sample, fmt="nvfp4"):
+    HL = host_layer(seed, fmt)
+    xs = x[sample]
+    y_or, ids_or, w_or, gap = oracle.forward_layer(xs, HL)
+    log = []
+    y_ref = parity.resolve_near_ties(xs, HL, ids[sample], y_or, ids_or, w_or, gap, log)
+    parity.check_weights(ids[sample], w[sample], ids_or, w_or, gap)
+    stats = parity.check_output(y[sample], y_ref, f"prefill seed {seed} T {x.shape[0]}")
+    if log:
+        print(f"near-ties: {log}")
+    return stats
+
+
+@pytest.mark.parametrize("T", [1, 33, 300])
+def test_prefill_small_matches_oracle(T):
+    x = testgen.make_x(7, T)
+    y, ids, w = run_prefill(1, x)
+    check_tokens(1, x, y, ids, w, np.arange(T))
+
+
+def test_prefill_bf16_weights():
+    x = testgen.make_x(8, 160)
+    y, ids, w = run_prefill(2, x, "bf16")
+    check_tokens(2, x, y, ids, w, np.arange(160), "bf16")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_prefill_8192_tokens_sampled(seed):
+    """The full 8,192-token layer; 96 sampled tokens (spread over every router
+    tile position) are checked against the oracle one by one, and every token
+    satisfies the routing invariants."""
+    T = 8192
+    x = testgen.make_x(100 + seed, T)
+    y, ids, w = run_prefill(seed, x)
+    assert np.all((ids >= 0) & (ids < 256))
+    assert all(len(set(r)) == 6 for r in ids.tolist())
+    np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-5)
+    assert np.isfinite(y).all()
+    rng = np.random.default_rng(seed)
+    sample = np.sort(np.concatenate([rng.choice(T, 90, replace=False), [0, 31, 32, 4095, 8190, 8191]]))
+    check_tokens(seed, x, y, ids, w, np.unique(sample))
+
+
+def test_prefill_is_token_permutation_equivariant():
+    """Shuffled tokens give the shuffled outputs, bit for bit: grouping and
+    scatter depend on no token's position."""
+    T = 1000
+    x = testgen.make_x(9, T)
+    perm = np.random.default_rng(3).permutation(T)
+    y, ids, _ = run_prefill(1, x)
+    y2, ids2, _ = run_prefill(1, x[perm].copy())
+    np.testing.assert_array_equal(ids2, ids[perm])
+    np.testing.assert_array_equal(y2, y[perm])
+
+
+def test_prefill_agrees_with_decode_path():
+    x = testgen.make_x(11, 8)
+    y, ids, _ = run_prefill(1, x)
+    L = dev_layer(1)
+    xd = moe.device.to_device_bf16(x)
+    out = torch.empty((8, 2048), dtype=torch.bfloat16, device="cuda")
+    idd = torch.empty((8, 6), dtype=torch.int32, device="cuda")
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(8))
+    moe.moe_decode_forward(xd, L.router, L.routed, L.shared, out, ws, idd)
+    torch.cuda.synchronize()
+    yd = parity.bf16_out_to_f64(out)
+    for t in range(8):
+        assert set(idd.cpu().numpy()[t].tolist()) == set(ids[t].tolist())
+    err = np.abs(y - yd).max()
+    assert err <= 2e-2, err
+
+
+def test_prefill_repeat_is_bitwise_stable():
+    x = testgen.make_x(12, 500)
+    y1, _, _ = run_prefill(1, x)
+    y2, _, _ = run_prefill(1, x)
+    np.testing.assert_array_equal(y1, y2)
