@@ -44,6 +44,22 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def measured_traffic() -> float | None:
+    """HBM bytes per launch of the fused batch-1 decode kernel from the
+    committed rocprofv3 counter summary, if that kernel's sources are
+    unchanged since the counters were taken (else None)."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "k_decode_fused_b1_traffic.json")))
+        src = b"".join(open(os.path.join(ROOT, "moe_decode_sigmoid_amd", "csrc", f), "rb").read()
+                       for f in ("decode_fused.hip", "common.h"))
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def layer_bytes(n_experts_read: int, B: int, fmt: str) -> int:
     per = NVFP4_EXPERT_BYTES if fmt == "nvfp4" else BF16_EXPERT_BYTES
     return n_experts_read * per + ROUTER_BYTES + 2 * B * H * 2
@@ -60,8 +76,9 @@ def main() -> int:
     ap.add_argument("--no-batch8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate host time spent on the oracle baseline (0 = skip)")
-    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill"],
-                    help="decode = the 47-layer stack only; prefill = the 8192-token layer only")
+    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill", "copy"],
+                    help="decode = the 47-layer stack only; prefill = the 8192-token layer only; "
+                         "copy = a plain 1 GiB device copy (reference for the traffic counters)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args()
 
@@ -79,6 +96,15 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = "cuda:0"
+    if args.workload == "copy":
+        nbytes = 1 << 30
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "copies": 3}))
+        return 0
     fmt = args.fmt
     L = 1 if args.workload == "prefill" else args.layers
 
@@ -216,7 +242,8 @@ def main() -> int:
 
     roof = {"bound": "hbm", "kernel": "k_decode_fused<1, nvfp4> (one launch per layer)",
             "achieved": r1["call_gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": r1["call_gbps"] / PEAK_HBM_GBS, "traffic": None,
+            "frac": r1["call_gbps"] / PEAK_HBM_GBS,
+            "traffic": measured_traffic() if fmt == "nvfp4" else None,
             "per_launch_bytes": r1["pass_bytes"] / L, "launch_us": r1["call_us_mean"]}
     res = {
         "metric": "MoE-layer decode µs/layer + achieved HBM GB/s (W4A16, batch 1 and 8)",
