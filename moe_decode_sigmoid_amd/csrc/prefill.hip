@@ -15,13 +15,20 @@
 //      of 128-row GEMM work items.
 //   P3 positions    each (token, slot) gets its row in the expert-grouped
 //      order; rows T*6 .. T*7-1 are the shared expert's (token order).
-//   P4 GEMM 1       per work item and 64-column slice: [gate; up] rows of the
+//   P4 GEMM 1       per work item and 128-column slice: [gate; up] rows of the
 //      expert, NVFP4 decoded to bf16 in LDS, times the gathered x rows;
 //      SiLU(g) * u in registers -> h (bf16) [T*7][512].
 //   P5 GEMM 2       h rows . D_e^T, times the routing weight -> fp16 partial
 //      rows [T*7][2048].
 //   P6 combine      y[t] = sum over the token's six routed rows (ascending
 //      expert id) + its shared row, fp32, rounded once to bf16.
+//
+// GEMM tiles are 128 x 256 with four waves of 128 x 64 each (8 MFMA blocks
+// per wave, so LDS serves ~380 bytes per MFMA); K advances 64 per stage with
+// two LDS buffers, and the global loads of the next kRing stages are held in
+// registers so the HBM / gather latency of one stage hides behind kRing
+// stages of MFMA work.  Work items are mapped so that the column slices of
+// one item run on one XCD (workgroup b lands on XCD b % 8) and share its L2.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  Lane l supplies A[row l%32][k 8(l/32)..+7]
 // and B[k 8(l/32)..+7][col l%32]; result element i of lane l is
@@ -41,8 +48,10 @@ constexpr int kLdsPad = 8;               // bf16 elements of padding per LDS row
 constexpr int kLdsRow = kBK + kLdsPad;   // LDS row pitch (bf16 elements)
 constexpr int kPTile = 32;               // router tile (tokens)
 constexpr int kGBM = 128;                // grouped GEMM rows per work item
-constexpr int kGBN = 128;                // grouped GEMM B rows per tile
+constexpr int kGBN = 256;                // grouped GEMM B rows per tile
 constexpr int kPThreads = 256;
+constexpr int kSlices1 = kI / (kGBN / 2);  // gate/up column slices (128 h columns each)
+constexpr int kSlices2 = kH / kGBN;        // down column slices
 
 // ------------------------------------------------------------------ workspace
 struct PrefillLayout {
@@ -133,28 +142,61 @@ struct TileAcc {
 // 16 bf16 (one uint4 pair) of a bf16 row segment into LDS
 __device__ __forceinline__ void st_lds16(__bf16* dst, uint4 v) { *reinterpret_cast<uint4*>(dst) = v; }
 
-// 32 NVFP4 codes + their two block scales -> 32 exact bf16 values in LDS.
-// e2m1 (exact in fp32) * e4m3 (exact) is exact in fp32 and, having at most
-// six significant bits, in bf16 too.
-__device__ __forceinline__ void dequant32_to_lds(__bf16* dst, uint4 c, uint32_t sc) {
-  const float s0 = e4m3_to_f32<0>(sc), s1 = e4m3_to_f32<1>(sc);
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  uint32_t o[16];
+// 8 NVFP4 codes (one dword) times their block scale -> 8 exact bf16 values
+// (4 dwords).  e2m1 (exact in fp32) * e4m3 (exact) is exact in fp32 and,
+// having at most six significant bits, in bf16 too, so truncation is exact.
+__device__ __forceinline__ uint4 dequant8(uint32_t w, float s) {
+  const f32x2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w), p2 = fp4x2_to_f32<2>(w),
+              p3 = fp4x2_to_f32<3>(w);
+  auto pk = [&](f32x2 p) {
+    return (__builtin_bit_cast(uint32_t, p.x * s) >> 16) |
+           (__builtin_bit_cast(uint32_t, p.y * s) & 0xFFFF0000u);
+  };
+  return make_uint4(pk(p0), pk(p1), pk(p2), pk(p3));
+}
+
+// 64 NVFP4 codes of one row (two uint4) with their 4 block scales -> 64 bf16
+// in LDS (one 128-byte row segment).
+__device__ __forceinline__ void dequant64_to_lds(__bf16* dst, uint4 c0, uint4 c1, uint32_t sc) {
+  const float s0 = e4m3_to_f32<0>(sc), s1 = e4m3_to_f32<1>(sc), s2 = e4m3_to_f32<2>(sc),
+              s3 = e4m3_to_f32<3>(sc);
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  d[0] = dequant8(c0.x, s0);
+  d[1] = dequant8(c0.y, s0);
+  d[2] = dequant8(c0.z, s1);
+  d[3] = dequant8(c0.w, s1);
+  d[4] = dequant8(c1.x, s2);
+  d[5] = dequant8(c1.y, s2);
+  d[6] = dequant8(c1.z, s3);
+  d[7] = dequant8(c1.w, s3);
+}
+
+// K pipeline over NK stages: register ring of D stages in flight, two LDS
+// buffers.  gload(slot, kt) issues stage kt's global loads into a ring slot;
+// sstore(slot, buf) writes a slot to LDS buffer buf; mma(buf) consumes it.
+// Slot of stage s is s % D; the loop is unrolled by D so slots are static.
+template <int D, int NK, typename Slot, typename GL, typename SS, typename MM>
+__device__ __forceinline__ void kpipeline(Slot (&ring)[D], GL gload, SS sstore, MM mma) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const float s = d < 2 ? s0 : s1;
-    f32x2 p[4] = {fp4x2_to_f32<0>(w[d]), fp4x2_to_f32<1>(w[d]), fp4x2_to_f32<2>(w[d]),
-                  fp4x2_to_f32<3>(w[d])};
+  for (int q = 0; q < D; ++q)
+    if (q < NK) gload(ring[q], q);
+  sstore(ring[0], 0);
+  if (D < NK) gload(ring[0], D);
+  __syncthreads();
+  for (int kt0 = 0; kt0 < NK; kt0 += D) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = __builtin_bit_cast(uint32_t, p[q].x * s) >> 16;
-      const uint32_t hi = __builtin_bit_cast(uint32_t, p[q].y * s) & 0xFFFF0000u;
-      o[4 * d + q] = lo | hi;
+    for (int q = 0; q < D; ++q) {
+      const int kt = kt0 + q;
+      if (kt < NK) {
+        mma(kt & 1);
+        if (kt + 1 < NK) {
+          sstore(ring[(q + 1) % D], (kt + 1) & 1);
+          if (kt + 1 + D < NK) gload(ring[(q + 1) % D], kt + 1 + D);
+        }
+        __syncthreads();
+      }
     }
   }
-  uint4* d4 = reinterpret_cast<uint4*>(dst);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) d4[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
 }
 
 // ------------------------------------------------------------------ P1 router + top-6
@@ -170,39 +212,26 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_route(const uint16_t* __r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ __align__(16) __bf16 sA[2][kPTile * kLdsRow];
   __shared__ __align__(16) __bf16 sB[2][kE * kLdsRow];
-  // loaders: A 32 rows x 128 B -> one uint4 per thread; B 256 rows x 128 B -> 8 per thread
+  // A: 32 rows x 128 B -> one uint4 per thread; B: router row tid, 8 uint4
   const int ar = tid >> 3, aseg = tid & 7;
-  const int at = min(t0 + ar, T - 1);
-  const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)at * kH) + aseg;
-  uint4 av, bv[8];
-  auto gload = [&](int kt) {
-    av = ap[kt * 8];
+  const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + ar, T - 1) * kH) + aseg;
+  const uint4* bp = reinterpret_cast<const uint4*>(rw + (size_t)tid * kH);
+  struct Slot { uint4 a, b[8]; };
+  Slot ring[2];
+  auto gload = [&](Slot& sl, int kt) {
+    sl.a = ap[kt * 8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + kPThreads * i, row = idx >> 3, seg = idx & 7;
-      bv[i] = reinterpret_cast<const uint4*>(rw + (size_t)row * kH)[kt * 8 + seg];
-    }
+    for (int i = 0; i < 8; ++i) sl.b[i] = bp[kt * 8 + i];
   };
-  auto sstore = [&](int st) {
-    st_lds16(&sA[st][ar * kLdsRow + aseg * 8], av);
+  auto sstore = [&](const Slot& sl, int buf) {
+    st_lds16(&sA[buf][ar * kLdsRow + aseg * 8], sl.a);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + kPThreads * i, row = idx >> 3, seg = idx & 7;
-      st_lds16(&sB[st][row * kLdsRow + seg * 8], bv[i]);
-    }
+    for (int i = 0; i < 8; ++i) st_lds16(&sB[buf][tid * kLdsRow + i * 8], sl.b[i]);
   };
   Acc acc;
   acc.zero();
-  constexpr int NK = kH / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < NK; ++kt) {
-    if (kt + 1 < NK) gload(kt + 1);
-    acc.mma(sA[kt & 1], sB[kt & 1], wave, lane);
-    if (kt + 1 < NK) sstore((kt + 1) & 1);
-    __syncthreads();
-  }
+  kpipeline<2, kH / kBK>(ring, gload, sstore,
+                         [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
   // logits tile -> LDS (reuse sB as fp32 [32][256 + 4])
   float* sL = reinterpret_cast<float*>(&sB[0][0]);
   constexpr int LP = kE + 4;
@@ -252,39 +281,80 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_route(const uint16_t* __r
 }
 
 // ------------------------------------------------------------------ P2 scan
-// One workgroup: thread e owns expert e.  Stable order: tiles in order, and
-// inside a tile tokens in order (positions kernel).  Work items of kGBM rows
-// per expert, then the shared expert's.
-__global__ __launch_bounds__(kPThreads) void k_prefill_scan(int T, uint8_t* __restrict__ ws) {
+// One workgroup of 1024 threads: thread (q, e) sums quarter q of the router
+// tiles for expert e, then the quarters are chained in order.  Stable order:
+// tiles in order, and inside a tile tokens in order (positions kernel).
+// Work items of kGBM rows per expert, then the shared expert's.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void k_prefill_scan(int T, uint8_t* __restrict__ ws) {
   const PrefillLayout L = prefill_layout(T);
-  const int e = threadIdx.x;
+  const int e = threadIdx.x % kE, q = threadIdx.x / kE;   // q in 0..3
   const int* hist = wsp<int>(ws, L.hist);
   int* base = wsp<int>(ws, L.base);
-  int run = 0;
-  for (int tile = 0; tile < L.ntiles; ++tile) {
-    base[(size_t)tile * kE + e] = run;
-    run += hist[(size_t)tile * kE + e];
+  const int per = (L.ntiles + 3) / 4, lo = q * per, hi = min(L.ntiles, lo + per);
+  __shared__ int s_q[4][kE];
+  int sum = 0;
+  for (int t0 = lo; t0 < hi; t0 += 16) {                 // 16 independent loads in flight
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = t0 + i < hi ? hist[(size_t)(t0 + i) * kE + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += v[i];
   }
-  __shared__ int s_cnt[kE], s_tiles[kE];
-  s_cnt[e] = run;
-  s_tiles[e] = (run + kGBM - 1) / kGBM;
-  wsp<int>(ws, L.cnt)[e] = run;
+  s_q[q][e] = sum;
   __syncthreads();
-  if (e == 0) {
-    int* off = wsp<int>(ws, L.off);
-    int2* items = wsp<int2>(ws, L.items);
-    int o = 0, n = 0;
-    for (int x = 0; x < kE; ++x) {
-      off[x] = o;
-      for (int m = 0; m < s_tiles[x]; ++m) items[n++] = make_int2(x, m * kGBM);
-      o += s_cnt[x];
-    }
-    off[kE] = o;                                       // = T * 6: shared rows start here
-    off[kE + 1] = o + T;
-    wsp<int>(ws, L.cnt)[kE] = T;
-    for (int m = 0; m < (T + kGBM - 1) / kGBM; ++m) items[n++] = make_int2(kE, m * kGBM);
-    wsp<int>(ws, L.nitems)[0] = n;
+  int run = 0;
+  for (int k = 0; k < q; ++k) run += s_q[k][e];
+  for (int t0 = lo; t0 < hi; t0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = t0 + i < hi ? hist[(size_t)(t0 + i) * kE + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (t0 + i < hi) {
+        base[(size_t)(t0 + i) * kE + e] = run;
+        run += v[i];
+      }
   }
+  __shared__ int s_cnt[kE], s_first[kE + 1];
+  if (q == 3) {
+    s_cnt[e] = run;
+    wsp<int>(ws, L.cnt)[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {                                // expert offsets and first work item
+    const int lane = threadIdx.x;
+    int o = 0, it = 0;
+    for (int c = 0; c < kE / 64; ++c) {
+      const int x = 64 * c + lane;
+      int cnt = s_cnt[x], tiles = (cnt + kGBM - 1) / kGBM;
+      // inclusive scans across the wave
+      int ic = cnt, itl = tiles;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int a = __shfl_up(ic, d, 64), b = __shfl_up(itl, d, 64);
+        if (lane >= d) { ic += a; itl += b; }
+      }
+      wsp<int>(ws, L.off)[x] = o + ic - cnt;
+      s_first[x] = it + itl - tiles;
+      o += __shfl(ic, 63, 64);
+      it += __shfl(itl, 63, 64);
+    }
+    if (lane == 0) {
+      int* off = wsp<int>(ws, L.off);
+      off[kE] = o;                                       // = T * 6: shared rows start here
+      off[kE + 1] = o + T;
+      wsp<int>(ws, L.cnt)[kE] = T;
+      s_first[kE] = it;
+      wsp<int>(ws, L.nitems)[0] = it + (T + kGBM - 1) / kGBM;
+    }
+  }
+  __syncthreads();
+  int2* items = wsp<int2>(ws, L.items);
+  for (int x = threadIdx.x; x < kE; x += kScanThreads)
+    for (int m = 0; m * kGBM < s_cnt[x]; ++m) items[s_first[x] + m] = make_int2(x, m * kGBM);
+  for (int m = threadIdx.x; m * kGBM < T; m += kScanThreads)
+    items[s_first[kE] + m] = make_int2(kE, m * kGBM);
 }
 
 // ------------------------------------------------------------------ P3 positions
@@ -315,55 +385,75 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_positions(int T, uint8_t*
   }
 }
 
-// ------------------------------------------------------------------ grouped GEMM loaders
-// B rows of a grouped GEMM tile: NVFP4 (one 32-element chunk per thread and
-// stage: 128 rows x 2 chunks) or bf16 (4 uint4 per thread).
+// ------------------------------------------------------------------ grouped GEMM stages
+// A stage: 128 rows x 64 bf16 (thread -> row tid / 2, 64-byte half tid % 2).
+// B stage: 256 rows x 64 elements (thread -> row tid): NVFP4 32 code bytes +
+// 4 scale bytes, or bf16 128 bytes.
 template <int FMT>
-struct BLoad;
-
+struct GSlot;
 template <>
-struct BLoad<FMT_NVFP4> {
-  uint4 c;
+struct GSlot<FMT_NVFP4> {
+  uint4 a[4], c0, c1;
   uint32_t s;
-  // row pointer to codes / scales of the B row; K chunk kt
-  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int K, int kt,
-                                       int chunk) {
-    c = *reinterpret_cast<const uint4*>(codes + (size_t)kt * (kBK / 2) + 16 * chunk);
-    s = *reinterpret_cast<const uint16_t*>(scales + (size_t)kt * (kBK / 16) + 2 * chunk);
-    (void)K;
-  }
-  __device__ __forceinline__ void store(__bf16* sB, int row, int chunk) const {
-    dequant32_to_lds(sB + row * kLdsRow + 32 * chunk, c, s);
-  }
 };
-
 template <>
-struct BLoad<FMT_BF16> {
-  uint4 v[2];
-  __device__ __forceinline__ void load(const uint8_t* rowp, const uint8_t*, int K, int kt, int chunk) {
-    (void)K;
-    const uint4* p = reinterpret_cast<const uint4*>(rowp) + (size_t)kt * (kBK / 8) + 2 * chunk;
-    v[0] = p[0];
-    v[1] = p[1];
-  }
-  __device__ __forceinline__ void store(__bf16* sB, int row, int chunk) const {
-    // chunk c of BF16 rows covers 16 elements [16c, 16c + 16) of the 64
-    st_lds16(sB + row * kLdsRow + 16 * chunk, v[0]);
-    st_lds16(sB + row * kLdsRow + 16 * chunk + 8, v[1]);
-  }
+struct GSlot<FMT_BF16> {
+  uint4 a[4], b[8];
 };
+template <int FMT>
+constexpr int kRingDepth = FMT == FMT_NVFP4 ? 4 : 2;
+
+// Work item and column slice of grouped-GEMM workgroup b with NS slices:
+// b = ((item / 8) * NS + slice) * 8 + item % 8, so one item's slices share
+// an XCD.
+template <int NS>
+__device__ __forceinline__ void item_slice(int b, int& item, int& slice) {
+  slice = (b / 8) % NS;
+  item = (b / (8 * NS)) * 8 + b % 8;
+}
+
+template <int FMT>
+__device__ __forceinline__ void g_load_b(GSlot<FMT>& sl, const uint8_t* bcodes,
+                                         const uint8_t* bscales, int kt) {
+  if constexpr (FMT == FMT_NVFP4) {
+    const uint4* cp = reinterpret_cast<const uint4*>(bcodes + (size_t)kt * (kBK / 2));
+    sl.c0 = cp[0];
+    sl.c1 = cp[1];
+    sl.s = *reinterpret_cast<const uint32_t*>(bscales + (size_t)kt * (kBK / 16));
+  } else {
+    const uint4* bp = reinterpret_cast<const uint4*>(bcodes) + (size_t)kt * (kBK / 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sl.b[i] = bp[i];
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void g_store(const GSlot<FMT>& sl, __bf16* sA, __bf16* sB, int tid) {
+  const int ar = tid >> 1, ah = tid & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st_lds16(sA + ar * kLdsRow + ah * 32 + 8 * i, sl.a[i]);
+  if constexpr (FMT == FMT_NVFP4) {
+    dequant64_to_lds(sB + tid * kLdsRow, sl.c0, sl.c1, sl.s);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st_lds16(sB + tid * kLdsRow + 8 * i, sl.b[i]);
+  }
+}
 
 // ------------------------------------------------------------------ P4 GEMM 1
-// Work item (expert e, row m0) x column slice n: the tile's 128 B rows are,
-// for wave column wn and block j, gate (j = 0) or up (j = 1) row
-// 64 n + 32 wn + r, so each lane holds gate and up of the same h element.
+// Work item (expert e, row m0) x column slice n (h columns [128 n, 128 n +
+// 128)): tile B row br is, for wave column br / 64 and block (br / 32) % 2,
+// the gate (block 0) or up (block 1) row 128 n + 32 (br / 64) + br % 32, so
+// each lane holds gate and up of the same h element.
 template <int FMT>
-__global__ __launch_bounds__(kPThreads) void k_prefill_gateup(const uint16_t* __restrict__ x, int T,
-                                                              ExpertsDev routed, ExpertsDev shared,
-                                                              uint8_t* __restrict__ ws) {
-  using Acc = TileAcc<kGBM, kGBN, 2, 2>;
+__global__ __launch_bounds__(kPThreads, 1) void k_prefill_gateup(const uint16_t* __restrict__ x,
+                                                                 int T, ExpertsDev routed,
+                                                                 ExpertsDev shared,
+                                                                 uint8_t* __restrict__ ws) {
+  using Acc = TileAcc<kGBM, kGBN, 1, 4>;
   const PrefillLayout L = prefill_layout(T);
-  const int n = blockIdx.x % (kI / 64), item = blockIdx.x / (kI / 64);
+  int item, n;
+  item_slice<kSlices1>(blockIdx.x, item, n);
   if (item >= wsp<int>(ws, L.nitems)[0]) return;
   const int2 it = wsp<int2>(ws, L.items)[item];
   const int e = it.x, m0 = it.y;
@@ -371,68 +461,27 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_gateup(const uint16_t* __
   const int rbase = wsp<int>(ws, L.off)[e] + m0;       // first grouped row of the item
   const ExpertsDev X = e < kE ? routed : shared;
   const size_t ee = e < kE ? (size_t)e : 0;
-  const int* perm = wsp<int>(ws, L.perm);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   __shared__ __align__(16) __bf16 sA[2][kGBM * kLdsRow];
   __shared__ __align__(16) __bf16 sB[2][kGBN * kLdsRow];
-  // A: 128 rows x 128 B: thread -> row tid / 2, half (64 B) tid % 2
-  const int ar = tid >> 1, ah = tid & 1;
-  const int tok = perm[rbase + min(ar, rows - 1)];
-  const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)tok * kH) + 4 * ah;
-  // B: tile row br = tid / 2 (0..127), chunk tid % 2
-  const int br = tid >> 1, bch = tid & 1;
-  const int bwn = br / 64, bj = (br / 32) % 2, brr = br % 32;
-  const int wrow = 64 * n + 32 * bwn + brr;              // row within gate / up
-  const int mat = bj;                                    // 0 gate, 1 up
-  const uint8_t* bcodes;
-  const uint8_t* bscales = nullptr;
-  if constexpr (FMT == FMT_NVFP4) {
-    bcodes = X.w13 + ((ee * 2 + mat) * kI + wrow) * (size_t)(kH / 2);
-    bscales = X.w13s + ((ee * 2 + mat) * kI + wrow) * (size_t)(kH / 16);
-  } else {
-    bcodes = X.w13 + ((ee * 2 + mat) * kI + wrow) * (size_t)kH * 2;
-  }
-  uint4 av[4];
-  BLoad<FMT> bl;
-  auto gload = [&](int kt) {
+  const int tok = wsp<int>(ws, L.perm)[rbase + min(tid >> 1, rows - 1)];
+  const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)tok * kH) + 4 * (tid & 1);
+  const int bwn = tid / 64, bj = (tid / 32) % 2, brr = tid % 32;
+  const size_t wrow = (ee * 2 + bj) * kI + 128 * n + 32 * bwn + brr;   // row of w13
+  const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w13 + wrow * (kH / 2) : X.w13 + wrow * kH * 2;
+  const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w13s + wrow * (kH / 16) : nullptr;
+  GSlot<FMT> ring[kRingDepth<FMT>];
+  auto gload = [&](GSlot<FMT>& sl, int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = ap[kt * 8 + i];
-    if constexpr (FMT == FMT_NVFP4) bl.load(bcodes, bscales, kH, kt, bch);
+    for (int i = 0; i < 4; ++i) sl.a[i] = ap[kt * 8 + i];
+    g_load_b<FMT>(sl, bcodes, bscales, kt);
   };
-  BLoad<FMT> bl2;
-  auto gload_bf = [&](int kt) {                          // BF16 B needs 4 chunks of 16 per row
-    if constexpr (FMT == FMT_BF16) {
-      bl.load(bcodes, nullptr, kH, kt, 2 * bch);
-      bl2.load(bcodes, nullptr, kH, kt, 2 * bch + 1);
-    }
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st_lds16(&sA[st][ar * kLdsRow + ah * 32 + 8 * i], av[i]);
-    if constexpr (FMT == FMT_NVFP4) {
-      bl.store(sB[st], br, bch);
-    } else {
-      bl.store(sB[st], br, 2 * bch);
-      bl2.store(sB[st], br, 2 * bch + 1);
-    }
-  };
+  auto sstore = [&](const GSlot<FMT>& sl, int buf) { g_store<FMT>(sl, sA[buf], sB[buf], tid); };
   Acc acc;
   acc.zero();
-  constexpr int NK = kH / kBK;
-  gload(0);
-  gload_bf(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < NK; ++kt) {
-    if (kt + 1 < NK) {
-      gload(kt + 1);
-      gload_bf(kt + 1);
-    }
-    acc.mma(sA[kt & 1], sB[kt & 1], wave, lane);
-    if (kt + 1 < NK) sstore((kt + 1) & 1);
-    __syncthreads();
-  }
+  kpipeline<kRingDepth<FMT>, kH / kBK>(ring, gload, sstore,
+                                       [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
   // epilogue: h = SiLU(g * sg) * (u * su) -> bf16
   float sg = 1.0f, su = 1.0f;
   if constexpr (FMT == FMT_NVFP4) {
@@ -440,7 +489,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_gateup(const uint16_t* __
     su = X.glob[ee * 3 + 1];
   }
   uint16_t* h = wsp<uint16_t>(ws, L.h);
-  const int hcol = 64 * n + 32 * (wave % 2) + (lane & 31);
+  const int hcol = 128 * n + 32 * wave + (lane & 31);
 #pragma unroll
   for (int i = 0; i < Acc::MB; ++i)
 #pragma unroll
@@ -454,15 +503,16 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_gateup(const uint16_t* __
 }
 
 // ------------------------------------------------------------------ P5 GEMM 2
-// Work item (expert e, row m0) x column slice n (128 of the 2048 outputs):
+// Work item (expert e, row m0) x column slice n (256 of the 2048 outputs):
 // partial[row][col] = w_row * global * (h_row . D_e[col]) as fp16.
 template <int FMT>
-__global__ __launch_bounds__(kPThreads) void k_prefill_down(int T, ExpertsDev routed,
-                                                            ExpertsDev shared,
-                                                            uint8_t* __restrict__ ws) {
-  using Acc = TileAcc<kGBM, kGBN, 2, 2>;
+__global__ __launch_bounds__(kPThreads, 1) void k_prefill_down(int T, ExpertsDev routed,
+                                                               ExpertsDev shared,
+                                                               uint8_t* __restrict__ ws) {
+  using Acc = TileAcc<kGBM, kGBN, 1, 4>;
   const PrefillLayout L = prefill_layout(T);
-  const int n = blockIdx.x % (kH / kGBN), item = blockIdx.x / (kH / kGBN);
+  int item, n;
+  item_slice<kSlices2>(blockIdx.x, item, n);
   if (item >= wsp<int>(ws, L.nitems)[0]) return;
   const int2 it = wsp<int2>(ws, L.items)[item];
   const int e = it.x, m0 = it.y;
@@ -475,54 +525,27 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_down(int T, ExpertsDev ro
   __shared__ __align__(16) __bf16 sA[2][kGBM * kLdsRow];
   __shared__ __align__(16) __bf16 sB[2][kGBN * kLdsRow];
   const uint16_t* hsrc = wsp<uint16_t>(ws, L.h);
-  const int ar = tid >> 1, ah = tid & 1;
-  const uint4* ap = reinterpret_cast<const uint4*>(hsrc + (size_t)(rbase + min(ar, rows - 1)) * kI) + 4 * ah;
-  const int br = tid >> 1, bch = tid & 1;
-  const int wrow = kGBN * n + br;                        // output column = D row
-  const uint8_t* bcodes;
-  const uint8_t* bscales = nullptr;
-  if constexpr (FMT == FMT_NVFP4) {
-    bcodes = X.w2 + (ee * kH + wrow) * (size_t)(kI / 2);
-    bscales = X.w2s + (ee * kH + wrow) * (size_t)(kI / 16);
-  } else {
-    bcodes = X.w2 + (ee * kH + wrow) * (size_t)kI * 2;
-  }
-  uint4 av[4];
-  BLoad<FMT> bl, bl2;
-  auto gload = [&](int kt) {
+  const uint4* ap =
+      reinterpret_cast<const uint4*>(hsrc + (size_t)(rbase + min(tid >> 1, rows - 1)) * kI) +
+      4 * (tid & 1);
+  const size_t wrow = ee * kH + (size_t)kGBN * n + tid;   // output column = row of w2
+  const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w2 + wrow * (kI / 2) : X.w2 + wrow * kI * 2;
+  const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w2s + wrow * (kI / 16) : nullptr;
+  GSlot<FMT> ring[kRingDepth<FMT>];
+  auto gload = [&](GSlot<FMT>& sl, int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = ap[kt * 8 + i];
-    if constexpr (FMT == FMT_NVFP4) {
-      bl.load(bcodes, bscales, kI, kt, bch);
-    } else {
-      bl.load(bcodes, nullptr, kI, kt, 2 * bch);
-      bl2.load(bcodes, nullptr, kI, kt, 2 * bch + 1);
-    }
+    for (int i = 0; i < 4; ++i) sl.a[i] = ap[kt * 8 + i];
+    g_load_b<FMT>(sl, bcodes, bscales, kt);
   };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st_lds16(&sA[st][ar * kLdsRow + ah * 32 + 8 * i], av[i]);
-    if constexpr (FMT == FMT_NVFP4) {
-      bl.store(sB[st], br, bch);
-    } else {
-      bl.store(sB[st], br, 2 * bch);
-      bl2.store(sB[st], br, 2 * bch + 1);
-    }
-  };
+  auto sstore = [&](const GSlot<FMT>& sl, int buf) { g_store<FMT>(sl, sA[buf], sB[buf], tid); };
   Acc acc;
   acc.zero();
-  constexpr int NK = kI / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < NK; ++kt) {
-    if (kt + 1 < NK) gload(kt + 1);
-    acc.mma(sA[kt & 1], sB[kt & 1], wave, lane);
-    if (kt + 1 < NK) sstore((kt + 1) & 1);
-    __syncthreads();
-  }
+  kpipeline<kRingDepth<FMT>, kI / kBK>(ring, gload, sstore,
+                                       [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
   const float gl = FMT == FMT_NVFP4 ? X.glob[ee * 3 + 2] : 1.0f;
-  const float* wpos = wsp<float>(ws, L.wpos);
+  __shared__ float s_wr[kGBM];                          // routing weight * global per row
+  if (tid < kGBM) s_wr[tid] = tid < rows ? wsp<float>(ws, L.wpos)[rbase + tid] * gl : 0.0f;
+  __syncthreads();
   f16* part = wsp<f16>(ws, L.part);
 #pragma unroll
   for (int i = 0; i < Acc::MB; ++i)
@@ -530,7 +553,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_down(int T, ExpertsDev ro
     for (int k = 0; k < 16; ++k) {
       const int r = Acc::row_of(wave, lane, i, k);
       if (r < rows) {
-        const float wr = wpos[rbase + r] * gl;
+        const float wr = s_wr[r];
 #pragma unroll
         for (int j = 0; j < Acc::NB; ++j)
           part[(size_t)(rbase + r) * kH + kGBN * n + Acc::col_of(wave, lane, j)] =
@@ -590,18 +613,19 @@ hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
                           int32_t* ids, float* w, uint8_t* ws, hipStream_t st) {
   const PrefillLayout L = prefill_layout(T);
   hipLaunchKernelGGL(k_prefill_route, dim3(L.ntiles), dim3(kPThreads), 0, st, x, rw, T, ws, ids, w);
-  hipLaunchKernelGGL(k_prefill_scan, dim3(1), dim3(kPThreads), 0, st, T, ws);
+  hipLaunchKernelGGL(k_prefill_scan, dim3(1), dim3(kScanThreads), 0, st, T, ws);
   hipLaunchKernelGGL(k_prefill_positions, dim3(L.ntiles), dim3(kPThreads), 0, st, T, ws);
+  const int items8 = (L.max_items + 7) / 8 * 8;
   if (fmt == FMT_NVFP4) {
-    hipLaunchKernelGGL(k_prefill_gateup<FMT_NVFP4>, dim3(L.max_items * (kI / 64)), dim3(kPThreads),
-                       0, st, x, T, routed, shared, ws);
-    hipLaunchKernelGGL(k_prefill_down<FMT_NVFP4>, dim3(L.max_items * (kH / kGBN)),
-                       dim3(kPThreads), 0, st, T, routed, shared, ws);
+    hipLaunchKernelGGL(k_prefill_gateup<FMT_NVFP4>, dim3(items8 * kSlices1), dim3(kPThreads), 0, st,
+                       x, T, routed, shared, ws);
+    hipLaunchKernelGGL(k_prefill_down<FMT_NVFP4>, dim3(items8 * kSlices2), dim3(kPThreads), 0, st,
+                       T, routed, shared, ws);
   } else {
-    hipLaunchKernelGGL(k_prefill_gateup<FMT_BF16>, dim3(L.max_items * (kI / 64)), dim3(kPThreads),
-                       0, st, x, T, routed, shared, ws);
-    hipLaunchKernelGGL(k_prefill_down<FMT_BF16>, dim3(L.max_items * (kH / kGBN)),
-                       dim3(kPThreads), 0, st, T, routed, shared, ws);
+    hipLaunchKernelGGL(k_prefill_gateup<FMT_BF16>, dim3(items8 * kSlices1), dim3(kPThreads), 0, st,
+                       x, T, routed, shared, ws);
+    hipLaunchKernelGGL(k_prefill_down<FMT_BF16>, dim3(items8 * kSlices2), dim3(kPThreads), 0, st,
+                       T, routed, shared, ws);
   }
   const int nthr = T * (kH / 8);
   hipLaunchKernelGGL(k_prefill_combine, dim3((nthr + kPThreads - 1) / kPThreads), dim3(kPThreads),
