@@ -43,8 +43,8 @@ namespace moe {
 constexpr int kFusedGrid = 256;             // workgroups (one per CU)
 constexpr int kFusedThreads = 256;          // 4 waves, 16 groups of 16 lanes
 constexpr int kRowsPerWg = kH / kFusedGrid; // 8 output rows per workgroup
-constexpr int kUnitRows = 4;                // rows per down work unit (half a tile)
 constexpr int kHBanks = 64;                 // h-ready counters, one 128-byte line each
+constexpr int kMaxRange = (kMaxB * kK * kI + kFusedGrid - 1) / kFusedGrid;  // routed rows per workgroup
 constexpr int kSpinLimit = 1 << 18;
 
 // ------------------------------------------------------------------ row chunks
@@ -157,7 +157,7 @@ struct Chunk<FMT_BF16> {
 __device__ __forceinline__ void trace_stamp(uint8_t* ws, int k) {
 #ifdef MOE_PHASE_TRACE
   if (threadIdx.x == 0)
-    reinterpret_cast<unsigned long long*>(ws + kTraceOff)[blockIdx.x * 8 + k] =
+    reinterpret_cast<unsigned long long*>(ws + kDecodeWsBytes)[blockIdx.x * 16 + k] =
         __builtin_amdgcn_s_memrealtime();
 #else
   (void)ws;
@@ -215,13 +215,93 @@ __device__ __forceinline__ void wait_slots(const uint64_t* p, int stride, uint32
   }
 }
 
-// One gate/up row pair of expert `ee` for the tokens in `mask`; the wave's
-// lanes cover the 2048 columns, lane 0 writes h = SiLU(g) * u.
+// Sortable integer key of a logit: order-preserving over all non-NaN floats,
+// with -0 taken as +0 so that equal values compare equal.
+__device__ __forceinline__ int logit_key(float f) {
+  int b = __builtin_bit_cast(int, f);
+  b = b == (int)0x80000000 ? 0 : b;
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key_logit(int k) {
+  return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Positions i, i + 1 of a lane's list, descending by key; a swap needs a
+// strictly larger key, so equal keys keep their order (lower expert first).
+__device__ __forceinline__ void cmpx(int (&k)[4], int (&q)[4], int i) {
+  const bool sw = k[i + 1] > k[i];
+  const int ka = k[i], qa = q[i];
+  k[i] = sw ? k[i + 1] : ka;
+  q[i] = sw ? q[i + 1] : qa;
+  k[i + 1] = sw ? ka : k[i + 1];
+  q[i + 1] = sw ? qa : q[i + 1];
+}
+
+// Top-6 of one token's 256 router logits (v[q] = logit of expert 64 q + lane)
+// under the order (logit descending, expert ascending), as the pages' router
+// selects ("Day-0 Support for Flint on vLLM", Model architecture).  Each lane
+// first sorts its 4 logits (odd-even transposition, stable); each round takes
+// the maximum of the lane heads and pops it.  Lane j < 6 returns choice j.
+__device__ __forceinline__ void wave_top6(const float (&v)[4], int lane, int& my_id, float& my_l) {
+  int k[4], q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    k[i] = logit_key(v[i]);
+    q[i] = i;
+  }
+  cmpx(k, q, 0); cmpx(k, q, 2); cmpx(k, q, 1);
+  cmpx(k, q, 0); cmpx(k, q, 2); cmpx(k, q, 1);
+  int myk = 0;
+  my_id = 0;
+#pragma unroll
+  for (int j = 0; j < kK; ++j) {
+    const int m = wave_max_i32(k[0]);
+    const uint64_t bal = __ballot(k[0] == m);
+    int sel;
+    if (__popcll(bal) == 1) {
+      sel = __builtin_ctzll(bal);
+    } else {               // equal heads: the lowest expert id among them
+      sel = wave_min_i32(k[0] == m ? 64 * q[0] + lane : 0x7FFFFFFF) & 63;
+    }
+    const int e = 64 * __builtin_amdgcn_readlane(q[0], sel) + sel;
+    if (lane == j) {
+      my_id = e;
+      myk = m;
+    }
+    if (lane == sel) {
+      k[0] = k[1]; k[1] = k[2]; k[2] = k[3]; k[3] = (int)0x80000000;
+      q[0] = q[1]; q[1] = q[2]; q[2] = q[3];
+    }
+  }
+  my_l = key_logit(myk);
+}
+
+// One gate/up row pair of an entry for the tokens in `mask`; the wave's lanes
+// cover the 2048 columns; lane 0 puts h = SiLU(g) * u of token t in hdst[t]
+// (LDS: the workgroup writes its h to the workspace in one go, so that no
+// store sits in front of the next weight loads in the wave's memory queue).
 template <int B, int FMT>
 __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk<FMT>& cu, float sg,
                                                float su, unsigned mask, const uint4* s_x,
-                                               const uint32_t (&x0)[16], int lane,
-                                               float* hrow /* entry h at row */) {
+                                               const uint32_t (&x0)[16], int lane, float* hdst) {
 #pragma unroll
   for (int t = 0; t < B; ++t) {
     if (!((mask >> t) & 1u)) continue;
@@ -238,36 +318,44 @@ __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk
     }
     const float g = wave_sum(cg.dot_x(xw)) * sg;
     const float u = wave_sum(cu.dot_x(xw)) * su;
-    if (lane == 0) store_coherent(hrow + (size_t)t * kI, silu_mul(g, u));
+    if (lane == 0) hdst[t] = silu_mul(g, u);
   }
 }
 
-// Down contribution of one unit (kUnitRows rows of one entry) for the tokens
-// in `mask`; acc[r][t] collects the 16-lane group's sums (same in every lane).
+// 32 consecutive h values (chunk c16) of pair p from LDS.  Pairs are stored
+// as float4 (p, 8 c + i) at p * 128 + 16 i + c, so the 16 lanes of a row
+// group read consecutive float4s.
+__device__ __forceinline__ void load_h(const float4* s_h4, int p, int c16, float (&h)[32]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = s_h4[p * 128 + 16 * i + c16];
+    h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
+  }
+}
+
+// Down contribution of one entry to the workgroup's 8 output rows.  Lanes
+// 16 j .. 16 j + 15 of a wave hold rows 2 j and 2 j + 1 (32 columns each);
+// acc[r][t] gathers the lane's unreduced partial sums, scaled by the routing
+// weight of token t and the tensor scale.  The entry's h pairs start at p0.
 template <int B, int FMT>
-__device__ __forceinline__ void down_unit(const Chunk<FMT> (&rows)[kUnitRows], float gl,
-                                          unsigned mask, const float* __restrict__ wt,
-                                          const float* hent /* entry h [kMaxB][kI] */, int c16,
-                                          float (&acc)[kUnitRows][B]) {
+__device__ __forceinline__ void down_entry(const Chunk<FMT> (&rows)[2], float gl, unsigned mask,
+                                           const float* wt /* by token */, const float4* s_h4,
+                                           int p0, int c16, float (&acc)[2][B]) {
+  int p = p0;
 #pragma unroll 1
   for (int t = 0; t < B; ++t) {
     if (!((mask >> t) & 1u)) continue;
     float h[32];
-    const float* hp = hent + (size_t)t * kI + 32 * c16;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const f32x2 v = load_coherent2(hp + 2 * i);
-      h[2 * i] = v.x;
-      h[2 * i + 1] = v.y;
-    }
+    load_h(s_h4, p, c16, h);
+    ++p;
     const float sc = wt[t] * gl;
+    const float d0 = rows[0].dot_h(h), d1 = rows[1].dot_h(h);
 #pragma unroll
-    for (int r = 0; r < kUnitRows; ++r) {
-      const float v = sc * group16_sum(rows[r].dot_h(h));
-#pragma unroll
-      for (int tt = 0; tt < B; ++tt)       // static register index for any t
-        if (tt == t) acc[r][tt] += v;
-    }
+    for (int tt = 0; tt < B; ++tt)       // static register index for any t
+      if (tt == t) {
+        acc[0][tt] = __builtin_fmaf(sc, d0, acc[0][tt]);
+        acc[1][tt] = __builtin_fmaf(sc, d1, acc[1][tt]);
+      }
   }
 }
 
@@ -283,33 +371,40 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, uint8_t* __restrict__ ws) {
   constexpr int kTB = FMT == FMT_NVFP4 ? 4 : 2;      // gate/up row pairs per batch
+  constexpr int kDepthC = FMT == FMT_NVFP4 ? 4 : 1;  // entries of down rows in flight
+  constexpr int kPairs = (kK + 1) * B;               // h pairs: 6 B routed + B shared
   const int g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = tid >> 4, c16 = tid & 15;
+  const int grp4 = lane >> 4, c16 = lane & 15;
   DecodeCtl* ctl = reinterpret_cast<DecodeCtl*>(ws);
   uint64_t* lslots = reinterpret_cast<uint64_t*>(ws + kSlotLogitOff);
   float* hbuf = reinterpret_cast<float*>(ws + kHOff);
 
-  __shared__ uint4 s_x[B * kH / 8];
+  // x (bf16 [B][2048]) in steps A and B; the h pairs (fp32 [7 B][512]) in step C
+  __shared__ uint4 s_xh[kPairs * kI * 4 / 16];
+  uint4* s_x = s_xh;
+  float4* s_h4 = reinterpret_cast<float4*>(s_xh);
   __shared__ float s_part[4][kMaxB];
-  __shared__ int s_ids[kMaxB][kK];
-  __shared__ float s_w[kMaxB][kK];
-  __shared__ unsigned s_mask[kE];
-  __shared__ int s_slot[kE];
-  __shared__ int s_act[kMaxActive];
+  __shared__ unsigned s_mask[kE];                    // tokens choosing each expert
+  __shared__ float s_wfull[kE][kMaxB];               // routing weight (expert, token)
+  __shared__ int s_act[kMaxActive];                  // entry -> expert (shared last)
   __shared__ unsigned s_amask[kMaxActive];
-  __shared__ float s_wt[kMaxActive][kMaxB];
+  __shared__ int s_pair0[kMaxActive];                // first h pair of each entry
   __shared__ int s_nr;
   __shared__ uint32_t s_epoch;
+  __shared__ float s_hsh[2][kMaxB];                  // this workgroup's shared-expert h
+  __shared__ float s_hout[kMaxRange][kMaxB];         // its routed h, by row of its range
 
   trace_stamp(ws, 0);
   // ---------------------------------------------------------------- step A
   // router row g: wave w covers columns [512 w, 512 w + 512), 8 per lane
   const uint4 wr = *reinterpret_cast<const uint4*>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
-  // shared expert gate/up: rows 2g and 2g + 1 (waves 0 and 1)
-  const int srow = 2 * g + wave;
+  // shared expert gate/up: row 2g + (w & 1) in wave w, for the tokens of
+  // parity w >> 1 (at B = 1 waves 0 and 1 only)
+  const int srow = 2 * g + (wave & 1);
+  const unsigned smask = ((1u << B) - 1u) & ((wave >> 1) ? 0xAAAAAAAAu : 0x55555555u);
   Chunk<FMT> scg, scu;
-  if (wave < 2) {
+  if (smask) {
     scg.load_gu(shared, 0, 0, srow, lane);
     scu.load_gu(shared, 0, 1, srow, lane);
   }
@@ -325,6 +420,11 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
     }
   }
+  // the shared expert's down rows of this workgroup (step C), in every wave
+  Chunk<FMT> dsh[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * grp4 + r, c16);
+  s_mask[tid] = 0u;
   if (tid == 0) {                                    // this call's epoch
     uint32_t* ctr = flag_ptr(ws, 0, g);
     const uint32_t e = load_flag(ctr) + 1u;
@@ -333,6 +433,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   }
   __syncthreads();
   const uint32_t epoch = s_epoch;
+  trace_stamp(ws, 1);
   {
     float acc[B];
 #pragma unroll
@@ -350,50 +451,44 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     }
   }
   __syncthreads();
-  if (tid < B)
-    put_slot(lslots + tid * kE + g, s_part[0][tid] + s_part[1][tid] + s_part[2][tid] + s_part[3][tid],
-             epoch);
-  if (wave < 2)
+  if (tid >= kFusedThreads - B) {                   // the last wave: wave 0 polls first
+    const int t = tid - (kFusedThreads - B);
+    put_slot(lslots + t * kE + g, s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t], epoch);
+  }
+  trace_stamp(ws, 2);
+  if (smask)
     gateup_compute<B, FMT>(scg, scu, Chunk<FMT>::gscale(shared, 0, 0),
-                           Chunk<FMT>::gscale(shared, 0, 1), (1u << B) - 1u, s_x, x0, lane,
-                           hbuf + (size_t)kShSlot * kMaxB * kI + srow);
-  trace_stamp(ws, 1);
+                           Chunk<FMT>::gscale(shared, 0, 1), smask, s_x, x0, lane,
+                           &s_hsh[wave & 1][0]);
+  trace_stamp(ws, 3);
 
   // ---------------------------------------------------------------- step B
-  // top-6 per token, repeated identically in every workgroup
+  // top-6 per token (wave t % 4 takes token t), repeated identically in every
+  // workgroup; sigmoid scores of the chosen six renormalised to sum to 1
   for (int t = wave; t < B; t += 4) {
     float v[4];
     wait_slots<4>(lslots + t * kE + lane, 64, epoch, v, &ctl->err);
-    float sel_l[kK];
-    int sel_i[kK];
-    wave_topk256<kK>(v, lane, sel_i, sel_l);
-    if (lane == 0) {
-      float s[kK], sum = 0.0f;
+    trace_stamp(ws, 4);
+    int my_id;
+    float my_l;
+    wave_top6(v, lane, my_id, my_l);
+    const float s = 1.0f / (1.0f + expf(-my_l));
+    float sum = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        s[j] = 1.0f / (1.0f + expf(-sel_l[j]));
-        sum += s[j];
-      }
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        s_ids[t][j] = sel_i[j];
-        s_w[t][j] = s[j] / sum;
+    for (int j = 0; j < kK; ++j) sum += readlane_f32(s, j);
+    if (lane < kK) {
+      const float wgt = s / sum;
+      atomicOr(&s_mask[my_id], 1u << t);
+      s_wfull[my_id][t] = wgt;
+      if (g == 0) {
+        if (ids_out) ids_out[t * kK + lane] = my_id;
+        if (w_out) w_out[t * kK + lane] = wgt;
       }
     }
   }
-  trace_stamp(ws, 2);
-  for (int e = tid; e < kE; e += kFusedThreads) s_mask[e] = 0u;
+  trace_stamp(ws, 5);
   __syncthreads();
-  if (tid < B * kK) {
-    const int t = tid / kK, j = tid % kK;
-    atomicOr(&s_mask[s_ids[t][j]], 1u << t);
-    if (g == 0) {
-      if (ids_out) ids_out[t * kK + j] = s_ids[t][j];
-      if (w_out) w_out[t * kK + j] = s_w[t][j];
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {                                   // touched experts, ascending id
+  if (wave == 0) {            // entries: touched experts in ascending id, then the shared one
     int base = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -404,62 +499,47 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       if (m != 0u) {
         s_act[pos] = e;
         s_amask[pos] = m;
-        s_slot[e] = pos;
       }
       base += __popcll(bal);
     }
-    if (lane == 0) s_nr = base;
+    // first h pair of each entry: exclusive prefix of the token counts
+    const unsigned ma = lane < base ? s_amask[lane] : 0u;
+    const int cnt = __popc(ma);
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane < base) s_pair0[lane] = incl - cnt;
+    if (lane == 0) {
+      s_nr = base;
+      s_act[base] = 0;
+      s_amask[base] = (1u << B) - 1u;
+      s_pair0[base] = kK * B;
+    }
   }
   __syncthreads();
   const int nr = s_nr;
-  for (int idx = tid; idx < nr * B; idx += kFusedThreads) {
-    const int a = idx / B, t = idx % B;
-    float wt = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kK; ++j)
-      if (s_slot[s_ids[t][j]] == a) wt = s_w[t][j];
-    s_wt[a][t] = wt;
-  }
-  if (tid == 0) {                                    // the shared expert is entry nr
-    s_act[nr] = 0;
-    s_amask[nr] = (1u << B) - 1u;
-#pragma unroll
-    for (int t = 0; t < kMaxB; ++t) s_wt[nr][t] = 1.0f;
-  }
-  __syncthreads();
-
-  // step-C work of this workgroup: its 8 output rows over every entry, as
-  // units of 4 rows (one half of the tile) of one entry.  Groups 0 and 1 take
-  // the shared expert's two halves; group k >= 2 takes routed units
-  // u = k - 2 + 14 p, u = (entry u / 2, half u % 2); a group always works on
-  // half k % 2.  The first kDepth units are fetched now.
-  constexpr int kDepth = FMT == FMT_NVFP4 ? 2 : 1;
-  const int half = grp & 1;
-  const int n_units = 2 * nr;
-  auto load_unit = [&](Chunk<FMT> (&dst)[kUnitRows], int p) {
-    const int u = grp - 2 + 14 * p;
-    if (grp >= 2 && u < n_units) {
-      const size_t ee = (size_t)s_act[u >> 1];
-#pragma unroll
-      for (int r = 0; r < kUnitRows; ++r)
-        dst[r].load_dn(routed, ee, g * kRowsPerWg + half * kUnitRows + r, c16);
-    }
-  };
-  Chunk<FMT> dsh[kUnitRows];
-  if (grp < 2) {
-#pragma unroll
-    for (int r = 0; r < kUnitRows; ++r)
-      dsh[r].load_dn(shared, 0, g * kRowsPerWg + half * kUnitRows + r, c16);
-  }
-  Chunk<FMT> dbuf[kDepth][kUnitRows];
-#pragma unroll
-  for (int q = 0; q < kDepth; ++q) load_unit(dbuf[q], q);
+  trace_stamp(ws, 6);
 
   // routed gate/up: the nr * 512 row pairs are cut into 256 contiguous
   // ranges, one per workgroup; wave w takes T0 + w, T0 + w + 4, ... in
   // batches of kTB, the next batch in flight while one computes
   const int T = nr * kI;
   const int T0 = (int)(((long long)g * T) >> 8), T1 = (int)(((long long)(g + 1) * T) >> 8);
+  // step-C work of this wave: routed entries a = wsel + 4 k (and the shared
+  // expert's tokens wave, wave + 4); the first kDepthC entries' down rows are
+  // fetched behind the first gate/up batch
+  const int wsel = (wave + 3) & 3;
+  auto load_entry = [&](Chunk<FMT> (&dst)[2], int a) {
+    if (a < nr) {
+      const size_t ee = (size_t)s_act[a];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) dst[r].load_dn(routed, ee, g * kRowsPerWg + 2 * grp4 + r, c16);
+    }
+  };
+  Chunk<FMT> dbuf[kDepthC][2];
   {
     Chunk<FMT> cg[2][kTB], cu[2][kTB];
     auto load_batch = [&](Chunk<FMT> (&bg)[kTB], Chunk<FMT> (&bu)[kTB], int j0) {
@@ -478,20 +558,42 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       for (int q = 0; q < kTB; ++q) {
         const int s = T0 + wave + 4 * (j0 + q);
         if (s < T1) {
-          const int a = s / kI, row = s % kI;
+          const int a = s / kI;
           const size_t ee = (size_t)s_act[a];
           gateup_compute<B, FMT>(bg[q], bu[q], Chunk<FMT>::gscale(routed, ee, 0),
                                  Chunk<FMT>::gscale(routed, ee, 1), s_amask[a], s_x, x0, lane,
-                                 hbuf + (size_t)a * kMaxB * kI + row);
+                                 &s_hout[s - T0][0]);
         }
       }
     };
     load_batch(cg[0], cu[0], 0);
+#pragma unroll
+    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
     for (int j0 = 0; T0 + wave + 4 * j0 < T1; j0 += 2 * kTB) {
       load_batch(cg[1], cu[1], j0 + kTB);
       run_batch(cg[0], cu[0], j0);
       load_batch(cg[0], cu[0], j0 + 2 * kTB);
       run_batch(cg[1], cu[1], j0 + kTB);
+    }
+  }
+  trace_stamp(ws, 7);
+  // write this workgroup's h to its pairs: shared (6 B + t, rows 2g, 2g + 1),
+  // routed (pair0[a] + rank of t in the entry's tokens, row), consecutive
+  // threads on consecutive rows
+  __syncthreads();
+  if (tid < 2 * B) {
+    const int r = tid / B, t = tid % B;
+    store_coherent(hbuf + (size_t)(kK * B + t) * kI + 2 * g + r, s_hsh[r][t]);
+  }
+  {
+    const int nloc = T1 - T0;
+    for (int idx = tid; idx < nloc * B; idx += kFusedThreads) {
+      const int t = idx / nloc, i = idx - t * nloc;
+      const int s = T0 + i, a = s / kI;
+      const unsigned m = s_amask[a];
+      if ((m >> t) & 1u)
+        store_coherent(hbuf + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kI + (s % kI),
+                       s_hout[i][t]);
     }
   }
   // publish: wait for this workgroup's h stores, then count in on bank g % 64
@@ -501,7 +603,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   if (tid == 0)
     __hip_atomic_fetch_add(hready_bank(ws, g % kHBanks), 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-  trace_stamp(ws, 3);
+  trace_stamp(ws, 8);
 
   // ---------------------------------------------------------------- step C
   // every bank gains 4 per call: wait until all 64 hold 4 * epoch
@@ -520,54 +622,103 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
   __syncthreads();
-  trace_stamp(ws, 4);
+  trace_stamp(ws, 9);
 
-  float acc[kUnitRows][B];
+  // all 7 B h pairs of the call into LDS: 16-byte device-coherent loads
+  // (buffer loads with the device-scope bit), 8 in flight per thread
+  {
+    constexpr int kN4 = kPairs * (kI / 4);
+    const __amdgpu_buffer_rsrc_t hr =
+        __builtin_amdgcn_make_buffer_rsrc(hbuf, 0, (int)(sizeof(float) * kPairs * kI), 0x00020000);
+#pragma unroll 1
+    for (int i0 = 0; i0 < kN4; i0 += 8 * kFusedThreads) {
+      uint4 v[8];
 #pragma unroll
-  for (int r = 0; r < kUnitRows; ++r)
-#pragma unroll
-    for (int t = 0; t < B; ++t) acc[r][t] = 0.0f;
-  if (grp < 2) {
-    down_unit<B, FMT>(dsh, Chunk<FMT>::gscale(shared, 0, 2), (1u << B) - 1u, s_wt[nr],
-                      hbuf + (size_t)kShSlot * kMaxB * kI, c16, acc);
-  } else {
-    for (int p = 0; grp - 2 + 14 * p < n_units; p += kDepth) {
-      Chunk<FMT> nxt[kDepth][kUnitRows];
-#pragma unroll
-      for (int q = 0; q < kDepth; ++q) load_unit(nxt[q], p + kDepth + q);
-#pragma unroll
-      for (int q = 0; q < kDepth; ++q) {
-        const int u = grp - 2 + 14 * (p + q);
-        if (u < n_units) {
-          const int a = u >> 1;
-          down_unit<B, FMT>(dbuf[q], Chunk<FMT>::gscale(routed, (size_t)s_act[a], 2), s_amask[a],
-                            s_wt[a], hbuf + (size_t)a * kMaxB * kI, c16, acc);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int idx = i0 + kFusedThreads * i + tid;
+        if (idx < kN4) v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hr, idx * 16, 0, 16));
       }
 #pragma unroll
-      for (int q = 0; q < kDepth; ++q)
-#pragma unroll
-        for (int r = 0; r < kUnitRows; ++r) dbuf[q][r] = nxt[q][r];
+      for (int i = 0; i < 8; ++i) {
+        const int idx = i0 + kFusedThreads * i + tid;
+        if (idx < kN4) {
+          const int c = idx & 127;
+          s_xh[(idx & ~127) + 16 * (c & 7) + (c >> 3)] = v[i];
+        }
+      }
     }
   }
-  trace_stamp(ws, 5);
-  __shared__ float s_acc[16][kUnitRows][kMaxB];
+  __syncthreads();
+  trace_stamp(ws, 10);
+
+  float acc[2][B], accs[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int t = 0; t < B; ++t) acc[r][t] = 0.0f;
+    accs[r][0] = accs[r][1] = 0.0f;
+  }
+  {                                                  // shared expert, tokens wave and wave + 4
+    const float gl = Chunk<FMT>::gscale(shared, 0, 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = wave + 4 * j;
+      if (t < B) {
+        float h[32];
+        load_h(s_h4, kK * B + t, c16, h);
+        accs[0][j] = __builtin_fmaf(gl, dsh[0].dot_h(h), accs[0][j]);
+        accs[1][j] = __builtin_fmaf(gl, dsh[1].dot_h(h), accs[1][j]);
+      }
+    }
+  }
+  const int n_mine = nr > wsel ? (nr - wsel + 3) >> 2 : 0;
+  for (int k0 = 0; k0 < n_mine; k0 += kDepthC) {
+    Chunk<FMT> nxt[kDepthC][2];
+#pragma unroll
+    for (int q = 0; q < kDepthC; ++q) load_entry(nxt[q], wsel + 4 * (k0 + kDepthC + q));
+#pragma unroll
+    for (int q = 0; q < kDepthC; ++q) {
+      if (k0 + q < n_mine) {
+        const int a = wsel + 4 * (k0 + q);
+        const int e = s_act[a];
+        down_entry<B, FMT>(dbuf[q], Chunk<FMT>::gscale(routed, (size_t)e, 2), s_amask[a],
+                           &s_wfull[e][0], s_h4, s_pair0[a], c16, acc);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kDepthC; ++q)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) dbuf[q][r] = nxt[q][r];
+  }
+  trace_stamp(ws, 11);
+  // reduce over the 16 lanes of each row group, then over the waves in a
+  // fixed order; the shared expert's term of token t comes from wave t % 4
+  __shared__ float s_red[4][kRowsPerWg][kMaxB];
+  __shared__ float s_redsh[4][kRowsPerWg][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int t = 0; t < B; ++t) acc[r][t] = group16_sum(acc[r][t]);
+    accs[r][0] = group16_sum(accs[r][0]);
+    accs[r][1] = group16_sum(accs[r][1]);
+  }
   if (c16 == 0) {
 #pragma unroll
-    for (int r = 0; r < kUnitRows; ++r)
+    for (int r = 0; r < 2; ++r) {
 #pragma unroll
-      for (int t = 0; t < B; ++t) s_acc[grp][r][t] = acc[r][t];
+      for (int t = 0; t < B; ++t) s_red[wave][2 * grp4 + r][t] = acc[r][t];
+      s_redsh[wave][2 * grp4 + r][0] = accs[r][0];
+      s_redsh[wave][2 * grp4 + r][1] = accs[r][1];
+    }
   }
   __syncthreads();
-  if (tid < kRowsPerWg * B) {                        // fixed order over the groups of the half
+  if (tid < kRowsPerWg * B) {
     const int r8 = tid / B, t = tid % B;
-    const int h2 = r8 / kUnitRows, r = r8 % kUnitRows;
-    float y = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) y += s_acc[2 * k + h2][r][t];
+    float y = (s_red[0][r8][t] + s_red[1][r8][t]) + (s_red[2][r8][t] + s_red[3][r8][t]);
+    y += s_redsh[t & 3][r8][t >> 2];
     out[(size_t)t * kH + g * kRowsPerWg + r8] = f32_to_bf16_rne(y);
   }
-  trace_stamp(ws, 6);
+  trace_stamp(ws, 12);
 }
 
 // ------------------------------------------------------------------ launcher
