@@ -227,19 +227,19 @@ __device__ __forceinline__ float key_logit(int k) {
 }
 
 __device__ __forceinline__ int wave_max_i32(int v) {
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false));
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
   return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 __device__ __forceinline__ int wave_min_i32(int v) {
-  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
-  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false));
-  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
-  v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
   return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
@@ -320,6 +320,47 @@ __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk
     const float u = wave_sum(cu.dot_x(xw)) * su;
     if (lane == 0) hdst[t] = silu_mul(g, u);
   }
+}
+
+// 32-lane and 16-lane half swaps of gfx950 (v_permlane32_swap: a keeps lanes
+// 0-31 and takes b's 0-31 as its 32-63, b gets a's 32-63 and its own 32-63;
+// v_permlane16_swap does the same within each 32-lane half).
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                  __builtin_bit_cast(unsigned, b), false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                  __builtin_bit_cast(unsigned, b), false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Wave totals of 8 per-lane values at once: value j's sum over the 64 lanes
+// ends in lanes 8 j .. 8 j + 7 (halving exchanges across 32 and 16 lanes,
+// then within rows: rotate by 8, half-row mirror, quad swaps).
+__device__ __forceinline__ float wave_sum8(const float (&v)[8], int lane) {
+  float w[4], u[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float a = v[j], b = v[4 + j];
+    swap32(a, b);
+    w[j] = a + b;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float a = w[j], b = w[2 + j];
+    swap16(a, b);
+    u[j] = a + b;
+  }
+  const bool hi = (lane & 8) != 0;
+  float z = (hi ? u[1] : u[0]) + dpp_f32<0x128>(hi ? u[0] : u[1]);
+  z += dpp_f32<0x141>(z);
+  z += dpp_f32<0x4E>(z);
+  z += dpp_f32<0xB1>(z);
+  return z;
 }
 
 // 32 consecutive h values (chunk c16) of pair p from LDS.  Pairs are stored
@@ -495,23 +536,26 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       const int e = 64 * q + lane;
       const unsigned m = s_mask[e];
       const uint64_t bal = __ballot(m != 0u);
-      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
       if (m != 0u) {
         s_act[pos] = e;
         s_amask[pos] = m;
       }
       base += __popcll(bal);
     }
-    // first h pair of each entry: exclusive prefix of the token counts
+    // first h pair of each entry: exclusive prefix of the token counts (0..8),
+    // bit by bit over ballots
     const unsigned ma = lane < base ? s_amask[lane] : 0u;
     const int cnt = __popc(ma);
-    int incl = cnt;
+    int excl = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
+    for (int b = 0; b < 4; ++b) {
+      const uint64_t bb = __ballot((cnt >> b) & 1);
+      excl += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u)) << b;
     }
-    if (lane < base) s_pair0[lane] = incl - cnt;
+    if (lane < base) s_pair0[lane] = excl;
     if (lane == 0) {
       s_nr = base;
       s_act[base] = 0;
@@ -553,17 +597,62 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
         }
       }
     };
+    // a batch for each token any of its row pairs uses: the 2 kTB gate and up
+    // partial sums reduced together; gate/up of pair q land in lanes
+    // 16 q .. 16 q + 7 / 16 q + 8 .. 16 q + 15, lane 16 q writes h
     auto run_batch = [&](const Chunk<FMT> (&bg)[kTB], const Chunk<FMT> (&bu)[kTB], int j0) {
+      unsigned mq[kTB], um = 0u;
+      float sgq[kTB], suq[kTB];
 #pragma unroll
       for (int q = 0; q < kTB; ++q) {
         const int s = T0 + wave + 4 * (j0 + q);
+        mq[q] = 0u;
+        sgq[q] = suq[q] = 0.0f;
         if (s < T1) {
           const int a = s / kI;
           const size_t ee = (size_t)s_act[a];
-          gateup_compute<B, FMT>(bg[q], bu[q], Chunk<FMT>::gscale(routed, ee, 0),
-                                 Chunk<FMT>::gscale(routed, ee, 1), s_amask[a], s_x, x0, lane,
-                                 &s_hout[s - T0][0]);
+          mq[q] = s_amask[a];
+          sgq[q] = Chunk<FMT>::gscale(routed, ee, 0);
+          suq[q] = Chunk<FMT>::gscale(routed, ee, 1);
+          um |= mq[q];
         }
+      }
+      if (um == 0u) return;
+      const int qme = lane >> 4;                     // the row pair this lane may write
+      unsigned mme = 0u;
+      float sgme = 0.0f, sume = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kTB; ++q)
+        if (qme == q) {
+          mme = mq[q];
+          sgme = sgq[q];
+          sume = suq[q];
+        }
+      const int ime = T0 + wave + 4 * (j0 + qme) - T0;
+#pragma unroll
+      for (int t = 0; t < B; ++t) {
+        if (!((um >> t) & 1u)) continue;
+        uint32_t xw[16];
+        if constexpr (B == 1) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xw[i] = x0[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 v = s_x[t * (kH / 8) + 4 * lane + i];
+            xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+          }
+        }
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] = q < kTB ? bg[q < kTB ? q : 0].dot_x(xw) : 0.0f;
+          v[2 * q + 1] = q < kTB ? bu[q < kTB ? q : 0].dot_x(xw) : 0.0f;
+        }
+        const float z = wave_sum8(v, lane);
+        const float zu = dpp_f32<0x128>(z);
+        if ((lane & 15) == 0 && ((mme >> t) & 1u))
+          s_hout[ime][t] = silu_mul(z * sgme, zu * sume);
       }
     };
     load_batch(cg[0], cu[0], 0);
