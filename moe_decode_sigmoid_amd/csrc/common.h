@@ -50,14 +50,17 @@ struct DecodeCtl {
 constexpr size_t kCtlBytes = (sizeof(DecodeCtl) + 255) / 256 * 256;
 constexpr size_t kLogitsOff = kCtlBytes;                          // f32 [kMaxB][kE]
 constexpr size_t kHOff = kLogitsOff + sizeof(float) * kMaxB * kE; // f32 [kMaxActive][kMaxB][kI]
-constexpr size_t kTraceOff = kHOff + sizeof(float) * kMaxActive * kMaxB * kI;  // u64 [256][8]
-// Fused kernel: tagged 8-byte logit slots {fp32 value, call epoch}; then
-// u32 words on 128-byte lines: per-workgroup epoch counters (and spare
-// per-workgroup words), then 64 h-ready counters.
-constexpr size_t kSlotLogitOff = kTraceOff + 256 * 8 * 8;                          // [kMaxB][kE]
-constexpr size_t kFlagOff = kSlotLogitOff + 8 * kMaxB * kE;
+// Fused kernel: tagged 8-byte logit slots {fp32 value, call epoch}, written
+// in kLogitReps copies (readers poll copy g % kLogitReps, which spreads the
+// polling over more memory lines); then u32 words on 128-byte lines: one
+// epoch counter per workgroup, then kBankReps copies of 64 h-ready counters.
+constexpr int kLogitReps = 4;
+constexpr int kBankReps = 4;
+constexpr size_t kSlotLogitRep = 8 * kMaxB * kE;                                  // [kMaxB][kE]
+constexpr size_t kSlotLogitOff = kHOff + sizeof(float) * kMaxActive * kMaxB * kI;
+constexpr size_t kFlagOff = kSlotLogitOff + kSlotLogitRep * kLogitReps;
 constexpr size_t kFlagStride = 128;
-constexpr size_t kDecodeWsBytes = kFlagOff + (4 * 256 + 64) * kFlagStride;
+constexpr size_t kDecodeWsBytes = kFlagOff + (256 + 64 * kBankReps) * kFlagStride;
 constexpr int kShSlot = kMaxActive - 1;  // h entry of the shared expert in the fused kernel
 
 // ---------------------------------------------------------------- numerics

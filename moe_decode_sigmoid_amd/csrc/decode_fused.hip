@@ -182,10 +182,9 @@ __device__ __forceinline__ void store_flag(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Per-workgroup words in the workspace, one 128-byte line each:
-// kind 0 = epoch counter, 1 = step A done, 2 = h rows done, 3 = partials done.
-__device__ __forceinline__ uint32_t* flag_ptr(uint8_t* ws, int kind, int wg) {
-  return reinterpret_cast<uint32_t*>(ws + kFlagOff + ((size_t)kind * kFusedGrid + wg) * kFlagStride);
+// Per-workgroup epoch counter in the workspace, one 128-byte line each.
+__device__ __forceinline__ uint32_t* epoch_ptr(uint8_t* ws, int wg) {
+  return reinterpret_cast<uint32_t*>(ws + kFlagOff + (size_t)wg * kFlagStride);
 }
 
 // Reads N slots per lane (p[k * stride], k < N) into out[], polling until all
@@ -400,9 +399,11 @@ __device__ __forceinline__ void down_entry(const Chunk<FMT> (&rows)[2], float gl
   }
 }
 
-// h-ready counter k (k < kHBanks), one 128-byte line each, after the flags.
-__device__ __forceinline__ uint32_t* hready_bank(uint8_t* ws, int k) {
-  return reinterpret_cast<uint32_t*>(ws + kFlagOff + ((size_t)4 * kFusedGrid + k) * kFlagStride);
+// h-ready counter k (k < kHBanks) of copy r, one 128-byte line each, after
+// the epoch counters.
+__device__ __forceinline__ uint32_t* hready_bank(uint8_t* ws, int r, int k) {
+  return reinterpret_cast<uint32_t*>(ws + kFlagOff +
+                                     ((size_t)kFusedGrid + (size_t)r * kHBanks + k) * kFlagStride);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   for (int r = 0; r < 2; ++r) dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * grp4 + r, c16);
   s_mask[tid] = 0u;
   if (tid == 0) {                                    // this call's epoch
-    uint32_t* ctr = flag_ptr(ws, 0, g);
+    uint32_t* ctr = epoch_ptr(ws, g);
     const uint32_t e = load_flag(ctr) + 1u;
     store_flag(ctr, e);
     s_epoch = e;
@@ -492,9 +493,10 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     }
   }
   __syncthreads();
-  if (tid >= kFusedThreads - B) {                   // the last wave: wave 0 polls first
-    const int t = tid - (kFusedThreads - B);
-    put_slot(lslots + t * kE + g, s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t], epoch);
+  if (tid >= kFusedThreads - B * kLogitReps) {      // the last wave: wave 0 polls first
+    const int i = tid - (kFusedThreads - B * kLogitReps), t = i % B, r = i / B;
+    put_slot(lslots + r * (kSlotLogitRep / 8) + t * kE + g,
+             s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t], epoch);
   }
   trace_stamp(ws, 2);
   if (smask)
@@ -508,7 +510,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   // workgroup; sigmoid scores of the chosen six renormalised to sum to 1
   for (int t = wave; t < B; t += 4) {
     float v[4];
-    wait_slots<4>(lslots + t * kE + lane, 64, epoch, v, &ctl->err);
+    wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + t * kE + lane, 64, epoch, v,
+                  &ctl->err);
     trace_stamp(ws, 4);
     int my_id;
     float my_l;
@@ -689,24 +692,25 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0)
-    __hip_atomic_fetch_add(hready_bank(ws, g % kHBanks), 1u, __ATOMIC_RELAXED,
+  if (tid < kBankReps)
+    __hip_atomic_fetch_add(hready_bank(ws, tid, g % kHBanks), 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   trace_stamp(ws, 8);
 
   // ---------------------------------------------------------------- step C
-  // every bank gains 4 per call: wait until all 64 hold 4 * epoch
+  // every bank of every copy gains 4 per call: wait until the 64 banks of
+  // copy g % kBankReps hold 4 * epoch
   if (tid < 64) {
     const uint32_t want = (uint32_t)(kFusedGrid / kHBanks) * epoch;
     for (int spin = 0;; ++spin) {
-      const uint32_t v = load_flag(hready_bank(ws, tid));
+      const uint32_t v = load_flag(hready_bank(ws, g % kBankReps, tid));
       if (__ballot(v != want) == 0) break;
       if (spin > kSpinLimit) {
         if (tid == 0)
           __hip_atomic_fetch_or(&ctl->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
