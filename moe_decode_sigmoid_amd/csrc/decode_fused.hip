@@ -66,7 +66,8 @@ struct Chunk<FMT_NVFP4> {
     c = *reinterpret_cast<const uint4*>(X.w2 + r * (kI / 2) + 16 * ch);
     s = *reinterpret_cast<const uint16_t*>(X.w2s + r * (kI / 16) + 2 * ch);
   }
-  // sum_k w_k x_k over the chunk, without the tensor scale
+  // sum_k w_k v_k over the chunk (v: 32 bf16 values in pairs), without the
+  // tensor scale; v is x for gate/up rows and h for down rows
   __device__ __forceinline__ float dot_x(const uint32_t (&xw)[16]) const {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     float b0 = 0.0f, b1 = 0.0f;
@@ -85,20 +86,6 @@ struct Chunk<FMT_NVFP4> {
       b1 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b1);
     }
     return b0 * e4m3_to_f32<0>(s) + b1 * e4m3_to_f32<1>(s);
-  }
-  __device__ __forceinline__ float dot_h(const float (&h)[32]) const {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float b[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      f32x2 p;
-      float& acc = b[d >> 1];
-      p = fp4x2_to_f32<0>(w[d]); acc += p.x * h[8 * d + 0]; acc += p.y * h[8 * d + 1];
-      p = fp4x2_to_f32<1>(w[d]); acc += p.x * h[8 * d + 2]; acc += p.y * h[8 * d + 3];
-      p = fp4x2_to_f32<2>(w[d]); acc += p.x * h[8 * d + 4]; acc += p.y * h[8 * d + 5];
-      p = fp4x2_to_f32<3>(w[d]); acc += p.x * h[8 * d + 6]; acc += p.y * h[8 * d + 7];
-    }
-    return b[0] * e4m3_to_f32<0>(s) + b[1] * e4m3_to_f32<1>(s);
   }
   __device__ __forceinline__ static float gscale(const ExpertsDev& X, size_t ee, int m) {
     return X.glob[ee * 3 + m];
@@ -133,20 +120,6 @@ struct Chunk<FMT_BF16> {
       b1 = dot2_bf16(w[i].y, xw[4 * i + 1], b1);
       b1 = dot2_bf16(w[i].z, xw[4 * i + 2], b1);
       b1 = dot2_bf16(w[i].w, xw[4 * i + 3], b1);
-    }
-    return b0 + b1;
-  }
-  __device__ __forceinline__ float dot_h(const float (&h)[32]) const {
-    float b0 = 0.0f, b1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t v[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-      float& acc = i < 2 ? b0 : b1;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc += bf16_lo(v[k]) * h[8 * i + 2 * k];
-        acc += bf16_hi(v[k]) * h[8 * i + 2 * k + 1];
-      }
     }
     return b0 + b1;
   }
@@ -362,13 +335,13 @@ __device__ __forceinline__ float wave_sum8(const float (&v)[8], int lane) {
   return z;
 }
 
-// 32 consecutive h values (chunk c16) of pair p from LDS.  Pairs are stored
-// as float4 (p, 8 c + i) at p * 128 + 16 i + c, so the 16 lanes of a row
-// group read consecutive float4s.
-__device__ __forceinline__ void load_h(const float4* s_h4, int p, int c16, float (&h)[32]) {
+// 32 consecutive bf16 h values (chunk c16, as 16 packed pairs) of pair p
+// from LDS.  A pair is 64 uint4s; uint4 (p, 4 c + i) sits at p * 64 + 16 i + c,
+// so the 16 lanes of a row group read consecutive uint4s.
+__device__ __forceinline__ void load_h(const uint4* s_h, int p, int c16, uint32_t (&h)[16]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 v = s_h4[p * 128 + 16 * i + c16];
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = s_h[p * 64 + 16 * i + c16];
     h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
   }
 }
@@ -379,17 +352,17 @@ __device__ __forceinline__ void load_h(const float4* s_h4, int p, int c16, float
 // weight of token t and the tensor scale.  The entry's h pairs start at p0.
 template <int B, int FMT>
 __device__ __forceinline__ void down_entry(const Chunk<FMT> (&rows)[2], float gl, unsigned mask,
-                                           const float* wt /* by token */, const float4* s_h4,
+                                           const float* wt /* by token */, const uint4* s_h,
                                            int p0, int c16, float (&acc)[2][B]) {
   int p = p0;
 #pragma unroll 1
   for (int t = 0; t < B; ++t) {
     if (!((mask >> t) & 1u)) continue;
-    float h[32];
-    load_h(s_h4, p, c16, h);
+    uint32_t h[16];
+    load_h(s_h, p, c16, h);
     ++p;
     const float sc = wt[t] * gl;
-    const float d0 = rows[0].dot_h(h), d1 = rows[1].dot_h(h);
+    const float d0 = rows[0].dot_x(h), d1 = rows[1].dot_x(h);
 #pragma unroll
     for (int tt = 0; tt < B; ++tt)       // static register index for any t
       if (tt == t) {
@@ -420,12 +393,12 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   const int grp4 = lane >> 4, c16 = lane & 15;
   DecodeCtl* ctl = reinterpret_cast<DecodeCtl*>(ws);
   uint64_t* lslots = reinterpret_cast<uint64_t*>(ws + kSlotLogitOff);
-  float* hbuf = reinterpret_cast<float*>(ws + kHOff);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + kHOff);
 
-  // x (bf16 [B][2048]) in steps A and B; the h pairs (fp32 [7 B][512]) in step C
-  __shared__ uint4 s_xh[kPairs * kI * 4 / 16];
+  // x (bf16 [B][2048]) in steps A and B; the h pairs (bf16 [7 B][512]) in step C
+  __shared__ uint4 s_xh[kPairs * kI * 2 / 16];
   uint4* s_x = s_xh;
-  float4* s_h4 = reinterpret_cast<float4*>(s_xh);
+  const uint4* s_h = s_xh;
   __shared__ float s_part[4][kMaxB];
   __shared__ unsigned s_mask[kE];                    // tokens choosing each expert
   __shared__ float s_wfull[kE][kMaxB];               // routing weight (expert, token)
@@ -675,7 +648,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   __syncthreads();
   if (tid < 2 * B) {
     const int r = tid / B, t = tid % B;
-    store_coherent(hbuf + (size_t)(kK * B + t) * kI + 2 * g + r, s_hsh[r][t]);
+    store_coherent_u16(hbuf + (size_t)(kK * B + t) * kI + 2 * g + r, f32_to_bf16_rne(s_hsh[r][t]));
   }
   {
     const int nloc = T1 - T0;
@@ -684,8 +657,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       const int s = T0 + i, a = s / kI;
       const unsigned m = s_amask[a];
       if ((m >> t) & 1u)
-        store_coherent(hbuf + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kI + (s % kI),
-                       s_hout[i][t]);
+        store_coherent_u16(hbuf + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kI + (s % kI),
+                           f32_to_bf16_rne(s_hout[i][t]));
     }
   }
   // publish: wait for this workgroup's h stores, then count in on bank g % 64
@@ -698,8 +671,15 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   trace_stamp(ws, 8);
 
   // ---------------------------------------------------------------- step C
-  // every bank of every copy gains 4 per call: wait until the 64 banks of
-  // copy g % kBankReps hold 4 * epoch
+  // the next kDepthC entries' down rows go out now (wave 0 first polls), so
+  // they arrive during the wait; then every bank of copy g % kBankReps must
+  // hold 4 * epoch (each bank gains 4 per call)
+  Chunk<FMT> dbuf2[kDepthC][2];
+  auto prefetch2 = [&]() {
+#pragma unroll
+    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf2[q], wsel + 4 * (kDepthC + q));
+  };
+  if (wave != 0) prefetch2();
   if (tid < 64) {
     const uint32_t want = (uint32_t)(kFusedGrid / kHBanks) * epoch;
     for (int spin = 0;; ++spin) {
@@ -714,29 +694,30 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
+  if (wave == 0) prefetch2();
   __syncthreads();
   trace_stamp(ws, 9);
 
   // all 7 B h pairs of the call into LDS: 16-byte device-coherent loads
   // (buffer loads with the device-scope bit), 8 in flight per thread
   {
-    constexpr int kN4 = kPairs * (kI / 4);
+    constexpr int kN16 = kPairs * (kI * 2 / 16);
     const __amdgpu_buffer_rsrc_t hr =
-        __builtin_amdgcn_make_buffer_rsrc(hbuf, 0, (int)(sizeof(float) * kPairs * kI), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(hbuf, 0, (int)(2 * kPairs * kI), 0x00020000);
 #pragma unroll 1
-    for (int i0 = 0; i0 < kN4; i0 += 8 * kFusedThreads) {
+    for (int i0 = 0; i0 < kN16; i0 += 8 * kFusedThreads) {
       uint4 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int idx = i0 + kFusedThreads * i + tid;
-        if (idx < kN4) v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hr, idx * 16, 0, 16));
+        if (idx < kN16) v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hr, idx * 16, 0, 16));
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int idx = i0 + kFusedThreads * i + tid;
-        if (idx < kN4) {
-          const int c = idx & 127;
-          s_xh[(idx & ~127) + 16 * (c & 7) + (c >> 3)] = v[i];
+        if (idx < kN16) {
+          const int c = idx & 63;
+          s_xh[(idx & ~63) + 16 * (c & 3) + (c >> 2)] = v[i];
         }
       }
     }
@@ -757,31 +738,33 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     for (int j = 0; j < 2; ++j) {
       const int t = wave + 4 * j;
       if (t < B) {
-        float h[32];
-        load_h(s_h4, kK * B + t, c16, h);
-        accs[0][j] = __builtin_fmaf(gl, dsh[0].dot_h(h), accs[0][j]);
-        accs[1][j] = __builtin_fmaf(gl, dsh[1].dot_h(h), accs[1][j]);
+        uint32_t h[16];
+        load_h(s_h, kK * B + t, c16, h);
+        accs[0][j] = __builtin_fmaf(gl, dsh[0].dot_x(h), accs[0][j]);
+        accs[1][j] = __builtin_fmaf(gl, dsh[1].dot_x(h), accs[1][j]);
       }
     }
   }
+  // routed entries of this wave in order, two sets of kDepthC in flight
   const int n_mine = nr > wsel ? (nr - wsel + 3) >> 2 : 0;
-  for (int k0 = 0; k0 < n_mine; k0 += kDepthC) {
-    Chunk<FMT> nxt[kDepthC][2];
-#pragma unroll
-    for (int q = 0; q < kDepthC; ++q) load_entry(nxt[q], wsel + 4 * (k0 + kDepthC + q));
+  auto run_set = [&](const Chunk<FMT> (&buf)[kDepthC][2], int k0) {
 #pragma unroll
     for (int q = 0; q < kDepthC; ++q) {
       if (k0 + q < n_mine) {
         const int a = wsel + 4 * (k0 + q);
         const int e = s_act[a];
-        down_entry<B, FMT>(dbuf[q], Chunk<FMT>::gscale(routed, (size_t)e, 2), s_amask[a],
-                           &s_wfull[e][0], s_h4, s_pair0[a], c16, acc);
+        down_entry<B, FMT>(buf[q], Chunk<FMT>::gscale(routed, (size_t)e, 2), s_amask[a],
+                           &s_wfull[e][0], s_h, s_pair0[a], c16, acc);
       }
     }
+  };
+  for (int k0 = 0; k0 < n_mine; k0 += 2 * kDepthC) {
+    run_set(dbuf, k0);
 #pragma unroll
-    for (int q = 0; q < kDepthC; ++q)
+    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * (k0 + 2 * kDepthC + q));
+    run_set(dbuf2, k0 + kDepthC);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) dbuf[q][r] = nxt[q][r];
+    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf2[q], wsel + 4 * (k0 + 3 * kDepthC + q));
   }
   trace_stamp(ws, 11);
   // reduce over the 16 lanes of each row group, then over the waves in a
