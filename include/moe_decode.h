@@ -117,9 +117,11 @@ moe_status moe_decode_route(const moe_shape* shape, const void* x, int32_t B,
 
 /* The whole layer for B = 1..8 tokens (the low-latency decode path):
  * route, then the SiLU-gated GEMVs of only the selected experts and of the
- * shared expert, then the weighted combine, all in fp32 with the output
- * rounded once to bf16.  At B > 1 each expert chosen by several tokens has
- * its weights read once for all of them.
+ * shared expert, then the weighted combine.  Products and sums are fp32;
+ * h = SiLU(gate x) * (up x) is handed to the down GEMV as bf16 (the
+ * activation type of W4A16) and the output is rounded once to bf16.  At
+ * B > 1 each expert chosen by several tokens has its weights read once for
+ * all of them.
  *   out      bf16 [B][H]   (written; must not overlap x)
  *   ids_out  int32 [B][top_k], w_out f32 [B][top_k]: the routing used
  *            (each nullable). */
@@ -127,6 +129,18 @@ moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
                               const void* router_w, const moe_experts* routed,
                               const moe_experts* shared, void* out, int32_t* ids_out,
                               float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_decode_forward that also records the layer's kernel execution on two
+ * caller-created HIP events (hipEvent_t, timing enabled): ev_start at the
+ * kernel's start and ev_stop at its end (through hipExtLaunchKernel), so
+ * hipEventElapsedTime gives the kernel's own duration without launch gaps.
+ * For measurement; when the single-launch path is not available the events
+ * bracket the three launches instead.  NULL events: MOE_ERR_INVALID_ARG. */
+moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32_t B,
+                                    const void* router_w, const moe_experts* routed,
+                                    const moe_experts* shared, void* out, int32_t* ids_out,
+                                    float* w_out, void* ws, size_t ws_bytes, void* stream,
+                                    void* ev_start, void* ev_stop);
 
 /* The same layer for T >= 1 tokens at prefill sizes (Optimization section:
  * the MoE kernels were also the largest prefill gain, measured on an

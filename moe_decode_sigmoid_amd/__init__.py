@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_forward.restype = ctypes.c_int
         L.moe_decode_forward.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp, vp,
                                          vp, vp, sz, vp]
+        L.moe_decode_forward_timed.restype = ctypes.c_int
+        L.moe_decode_forward_timed.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp,
+                                               vp, vp, vp, sz, vp, vp, vp]
         L.moe_prefill_forward.restype = ctypes.c_int
         L.moe_prefill_forward.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp, vp,
                                           vp, vp, sz, vp]
@@ -140,6 +143,28 @@ def moe_decode_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_out
                                   ctypes.byref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_decode_forward")
+
+
+def moe_decode_forward_timed(x, router_w, routed, shared, out, ws, ev_start, ev_stop,
+                             ids_out=None, w_out=None, fmt=MOE_W_NVFP4, stream=None,
+                             S: Shape | None = None, B: int | None = None):
+    """moe_decode_forward recording the kernel's own start / end on two
+    torch.cuda.Event(enable_timing=True) (ev_start.elapsed_time(ev_stop) after
+    a synchronize is the kernel's execution time)."""
+    S = S or shape(_fmt(fmt))
+    B = x.shape[0] if B is None else B
+    R, Sh = experts_struct(routed), experts_struct(shared)
+    import torch
+    for ev in (ev_start, ev_stop):
+        if not ev.cuda_event:           # torch creates its events at their first record
+            ev.record(torch.cuda.current_stream())
+    st = lib().moe_decode_forward_timed(ctypes.byref(S), _ptr(x), B, _ptr(router_w),
+                                        ctypes.byref(R), ctypes.byref(Sh), _ptr(out),
+                                        _ptr(ids_out), _ptr(w_out), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream),
+                                        ctypes.c_void_p(ev_start.cuda_event),
+                                        ctypes.c_void_p(ev_stop.cuda_event))
+    _check(st, "moe_decode_forward_timed")
 
 
 def moe_prefill_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_out=None,

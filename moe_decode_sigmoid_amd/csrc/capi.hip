@@ -141,10 +141,46 @@ moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
                                 ws_bytes, moe::kDecodeWsBytes);
   if (st != MOE_OK) return st;
   const bool fused = moe::fused_supported() && !split_path_forced();
-  hipError_t e = (fused ? moe::launch_decode_fused : moe::launch_decode_split)(
-      B, shape->wfmt, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w),
-      to_dev(routed), to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
-      static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      fused ? moe::launch_decode_fused(B, shape->wfmt, static_cast<const uint16_t*>(x),
+                                       static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                       to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                       static_cast<uint8_t*>(ws), s)
+            : moe::launch_decode_split(B, shape->wfmt, static_cast<const uint16_t*>(x),
+                                       static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                       to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                       static_cast<uint8_t*>(ws), s);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32_t B,
+                                    const void* router_w, const moe_experts* routed,
+                                    const moe_experts* shared, void* out, int32_t* ids_out,
+                                    float* w_out, void* ws, size_t ws_bytes, void* stream,
+                                    void* ev_start, void* ev_stop) {
+  if (!ev_start || !ev_stop) return MOE_ERR_INVALID_ARG;
+  if (shape && check_shape(shape) == MOE_OK && B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
+  moe_status st = check_forward(shape, x, B, router_w, routed, shared, out, ids_out, w_out, ws,
+                                ws_bytes, moe::kDecodeWsBytes);
+  if (st != MOE_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
+  hipError_t e;
+  if (moe::fused_supported() && !split_path_forced()) {
+    e = moe::launch_decode_fused(B, shape->wfmt, static_cast<const uint16_t*>(x),
+                                 static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                 to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                 static_cast<uint8_t*>(ws), s, e0, e1);
+  } else {
+    e = hipEventRecord(e0, s);
+    if (e == hipSuccess)
+      e = moe::launch_decode_split(B, shape->wfmt, static_cast<const uint16_t*>(x),
+                                   static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                   to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                   static_cast<uint8_t*>(ws), s);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+  }
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -35,6 +35,8 @@
 // workspace error word and carries on, so the kernel always terminates.
 // Results are reproducible bit for bit (fixed summation orders, no atomics
 // on data).
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -127,14 +129,28 @@ struct Chunk<FMT_BF16> {
 };
 
 // ------------------------------------------------------------------ helpers
+// Phase timestamps of a traced build (-DMOE_PHASE_TRACE): kept in LDS and
+// written after the kernel's last step, so they add no stores to the
+// memory queue of the phases they time.
+#ifdef MOE_PHASE_TRACE
+__shared__ unsigned long long s_trace[16];
+#endif
 __device__ __forceinline__ void trace_stamp(uint8_t* ws, int k) {
 #ifdef MOE_PHASE_TRACE
-  if (threadIdx.x == 0)
-    reinterpret_cast<unsigned long long*>(ws + kDecodeWsBytes)[blockIdx.x * 16 + k] =
-        __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) s_trace[k] = __builtin_amdgcn_s_memrealtime();
 #else
   (void)ws;
   (void)k;
+#endif
+}
+__device__ __forceinline__ void trace_flush(uint8_t* ws) {
+#ifdef MOE_PHASE_TRACE
+  __syncthreads();
+  if (threadIdx.x < 16)
+    reinterpret_cast<unsigned long long*>(ws + kDecodeWsBytes)[blockIdx.x * 16 + threadIdx.x] =
+        s_trace[threadIdx.x];
+#else
+  (void)ws;
 #endif
 }
 
@@ -405,6 +421,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   __shared__ int s_act[kMaxActive];                  // entry -> expert (shared last)
   __shared__ unsigned s_amask[kMaxActive];
   __shared__ int s_pair0[kMaxActive];                // first h pair of each entry
+  __shared__ float s_gs[kMaxActive][3];              // tensor scales of each routed entry
   __shared__ int s_nr;
   __shared__ uint32_t s_epoch;
   __shared__ float s_hsh[2][kMaxB];                  // this workgroup's shared-expert h
@@ -435,7 +452,10 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
     }
   }
-  // the shared expert's down rows of this workgroup (step C), in every wave
+  // the shared expert's tensor scales and down rows of this workgroup (step
+  // C), in every wave
+  const float sh_sg = Chunk<FMT>::gscale(shared, 0, 0), sh_su = Chunk<FMT>::gscale(shared, 0, 1),
+              sh_sd = Chunk<FMT>::gscale(shared, 0, 2);
   Chunk<FMT> dsh[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * grp4 + r, c16);
@@ -473,8 +493,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   }
   trace_stamp(ws, 2);
   if (smask)
-    gateup_compute<B, FMT>(scg, scu, Chunk<FMT>::gscale(shared, 0, 0),
-                           Chunk<FMT>::gscale(shared, 0, 1), smask, s_x, x0, lane,
+    gateup_compute<B, FMT>(scg, scu, sh_sg, sh_su, smask, s_x, x0, lane,
                            &s_hsh[wave & 1][0]);
   trace_stamp(ws, 3);
 
@@ -586,10 +605,9 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
         sgq[q] = suq[q] = 0.0f;
         if (s < T1) {
           const int a = s / kI;
-          const size_t ee = (size_t)s_act[a];
           mq[q] = s_amask[a];
-          sgq[q] = Chunk<FMT>::gscale(routed, ee, 0);
-          suq[q] = Chunk<FMT>::gscale(routed, ee, 1);
+          sgq[q] = s_gs[a][0];
+          suq[q] = s_gs[a][1];
           um |= mq[q];
         }
       }
@@ -631,9 +649,16 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
           s_hout[ime][t] = silu_mul(z * sgme, zu * sume);
       }
     };
+    // the routed entries' tensor scales: one thread each, fetched beside the
+    // first weights and parked in LDS (no wave waits on them in its loop)
+    const bool gs_mine = tid < 3 * nr;
+    float gsv = 1.0f;
+    if (gs_mine) gsv = Chunk<FMT>::gscale(routed, (size_t)s_act[tid / 3], tid % 3);
     load_batch(cg[0], cu[0], 0);
 #pragma unroll
     for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
+    if (gs_mine) s_gs[tid / 3][tid % 3] = gsv;
+    __syncthreads();
     for (int j0 = 0; T0 + wave + 4 * j0 < T1; j0 += 2 * kTB) {
       load_batch(cg[1], cu[1], j0 + kTB);
       run_batch(cg[0], cu[0], j0);
@@ -733,7 +758,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     accs[r][0] = accs[r][1] = 0.0f;
   }
   {                                                  // shared expert, tokens wave and wave + 4
-    const float gl = Chunk<FMT>::gscale(shared, 0, 2);
+    const float gl = sh_sd;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int t = wave + 4 * j;
@@ -753,7 +778,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       if (k0 + q < n_mine) {
         const int a = wsel + 4 * (k0 + q);
         const int e = s_act[a];
-        down_entry<B, FMT>(buf[q], Chunk<FMT>::gscale(routed, (size_t)e, 2), s_amask[a],
+        down_entry<B, FMT>(buf[q], s_gs[a][2], s_amask[a],
                            &s_wfull[e][0], s_h, s_pair0[a], c16, acc);
       }
     }
@@ -795,6 +820,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     out[(size_t)t * kH + g * kRowsPerWg + r8] = f32_to_bf16_rne(y);
   }
   trace_stamp(ws, 12);
+  trace_flush(ws);
 }
 
 // ------------------------------------------------------------------ launcher
@@ -819,27 +845,29 @@ bool fused_supported() {
 template <int B>
 static void launch_fused_b(int fmt, const uint16_t* x, const uint16_t* rw, const ExpertsDev& routed,
                            const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
-                           uint8_t* ws, hipStream_t st) {
-  if (fmt == FMT_NVFP4)
-    hipLaunchKernelGGL((k_decode_fused<B, FMT_NVFP4>), dim3(kFusedGrid), dim3(kFusedThreads), 0, st,
-                       x, rw, routed, shared, out, ids, w, ws);
+                           uint8_t* ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  auto k = fmt == FMT_NVFP4 ? k_decode_fused<B, FMT_NVFP4> : k_decode_fused<B, FMT_BF16>;
+  if (e0 && e1)
+    hipExtLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, e0, e1, 0, x, rw, routed,
+                          shared, out, ids, w, ws);
   else
-    hipLaunchKernelGGL((k_decode_fused<B, FMT_BF16>), dim3(kFusedGrid), dim3(kFusedThreads), 0, st,
-                       x, rw, routed, shared, out, ids, w, ws);
+    hipLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, x, rw, routed, shared, out,
+                       ids, w, ws);
 }
 
 hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t* rw,
                                const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
-                               int32_t* ids, float* w, uint8_t* ws, hipStream_t st) {
+                               int32_t* ids, float* w, uint8_t* ws, hipStream_t st, hipEvent_t e0,
+                               hipEvent_t e1) {
   switch (B) {
-    case 1: launch_fused_b<1>(fmt, x, rw, routed, shared, out, ids, w, ws, st); break;
-    case 2: launch_fused_b<2>(fmt, x, rw, routed, shared, out, ids, w, ws, st); break;
-    case 3: launch_fused_b<3>(fmt, x, rw, routed, shared, out, ids, w, ws, st); break;
-    case 4: launch_fused_b<4>(fmt, x, rw, routed, shared, out, ids, w, ws, st); break;
-    case 5: launch_fused_b<5>(fmt, x, rw, routed, shared, out, ids, w, ws, st); break;
-    case 6: launch_fused_b<6>(fmt, x, rw, routed, shared, out, ids, w, ws, st); break;
-    case 7: launch_fused_b<7>(fmt, x, rw, routed, shared, out, ids, w, ws, st); break;
-    case 8: launch_fused_b<8>(fmt, x, rw, routed, shared, out, ids, w, ws, st); break;
+    case 1: launch_fused_b<1>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
+    case 2: launch_fused_b<2>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
+    case 3: launch_fused_b<3>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
+    case 4: launch_fused_b<4>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
+    case 5: launch_fused_b<5>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
+    case 6: launch_fused_b<6>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
+    case 7: launch_fused_b<7>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
+    case 8: launch_fused_b<8>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -16,10 +16,13 @@ hipError_t launch_decode_split(int B, int fmt, const uint16_t* x, const uint16_t
                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
 
 // Fused single-launch decode path, B = 1..8 (needs 256 co-resident workgroups).
+// With both events given, the launch records the kernel's own start and end
+// on them (hipExtLaunchKernel).
 bool fused_supported();
 hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t* rw,
                                const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
-                               int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
+                               int32_t* ids, float* w, uint8_t* ws, hipStream_t st,
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Parity probe: one NVFP4 tensor [rows][cols] decoded to fp32.
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob, int rows,

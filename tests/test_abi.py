@@ -18,7 +18,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["moe_decode_route", "moe_decode_forward", "moe_prefill_forward",
+    for n in ["moe_decode_route", "moe_decode_forward", "moe_decode_forward_timed",
+              "moe_prefill_forward",
               "moe_nvfp4_dequant", "moe_workspace_bytes", "moe_status_string",
               "moe_abi_version"]:
         assert n in names
@@ -98,6 +99,21 @@ def test_forward_argument_errors(prefill):
                dict(n_shared=2)]:
         assert _forward(S=moe.shape(**kw), prefill=prefill) == E.MOE_ERR_UNSUPPORTED
     assert _forward(S=moe.shape(7), prefill=prefill) == E.MOE_ERR_UNSUPPORTED
+
+
+def test_timed_forward_needs_both_events_and_checks_like_forward():
+    S = moe.shape()
+    R = moe.experts_struct(_FakeExperts(A + 0x4000000))
+    Sh = moe.experts_struct(_FakeExperts(A + 0x5000000))
+    fn = moe.lib().moe_decode_forward_timed
+
+    def call(ev0, ev1, x=A, B=1):
+        return fn(ctypes.byref(S), x, B, A + 0x1000000, ctypes.byref(R), ctypes.byref(Sh),
+                  A + 0x2000000, None, None, A + 0x3000000, WS_BIG, 0, ev0, ev1)
+    assert call(None, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(A, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(A, A, x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(A, A, B=9) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_decode_batch_limit_is_unsupported_not_invalid():

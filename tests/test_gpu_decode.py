@@ -203,6 +203,24 @@ def test_fused_and_split_paths_agree(monkeypatch):
         assert np.abs(yf - ys).max() <= 2 ** -7 * max(1.0, np.abs(ys).max())
 
 
+def test_timed_entry_point_matches_and_times_the_kernel():
+    """The timed variant computes the same layer and records a positive kernel
+    duration on the caller's events."""
+    L = dev_layer(2)
+    for B in (1, 8):
+        x = testgen.make_x(6, B)
+        xd = moe.device.to_device_bf16(x)
+        outs = [torch.empty((B, 2048), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+        ws = moe.alloc_workspace(moe.moe_workspace_bytes(B))
+        moe.moe_decode_forward(xd, L.router, L.routed, L.shared, outs[0], ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        moe.moe_decode_forward_timed(xd, L.router, L.routed, L.shared, outs[1], ws, e0, e1)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
+        ms = e0.elapsed_time(e1)
+        assert 0.0 < ms < 50.0, ms
+
+
 def test_workspace_error_word_stays_clear():
     """Byte offset 8 of the workspace is the device-side wait time-out flag."""
     ws = moe.alloc_workspace(moe.moe_workspace_bytes(8))
