@@ -486,10 +486,16 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     }
   }
   __syncthreads();
-  if (tid >= kFusedThreads - B * kLogitReps) {      // the last wave: wave 0 polls first
-    const int i = tid - (kFusedThreads - B * kLogitReps), t = i % B, r = i / B;
-    put_slot(lslots + r * (kSlotLogitRep / 8) + t * kE + g,
-             s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t], epoch);
+  // the last wave stores (wave 0 polls first).  Once every 65536 calls the
+  // slots of tokens t >= B are stamped too, so no slot is ever 2^32 calls old
+  // and a 32-bit tag cannot match a stale value.
+  {
+    const int nt = (epoch & 0xFFFFu) == 0u ? kMaxB : B;
+    const int i = tid - (kFusedThreads - kMaxB * kLogitReps), t = i % kMaxB, r = i / kMaxB;
+    if (i >= 0 && t < nt) {
+      const float v = t < B ? s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t] : 0.0f;
+      put_slot(lslots + r * (kSlotLogitRep / 8) + t * kE + g, v, epoch);
+    }
   }
   trace_stamp(ws, 2);
   if (smask)
@@ -655,6 +661,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     float gsv = 1.0f;
     if (gs_mine) gsv = Chunk<FMT>::gscale(routed, (size_t)s_act[tid / 3], tid % 3);
     load_batch(cg[0], cu[0], 0);
+    // the first kDepthC entries' down rows of step C, behind the first batch
 #pragma unroll
     for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
     if (gs_mine) s_gs[tid / 3][tid % 3] = gsv;
@@ -696,30 +703,32 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   trace_stamp(ws, 8);
 
   // ---------------------------------------------------------------- step C
-  // the next kDepthC entries' down rows go out now (wave 0 first polls), so
-  // they arrive during the wait; then every bank of copy g % kBankReps must
-  // hold 4 * epoch (each bank gains 4 per call)
+  // The next kDepthC entries' down rows go out now (not earlier: the h
+  // stores above must not wait behind them), so they arrive during the wait.
+  // Wave 3 polls, and issues its rows after the wait (its polls would
+  // otherwise queue behind them).  Every bank of copy g % kBankReps must
+  // reach 4 * epoch (each bank gains 4 per call).
   Chunk<FMT> dbuf2[kDepthC][2];
-  auto prefetch2 = [&]() {
+  auto prefetch = [&]() {
 #pragma unroll
     for (int q = 0; q < kDepthC; ++q) load_entry(dbuf2[q], wsel + 4 * (kDepthC + q));
   };
-  if (wave != 0) prefetch2();
-  if (tid < 64) {
+  if (wave != 3) prefetch();
+  if (wave == 3) {
     const uint32_t want = (uint32_t)(kFusedGrid / kHBanks) * epoch;
     for (int spin = 0;; ++spin) {
-      const uint32_t v = load_flag(hready_bank(ws, g % kBankReps, tid));
+      const uint32_t v = load_flag(hready_bank(ws, g % kBankReps, lane));
       if (__ballot(v != want) == 0) break;
       if (spin > kSpinLimit) {
-        if (tid == 0)
+        if (lane == 0)
           __hip_atomic_fetch_or(&ctl->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    prefetch();
   }
-  if (wave == 0) prefetch2();
   __syncthreads();
   trace_stamp(ws, 9);
 
