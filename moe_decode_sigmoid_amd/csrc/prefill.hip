@@ -24,11 +24,14 @@
 //      expert id) + its shared row, fp32, rounded once to bf16.
 //
 // GEMM tiles are 128 x 256 with four waves of 128 x 64 each (8 MFMA blocks
-// per wave, so LDS serves ~380 bytes per MFMA); K advances 64 per stage with
-// two LDS buffers, and the global loads of the next kRing stages are held in
-// registers so the HBM / gather latency of one stage hides behind kRing
-// stages of MFMA work.  Work items are mapped so that the column slices of
-// one item run on one XCD (workgroup b lands on XCD b % 8) and share its L2.
+// per wave, so LDS serves ~380 bytes per MFMA); K advances 32 per stage with
+// two LDS buffers (61 KB, so two workgroups share a CU and one's MFMAs run
+// while the other decodes weights or waits at a barrier), and the global
+// loads of the next kRing stages are held in registers so the HBM / gather
+// latency of one stage hides behind kRing stages of MFMA work.  The router
+// GEMM keeps K = 64 per stage.  Work items are mapped so that the column
+// slices of one item run on one XCD (workgroup b lands on XCD b % 8) and
+// share its L2.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  Lane l supplies A[row l%32][k 8(l/32)..+7]
 // and B[k 8(l/32)..+7][col l%32]; result element i of lane l is
@@ -43,9 +46,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16;
 
-constexpr int kBK = 64;                  // K per pipeline stage
 constexpr int kLdsPad = 8;               // bf16 elements of padding per LDS row
-constexpr int kLdsRow = kBK + kLdsPad;   // LDS row pitch (bf16 elements)
+constexpr int kRBK = 64;                 // router GEMM: K per pipeline stage
+constexpr int kRLdsRow = kRBK + kLdsPad; //   and its LDS row pitch (bf16 elements)
+constexpr int kGBK1 = 64;                // GEMM 1 (gate/up): K per pipeline stage
+constexpr int kGBK2 = 32;                // GEMM 2 (down): K per pipeline stage
 constexpr int kPTile = 32;               // router tile (tokens)
 constexpr int kGBM = 128;                // grouped GEMM rows per work item
 constexpr int kGBN = 256;                // grouped GEMM B rows per tile
@@ -96,10 +101,11 @@ __device__ __forceinline__ P* wsp(uint8_t* ws, size_t off) {
 
 // ------------------------------------------------------------------ MFMA tile core
 // One workgroup tile: C[BM][BN] += A[BM][K] . B[BN][K]^T with A, B staged in
-// LDS as bf16 [rows][kLdsRow].  WM x WN waves; wave tile (BM/WM) x (BN/WN)
+// LDS as bf16 [rows][BK + kLdsPad].  WM x WN waves; wave tile (BM/WM) x (BN/WN)
 // made of 32x32 blocks.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK>
 struct TileAcc {
+  static constexpr int LR = BK + kLdsPad;   // LDS row pitch
   static constexpr int MB = BM / WM / 32, NB = BN / WN / 32;
   f32x16 c[MB][NB];
   __device__ __forceinline__ void zero() {
@@ -110,19 +116,19 @@ struct TileAcc {
 #pragma unroll
         for (int k = 0; k < 16; ++k) c[i][j][k] = 0.0f;
   }
-  // one kBK stage from LDS
+  // one BK stage from LDS
   __device__ __forceinline__ void mma(const __bf16* sA, const __bf16* sB, int wave, int lane) {
     const int wm = wave / WN, wn = wave % WN;
     const int r = lane & 31, kh = (lane >> 5) * 8;
 #pragma unroll
-    for (int ks = 0; ks < kBK; ks += 16) {
+    for (int ks = 0; ks < BK; ks += 16) {
       bf16x8 a[MB], b[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * (BM / WM) + 32 * i + r) * kLdsRow + ks + kh);
+        a[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * (BM / WM) + 32 * i + r) * LR + ks + kh);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(sB + (wn * (BN / WN) + 32 * j + r) * kLdsRow + ks + kh);
+        b[j] = *reinterpret_cast<const bf16x8*>(sB + (wn * (BN / WN) + 32 * j + r) * LR + ks + kh);
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -142,33 +148,38 @@ struct TileAcc {
 // 16 bf16 (one uint4 pair) of a bf16 row segment into LDS
 __device__ __forceinline__ void st_lds16(__bf16* dst, uint4 v) { *reinterpret_cast<uint4*>(dst) = v; }
 
+// E4M3 byte j (static after unrolling) of a word, as fp32.
+__device__ __forceinline__ float e4m3_sel(uint32_t w, int j) {
+  return j == 0 ? e4m3_to_f32<0>(w) : j == 1 ? e4m3_to_f32<1>(w) : j == 2 ? e4m3_to_f32<2>(w)
+                                                                           : e4m3_to_f32<3>(w);
+}
+
 // 8 NVFP4 codes (one dword) times their block scale -> 8 exact bf16 values
 // (4 dwords).  e2m1 (exact in fp32) * e4m3 (exact) is exact in fp32 and,
 // having at most six significant bits, in bf16 too, so truncation is exact.
 __device__ __forceinline__ uint4 dequant8(uint32_t w, float s) {
   const f32x2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w), p2 = fp4x2_to_f32<2>(w),
               p3 = fp4x2_to_f32<3>(w);
-  auto pk = [&](f32x2 p) {
-    return (__builtin_bit_cast(uint32_t, p.x * s) >> 16) |
-           (__builtin_bit_cast(uint32_t, p.y * s) & 0xFFFF0000u);
+  auto pk = [&](f32x2 p) {           // high halves of the two products, one byte permute
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, p.y * s),
+                                 __builtin_bit_cast(uint32_t, p.x * s), 0x07060302u);
   };
   return make_uint4(pk(p0), pk(p1), pk(p2), pk(p3));
 }
 
-// 64 NVFP4 codes of one row (two uint4) with their 4 block scales -> 64 bf16
-// in LDS (one 128-byte row segment).
-__device__ __forceinline__ void dequant64_to_lds(__bf16* dst, uint4 c0, uint4 c1, uint32_t sc) {
-  const float s0 = e4m3_to_f32<0>(sc), s1 = e4m3_to_f32<1>(sc), s2 = e4m3_to_f32<2>(sc),
-              s3 = e4m3_to_f32<3>(sc);
+// BK NVFP4 codes of one row (BK / 32 uint4) with their BK / 16 block scales
+// (bytes of sc) -> BK bf16 in LDS.
+template <int BK>
+__device__ __forceinline__ void dequant_to_lds(__bf16* dst, const uint4 (&c)[BK / 32], uint32_t sc) {
   uint4* d = reinterpret_cast<uint4*>(dst);
-  d[0] = dequant8(c0.x, s0);
-  d[1] = dequant8(c0.y, s0);
-  d[2] = dequant8(c0.z, s1);
-  d[3] = dequant8(c0.w, s1);
-  d[4] = dequant8(c1.x, s2);
-  d[5] = dequant8(c1.y, s2);
-  d[6] = dequant8(c1.z, s3);
-  d[7] = dequant8(c1.w, s3);
+#pragma unroll
+  for (int i = 0; i < BK / 32; ++i) {
+    const float s0 = e4m3_sel(sc, 2 * i), s1 = e4m3_sel(sc, 2 * i + 1);
+    d[4 * i + 0] = dequant8(c[i].x, s0);
+    d[4 * i + 1] = dequant8(c[i].y, s0);
+    d[4 * i + 2] = dequant8(c[i].z, s1);
+    d[4 * i + 3] = dequant8(c[i].w, s1);
+  }
 }
 
 // K pipeline over NK stages: register ring of D stages in flight, two LDS
@@ -206,12 +217,12 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_route(const uint16_t* __r
                                                              uint8_t* __restrict__ ws,
                                                              int32_t* __restrict__ ids_out,
                                                              float* __restrict__ w_out) {
-  using Acc = TileAcc<kPTile, kE, 1, 4>;
+  using Acc = TileAcc<kPTile, kE, 1, 4, kRBK>;
   const PrefillLayout L = prefill_layout(T);
   const int tile = blockIdx.x, t0 = tile * kPTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ __align__(16) __bf16 sA[2][kPTile * kLdsRow];
-  __shared__ __align__(16) __bf16 sB[2][kE * kLdsRow];
+  __shared__ __align__(16) __bf16 sA[2][kPTile * kRLdsRow];
+  __shared__ __align__(16) __bf16 sB[2][kE * kRLdsRow];
   // A: 32 rows x 128 B -> one uint4 per thread; B: router row tid, 8 uint4
   const int ar = tid >> 3, aseg = tid & 7;
   const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + ar, T - 1) * kH) + aseg;
@@ -224,14 +235,14 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_route(const uint16_t* __r
     for (int i = 0; i < 8; ++i) sl.b[i] = bp[kt * 8 + i];
   };
   auto sstore = [&](const Slot& sl, int buf) {
-    st_lds16(&sA[buf][ar * kLdsRow + aseg * 8], sl.a);
+    st_lds16(&sA[buf][ar * kRLdsRow + aseg * 8], sl.a);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st_lds16(&sB[buf][tid * kLdsRow + i * 8], sl.b[i]);
+    for (int i = 0; i < 8; ++i) st_lds16(&sB[buf][tid * kRLdsRow + i * 8], sl.b[i]);
   };
   Acc acc;
   acc.zero();
-  kpipeline<2, kH / kBK>(ring, gload, sstore,
-                         [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
+  kpipeline<2, kH / kRBK>(ring, gload, sstore,
+                          [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
   // logits tile -> LDS (reuse sB as fp32 [32][256 + 4])
   float* sL = reinterpret_cast<float*>(&sB[0][0]);
   constexpr int LP = kE + 4;
@@ -386,19 +397,19 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_positions(int T, uint8_t*
 }
 
 // ------------------------------------------------------------------ grouped GEMM stages
-// A stage: 128 rows x 64 bf16 (thread -> row tid / 2, 64-byte half tid % 2).
-// B stage: 256 rows x 64 elements (thread -> row tid): NVFP4 32 code bytes +
-// 4 scale bytes, or bf16 128 bytes.
-template <int FMT>
+// A stage: 128 rows x BK bf16 (thread -> row tid / 2, half tid % 2).
+// B stage: 256 rows x BK elements (thread -> row tid): NVFP4 BK / 2 code
+// bytes + BK / 16 scale bytes, or bf16 2 BK bytes.
+template <int FMT, int BK>
 struct GSlot;
-template <>
-struct GSlot<FMT_NVFP4> {
-  uint4 a[4], c0, c1;
+template <int BK>
+struct GSlot<FMT_NVFP4, BK> {
+  uint4 a[BK / 16], c[BK / 32];
   uint32_t s;
 };
-template <>
-struct GSlot<FMT_BF16> {
-  uint4 a[4], b[8];
+template <int BK>
+struct GSlot<FMT_BF16, BK> {
+  uint4 a[BK / 16], b[BK / 8];
 };
 template <int FMT>
 constexpr int kRingDepth = FMT == FMT_NVFP4 ? 4 : 2;
@@ -412,31 +423,35 @@ __device__ __forceinline__ void item_slice(int b, int& item, int& slice) {
   item = (b / (8 * NS)) * 8 + b % 8;
 }
 
-template <int FMT>
-__device__ __forceinline__ void g_load_b(GSlot<FMT>& sl, const uint8_t* bcodes,
+template <int FMT, int BK>
+__device__ __forceinline__ void g_load_b(GSlot<FMT, BK>& sl, const uint8_t* bcodes,
                                          const uint8_t* bscales, int kt) {
   if constexpr (FMT == FMT_NVFP4) {
-    const uint4* cp = reinterpret_cast<const uint4*>(bcodes + (size_t)kt * (kBK / 2));
-    sl.c0 = cp[0];
-    sl.c1 = cp[1];
-    sl.s = *reinterpret_cast<const uint32_t*>(bscales + (size_t)kt * (kBK / 16));
-  } else {
-    const uint4* bp = reinterpret_cast<const uint4*>(bcodes) + (size_t)kt * (kBK / 8);
+    const uint4* cp = reinterpret_cast<const uint4*>(bcodes + (size_t)kt * (BK / 2));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sl.b[i] = bp[i];
+    for (int i = 0; i < BK / 32; ++i) sl.c[i] = cp[i];
+    if constexpr (BK == 64)
+      sl.s = *reinterpret_cast<const uint32_t*>(bscales + (size_t)kt * (BK / 16));
+    else
+      sl.s = *reinterpret_cast<const uint16_t*>(bscales + (size_t)kt * (BK / 16));
+  } else {
+    const uint4* bp = reinterpret_cast<const uint4*>(bcodes) + (size_t)kt * (BK / 8);
+#pragma unroll
+    for (int i = 0; i < BK / 8; ++i) sl.b[i] = bp[i];
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void g_store(const GSlot<FMT>& sl, __bf16* sA, __bf16* sB, int tid) {
+template <int FMT, int BK>
+__device__ __forceinline__ void g_store(const GSlot<FMT, BK>& sl, __bf16* sA, __bf16* sB, int tid) {
+  constexpr int LR = BK + kLdsPad;
   const int ar = tid >> 1, ah = tid & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st_lds16(sA + ar * kLdsRow + ah * 32 + 8 * i, sl.a[i]);
+  for (int i = 0; i < BK / 16; ++i) st_lds16(sA + ar * LR + ah * (BK / 2) + 8 * i, sl.a[i]);
   if constexpr (FMT == FMT_NVFP4) {
-    dequant64_to_lds(sB + tid * kLdsRow, sl.c0, sl.c1, sl.s);
+    dequant_to_lds<BK>(sB + tid * LR, sl.c, sl.s);
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st_lds16(sB + tid * kLdsRow + 8 * i, sl.b[i]);
+    for (int i = 0; i < BK / 8; ++i) st_lds16(sB + tid * LR + 8 * i, sl.b[i]);
   }
 }
 
@@ -450,7 +465,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_prefill_gateup(const uint16_t*
                                                                  int T, ExpertsDev routed,
                                                                  ExpertsDev shared,
                                                                  uint8_t* __restrict__ ws) {
-  using Acc = TileAcc<kGBM, kGBN, 1, 4>;
+  using Acc = TileAcc<kGBM, kGBN, 1, 4, kGBK1>;
+  constexpr int LR = kGBK1 + kLdsPad;
   const PrefillLayout L = prefill_layout(T);
   int item, n;
   item_slice<kSlices1>(blockIdx.x, item, n);
@@ -463,24 +479,26 @@ __global__ __launch_bounds__(kPThreads, 1) void k_prefill_gateup(const uint16_t*
   const size_t ee = e < kE ? (size_t)e : 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  __shared__ __align__(16) __bf16 sA[2][kGBM * kLdsRow];
-  __shared__ __align__(16) __bf16 sB[2][kGBN * kLdsRow];
+  __shared__ __align__(16) __bf16 sA[2][kGBM * LR];
+  __shared__ __align__(16) __bf16 sB[2][kGBN * LR];
   const int tok = wsp<int>(ws, L.perm)[rbase + min(tid >> 1, rows - 1)];
-  const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)tok * kH) + 4 * (tid & 1);
+  const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)tok * kH) + (kGBK1 / 16) * (tid & 1);
   const int bwn = tid / 64, bj = (tid / 32) % 2, brr = tid % 32;
   const size_t wrow = (ee * 2 + bj) * kI + 128 * n + 32 * bwn + brr;   // row of w13
   const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w13 + wrow * (kH / 2) : X.w13 + wrow * kH * 2;
   const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w13s + wrow * (kH / 16) : nullptr;
-  GSlot<FMT> ring[kRingDepth<FMT>];
-  auto gload = [&](GSlot<FMT>& sl, int kt) {
+  GSlot<FMT, kGBK1> ring[kRingDepth<FMT>];
+  auto gload = [&](GSlot<FMT, kGBK1>& sl, int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sl.a[i] = ap[kt * 8 + i];
-    g_load_b<FMT>(sl, bcodes, bscales, kt);
+    for (int i = 0; i < kGBK1 / 16; ++i) sl.a[i] = ap[kt * (kGBK1 / 8) + i];
+    g_load_b<FMT, kGBK1>(sl, bcodes, bscales, kt);
   };
-  auto sstore = [&](const GSlot<FMT>& sl, int buf) { g_store<FMT>(sl, sA[buf], sB[buf], tid); };
+  auto sstore = [&](const GSlot<FMT, kGBK1>& sl, int buf) {
+    g_store<FMT, kGBK1>(sl, sA[buf], sB[buf], tid);
+  };
   Acc acc;
   acc.zero();
-  kpipeline<kRingDepth<FMT>, kH / kBK>(ring, gload, sstore,
+  kpipeline<kRingDepth<FMT>, kH / kGBK1>(ring, gload, sstore,
                                        [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
   // epilogue: h = SiLU(g * sg) * (u * su) -> bf16
   float sg = 1.0f, su = 1.0f;
@@ -506,10 +524,11 @@ __global__ __launch_bounds__(kPThreads, 1) void k_prefill_gateup(const uint16_t*
 // Work item (expert e, row m0) x column slice n (256 of the 2048 outputs):
 // partial[row][col] = w_row * global * (h_row . D_e[col]) as fp16.
 template <int FMT>
-__global__ __launch_bounds__(kPThreads, 1) void k_prefill_down(int T, ExpertsDev routed,
+__global__ __launch_bounds__(kPThreads, 2) void k_prefill_down(int T, ExpertsDev routed,
                                                                ExpertsDev shared,
                                                                uint8_t* __restrict__ ws) {
-  using Acc = TileAcc<kGBM, kGBN, 1, 4>;
+  using Acc = TileAcc<kGBM, kGBN, 1, 4, kGBK2>;
+  constexpr int LR = kGBK2 + kLdsPad;
   const PrefillLayout L = prefill_layout(T);
   int item, n;
   item_slice<kSlices2>(blockIdx.x, item, n);
@@ -522,25 +541,27 @@ __global__ __launch_bounds__(kPThreads, 1) void k_prefill_down(int T, ExpertsDev
   const size_t ee = e < kE ? (size_t)e : 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  __shared__ __align__(16) __bf16 sA[2][kGBM * kLdsRow];
-  __shared__ __align__(16) __bf16 sB[2][kGBN * kLdsRow];
+  __shared__ __align__(16) __bf16 sA[2][kGBM * LR];
+  __shared__ __align__(16) __bf16 sB[2][kGBN * LR];
   const uint16_t* hsrc = wsp<uint16_t>(ws, L.h);
   const uint4* ap =
       reinterpret_cast<const uint4*>(hsrc + (size_t)(rbase + min(tid >> 1, rows - 1)) * kI) +
-      4 * (tid & 1);
+      (kGBK2 / 16) * (tid & 1);
   const size_t wrow = ee * kH + (size_t)kGBN * n + tid;   // output column = row of w2
   const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w2 + wrow * (kI / 2) : X.w2 + wrow * kI * 2;
   const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w2s + wrow * (kI / 16) : nullptr;
-  GSlot<FMT> ring[kRingDepth<FMT>];
-  auto gload = [&](GSlot<FMT>& sl, int kt) {
+  GSlot<FMT, kGBK2> ring[kRingDepth<FMT>];
+  auto gload = [&](GSlot<FMT, kGBK2>& sl, int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sl.a[i] = ap[kt * 8 + i];
-    g_load_b<FMT>(sl, bcodes, bscales, kt);
+    for (int i = 0; i < kGBK2 / 16; ++i) sl.a[i] = ap[kt * (kGBK2 / 8) + i];
+    g_load_b<FMT, kGBK2>(sl, bcodes, bscales, kt);
   };
-  auto sstore = [&](const GSlot<FMT>& sl, int buf) { g_store<FMT>(sl, sA[buf], sB[buf], tid); };
+  auto sstore = [&](const GSlot<FMT, kGBK2>& sl, int buf) {
+    g_store<FMT, kGBK2>(sl, sA[buf], sB[buf], tid);
+  };
   Acc acc;
   acc.zero();
-  kpipeline<kRingDepth<FMT>, kI / kBK>(ring, gload, sstore,
+  kpipeline<kRingDepth<FMT>, kI / kGBK2>(ring, gload, sstore,
                                        [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
   const float gl = FMT == FMT_NVFP4 ? X.glob[ee * 3 + 2] : 1.0f;
   __shared__ float s_wr[kGBM];                          // routing weight * global per row
