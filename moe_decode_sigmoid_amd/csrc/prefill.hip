@@ -167,13 +167,13 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, float s) {
   return make_uint4(pk(p0), pk(p1), pk(p2), pk(p3));
 }
 
-// BK NVFP4 codes of one row (BK / 32 uint4) with their BK / 16 block scales
-// (bytes of sc) -> BK bf16 in LDS.
-template <int BK>
-__device__ __forceinline__ void dequant_to_lds(__bf16* dst, const uint4 (&c)[BK / 32], uint32_t sc) {
+// E NVFP4 codes of one row (E / 32 uint4) with their E / 16 block scales
+// (bytes of sc) -> E bf16 in LDS.
+template <int E>
+__device__ __forceinline__ void dequant_to_lds(__bf16* dst, const uint4 (&c)[E / 32], uint32_t sc) {
   uint4* d = reinterpret_cast<uint4*>(dst);
 #pragma unroll
-  for (int i = 0; i < BK / 32; ++i) {
+  for (int i = 0; i < E / 32; ++i) {
     const float s0 = e4m3_sel(sc, 2 * i), s1 = e4m3_sel(sc, 2 * i + 1);
     d[4 * i + 0] = dequant8(c[i].x, s0);
     d[4 * i + 1] = dequant8(c[i].y, s0);
@@ -397,19 +397,27 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_positions(int T, uint8_t*
 }
 
 // ------------------------------------------------------------------ grouped GEMM stages
-// A stage: 128 rows x BK bf16 (thread -> row tid / 2, half tid % 2).
-// B stage: 256 rows x BK elements (thread -> row tid): NVFP4 BK / 2 code
-// bytes + BK / 16 scale bytes, or bf16 2 BK bytes.
-template <int FMT, int BK>
+// One pipeline stage of a grouped GEMM with NT threads: A = 128 rows x BK
+// bf16, TA = NT / 128 threads per row, EA elements each; B = 256 rows x BK
+// weights, TB = NT / 256 threads per row, EB elements each (NVFP4: EB / 2
+// code bytes + EB / 16 scale bytes; bf16: 2 EB bytes).
+template <int BK, int NT>
+struct GShape {
+  static constexpr int TA = NT / kGBM, TB = NT / kGBN;
+  static constexpr int EA = BK / TA, EB = BK / TB;
+  static constexpr int LR = BK + kLdsPad;       // LDS row pitch (bf16)
+};
+
+template <int FMT, int EA, int EB>
 struct GSlot;
-template <int BK>
-struct GSlot<FMT_NVFP4, BK> {
-  uint4 a[BK / 16], c[BK / 32];
+template <int EA, int EB>
+struct GSlot<FMT_NVFP4, EA, EB> {
+  uint4 a[EA / 8], c[EB / 32];
   uint32_t s;
 };
-template <int BK>
-struct GSlot<FMT_BF16, BK> {
-  uint4 a[BK / 16], b[BK / 8];
+template <int EA, int EB>
+struct GSlot<FMT_BF16, EA, EB> {
+  uint4 a[EA / 8], b[EB / 8];
 };
 template <int FMT>
 constexpr int kRingDepth = FMT == FMT_NVFP4 ? 4 : 2;
@@ -423,50 +431,60 @@ __device__ __forceinline__ void item_slice(int b, int& item, int& slice) {
   item = (b / (8 * NS)) * 8 + b % 8;
 }
 
-template <int FMT, int BK>
-__device__ __forceinline__ void g_load_b(GSlot<FMT, BK>& sl, const uint8_t* bcodes,
+// Stage kt of a thread's B share: bcodes / bscales already point at the
+// thread's first element of its row.
+template <int FMT, int BK, int EA, int EB>
+__device__ __forceinline__ void g_load_b(GSlot<FMT, EA, EB>& sl, const uint8_t* bcodes,
                                          const uint8_t* bscales, int kt) {
   if constexpr (FMT == FMT_NVFP4) {
     const uint4* cp = reinterpret_cast<const uint4*>(bcodes + (size_t)kt * (BK / 2));
 #pragma unroll
-    for (int i = 0; i < BK / 32; ++i) sl.c[i] = cp[i];
-    if constexpr (BK == 64)
+    for (int i = 0; i < EB / 32; ++i) sl.c[i] = cp[i];
+    if constexpr (EB == 64)
       sl.s = *reinterpret_cast<const uint32_t*>(bscales + (size_t)kt * (BK / 16));
     else
       sl.s = *reinterpret_cast<const uint16_t*>(bscales + (size_t)kt * (BK / 16));
   } else {
-    const uint4* bp = reinterpret_cast<const uint4*>(bcodes) + (size_t)kt * (BK / 8);
+    const uint4* bp = reinterpret_cast<const uint4*>(bcodes + (size_t)kt * BK * 2);
 #pragma unroll
-    for (int i = 0; i < BK / 8; ++i) sl.b[i] = bp[i];
+    for (int i = 0; i < EB / 8; ++i) sl.b[i] = bp[i];
   }
 }
 
-template <int FMT, int BK>
-__device__ __forceinline__ void g_store(const GSlot<FMT, BK>& sl, __bf16* sA, __bf16* sB, int tid) {
-  constexpr int LR = BK + kLdsPad;
-  const int ar = tid >> 1, ah = tid & 1;
+// A slot into LDS: A row tid / TA at column (tid % TA) EA; B row tid / TB at
+// column (tid % TB) EB, NVFP4 decoded to bf16.
+template <int FMT, int BK, int NT, int EA, int EB>
+__device__ __forceinline__ void g_store(const GSlot<FMT, EA, EB>& sl, __bf16* sA, __bf16* sB,
+                                        int tid) {
+  using G = GShape<BK, NT>;
+  __bf16* da = sA + (tid / G::TA) * G::LR + (tid % G::TA) * EA;
 #pragma unroll
-  for (int i = 0; i < BK / 16; ++i) st_lds16(sA + ar * LR + ah * (BK / 2) + 8 * i, sl.a[i]);
+  for (int i = 0; i < EA / 8; ++i) st_lds16(da + 8 * i, sl.a[i]);
+  __bf16* db = sB + (tid / G::TB) * G::LR + (tid % G::TB) * EB;
   if constexpr (FMT == FMT_NVFP4) {
-    dequant_to_lds<BK>(sB + tid * LR, sl.c, sl.s);
+    dequant_to_lds<EB>(db, sl.c, sl.s);
   } else {
 #pragma unroll
-    for (int i = 0; i < BK / 8; ++i) st_lds16(sB + tid * LR + 8 * i, sl.b[i]);
+    for (int i = 0; i < EB / 8; ++i) st_lds16(db + 8 * i, sl.b[i]);
   }
 }
 
 // ------------------------------------------------------------------ P4 GEMM 1
 // Work item (expert e, row m0) x column slice n (h columns [128 n, 128 n +
-// 128)): tile B row br is, for wave column br / 64 and block (br / 32) % 2,
-// the gate (block 0) or up (block 1) row 128 n + 32 (br / 64) + br % 32, so
-// each lane holds gate and up of the same h element.
+// 128)), 512 threads as 2 x 4 waves of 64 x 64: tile B row br is, for wave
+// column br / 64 and block (br / 32) % 2, the gate (block 0) or up (block 1)
+// row 128 n + 32 (br / 64) + br % 32, so each lane holds gate and up of the
+// same h element.  Two waves per SIMD: one's MFMAs run while the other
+// decodes weights or waits.
+constexpr int kGThreads1 = 512;
 template <int FMT>
-__global__ __launch_bounds__(kPThreads, 1) void k_prefill_gateup(const uint16_t* __restrict__ x,
-                                                                 int T, ExpertsDev routed,
-                                                                 ExpertsDev shared,
-                                                                 uint8_t* __restrict__ ws) {
-  using Acc = TileAcc<kGBM, kGBN, 1, 4, kGBK1>;
-  constexpr int LR = kGBK1 + kLdsPad;
+__global__ __launch_bounds__(kGThreads1, 1) void k_prefill_gateup(const uint16_t* __restrict__ x,
+                                                                  int T, ExpertsDev routed,
+                                                                  ExpertsDev shared,
+                                                                  uint8_t* __restrict__ ws) {
+  using Acc = TileAcc<kGBM, kGBN, 2, 4, kGBK1>;
+  using G = GShape<kGBK1, kGThreads1>;
+  using Slot = GSlot<FMT, G::EA, G::EB>;
   const PrefillLayout L = prefill_layout(T);
   int item, n;
   item_slice<kSlices1>(blockIdx.x, item, n);
@@ -479,27 +497,29 @@ __global__ __launch_bounds__(kPThreads, 1) void k_prefill_gateup(const uint16_t*
   const size_t ee = e < kE ? (size_t)e : 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  __shared__ __align__(16) __bf16 sA[2][kGBM * LR];
-  __shared__ __align__(16) __bf16 sB[2][kGBN * LR];
-  const int tok = wsp<int>(ws, L.perm)[rbase + min(tid >> 1, rows - 1)];
-  const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)tok * kH) + (kGBK1 / 16) * (tid & 1);
-  const int bwn = tid / 64, bj = (tid / 32) % 2, brr = tid % 32;
+  __shared__ __align__(16) __bf16 sA[2][kGBM * G::LR];
+  __shared__ __align__(16) __bf16 sB[2][kGBN * G::LR];
+  const int tok = wsp<int>(ws, L.perm)[rbase + min(tid / G::TA, rows - 1)];
+  const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)tok * kH) + (tid % G::TA) * (G::EA / 8);
+  const int brow = tid / G::TB, bcol = (tid % G::TB) * G::EB;
+  const int bwn = brow / 64, bj = (brow / 32) % 2, brr = brow % 32;
   const size_t wrow = (ee * 2 + bj) * kI + 128 * n + 32 * bwn + brr;   // row of w13
-  const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w13 + wrow * (kH / 2) : X.w13 + wrow * kH * 2;
-  const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w13s + wrow * (kH / 16) : nullptr;
-  GSlot<FMT, kGBK1> ring[kRingDepth<FMT>];
-  auto gload = [&](GSlot<FMT, kGBK1>& sl, int kt) {
+  const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w13 + wrow * (kH / 2) + bcol / 2
+                                           : X.w13 + (wrow * kH + bcol) * 2;
+  const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w13s + wrow * (kH / 16) + bcol / 16 : nullptr;
+  Slot ring[kRingDepth<FMT>];
+  auto gload = [&](Slot& sl, int kt) {
 #pragma unroll
-    for (int i = 0; i < kGBK1 / 16; ++i) sl.a[i] = ap[kt * (kGBK1 / 8) + i];
+    for (int i = 0; i < G::EA / 8; ++i) sl.a[i] = ap[kt * (kGBK1 / 8) + i];
     g_load_b<FMT, kGBK1>(sl, bcodes, bscales, kt);
   };
-  auto sstore = [&](const GSlot<FMT, kGBK1>& sl, int buf) {
-    g_store<FMT, kGBK1>(sl, sA[buf], sB[buf], tid);
+  auto sstore = [&](const Slot& sl, int buf) {
+    g_store<FMT, kGBK1, kGThreads1>(sl, sA[buf], sB[buf], tid);
   };
   Acc acc;
   acc.zero();
   kpipeline<kRingDepth<FMT>, kH / kGBK1>(ring, gload, sstore,
-                                       [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
+                                        [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
   // epilogue: h = SiLU(g * sg) * (u * su) -> bf16
   float sg = 1.0f, su = 1.0f;
   if constexpr (FMT == FMT_NVFP4) {
@@ -507,7 +527,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_prefill_gateup(const uint16_t*
     su = X.glob[ee * 3 + 1];
   }
   uint16_t* h = wsp<uint16_t>(ws, L.h);
-  const int hcol = 128 * n + 32 * wave + (lane & 31);
+  const int hcol = 128 * n + 32 * (wave % 4) + (lane & 31);
 #pragma unroll
   for (int i = 0; i < Acc::MB; ++i)
 #pragma unroll
@@ -522,13 +542,15 @@ __global__ __launch_bounds__(kPThreads, 1) void k_prefill_gateup(const uint16_t*
 
 // ------------------------------------------------------------------ P5 GEMM 2
 // Work item (expert e, row m0) x column slice n (256 of the 2048 outputs):
-// partial[row][col] = w_row * global * (h_row . D_e[col]) as fp16.
+// partial[row][col] = w_row * global * (h_row . D_e[col]) as fp16.  256
+// threads, 61 KB of LDS: two workgroups per CU.
 template <int FMT>
 __global__ __launch_bounds__(kPThreads, 2) void k_prefill_down(int T, ExpertsDev routed,
                                                                ExpertsDev shared,
                                                                uint8_t* __restrict__ ws) {
   using Acc = TileAcc<kGBM, kGBN, 1, 4, kGBK2>;
-  constexpr int LR = kGBK2 + kLdsPad;
+  using G = GShape<kGBK2, kPThreads>;
+  using Slot = GSlot<FMT, G::EA, G::EB>;
   const PrefillLayout L = prefill_layout(T);
   int item, n;
   item_slice<kSlices2>(blockIdx.x, item, n);
@@ -541,28 +563,30 @@ __global__ __launch_bounds__(kPThreads, 2) void k_prefill_down(int T, ExpertsDev
   const size_t ee = e < kE ? (size_t)e : 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  __shared__ __align__(16) __bf16 sA[2][kGBM * LR];
-  __shared__ __align__(16) __bf16 sB[2][kGBN * LR];
+  __shared__ __align__(16) __bf16 sA[2][kGBM * G::LR];
+  __shared__ __align__(16) __bf16 sB[2][kGBN * G::LR];
   const uint16_t* hsrc = wsp<uint16_t>(ws, L.h);
   const uint4* ap =
-      reinterpret_cast<const uint4*>(hsrc + (size_t)(rbase + min(tid >> 1, rows - 1)) * kI) +
-      (kGBK2 / 16) * (tid & 1);
-  const size_t wrow = ee * kH + (size_t)kGBN * n + tid;   // output column = row of w2
-  const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w2 + wrow * (kI / 2) : X.w2 + wrow * kI * 2;
-  const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w2s + wrow * (kI / 16) : nullptr;
-  GSlot<FMT, kGBK2> ring[kRingDepth<FMT>];
-  auto gload = [&](GSlot<FMT, kGBK2>& sl, int kt) {
+      reinterpret_cast<const uint4*>(hsrc + (size_t)(rbase + min(tid / G::TA, rows - 1)) * kI) +
+      (tid % G::TA) * (G::EA / 8);
+  const int bcol = (tid % G::TB) * G::EB;
+  const size_t wrow = ee * kH + (size_t)kGBN * n + tid / G::TB;   // output column = row of w2
+  const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w2 + wrow * (kI / 2) + bcol / 2
+                                           : X.w2 + (wrow * kI + bcol) * 2;
+  const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w2s + wrow * (kI / 16) + bcol / 16 : nullptr;
+  Slot ring[kRingDepth<FMT>];
+  auto gload = [&](Slot& sl, int kt) {
 #pragma unroll
-    for (int i = 0; i < kGBK2 / 16; ++i) sl.a[i] = ap[kt * (kGBK2 / 8) + i];
+    for (int i = 0; i < G::EA / 8; ++i) sl.a[i] = ap[kt * (kGBK2 / 8) + i];
     g_load_b<FMT, kGBK2>(sl, bcodes, bscales, kt);
   };
-  auto sstore = [&](const GSlot<FMT, kGBK2>& sl, int buf) {
-    g_store<FMT, kGBK2>(sl, sA[buf], sB[buf], tid);
+  auto sstore = [&](const Slot& sl, int buf) {
+    g_store<FMT, kGBK2, kPThreads>(sl, sA[buf], sB[buf], tid);
   };
   Acc acc;
   acc.zero();
   kpipeline<kRingDepth<FMT>, kI / kGBK2>(ring, gload, sstore,
-                                       [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
+                                        [&](int buf) { acc.mma(sA[buf], sB[buf], wave, lane); });
   const float gl = FMT == FMT_NVFP4 ? X.glob[ee * 3 + 2] : 1.0f;
   __shared__ float s_wr[kGBM];                          // routing weight * global per row
   if (tid < kGBM) s_wr[tid] = tid < rows ? wsp<float>(ws, L.wpos)[rbase + tid] * gl : 0.0f;
@@ -638,12 +662,12 @@ hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
   hipLaunchKernelGGL(k_prefill_positions, dim3(L.ntiles), dim3(kPThreads), 0, st, T, ws);
   const int items8 = (L.max_items + 7) / 8 * 8;
   if (fmt == FMT_NVFP4) {
-    hipLaunchKernelGGL(k_prefill_gateup<FMT_NVFP4>, dim3(items8 * kSlices1), dim3(kPThreads), 0, st,
+    hipLaunchKernelGGL(k_prefill_gateup<FMT_NVFP4>, dim3(items8 * kSlices1), dim3(kGThreads1), 0, st,
                        x, T, routed, shared, ws);
     hipLaunchKernelGGL(k_prefill_down<FMT_NVFP4>, dim3(items8 * kSlices2), dim3(kPThreads), 0, st,
                        T, routed, shared, ws);
   } else {
-    hipLaunchKernelGGL(k_prefill_gateup<FMT_BF16>, dim3(items8 * kSlices1), dim3(kPThreads), 0, st,
+    hipLaunchKernelGGL(k_prefill_gateup<FMT_BF16>, dim3(items8 * kSlices1), dim3(kGThreads1), 0, st,
                        x, T, routed, shared, ws);
     hipLaunchKernelGGL(k_prefill_down<FMT_BF16>, dim3(items8 * kSlices2), dim3(kPThreads), 0, st,
                        T, routed, shared, ws);
