@@ -50,7 +50,7 @@ constexpr int kLdsPad = 8;               // bf16 elements of padding per LDS row
 constexpr int kRBK = 64;                 // router GEMM: K per pipeline stage
 constexpr int kRLdsRow = kRBK + kLdsPad; //   and its LDS row pitch (bf16 elements)
 constexpr int kGBK1 = 64;                // GEMM 1 (gate/up): K per pipeline stage
-constexpr int kGBK2 = 32;                // GEMM 2 (down): K per pipeline stage
+constexpr int kGBK2 = 64;                // GEMM 2 (down): K per pipeline stage
 constexpr int kPTile = 32;               // router tile (tokens)
 constexpr int kGBM = 128;                // grouped GEMM rows per work item
 constexpr int kGBN = 256;                // grouped GEMM B rows per tile
@@ -542,14 +542,15 @@ __global__ __launch_bounds__(kGThreads1, 1) void k_prefill_gateup(const uint16_t
 
 // ------------------------------------------------------------------ P5 GEMM 2
 // Work item (expert e, row m0) x column slice n (256 of the 2048 outputs):
-// partial[row][col] = w_row * global * (h_row . D_e[col]) as fp16.  256
-// threads, 61 KB of LDS: two workgroups per CU.
+// partial[row][col] = w_row * global * (h_row . D_e[col]) as fp16.  512
+// threads as 2 x 4 waves, like GEMM 1.
+constexpr int kGThreads2 = 512;
 template <int FMT>
-__global__ __launch_bounds__(kPThreads, 2) void k_prefill_down(int T, ExpertsDev routed,
-                                                               ExpertsDev shared,
-                                                               uint8_t* __restrict__ ws) {
-  using Acc = TileAcc<kGBM, kGBN, 1, 4, kGBK2>;
-  using G = GShape<kGBK2, kPThreads>;
+__global__ __launch_bounds__(kGThreads2, 1) void k_prefill_down(int T, ExpertsDev routed,
+                                                                ExpertsDev shared,
+                                                                uint8_t* __restrict__ ws) {
+  using Acc = TileAcc<kGBM, kGBN, 2, 4, kGBK2>;
+  using G = GShape<kGBK2, kGThreads2>;
   using Slot = GSlot<FMT, G::EA, G::EB>;
   const PrefillLayout L = prefill_layout(T);
   int item, n;
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(kPThreads, 2) void k_prefill_down(int T, ExpertsDev
     g_load_b<FMT, kGBK2>(sl, bcodes, bscales, kt);
   };
   auto sstore = [&](const Slot& sl, int buf) {
-    g_store<FMT, kGBK2, kPThreads>(sl, sA[buf], sB[buf], tid);
+    g_store<FMT, kGBK2, kGThreads2>(sl, sA[buf], sB[buf], tid);
   };
   Acc acc;
   acc.zero();
@@ -664,12 +665,12 @@ hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
   if (fmt == FMT_NVFP4) {
     hipLaunchKernelGGL(k_prefill_gateup<FMT_NVFP4>, dim3(items8 * kSlices1), dim3(kGThreads1), 0, st,
                        x, T, routed, shared, ws);
-    hipLaunchKernelGGL(k_prefill_down<FMT_NVFP4>, dim3(items8 * kSlices2), dim3(kPThreads), 0, st,
+    hipLaunchKernelGGL(k_prefill_down<FMT_NVFP4>, dim3(items8 * kSlices2), dim3(kGThreads2), 0, st,
                        T, routed, shared, ws);
   } else {
     hipLaunchKernelGGL(k_prefill_gateup<FMT_BF16>, dim3(items8 * kSlices1), dim3(kGThreads1), 0, st,
                        x, T, routed, shared, ws);
-    hipLaunchKernelGGL(k_prefill_down<FMT_BF16>, dim3(items8 * kSlices2), dim3(kPThreads), 0, st,
+    hipLaunchKernelGGL(k_prefill_down<FMT_BF16>, dim3(items8 * kSlices2), dim3(kGThreads2), 0, st,
                        T, routed, shared, ws);
   }
   const int nthr = T * (kH / 8);
