@@ -12,25 +12,34 @@
 //
 //   A  router GEMV, one expert row per workgroup (the 4 waves split the 2048
 //      columns) -> logit slots; the shared expert's gate/up rows 2g, 2g+1
-//      (routing-independent) -> h.
+//      (routing-independent) -> h; the shared expert's down rows of the
+//      workgroup's 8 outputs are fetched.
 //   B  every workgroup waits for the 256 x B logits and repeats the sigmoid /
 //      top-6 / renormalisation / dispatch itself (identical result everywhere,
-//      no extra round trip); it fetches the first down rows of its step-C
-//      work; the routed experts' gate/up row pairs, cut into 256 contiguous
-//      ranges, SiLU(g) * u -> h; then it counts in on an h-ready counter.
-//   C  once all h is in: the down GEMV of the workgroup's 8 output rows over
-//      every entry (shared + routed), weighted by the routing, summed in a
-//      fixed order, rounded once to bf16.
+//      no extra round trip): touched experts become entries in ascending id,
+//      and each (entry, token) pair a slot of a compact h array (routed
+//      pairs first, then the shared expert's).  The routed gate/up row pairs,
+//      cut into 256 contiguous ranges, give SiLU(g) * u per token; the
+//      workgroup writes its h once, as bf16, then counts in on an h-ready
+//      counter.
+//   C  once all h is in: the 7 B h pairs are copied to LDS, then the down GEMV
+//      of the workgroup's 8 output rows over every entry (wave w takes routed
+//      entries a = w - 1 mod 4 and the shared expert's tokens w, w + 4),
+//      weighted by the routing, summed in a fixed order, rounded once to bf16.
 //
 // Hand-over between workgroups uses only device-coherent accesses (relaxed
 // agent-scope atomics: no cache write-back or invalidation):
 //  - call epoch: workgroup g keeps a private counter in the workspace; every
 //    call adds one, so all counters agree (the workspace starts zeroed).
-//  - logits: 8-byte slots {fp32 value, epoch}, one store each; readers poll
-//    the slots until their epoch matches.
-//  - h: plain coherent stores; after waiting for its stores a workgroup adds
-//    1 to h-ready counter g % 64 (one 128-byte line each, so only 4 adds meet
-//    on a line); readers poll the 64 counters until each holds 4 * epoch.
+//  - logits: 8-byte slots {fp32 value, epoch} in kLogitReps copies; readers
+//    poll copy g % kLogitReps until the epochs match.
+//  - h: coherent stores; after waiting for them a workgroup adds 1 to
+//    h-ready counter g % 64 of each of kBankReps copies (one 128-byte line
+//    each); readers poll the 64 counters of copy g % kBankReps until each
+//    holds 4 * epoch.
+// A wave's loads and stores complete in issue order, so the kernel keeps
+// stores out of the way of loads it waits for: h is staged in LDS and stored
+// in one go, and the polling wave issues its prefetches after its wait.
 // Every wait is bounded (tens of ms); on time-out the workgroup sets the
 // workspace error word and carries on, so the kernel always terminates.
 // Results are reproducible bit for bit (fixed summation orders, no atomics
