@@ -221,6 +221,48 @@ def test_timed_entry_point_matches_and_times_the_kernel():
         assert 0.0 < ms < 50.0, ms
 
 
+def test_layer_stack_in_a_hip_graph_matches_eager_and_oracle():
+    """A stack of distinct layers captured in one HIP graph (the 47-layer
+    configuration, here 4 layers): every replay, with eager work between
+    replays, equals the eager pass bit for bit, and each layer matches the
+    oracle."""
+    nl, B = 4, 1
+    host = [testgen.make_layer(1, l, "nvfp4") for l in range(nl)]
+    dev = [moe.DeviceLayer.from_host(h) for h in host]
+    x = testgen.make_x(21, B)
+    xd = moe.device.to_device_bf16(x)
+    outs = torch.empty((nl, B, 2048), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((nl, B, 6), dtype=torch.int32, device="cuda")
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(B))
+
+    def one_pass():
+        for l, d in enumerate(dev):
+            moe.moe_decode_forward(xd, d.router, d.routed, d.shared, outs[l], ws, ids[l])
+
+    one_pass()
+    torch.cuda.synchronize()
+    eager = outs.clone()
+    ids_h = ids.cpu().numpy()
+    for l in range(nl):
+        y_or, ids_or, w_or, gap = oracle.forward_layer(x, host[l])
+        y_ref = parity.resolve_near_ties(x, host[l], ids_h[l], y_or, ids_or, w_or, gap, [])
+        parity.check_output(parity.bf16_out_to_f64(eager[l]), y_ref, f"stack layer {l}")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            one_pass()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        outs.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, eager), f"replay {rep}"
+        one_pass()                                   # eager work between replays
+        torch.cuda.synchronize()
+    assert int(ws[8:12].view(torch.int32).item()) == 0
+
+
 def test_workspace_error_word_stays_clear():
     """Byte offset 8 of the workspace is the device-side wait time-out flag."""
     ws = moe.alloc_workspace(moe.moe_workspace_bytes(8))
