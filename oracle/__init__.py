@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(_Experts), vp, vp, vp, vp, vp]
         L.or_forward_dense.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp,
                                        ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), vp]
+        L.or_gemv_nvfp4.argtypes = [vp, i32, i32, i32, vp, vp, f32, vp]
         L.or_num_threads.restype = ctypes.c_int
         L.or_set_num_threads.argtypes = [ctypes.c_int]
         _LIB = L
@@ -201,6 +202,20 @@ def forward_dense(x: np.ndarray, router: np.ndarray, routed, shared, k: int, I: 
 def forward_layer(x: np.ndarray, layer, forced_ids=None):
     """Convenience: the layer for an input generator Layer object."""
     return forward(x, layer.router, layer.routed, layer.shared, layer.K, layer.I, forced_ids)
+
+
+# ----------------------------------------------------------------- dense GEMV
+def gemv_nvfp4(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, glob: float) -> np.ndarray:
+    """x u16 [B, K]; codes u8 [N, K/2]; scales u8 [N, K/16] -> fp64 [B, N] = x . W^T."""
+    x = np.ascontiguousarray(x, np.uint16)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    B, K = x.shape
+    N = codes.shape[0]
+    assert codes.shape == (N, K // 2) and scales.shape == (N, K // 16)
+    out = np.empty((B, N), np.float64)
+    lib().or_gemv_nvfp4(_p(x), B, K, N, _p(codes), _p(scales), glob, _p(out))
+    return out
 
 
 def num_threads() -> int:

@@ -346,6 +346,30 @@ void or_forward_dense(const or_shape* S, const uint16_t* xb, int32_t B, const ui
   free(w);
 }
 
+/* ------------------------------------------------------------------ dense GEMV */
+
+/* Small-batch dense GEMV on packed NVFP4 weights, the kernel the pages list
+ * for the non-expert projections ("Day-0 Support for Flint on vLLM",
+ * Optimization section, Fig. 2 change list): y[t][n] = sum_k W[n][k] x[t][k]
+ * with W at its exact fp64 value e2m1 * e4m3 * global, k ascending.
+ * x bf16 [B][K]; codes u8 [N][K/2]; scales u8 [N][K/16]; y fp64 [B][N]. */
+void or_gemv_nvfp4(const uint16_t* x, int32_t B, int32_t K, int32_t N, const uint8_t* codes,
+                   const uint8_t* scales, float global, double* y) {
+  or_tables();
+  #pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t t = 0; t < B; ++t) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        uint8_t byte = codes[n * (K / 2) + k / 2];
+        uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
+        double w = g_e2m1[nib] * g_e4m3[scales[n * (K / 16) + k / 16]] * (double)global;
+        acc += w * or_bf16(x[t * K + k]);
+      }
+      y[t * N + n] = acc;
+    }
+}
+
 int or_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -19,7 +19,7 @@ HERE = pathlib.Path(__file__).resolve().parent
 _LIB = None
 
 # Tensor ids of the random streams.
-T_ROUTER, T_GATE, T_UP, T_DOWN, T_X = 0, 1, 2, 3, 4
+T_ROUTER, T_GATE, T_UP, T_DOWN, T_X, T_DENSE = 0, 1, 2, 3, 4, 5
 
 HIDDEN, INTER, N_EXPERTS, TOP_K = 2048, 512, 256, 6
 SIGMA_W = 0.02
@@ -120,6 +120,13 @@ def make_router(seed: int, layer: int, E: int = N_EXPERTS, H: int = HIDDEN,
     out = np.empty((E, H), np.uint16)
     lib().tg_make_router(seed, layer, E, H, sigma, _p(out))
     return out
+
+
+def make_dense(seed: int, layer: int, which: int, N: int, K: int, sigma: float = SIGMA_W):
+    """A dense [N, K] weight ~ N(0, sigma) (bf16), packed to NVFP4: (codes u8 [N, K/2],
+    scales u8 [N, K/16], global f32).  `which` tells apart matrices of one layer."""
+    w = normal_bf16(seed, layer, which, T_DENSE, sigma, N * K).reshape(N, K)
+    return quantize_nvfp4(w)
 
 
 @dataclasses.dataclass

@@ -15,7 +15,7 @@ from scipy.special import expit
 
 import oracle
 import testgen
-from tests.helpers import bf16_bits_to_f32, f32_to_bf16_bits_exact
+from tests.helpers import bf16_bits_to_f32, f32_to_bf16_bits_exact, load_table
 
 H, I, E, K = 32, 16, 8, 2
 
@@ -272,3 +272,64 @@ def test_nvfp4_layer_equals_bf16_layer_on_grid_weights():
     y_bf, ids_bf, _, _ = oracle.forward(x, L.router, bf(slice(0, E)), bf(slice(E, E + 1)), K, I)
     np.testing.assert_array_equal(ids_nv, ids_bf)
     np.testing.assert_array_equal(y_nv, y_bf)
+
+
+# ----------------------------------------------------------------- dense NVFP4 GEMV
+def _spec_decode(codes, scales, glob):
+    """W [N, K] decoded in the test from the hand-written OCP tables (not the oracle)."""
+    e2m1 = load_table("e2m1_values.txt")
+    e4m3 = load_table("e4m3_values.txt")
+    N, half = codes.shape
+    K = half * 2
+    W = np.empty((N, K), np.float64)
+    for n in range(N):
+        for k in range(K):
+            byte = int(codes[n, k // 2])
+            nib = (byte >> 4) if (k & 1) else (byte & 15)
+            W[n, k] = e2m1[nib] * e4m3[int(scales[n, k // 16])] * glob
+    return W
+
+
+def _finite_scale_bytes(rng, shape):
+    """Scale bytes drawn from the hand-written E4M3 table's finite entries."""
+    table = load_table("e4m3_values.txt")
+    ok = np.array(sorted(b for b, v in table.items() if v == v), np.uint8)
+    return rng.choice(ok, size=shape).astype(np.uint8)
+
+
+def test_gemv_one_hot_input_reads_one_decoded_column():
+    """x = e_c gives y[n] = W[n][c] exactly, with W from the spec tables."""
+    rng = np.random.default_rng(5)
+    N, K = 11, 64
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = _finite_scale_bytes(rng, (N, K // 16))
+    glob = 0.75
+    W = _spec_decode(codes, scales, glob)
+    for c in (0, 1, 17, 62, 63):
+        x = np.zeros((1, K), np.uint16)
+        x[0, c] = 0x3F80                                   # bf16 1.0
+        y = oracle.gemv_nvfp4(x, codes, scales, glob)
+        np.testing.assert_array_equal(y[0], W[:, c])
+
+
+@pytest.mark.parametrize("N,K,B", [(7, 32, 1), (40, 96, 3), (5, 256, 8)])
+def test_gemv_matches_spec_decode_times_numpy(N, K, B):
+    """Against numpy's product of the spec-table decode (a non-square W catches a
+    transposed operand, random bytes a wrong nibble or scale index)."""
+    rng = np.random.default_rng(N * K + B)
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = _finite_scale_bytes(rng, (N, K // 16))
+    glob = 2.0 ** -7
+    x = testgen.make_x(N + K, B, K)
+    y = oracle.gemv_nvfp4(x, codes, scales, glob)
+    ref = bf16_bits_to_f32(x).astype(np.float64) @ _spec_decode(codes, scales, glob).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-300)
+
+
+def test_gemv_is_linear_in_the_global_scale_and_rows_are_independent():
+    c, s, g = testgen.make_dense(2, 0, 3, 24, 128)
+    x = testgen.make_x(9, 2, 128)
+    y = oracle.gemv_nvfp4(x, c, s, g)
+    np.testing.assert_array_equal(oracle.gemv_nvfp4(x, c, s, 2.0 * g), 2.0 * y)
+    perm = np.random.default_rng(1).permutation(24)
+    np.testing.assert_array_equal(oracle.gemv_nvfp4(x, c[perm].copy(), s[perm].copy(), g), y[:, perm])
