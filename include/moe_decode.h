@@ -142,6 +142,22 @@ moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32
                                     float* w_out, void* ws, size_t ws_bytes, void* stream,
                                     void* ev_start, void* ev_stop);
 
+/* Small-batch dense GEMV on packed NVFP4 weights, for the non-expert
+ * projections and the dense MLP of the first two layers (Optimization
+ * section, Fig. 2 change list: a dense GEMV on the packed weights; Model
+ * architecture section: layers 0 and 1 use a dense MLP):
+ *   y[t][n] = global * sum_k e2m1(codes[n][k]) * e4m3(scales[n][k / 16]) * x[t][k]
+ * with fp32 accumulation and y rounded once to bf16.  The weight uses the
+ * expert tensors' packing (element 2j in the low nibble of byte j, one E4M3
+ * scale per 16 consecutive k, one fp32 tensor scale).
+ *   x       bf16 [B][K], 16-byte aligned      codes  u8 [N][K/2], 16-byte aligned
+ *   scales  u8 [N][K/16], 2-byte aligned      global f32 [1] (device)
+ *   y       bf16 [B][N] (written; must not overlap x)
+ * B = 1..8, K a multiple of 32, N >= 1; K > 8192 or B * K > 32768 returns
+ * MOE_ERR_UNSUPPORTED.  Needs no workspace; stream-ordered, no sync. */
+moe_status moe_nvfp4_gemv(const void* x, int32_t B, int32_t K, int32_t N, const void* codes,
+                          const void* scales, const float* global, void* y, void* stream);
+
 /* The same layer for T >= 1 tokens at prefill sizes (Optimization section:
  * the MoE kernels were also the largest prefill gain, measured on an
  * 8,192-token prefill): tokens are grouped by expert and each expert runs as

@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_forward.restype = ctypes.c_int
         L.moe_decode_forward.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp, vp,
                                          vp, vp, sz, vp]
+        L.moe_nvfp4_gemv.restype = ctypes.c_int
+        L.moe_nvfp4_gemv.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.moe_decode_forward_timed.restype = ctypes.c_int
         L.moe_decode_forward_timed.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp,
                                                vp, vp, vp, sz, vp, vp, vp]
@@ -165,6 +167,17 @@ def moe_decode_forward_timed(x, router_w, routed, shared, out, ws, ev_start, ev_
                                         ctypes.c_void_p(ev_start.cuda_event),
                                         ctypes.c_void_p(ev_stop.cuda_event))
     _check(st, "moe_decode_forward_timed")
+
+
+def moe_nvfp4_gemv(x, codes, scales, glob, y, stream=None, B: int | None = None):
+    """Dense NVFP4 GEMV: x bf16 [B, K], codes u8 [N, K/2], scales u8 [N, K/16],
+    glob f32 [1] (device) -> y bf16 [B, N]."""
+    B = x.shape[0] if B is None else B
+    K = x.shape[-1]
+    N = codes.shape[0]
+    st = lib().moe_nvfp4_gemv(_ptr(x), B, K, N, _ptr(codes), _ptr(scales), _ptr(glob), _ptr(y),
+                              _stream(stream))
+    _check(st, "moe_nvfp4_gemv")
 
 
 def moe_prefill_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_out=None,

@@ -6,7 +6,7 @@ import subprocess
 HERE = pathlib.Path(__file__).resolve().parent
 CSRC = HERE / "csrc"
 LIB = HERE / "libmoe_decode.so"
-SOURCES = ["capi.hip", "decode.hip", "decode_fused.hip", "prefill.hip"]
+SOURCES = ["capi.hip", "decode.hip", "decode_fused.hip", "prefill.hip", "gemv.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

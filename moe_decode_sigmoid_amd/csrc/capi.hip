@@ -229,4 +229,22 @@ moe_status moe_nvfp4_dequant(const moe_shape* shape, const moe_experts* set, int
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+moe_status moe_nvfp4_gemv(const void* x, int32_t B, int32_t K, int32_t N, const void* codes,
+                          const void* scales, const float* global, void* y, void* stream) {
+  moe_status st;
+  if ((st = check_ptr(x)) != MOE_OK) return st;
+  if ((st = check_ptr(codes)) != MOE_OK) return st;
+  if ((st = check_ptr(scales, 2)) != MOE_OK) return st;
+  if ((st = check_ptr(global, 4)) != MOE_OK) return st;
+  if ((st = check_ptr(y, 2)) != MOE_OK) return st;
+  if (B < 1 || N < 1 || K < 32 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (B > moe::kMaxB || K > moe::kGemvMaxK || B * K > moe::kGemvMaxBK) return MOE_ERR_UNSUPPORTED;
+  if (overlap(y, (size_t)B * N * 2, x, (size_t)B * K * 2)) return MOE_ERR_INVALID_ARG;
+  hipError_t e = moe::launch_nvfp4_gemv(B, K, N, static_cast<const uint16_t*>(x),
+                                        static_cast<const uint8_t*>(codes),
+                                        static_cast<const uint8_t*>(scales), global,
+                                        static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 }  // extern "C"

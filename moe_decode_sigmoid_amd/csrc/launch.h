@@ -24,6 +24,13 @@ hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t
                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
+// Dense NVFP4 GEMV, B = 1..8, K % 32 == 0, K <= 8192, B * K <= 32768.
+constexpr int kGemvMaxK = 8192;
+constexpr int kGemvMaxBK = 32768;                  // x staged in LDS: B * K * 2 bytes <= 64 KiB
+hipError_t launch_nvfp4_gemv(int B, int K, int N, const uint16_t* x, const uint8_t* codes,
+                             const uint8_t* scales, const float* glob, uint16_t* y,
+                             hipStream_t st);
+
 // Parity probe: one NVFP4 tensor [rows][cols] decoded to fp32.
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob, int rows,
                           int cols, float* out, hipStream_t st);

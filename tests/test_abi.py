@@ -19,7 +19,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["moe_decode_route", "moe_decode_forward", "moe_decode_forward_timed",
-              "moe_prefill_forward",
+              "moe_prefill_forward", "moe_nvfp4_gemv",
               "moe_nvfp4_dequant", "moe_workspace_bytes", "moe_status_string",
               "moe_abi_version"]:
         assert n in names
@@ -114,6 +114,30 @@ def test_timed_forward_needs_both_events_and_checks_like_forward():
     assert call(A, None) == moe.MOE_ERR_INVALID_ARG
     assert call(A, A, x=None) == moe.MOE_ERR_INVALID_ARG
     assert call(A, A, B=9) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_gemv_argument_errors():
+    fn = moe.lib().moe_nvfp4_gemv
+
+    def call(x=A, B=1, K=2048, N=64, codes=A + 0x1000000, scales=A + 0x2000000,
+             glob=A + 0x3000000, y=A + 0x4000000):
+        return fn(x, B, K, N, codes, scales, glob, y, 0)
+    E = moe
+    assert call(x=None) == E.MOE_ERR_INVALID_ARG
+    assert call(codes=None) == E.MOE_ERR_INVALID_ARG
+    assert call(y=None) == E.MOE_ERR_INVALID_ARG
+    assert call(glob=None) == E.MOE_ERR_INVALID_ARG
+    assert call(x=A + 8) == E.MOE_ERR_MISALIGNED
+    assert call(codes=A + 0x1000008) == E.MOE_ERR_MISALIGNED
+    assert call(scales=A + 0x2000001) == E.MOE_ERR_MISALIGNED
+    assert call(B=0) == E.MOE_ERR_INVALID_ARG
+    assert call(N=0) == E.MOE_ERR_INVALID_ARG
+    assert call(K=48) == E.MOE_ERR_INVALID_ARG                 # not a multiple of 32
+    assert call(K=0) == E.MOE_ERR_INVALID_ARG
+    assert call(B=9) == E.MOE_ERR_UNSUPPORTED
+    assert call(K=16384) == E.MOE_ERR_UNSUPPORTED
+    assert call(B=8, K=8192) == E.MOE_ERR_UNSUPPORTED          # x no longer fits LDS
+    assert call(y=A + 64) == E.MOE_ERR_INVALID_ARG             # y overlaps x
 
 
 def test_decode_batch_limit_is_unsupported_not_invalid():
