@@ -107,6 +107,56 @@ def layer_bytes(n_experts_read: int, B: int, fmt: str) -> int:
     return n_experts_read * per + ROUTER_BYTES + 2 * B * H * 2
 
 
+# the non-expert projections of one attention block: fused q/k/v (32 query + 2 x 4
+# key/value heads of 128 over hidden 2048) and the output projection
+DENSE_SHAPES = {"qkv_proj": (5120, 2048), "o_proj": (2048, 4096)}
+
+
+def dense_bytes(N: int, K: int, B: int) -> int:
+    """HBM bytes one GEMV must move: codes + E4M3 scales + global, x in, y out."""
+    return N * K // 2 + N * K // 16 + 4 + 2 * B * K + 2 * B * N
+
+
+def run_dense(args, moe, testgen, torch, dev) -> dict:
+    """Each projection at batch 1 and 8: one graph of `layers` launches over as
+    many weight copies (so no launch finds its weights in cache), timed by HIP
+    events around the replays."""
+    out = {}
+    for name, (N, K) in DENSE_SHAPES.items():
+        codes, scales, glob = testgen.make_dense(args.seed, 0, 90 + len(out), N, K)
+        c0, s0 = torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev)
+        ws = [(c0.clone(), s0.clone()) for _ in range(args.layers)]
+        g0 = torch.tensor([glob], dtype=torch.float32, device=dev)
+        del c0, s0
+        for B in (1, 8):
+            x = moe.device.to_device_bf16(testgen.make_x(args.seed, B, K), dev)
+            y = torch.empty((args.layers, B, N), dtype=torch.bfloat16, device=dev)
+            for l, (c, sc) in enumerate(ws):
+                moe.moe_nvfp4_gemv(x, c, sc, g0, y[l])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for l, (c, sc) in enumerate(ws):
+                    moe.moe_nvfp4_gemv(x, c, sc, g0, y[l])
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000 / (args.steps * args.layers)
+            nb = dense_bytes(N, K, B)
+            out[f"{name}_b{B}"] = dict(N=N, K=K, B=B, us_per_launch=round(us, 3),
+                                       bytes_per_launch=nb, gbps=round(nb / (us * 1e-6) / 1e9, 1))
+            log(f"dense {name} [{N}x{K}] B={B}: {us:.2f} us, {nb / (us * 1e-6) / 1e9:.0f} GB/s")
+            del g
+        del ws
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,8 +168,10 @@ def main() -> int:
     ap.add_argument("--no-batch8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate host time spent on the oracle baseline (0 = skip)")
-    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill", "copy"],
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "decode", "prefill", "dense", "copy"],
                     help="decode = the 47-layer stack only; prefill = the 8192-token layer only; "
+                         "dense = the NVFP4 attention-projection GEMVs only; "
                          "copy = a plain 1 GiB device copy (reference for the traffic counters)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--traffic-record", nargs=4, metavar="CSV",
@@ -154,6 +206,9 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "copies": 3}))
         return 0
     fmt = args.fmt
+    if args.workload == "dense":
+        print(json.dumps({"dense_gemv": run_dense(args, moe, testgen, torch, dev)}), flush=True)
+        return 0
     L = 1 if args.workload == "prefill" else args.layers
 
     # ---------------------------------------------------------------- weights
@@ -250,7 +305,7 @@ def main() -> int:
         return dict(tokens=T, ms_per_layer=ms, tflops=tf, mfma_util=tf / PEAK_BF16_TFLOPS,
                     flop=prefill_flop(T))
 
-    r1 = r8 = rp = None
+    r1 = r8 = rp = rd = None
     if args.workload in ("all", "decode"):
         r1 = run_batch(1)
         log(f"B=1: {r1['us_per_layer']:.2f} us/layer, {r1['gbps']:.0f} GB/s")
@@ -261,6 +316,8 @@ def main() -> int:
         rp = run_prefill()
         log(f"prefill {rp['tokens']} tokens: {rp['ms_per_layer']:.3f} ms/layer, "
             f"{rp['tflops']:.0f} TFLOP/s ({100 * rp['mfma_util']:.1f}% of bf16 peak)")
+    if args.workload == "all":
+        rd = run_dense(args, moe, testgen, torch, dev)
     if r1 is None:
         print(json.dumps({"prefill": rp}), flush=True)
         return 0
@@ -310,7 +367,8 @@ def main() -> int:
                    "hidden": H, "inter": I, "experts": E, "top_k": K, "shared": 1,
                    "layers": L, "batch": 1, "weight_format": fmt,
                    "resident_weight_bytes": int(resident)},
-        "batch1": r1, "batch8": r8, "prefill": rp, "roofline": roof, "cpu_baseline": cpu,
+        "batch1": r1, "batch8": r8, "prefill": rp, "dense_gemv": rd,
+        "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
     return 0
