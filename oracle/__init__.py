@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.or_forward_dense.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp,
                                        ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), vp]
         L.or_gemv_nvfp4.argtypes = [vp, i32, i32, i32, vp, vp, f32, vp]
+        L.or_bf16_rne.restype = ctypes.c_uint16
+        L.or_bf16_rne.argtypes = [d]
+        L.or_bf16_rne_array.argtypes = [vp, i64, vp]
+        L.or_rmsnorm_bf16.argtypes = [vp, i32, i32, vp, d, vp]
         L.or_num_threads.restype = ctypes.c_int
         L.or_set_num_threads.argtypes = [ctypes.c_int]
         _LIB = L
@@ -216,6 +220,43 @@ def gemv_nvfp4(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, glob: float
     out = np.empty((B, N), np.float64)
     lib().or_gemv_nvfp4(_p(x), B, K, N, _p(codes), _p(scales), glob, _p(out))
     return out
+
+
+# ----------------------------------------------------------------- RMSNorm + residual
+def bf16_rne(v) -> np.ndarray:
+    """fp64 values rounded once to bf16 (ties to even) -> u16 bit patterns."""
+    a = np.ascontiguousarray(np.asarray(v, np.float64))
+    out = np.empty(a.shape, np.uint16)
+    lib().or_bf16_rne_array(_p(a), a.size, _p(out))
+    return out
+
+
+def rmsnorm_bf16(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """x u16 [T, H], w u16 [H] -> u16 [T, H]: x * w / sqrt(mean x^2 + eps), rounded to bf16."""
+    x = np.ascontiguousarray(x, np.uint16)
+    w = np.ascontiguousarray(w, np.uint16)
+    T, H = x.shape
+    assert w.shape == (H,)
+    out = np.empty((T, H), np.uint16)
+    lib().or_rmsnorm_bf16(_p(x), T, H, _p(w), float(eps), _p(out))
+    return out
+
+
+def forward_fused(x: np.ndarray, layer, norm_w=None, eps: float = 0.0, residual=None,
+                  xn=None, forced_ids=None):
+    """The layer with its neighbours fused: out = residual + layer(rmsnorm(x)).
+    norm_w None skips the norm; residual None adds nothing.  xn, when given,
+    replaces the oracle's own normalised input (u16 [B, H]), so that routing
+    decisions can be taken on the same bf16 input as another implementation.
+    Returns (out f64 [B, H], ids, w, gap, the normalised input u16 [B, H])."""
+    x = np.ascontiguousarray(x, np.uint16)
+    if xn is None:
+        xn = rmsnorm_bf16(x, norm_w, eps) if norm_w is not None else x
+    y, ids, w, gap = forward_layer(xn, layer, forced_ids)
+    if residual is not None:
+        r = np.ascontiguousarray(residual, np.uint16).astype(np.uint32) << 16
+        y = y + r.view(np.float32).astype(np.float64)
+    return y, ids, w, gap, xn
 
 
 def num_threads() -> int:

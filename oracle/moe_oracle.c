@@ -19,6 +19,9 @@
  *    sparse evaluation of the dense masked sum (pinned by or_forward_dense).
  *  - Optimization section: the SiLU kernels (SiLU-gated expert FFN).
  *  - Optimization section, low-latency path: routing and the expert combine.
+ *  - Optimization section, low-latency path: the pre-MoE RMSNorm and the
+ *    residual add fused into the adjacent GEMVs (or_rmsnorm_bf16; the
+ *    residual is a plain fp64 addition done by the Python wrapper).
  *  - Inkling-2-Small article, 48-layer MoE section: NVFP4 blocks of 16 with
  *    an FP4 maximum of 6; accuracy section: the router is kept in FP32 (the
  *    oracle keeps it in fp64).
@@ -368,6 +371,56 @@ void or_gemv_nvfp4(const uint16_t* x, int32_t B, int32_t K, int32_t N, const uin
       }
       y[t * N + n] = acc;
     }
+}
+
+/* ------------------------------------------------------------------ RMSNorm */
+
+/* Round an fp64 value once to bf16 (round to nearest, ties to even), from the
+ * format's definition: bf16 keeps 8 significant bits (7 stored) with fp32's
+ * exponent range, so the value is snapped to the grid 2^(e - 7) of its
+ * binade (2^-133 below the smallest normal 2^-126) with rint() in the default
+ * ties-to-even mode; the snapped value has at most 9 significant bits, so it
+ * converts to fp32 exactly and bf16 is its upper half.  Overflow gives inf. */
+uint16_t or_bf16_rne(double v) {
+  if (v != v) return 0x7FC0;
+  const uint16_t sign = signbit(v) ? 0x8000 : 0;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e = 0;
+  (void)frexp(a, &e);                              /* a = m 2^e, m in [0.5, 1) */
+  const int lead = e - 1;                          /* exponent of the leading bit */
+  const int qexp = lead >= -126 ? lead - 7 : -133; /* grid spacing 2^qexp */
+  const double r = ldexp(rint(ldexp(a, -qexp)), qexp);
+  const float f = (float)r;                        /* exact, or inf on overflow */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(sign | (u >> 16));
+}
+
+void or_bf16_rne_array(const double* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_bf16_rne(v[i]);
+}
+
+/* The pre-MoE RMSNorm that the pages' low-latency path fuses into the
+ * adjacent GEMVs ("Day-0 Support for Flint on vLLM", Optimization section,
+ * low-latency MoE path and Fig. 3; the norm kernels are one of the Fig. 2
+ * steps): xn[k] = x[k] * w[k] / sqrt(mean_j x[j]^2 + eps), in fp64 with the
+ * sum over j in index order, then rounded once to bf16, since the router and
+ * the experts take bf16 activations (Model architecture section, W4A16).
+ * x bf16 [T][H]; w bf16 [H]; xn bf16 [T][H]. */
+void or_rmsnorm_bf16(const uint16_t* x, int32_t T, int32_t H, const uint16_t* w, double eps,
+                     uint16_t* xn) {
+  #pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < H; ++k) {
+      const double v = or_bf16(x[t * H + k]);
+      ss += v * v;
+    }
+    const double r = 1.0 / sqrt(ss / (double)H + eps);
+    for (int64_t k = 0; k < H; ++k)
+      xn[t * H + k] = or_bf16_rne(or_bf16(x[t * H + k]) * or_bf16(w[k]) * r);
+  }
 }
 
 int or_num_threads(void) {

@@ -333,3 +333,111 @@ def test_gemv_is_linear_in_the_global_scale_and_rows_are_independent():
     np.testing.assert_array_equal(oracle.gemv_nvfp4(x, c, s, 2.0 * g), 2.0 * y)
     perm = np.random.default_rng(1).permutation(24)
     np.testing.assert_array_equal(oracle.gemv_nvfp4(x, c[perm].copy(), s[perm].copy(), g), y[:, perm])
+
+
+# ----------------------------------------------------------------- RMSNorm, residual
+def _bf16(v: float) -> int:
+    """bf16 bits of a value known to be exactly representable."""
+    b = int(f32_to_bf16_bits_exact(np.array([v], np.float32))[0])
+    assert float(f64(np.array([b], np.uint16))[0]) == v
+    return b
+
+
+def test_bf16_rounding_is_identity_on_every_finite_bf16():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    vals = f64(bits[finite])
+    assert np.array_equal(oracle.bf16_rne(vals), bits[finite])
+
+
+def test_bf16_rounding_ties_go_to_even_and_off_ties_to_nearest():
+    # 1 + 2^-8 lies halfway between 1 (mantissa 0, even) and 1 + 2^-7 (odd)
+    assert oracle.bf16_rne(1.0 + 2.0 ** -8) == 0x3F80
+    # 1 + 3 * 2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+    assert oracle.bf16_rne(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    assert oracle.bf16_rne(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
+    assert oracle.bf16_rne(-(1.0 + 2.0 ** -8 - 2.0 ** -40)) == 0xBF80
+    assert oracle.bf16_rne(-0.0) == 0x8000
+    # the largest finite bf16 is (2 - 2^-7) 2^127; beyond the last tie -> inf
+    assert oracle.bf16_rne((2 - 2.0 ** -7) * 2.0 ** 127) == 0x7F7F
+    assert oracle.bf16_rne((2 - 2.0 ** -8) * 2.0 ** 127) == 0x7F80
+    # subnormal grid 2^-133: 1.5 steps rounds to 2 steps (even), 2.5 to 2
+    assert oracle.bf16_rne(1.5 * 2.0 ** -133) == 0x0002
+    assert oracle.bf16_rne(2.5 * 2.0 ** -133) == 0x0002
+    assert oracle.bf16_rne(0.5 * 2.0 ** -133) == 0x0000
+
+
+def test_rmsnorm_worked_example():
+    # x = (3, 4): mean square 12.5, 1/sqrt(12.5) = 0.282842712...; so
+    # xn = (0.848528..., 1.131370...), which lie in [0.5, 1) and [1, 2) with bf16
+    # spacing 2^-8 and 2^-7: 217.2 and 144.8 steps -> 217 * 2^-8 and 145 * 2^-7.
+    x = np.array([[_bf16(3.0), _bf16(4.0)]], np.uint16)
+    w = np.array([_bf16(1.0), _bf16(1.0)], np.uint16)
+    got = f64(oracle.rmsnorm_bf16(x, w, 0.0))[0]
+    assert got.tolist() == [217 * 2.0 ** -8, 145 * 2.0 ** -7]
+
+
+def test_rmsnorm_of_a_constant_row_is_the_weight():
+    """mean of c^2 over the row is c^2: xn = sign(c) w exactly (eps = 0) for
+    any c and any row length; a wrong mean (sum, or a dropped square) fails."""
+    H = 48
+    w = np.array([_bf16(v) for v in [0.5, -1.25, 3.0, 0.0] * (H // 4)], np.uint16)
+    for c in [1.0, -2.0, 0.375, 40.0]:
+        x = np.full((1, H), _bf16(c), np.uint16)
+        got = f64(oracle.rmsnorm_bf16(x, w, 0.0))[0]
+        assert np.array_equal(got, np.sign(c) * f64(w)), c
+
+
+def test_rmsnorm_epsilon_sits_inside_the_root():
+    # x = 1 everywhere: 1 / sqrt(1 + 3) = 1/2 exactly
+    x = np.full((2, 16), _bf16(1.0), np.uint16)
+    w = np.full(16, _bf16(1.0), np.uint16)
+    assert np.all(f64(oracle.rmsnorm_bf16(x, w, 3.0)) == 0.5)
+    # x = 0 with eps > 0 gives 0, not NaN
+    z = np.zeros((1, 16), np.uint16)
+    assert np.all(f64(oracle.rmsnorm_bf16(z, w, 1e-6)) == 0.0)
+
+
+def test_rmsnorm_symmetries():
+    x = testgen.make_x(9, 3, 256)
+    w = testgen.make_x(10, 1, 256)[0]
+    base = f64(oracle.rmsnorm_bf16(x, w, 0.0))
+    # sign flip of x (bf16 sign bit) flips the output
+    assert np.array_equal(f64(oracle.rmsnorm_bf16(x ^ np.uint16(0x8000), w, 0.0)), -base)
+    # x scaled by a power of two (exponent field + 3) leaves it unchanged
+    assert np.array_equal(f64(oracle.rmsnorm_bf16(x + np.uint16(3 << 7), w, 0.0)), base)
+    # w scaled by 2 scales the output by 2 (the rounding commutes with it)
+    assert np.array_equal(f64(oracle.rmsnorm_bf16(x, w + np.uint16(1 << 7), 0.0)), 2 * base)
+    # rows are independent
+    assert np.array_equal(f64(oracle.rmsnorm_bf16(x[1:2], w, 0.0)), base[1:2])
+
+
+def test_fused_layer_reduces_to_the_plain_layer():
+    """x with entries +-1 has mean square 1, so with w = 1 and eps = 0 the norm
+    returns x itself and the fused layer is the plain one; a residual of zeros
+    adds nothing; a residual r adds r exactly (to fp64 rounding)."""
+    L = tiny_layer(seed=4)
+    rng = np.random.default_rng(3)
+    x = np.where(rng.random((3, H)) < 0.5, _bf16(1.0), _bf16(-1.0)).astype(np.uint16)
+    ones = np.full(H, _bf16(1.0), np.uint16)
+    y0, ids0, w0, _ = oracle.forward_layer(x, L)
+    y1, ids1, w1, _, xn = oracle.forward_fused(x, L, norm_w=ones, eps=0.0,
+                                               residual=np.zeros_like(x))
+    assert np.array_equal(xn, x)
+    assert np.array_equal(ids0, ids1) and np.array_equal(w0, w1)
+    assert np.array_equal(y0, y1)
+    r = testgen.make_x(12, 3, H)
+    y2 = oracle.forward_fused(x, L, norm_w=ones, eps=0.0, residual=r)[0]
+    assert np.allclose(y2 - y0, f64(r), rtol=0, atol=1e-12 * np.abs(y0).max())
+
+
+def test_fused_layer_normalises_before_routing():
+    """Scaling x by a power of two changes the plain layer but not the fused one."""
+    L = tiny_layer(seed=6)
+    x = testgen.make_x(13, 2, H)
+    w = testgen.make_x(14, 1, H)[0]
+    a = oracle.forward_fused(x, L, norm_w=w, eps=0.0)
+    b = oracle.forward_fused(x + np.uint16(2 << 7), L, norm_w=w, eps=0.0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert not np.array_equal(oracle.forward_layer(x, L)[0],
+                              oracle.forward_layer(x + np.uint16(2 << 7), L)[0])
