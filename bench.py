@@ -229,9 +229,13 @@ def main() -> int:
                                           for f in ("w13", "w2", "w13_scale", "w2_scale", "glob"))
                    for d in layers)
 
-    def run_batch(B: int) -> dict:
+    def run_batch(B: int, fused: bool = False) -> dict:
+        """fused: each layer also applies the pre-MoE RMSNorm to x and adds a
+        residual to its output, inside the same kernel."""
         x = testgen.make_x(args.seed, B)
         xd = moe.device.to_device_bf16(x, dev)
+        nw = moe.device.to_device_bf16(testgen.make_x(args.seed + 7, 1)[0], dev)
+        res = moe.device.to_device_bf16(testgen.make_x(args.seed + 8, B), dev)
         outs = torch.empty((L, B, H), dtype=torch.bfloat16, device=dev)
         ids = torch.empty((L, B, K), dtype=torch.int32, device=dev)
         ws = moe.alloc_workspace(moe.moe_workspace_bytes(B, fmt=fmt), dev)
@@ -239,8 +243,13 @@ def main() -> int:
 
         def one_pass(with_ids: bool):
             for l, d in enumerate(layers):
-                moe.moe_decode_forward(xd, d.router, d.routed, d.shared, outs[l], ws,
-                                       ids[l] if with_ids else None, None, S=S, B=B)
+                if fused:
+                    moe.moe_decode_forward_ex(xd, d.router, d.routed, d.shared, outs[l], ws,
+                                              norm_w=nw, eps=1e-5, residual=res,
+                                              ids_out=ids[l] if with_ids else None, S=S, B=B)
+                else:
+                    moe.moe_decode_forward(xd, d.router, d.routed, d.shared, outs[l], ws,
+                                           ids[l] if with_ids else None, None, S=S, B=B)
 
         one_pass(True)                                   # eager, records the routing
         torch.cuda.synchronize()
@@ -250,13 +259,15 @@ def main() -> int:
 
         # the kernel's own execution time per launch: start / end recorded by
         # the launch itself (hipExtLaunchKernel events on the launch stream)
-        st = torch.cuda.current_stream()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
-        for l, d in enumerate(layers):
-            moe.moe_decode_forward_timed(xd, d.router, d.routed, d.shared, outs[l], ws,
-                                         ev[2 * l], ev[2 * l + 1], S=S, B=B, stream=st)
-        torch.cuda.synchronize()
-        call_ms = [ev[2 * l].elapsed_time(ev[2 * l + 1]) for l in range(L)]
+        call_ms = [float("nan")] * L
+        if not fused:
+            st = torch.cuda.current_stream()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+            for l, d in enumerate(layers):
+                moe.moe_decode_forward_timed(xd, d.router, d.routed, d.shared, outs[l], ws,
+                                             ev[2 * l], ev[2 * l + 1], S=S, B=B, stream=st)
+            torch.cuda.synchronize()
+            call_ms = [ev[2 * l].elapsed_time(ev[2 * l + 1]) for l in range(L)]
 
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -277,6 +288,10 @@ def main() -> int:
         g.replay()
         torch.cuda.synchronize()
         same = bool(torch.equal(ref, outs))
+        if fused:
+            return dict(B=B, ms_per_pass=ms, us_per_layer=ms * 1000 / L, pass_bytes=pass_bytes,
+                        gbps=pass_bytes / (ms * 1e-3) / 1e9, graph_matches_eager=same,
+                        fused="rmsnorm on x + residual add on out")
         return dict(B=B, ms_per_pass=ms, us_per_layer=ms * 1000 / L, pass_bytes=pass_bytes,
                     gbps=pass_bytes / (ms * 1e-3) / 1e9, experts_read_mean=float(np.mean(n_read)),
                     kernel_us_mean=float(np.mean(call_ms)) * 1000,
@@ -302,13 +317,28 @@ def main() -> int:
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.prefill_steps
         tf = prefill_flop(T) / (ms * 1e-3) / 1e12
+        # the same layer with the RMSNorm pass and the residual add fused in
+        nw = moe.device.to_device_bf16(testgen.make_x(args.seed + 7, 1)[0], dev)
+        res = moe.device.to_device_bf16(testgen.make_x(args.seed + 1001, T), dev)
+        moe.moe_prefill_forward_ex(x, d.router, d.routed, d.shared, out, ws, norm_w=nw, eps=1e-5,
+                                   residual=res, S=S, T=T)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.prefill_steps):
+            moe.moe_prefill_forward_ex(x, d.router, d.routed, d.shared, out, ws, norm_w=nw,
+                                       eps=1e-5, residual=res, S=S, T=T)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_f = e0.elapsed_time(e1) / args.prefill_steps
         return dict(tokens=T, ms_per_layer=ms, tflops=tf, mfma_util=tf / PEAK_BF16_TFLOPS,
-                    flop=prefill_flop(T))
+                    flop=prefill_flop(T), ms_per_layer_fused_norm_residual=ms_f)
 
-    r1 = r8 = rp = rd = None
+    r1 = r8 = rp = rd = rf = None
     if args.workload in ("all", "decode"):
         r1 = run_batch(1)
         log(f"B=1: {r1['us_per_layer']:.2f} us/layer, {r1['gbps']:.0f} GB/s")
+        rf = run_batch(1, fused=True)
+        log(f"B=1 with RMSNorm + residual fused: {rf['us_per_layer']:.2f} us/layer")
         if not args.no_batch8:
             r8 = run_batch(8)
             log(f"B=8: {r8['us_per_layer']:.2f} us/layer, {r8['gbps']:.0f} GB/s")
@@ -367,7 +397,7 @@ def main() -> int:
                    "hidden": H, "inter": I, "experts": E, "top_k": K, "shared": 1,
                    "layers": L, "batch": 1, "weight_format": fmt,
                    "resident_weight_bytes": int(resident)},
-        "batch1": r1, "batch8": r8, "prefill": rp, "dense_gemv": rd,
+        "batch1": r1, "batch8": r8, "batch1_fused_norm_residual": rf, "prefill": rp, "dense_gemv": rd,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

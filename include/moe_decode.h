@@ -169,6 +169,50 @@ moe_status moe_prefill_forward(const moe_shape* shape, const void* x, int32_t T,
                                const moe_experts* shared, void* out, int32_t* ids_out,
                                float* w_out, void* ws, size_t ws_bytes, void* stream);
 
+/* The layer's neighbours, fused into it (Optimization section, low-latency
+ * path: the norm and the combine fused into the adjacent GEMV kernels; the
+ * norm kernels are one of the Fig. 2 steps).  Each part is optional.
+ *   norm_w    bf16 [H] or NULL.  When set, the layer runs on
+ *             xn[t][k] = bf16(x[t][k] * norm_w[k] / sqrt(mean_j x[t][j]^2 + norm_eps)),
+ *             the pre-MoE RMSNorm, computed in fp32 and rounded once to
+ *             bf16 (router and experts take bf16 activations, W4A16).
+ *   norm_eps  > 0 and finite when norm_w is set (ignored otherwise).
+ *   residual  bf16 [T][H] or NULL.  When set, out = bf16(residual + y), the
+ *             residual add done in fp32 before the single rounding of the
+ *             output.  It may be x itself, or out itself (an in-place
+ *             update of the residual stream); it must not partly overlap
+ *             out.
+ *   xn_out    bf16 [T][H] or NULL: receives the normalised input exactly as
+ *             the layer used it (needs norm_w; must not overlap x, out or
+ *             residual).  For checking routing decisions against a
+ *             reference on the same bf16 input. */
+typedef struct {
+  const void* norm_w;
+  float norm_eps;
+  const void* residual;
+  void* xn_out;
+} moe_fuse;
+
+/* moe_decode_forward with the neighbours of moe_fuse fused in (fuse may be
+ * NULL: then the result equals moe_decode_forward's bit for bit).  Runs only
+ * as the single-launch decode kernel: where that cannot run (a GPU with
+ * fewer than 256 compute units) it returns MOE_ERR_UNSUPPORTED. */
+moe_status moe_decode_forward_ex(const moe_shape* shape, const void* x, int32_t B,
+                                 const moe_fuse* fuse, const void* router_w,
+                                 const moe_experts* routed, const moe_experts* shared, void* out,
+                                 int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* moe_prefill_forward with the neighbours of moe_fuse fused in (fuse may be
+ * NULL).  The norm runs as one pass over x ahead of the routing GEMM (each
+ * token's mean square is needed before its first product); the residual add
+ * is done in the combine.  Same workspace as moe_prefill_forward. */
+moe_status moe_prefill_forward_ex(const moe_shape* shape, const void* x, int32_t T,
+                                  const moe_fuse* fuse, const void* router_w,
+                                  const moe_experts* routed, const moe_experts* shared, void* out,
+                                  int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Parity probe of the in-register NVFP4 decode: writes tensor `tensor`
  * (0 gate, 1 up, 2 down) of expert `expert` of an NVFP4 set as fp32,
  * out[r][c] = fp32(e2m1 * e4m3) * global (the first product is exact, so this

@@ -35,6 +35,11 @@ class Shape(ctypes.Structure):
                 ("n_shared", ctypes.c_int32), ("wfmt", ctypes.c_int32)]
 
 
+class Fuse(ctypes.Structure):
+    _fields_ = [("norm_w", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("residual", ctypes.c_void_p), ("xn_out", ctypes.c_void_p)]
+
+
 class Experts(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
@@ -68,6 +73,12 @@ def lib() -> ctypes.CDLL:
         L.moe_prefill_forward.restype = ctypes.c_int
         L.moe_prefill_forward.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp, vp,
                                           vp, vp, sz, vp]
+        L.moe_decode_forward_ex.restype = ctypes.c_int
+        L.moe_decode_forward_ex.argtypes = [P(Shape), vp, i32, P(Fuse), vp, P(Experts),
+                                            P(Experts), vp, vp, vp, vp, sz, vp]
+        L.moe_prefill_forward_ex.restype = ctypes.c_int
+        L.moe_prefill_forward_ex.argtypes = [P(Shape), vp, i32, P(Fuse), vp, P(Experts),
+                                             P(Experts), vp, vp, vp, vp, sz, vp]
         L.moe_nvfp4_dequant.restype = ctypes.c_int
         L.moe_nvfp4_dequant.argtypes = [P(Shape), P(Experts), i32, i32, vp, vp]
         _LIB = L
@@ -190,6 +201,43 @@ def moe_prefill_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_ou
                                    ctypes.byref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_prefill_forward")
+
+
+def fuse_struct(norm_w=None, eps: float = 1e-6, residual=None, xn_out=None) -> Fuse:
+    """The fused neighbours: RMSNorm weight bf16 [H] and epsilon, residual
+    bf16 [T, H], normalised-input output bf16 [T, H] (each None = off)."""
+    return Fuse(_ptr(norm_w), float(eps), _ptr(residual), _ptr(xn_out))
+
+
+def moe_decode_forward_ex(x, router_w, routed, shared, out, ws, norm_w=None, eps: float = 1e-6,
+                          residual=None, xn_out=None, ids_out=None, w_out=None, fmt=MOE_W_NVFP4,
+                          stream=None, S: Shape | None = None, B: int | None = None):
+    """out = residual + layer(rmsnorm(x)) for x bf16 [B, H] (B <= 8), each part optional."""
+    S = S or shape(_fmt(fmt))
+    B = x.shape[0] if B is None else B
+    R, Sh = experts_struct(routed), experts_struct(shared)
+    F = fuse_struct(norm_w, eps, residual, xn_out)
+    st = lib().moe_decode_forward_ex(ctypes.byref(S), _ptr(x), B, ctypes.byref(F),
+                                     _ptr(router_w), ctypes.byref(R), ctypes.byref(Sh),
+                                     _ptr(out), _ptr(ids_out), _ptr(w_out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_decode_forward_ex")
+
+
+def moe_prefill_forward_ex(x, router_w, routed, shared, out, ws, norm_w=None, eps: float = 1e-6,
+                           residual=None, xn_out=None, ids_out=None, w_out=None,
+                           fmt=MOE_W_NVFP4, stream=None, S: Shape | None = None,
+                           T: int | None = None):
+    """out = residual + layer(rmsnorm(x)) for x bf16 [T, H] at prefill sizes."""
+    S = S or shape(_fmt(fmt))
+    T = x.shape[0] if T is None else T
+    R, Sh = experts_struct(routed), experts_struct(shared)
+    F = fuse_struct(norm_w, eps, residual, xn_out)
+    st = lib().moe_prefill_forward_ex(ctypes.byref(S), _ptr(x), T, ctypes.byref(F),
+                                      _ptr(router_w), ctypes.byref(R), ctypes.byref(Sh),
+                                      _ptr(out), _ptr(ids_out), _ptr(w_out), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_prefill_forward_ex")
 
 
 def moe_nvfp4_dequant(expert_set, expert: int, tensor: int, out, stream=None):

@@ -1,16 +1,20 @@
-"""Compile the gfx950 HIP library (libmoe_decode.so) in place with hipcc."""
+"""Compile the gfx950 HIP library (libmoe_decode.so) in place with hipcc:
+each source to an object in parallel (the decode kernel file alone holds 64
+kernel instances), then one link."""
+import concurrent.futures
 import os
 import pathlib
 import subprocess
 
 HERE = pathlib.Path(__file__).resolve().parent
 CSRC = HERE / "csrc"
+OBJ = HERE / "_build"
 LIB = HERE / "libmoe_decode.so"
 SOURCES = ["capi.hip", "decode.hip", "decode_fused.hip", "prefill.hip", "gemv.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     # packed fp32 VALU forms stay off: ordinary fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -20,10 +24,23 @@ FLAGS = [
 
 def build(verbose: bool = False) -> pathlib.Path:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    OBJ.mkdir(exist_ok=True)
+    objs = [OBJ / (pathlib.Path(s).stem + ".o") for s in SOURCES]
+
+    def compile_one(src_obj):
+        src, obj = src_obj
+        cmd = [hipcc, *FLAGS, "-c", "-o", str(obj), str(CSRC / src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+
+    workers = max(1, min(len(SOURCES), os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+        list(pool.map(compile_one, zip(SOURCES, objs)))
     tmp = LIB.with_suffix(".so.tmp")
-    cmd = [hipcc, *FLAGS, "-o", str(tmp), *[str(CSRC / s) for s in SOURCES]]
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
     if verbose:
-        print(" ".join(cmd))
+        print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

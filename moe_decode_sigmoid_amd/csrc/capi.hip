@@ -1,6 +1,7 @@
 // C ABI of the gfx950 MoE layer library: argument checks, workspace sizing and
 // launches on the caller's stream.  Declarations and the contract of each
 // entry point are in include/moe_decode.h.
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -77,6 +78,40 @@ moe_status check_forward(const moe_shape* shape, const void* x, int32_t T, const
   const size_t xb = (size_t)T * moe::kH * 2;
   if (overlap(out, xb, x, xb)) return MOE_ERR_INVALID_ARG;
   if (overlap(out, xb, ws, ws_bytes)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// Checks of the fused neighbours for T tokens (fuse may be NULL) and their
+// device form.
+moe_status check_fuse(const moe_fuse* f, int32_t T, const void* x, const void* out,
+                      const void* ws, size_t ws_bytes, moe::FuseDev* dev) {
+  *dev = moe::FuseDev{};
+  if (!f) return MOE_OK;
+  moe_status st;
+  const size_t xb = (size_t)T * moe::kH * 2, wb = (size_t)moe::kH * 2;
+  if (f->norm_w) {
+    if ((st = check_ptr(f->norm_w)) != MOE_OK) return st;
+    if (!(f->norm_eps > 0.0f) || !(f->norm_eps < INFINITY)) return MOE_ERR_INVALID_ARG;
+    if (overlap(f->norm_w, wb, out, xb) || overlap(f->norm_w, wb, ws, ws_bytes))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (f->residual) {
+    if ((st = check_ptr(f->residual)) != MOE_OK) return st;
+    if (f->residual != out && overlap(f->residual, xb, out, xb)) return MOE_ERR_INVALID_ARG;
+    if (overlap(f->residual, xb, ws, ws_bytes)) return MOE_ERR_INVALID_ARG;
+  }
+  if (f->xn_out) {
+    if (!f->norm_w) return MOE_ERR_INVALID_ARG;
+    if ((st = check_ptr(f->xn_out)) != MOE_OK) return st;
+    if (overlap(f->xn_out, xb, x, xb) || overlap(f->xn_out, xb, out, xb) ||
+        overlap(f->xn_out, xb, ws, ws_bytes) || overlap(f->xn_out, xb, f->norm_w, wb) ||
+        (f->residual && overlap(f->xn_out, xb, f->residual, xb)))
+      return MOE_ERR_INVALID_ARG;
+  }
+  dev->norm_w = static_cast<const uint16_t*>(f->norm_w);
+  dev->eps = f->norm_eps;
+  dev->resid = static_cast<const uint16_t*>(f->residual);
+  dev->xn_out = static_cast<uint16_t*>(f->xn_out);
   return MOE_OK;
 }
 
@@ -197,6 +232,45 @@ moe_status moe_prefill_forward(const moe_shape* shape, const void* x, int32_t T,
                                      static_cast<const uint16_t*>(router_w), to_dev(routed),
                                      to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
                                      static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_decode_forward_ex(const moe_shape* shape, const void* x, int32_t B,
+                                 const moe_fuse* fuse, const void* router_w,
+                                 const moe_experts* routed, const moe_experts* shared, void* out,
+                                 int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (shape && check_shape(shape) == MOE_OK && B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
+  moe_status st = check_forward(shape, x, B, router_w, routed, shared, out, ids_out, w_out, ws,
+                                ws_bytes, moe::kDecodeWsBytes);
+  if (st != MOE_OK) return st;
+  moe::FuseDev fz;
+  if ((st = check_fuse(fuse, B, x, out, ws, ws_bytes, &fz)) != MOE_OK) return st;
+  if (!moe::fused_supported()) return MOE_ERR_UNSUPPORTED;
+  const hipError_t e = moe::launch_decode_fused(
+      B, shape->wfmt, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w),
+      to_dev(routed), to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+      static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream), nullptr, nullptr, fz);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_prefill_forward_ex(const moe_shape* shape, const void* x, int32_t T,
+                                  const moe_fuse* fuse, const void* router_w,
+                                  const moe_experts* routed, const moe_experts* shared, void* out,
+                                  int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  const size_t need = (shape && check_shape(shape) == MOE_OK && T >= 1) ? moe::prefill_ws_bytes(T) : 0;
+  moe_status st = check_forward(shape, x, T, router_w, routed, shared, out, ids_out, w_out, ws,
+                                ws_bytes, need == 0 ? 1 : need);
+  if (st != MOE_OK) return st;
+  if (need == 0) return MOE_ERR_UNSUPPORTED;
+  moe::FuseDev fz;
+  if ((st = check_fuse(fuse, T, x, out, ws, ws_bytes, &fz)) != MOE_OK) return st;
+  hipError_t e = moe::launch_prefill(T, shape->wfmt, static_cast<const uint16_t*>(x),
+                                     static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                     to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                     static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream),
+                                     fz);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

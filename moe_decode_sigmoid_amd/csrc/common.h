@@ -158,6 +158,48 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
+// ------------------------------------------------------------ fused neighbours
+// The pre-MoE RMSNorm and the residual add, fused into the layer's kernels
+// ("Day-0 Support for Flint on vLLM", Optimization section, low-latency
+// path).  A null pointer switches each part off.
+struct FuseDev {
+  const uint16_t* norm_w;   // bf16 [H]
+  float eps;
+  const uint16_t* resid;    // bf16 [T][H]: out = bf16(resid + y)
+  uint16_t* xn_out;         // bf16 [T][H]: the normalised input, as used
+};
+
+// 1 / sqrt(mean square + eps) of a row of kH bf16 values held by one wave,
+// 32 per lane (lane l: elements 32 l .. 32 l + 31, as 16 bf16 pairs): each
+// lane sums its squares in element order, then the wave sums the lanes
+// (wave_sum's fixed order).  Every path that normalises a row uses this one
+// order.  Division and square root are the correctly rounded fp32 ones.
+__device__ __forceinline__ float row_rms_inv(const uint32_t (&v)[16], float eps) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = bf16_lo(v[i]), b = bf16_hi(v[i]);
+    s = __builtin_fmaf(a, a, s);
+    s = __builtin_fmaf(b, b, s);
+  }
+  const float ss = wave_sum(s);
+  return 1.0f / sqrtf(ss * (1.0f / kH) + eps);
+}
+
+// bf16(x * r * w) for the 8 elements of one 16-byte piece: x * r and then
+// * w in fp32, rounded once to bf16.
+__device__ __forceinline__ uint4 rmsnorm8(uint4 x, uint4 w, float r) {
+  const uint32_t xu[4] = {x.x, x.y, x.z, x.w}, wu[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = f32_to_bf16_rne((bf16_lo(xu[i]) * r) * bf16_lo(wu[i]));
+    const uint32_t hi = f32_to_bf16_rne((bf16_hi(xu[i]) * r) * bf16_hi(wu[i]));
+    o[i] = lo | (hi << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Maximum over the 64 lanes of a wave, returned uniformly.
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f32<0x128>(v));

@@ -27,6 +27,12 @@
 //      entries a = w - 1 mod 4 and the shared expert's tokens w, w + 4),
 //      weighted by the routing, summed in a fixed order, rounded once to bf16.
 //
+// The layer's neighbours can be fused in (template parameters NORM, RESID;
+// the same section's low-latency path fuses norm and combine into the
+// adjacent GEMVs): the pre-MoE RMSNorm of x at the start of step A (every
+// workgroup normalises the same x, so no exchange is needed), and the
+// residual add before the output rounding of step C.
+//
 // Hand-over between workgroups uses only device-coherent accesses (relaxed
 // agent-scope atomics: no cache write-back or invalidation):
 //  - call epoch: workgroup g keeps a private counter in the workspace; every
@@ -405,11 +411,11 @@ __device__ __forceinline__ uint32_t* hready_bank(uint8_t* ws, int r, int k) {
 }
 
 // ------------------------------------------------------------------ kernel
-template <int B, int FMT>
+template <int B, int FMT, bool NORM, bool RESID>
 __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, ExpertsDev routed,
     ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, uint8_t* __restrict__ ws) {
+    float* __restrict__ w_out, uint8_t* __restrict__ ws, FuseDev fz) {
   constexpr int kTB = FMT == FMT_NVFP4 ? 4 : 2;      // gate/up row pairs per batch
   constexpr int kDepthC = FMT == FMT_NVFP4 ? 4 : 1;  // entries of down rows in flight
   constexpr int kPairs = (kK + 1) * B;               // h pairs: 6 B routed + B shared
@@ -449,9 +455,22 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     scg.load_gu(shared, 0, 0, srow, lane);
     scu.load_gu(shared, 0, 1, srow, lane);
   }
+  // Every load of step A goes out before any of them is used (loads return
+  // in issue order, so a wait for one is a wait for all before it): x, piece
+  // tid of each token; the norm weight and the residual of this workgroup's
+  // output elements (row g * 8 + tid / B, token tid % B), read from x when
+  // not fused so that no branch splits the loads; x in registers at B = 1;
+  // the shared expert's down rows of this workgroup (step C).
+  __shared__ float s_rinv[kMaxB];
+  uint4 xr[B], nw = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-  for (int k = 0; k < B; ++k)
-    s_x[k * (kH / 8) + tid] = reinterpret_cast<const uint4*>(x)[k * (kH / 8) + tid];
+  for (int k = 0; k < B; ++k) xr[k] = reinterpret_cast<const uint4*>(x)[k * (kH / 8) + tid];
+  if constexpr (NORM) nw = reinterpret_cast<const uint4*>(fz.norm_w)[tid];
+  uint16_t rv = 0;
+  if constexpr (RESID) {
+    const int ro = tid < kRowsPerWg * B ? (tid % B) * kH + g * kRowsPerWg + tid / B : 0;
+    rv = fz.resid[ro];
+  }
   uint32_t x0[16];
   if constexpr (B == 1) {
     const uint4* p = reinterpret_cast<const uint4*>(x + 32 * lane);
@@ -461,13 +480,42 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
     }
   }
-  // the shared expert's tensor scales and down rows of this workgroup (step
-  // C), in every wave
   const float sh_sg = Chunk<FMT>::gscale(shared, 0, 0), sh_su = Chunk<FMT>::gscale(shared, 0, 1),
               sh_sd = Chunk<FMT>::gscale(shared, 0, 2);
   Chunk<FMT> dsh[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * grp4 + r, c16);
+  const float resid = __builtin_bit_cast(float, (uint32_t)rv << 16);
+  // x to LDS as is, or through the fused RMSNorm.  A row's mean square is
+  // summed by one wave holding the row 32 elements per lane (the same order
+  // on every path).  At B = 1 every wave already holds the row in x0, so
+  // each thread normalises its piece before the barrier below and x0 is
+  // reread from LDS after it; at B > 1 wave w sums the rows of tokens w and
+  // w + 4 and the pieces are normalised after the barrier, behind a second
+  // one.
+  if constexpr (NORM) {
+    if constexpr (B == 1) {
+      const float r = row_rms_inv(x0, fz.eps);
+      const uint4 v = rmsnorm8(xr[0], nw, r);
+      s_x[tid] = v;
+      if (fz.xn_out && g == 0) reinterpret_cast<uint4*>(fz.xn_out)[tid] = v;
+    } else {
+      for (int t = wave; t < B; t += 4) {
+        const uint4* q = reinterpret_cast<const uint4*>(x + t * kH + 32 * lane);
+        uint32_t v[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 u = q[i];
+          v[4 * i] = u.x; v[4 * i + 1] = u.y; v[4 * i + 2] = u.z; v[4 * i + 3] = u.w;
+        }
+        const float r = row_rms_inv(v, fz.eps);
+        if (lane == 0) s_rinv[t] = r;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < B; ++k) s_x[k * (kH / 8) + tid] = xr[k];
+  }
   s_mask[tid] = 0u;
   if (tid == 0) {                                    // this call's epoch
     uint32_t* ctr = epoch_ptr(ws, g);
@@ -477,6 +525,22 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   }
   __syncthreads();
   const uint32_t epoch = s_epoch;
+  if constexpr (NORM && B == 1) {          // x0 again, normalised
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = s_x[4 * lane + i];
+      x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
+    }
+  }
+  if constexpr (NORM && B > 1) {
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const uint4 v = rmsnorm8(xr[k], nw, s_rinv[k]);
+      s_x[k * (kH / 8) + tid] = v;
+      if (fz.xn_out && g == 0) reinterpret_cast<uint4*>(fz.xn_out)[k * (kH / 8) + tid] = v;
+    }
+    __syncthreads();
+  }
   trace_stamp(ws, 1);
   {
     float acc[B];
@@ -835,6 +899,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     const int r8 = tid / B, t = tid % B;
     float y = (s_red[0][r8][t] + s_red[1][r8][t]) + (s_red[2][r8][t] + s_red[3][r8][t]);
     y += s_redsh[t & 3][r8][t >> 2];
+    if constexpr (RESID) y += resid;
     out[(size_t)t * kH + g * kRowsPerWg + r8] = f32_to_bf16_rne(y);
   }
   trace_stamp(ws, 12);
@@ -848,14 +913,19 @@ bool fused_supported() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   if (g_fused_ok[dev] == 0) {
-    int cus = 0, occ_nv = 0, occ_bf = 0;
+    int cus = 0, occ_nv = 0, occ_bf = 0, occ_nn = 0, occ_bn = 0;
     const bool ok =
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_nv, k_decode_fused<8, FMT_NVFP4>,
-                                                     kFusedThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_bf, k_decode_fused<8, FMT_BF16>,
-                                                     kFusedThreads, 0) == hipSuccess;
-    g_fused_ok[dev] = (ok && cus >= kFusedGrid && occ_nv >= 1 && occ_bf >= 1) ? 1 : -1;
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ_nv, k_decode_fused<8, FMT_NVFP4, false, false>, kFusedThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ_bf, k_decode_fused<8, FMT_BF16, false, false>, kFusedThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ_nn, k_decode_fused<8, FMT_NVFP4, true, true>, kFusedThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ_bn, k_decode_fused<8, FMT_BF16, true, true>, kFusedThreads, 0) == hipSuccess;
+    g_fused_ok[dev] = (ok && cus >= kFusedGrid && occ_nv >= 1 && occ_bf >= 1 && occ_nn >= 1 &&
+                       occ_bn >= 1) ? 1 : -1;
   }
   return g_fused_ok[dev] == 1;
 }
@@ -863,29 +933,38 @@ bool fused_supported() {
 template <int B>
 static void launch_fused_b(int fmt, const uint16_t* x, const uint16_t* rw, const ExpertsDev& routed,
                            const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
-                           uint8_t* ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  auto k = fmt == FMT_NVFP4 ? k_decode_fused<B, FMT_NVFP4> : k_decode_fused<B, FMT_BF16>;
+                           uint8_t* ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1,
+                           const FuseDev& fz) {
+  // one instance per fused combination: without fusion the kernel carries
+  // none of its code (the schedule of the plain layer is left as it is)
+  using K = decltype(&k_decode_fused<B, FMT_NVFP4, false, false>);
+  static const K table[2][2][2] = {
+      {{k_decode_fused<B, FMT_NVFP4, false, false>, k_decode_fused<B, FMT_NVFP4, false, true>},
+       {k_decode_fused<B, FMT_NVFP4, true, false>, k_decode_fused<B, FMT_NVFP4, true, true>}},
+      {{k_decode_fused<B, FMT_BF16, false, false>, k_decode_fused<B, FMT_BF16, false, true>},
+       {k_decode_fused<B, FMT_BF16, true, false>, k_decode_fused<B, FMT_BF16, true, true>}}};
+  const K k = table[fmt == FMT_NVFP4 ? 0 : 1][fz.norm_w ? 1 : 0][fz.resid ? 1 : 0];
   if (e0 && e1)
     hipExtLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, e0, e1, 0, x, rw, routed,
-                          shared, out, ids, w, ws);
+                          shared, out, ids, w, ws, fz);
   else
     hipLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, x, rw, routed, shared, out,
-                       ids, w, ws);
+                       ids, w, ws, fz);
 }
 
 hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t* rw,
                                const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st, hipEvent_t e0,
-                               hipEvent_t e1) {
+                               hipEvent_t e1, const FuseDev& fz) {
   switch (B) {
-    case 1: launch_fused_b<1>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
-    case 2: launch_fused_b<2>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
-    case 3: launch_fused_b<3>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
-    case 4: launch_fused_b<4>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
-    case 5: launch_fused_b<5>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
-    case 6: launch_fused_b<6>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
-    case 7: launch_fused_b<7>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
-    case 8: launch_fused_b<8>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1); break;
+    case 1: launch_fused_b<1>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
+    case 2: launch_fused_b<2>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
+    case 3: launch_fused_b<3>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
+    case 4: launch_fused_b<4>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
+    case 5: launch_fused_b<5>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
+    case 6: launch_fused_b<6>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
+    case 7: launch_fused_b<7>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
+    case 8: launch_fused_b<8>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -22,7 +22,8 @@ bool fused_supported();
 hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t* rw,
                                const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st,
-                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                               const FuseDev& fuse = FuseDev{});
 
 // Dense NVFP4 GEMV, B = 1..8, K % 32 == 0, K <= 8192, B * K <= 32768.
 constexpr int kGemvMaxK = 8192;
@@ -38,7 +39,8 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
 // Prefill path, T >= 1 tokens.
 hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
                           const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
-                          int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
+                          int32_t* ids, float* w, uint8_t* ws, hipStream_t st,
+                          const FuseDev& fuse = FuseDev{});
 
 // Workspace bytes of the prefill path for T tokens (0 = not served).
 size_t prefill_ws_bytes(int T);

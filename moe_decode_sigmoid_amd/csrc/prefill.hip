@@ -60,7 +60,7 @@ constexpr int kSlices2 = kH / kGBN;        // down column slices
 
 // ------------------------------------------------------------------ workspace
 struct PrefillLayout {
-  size_t ids, w, hist, base, cnt, off, nitems, items, perm, pos, wpos, h, part, total;
+  size_t ids, w, hist, base, cnt, off, nitems, items, perm, pos, wpos, h, part, xn, total;
   int T, ntiles, max_items;
 };
 
@@ -85,6 +85,7 @@ __host__ __device__ inline PrefillLayout prefill_layout(int T) {
   L.wpos = o;   o = al256(o + sizeof(float) * (size_t)T * (kK + 1));
   L.h = o;      o = al256(o + 2 * (size_t)T * (kK + 1) * kI);
   L.part = o;   o = al256(o + 2 * (size_t)T * (kK + 1) * kH);
+  L.xn = o;     o = al256(o + 2 * (size_t)T * kH);   // normalised input (fused RMSNorm)
   L.total = o;
   return L;
 }
@@ -608,10 +609,42 @@ __global__ __launch_bounds__(kGThreads2, 1) void k_prefill_down(int T, ExpertsDe
     }
 }
 
+// ------------------------------------------------------------------ P0 RMSNorm
+// One wave per token, lane l on elements 32 l .. 32 l + 31: the mean square
+// is summed in the same order as in the decode kernel's fused norm, so a
+// token normalises to the same bf16 values on both paths.
+__global__ __launch_bounds__(kPThreads) void k_prefill_rmsnorm(int T, const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ nw,
+                                                               float eps,
+                                                               uint16_t* __restrict__ xn) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kPThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * kH + 32 * lane);
+  const uint4* q = reinterpret_cast<const uint4*>(nw + 32 * lane);
+  uint4 a[4], w[4];
+  uint32_t v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = p[i];
+    w[i] = q[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[4 * i] = a[i].x; v[4 * i + 1] = a[i].y; v[4 * i + 2] = a[i].z; v[4 * i + 3] = a[i].w;
+  }
+  const float r = row_rms_inv(v, eps);
+  uint4* o = reinterpret_cast<uint4*>(xn + (size_t)t * kH + 32 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = rmsnorm8(a[i], w[i], r);
+}
+
 // ------------------------------------------------------------------ P6 combine
-// Thread -> (token, 8 columns); routed rows in ascending expert id, then shared.
+// Thread -> (token, 8 columns); routed rows in ascending expert id, then shared,
+// then the residual when one is fused in.
 __global__ __launch_bounds__(kPThreads) void k_prefill_combine(int T, uint8_t* __restrict__ ws,
-                                                               uint16_t* __restrict__ out) {
+                                                               const uint16_t* resid,
+                                                               uint16_t* out) {
   const PrefillLayout L = prefill_layout(T);
   const int gid = blockIdx.x * kPThreads + threadIdx.x;
   const int t = gid / (kH / 8), c8 = (gid % (kH / 8)) * 8;
@@ -646,6 +679,15 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_combine(int T, uint8_t* _
 #pragma unroll
   for (int j = 0; j < kK; ++j) add_row(pos[(size_t)t * kK + order[j]]);
   add_row(T * kK + t);
+  if (resid) {
+    const uint4 v = *reinterpret_cast<const uint4*>(resid + (size_t)t * kH + c8);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      y[2 * q] += bf16_lo(u[q]);
+      y[2 * q + 1] += bf16_hi(u[q]);
+    }
+  }
   uint32_t o[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -656,8 +698,15 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_combine(int T, uint8_t* _
 // ------------------------------------------------------------------ launcher
 hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
                           const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
-                          int32_t* ids, float* w, uint8_t* ws, hipStream_t st) {
+                          int32_t* ids, float* w, uint8_t* ws, hipStream_t st,
+                          const FuseDev& fz) {
   const PrefillLayout L = prefill_layout(T);
+  if (fz.norm_w) {
+    uint16_t* xn = fz.xn_out ? fz.xn_out : reinterpret_cast<uint16_t*>(ws + L.xn);
+    hipLaunchKernelGGL(k_prefill_rmsnorm, dim3((T + kPThreads / 64 - 1) / (kPThreads / 64)),
+                       dim3(kPThreads), 0, st, T, x, fz.norm_w, fz.eps, xn);
+    x = xn;
+  }
   hipLaunchKernelGGL(k_prefill_route, dim3(L.ntiles), dim3(kPThreads), 0, st, x, rw, T, ws, ids, w);
   hipLaunchKernelGGL(k_prefill_scan, dim3(1), dim3(kScanThreads), 0, st, T, ws);
   hipLaunchKernelGGL(k_prefill_positions, dim3(L.ntiles), dim3(kPThreads), 0, st, T, ws);
@@ -675,7 +724,7 @@ hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
   }
   const int nthr = T * (kH / 8);
   hipLaunchKernelGGL(k_prefill_combine, dim3((nthr + kPThreads - 1) / kPThreads), dim3(kPThreads),
-                     0, st, T, ws, out);
+                     0, st, T, ws, fz.resid, out);
   return hipGetLastError();
 }
 

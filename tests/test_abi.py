@@ -19,7 +19,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["moe_decode_route", "moe_decode_forward", "moe_decode_forward_timed",
-              "moe_prefill_forward", "moe_nvfp4_gemv",
+              "moe_prefill_forward", "moe_nvfp4_gemv", "moe_decode_forward_ex",
+              "moe_prefill_forward_ex",
               "moe_nvfp4_dequant", "moe_workspace_bytes", "moe_status_string",
               "moe_abi_version"]:
         assert n in names
@@ -138,6 +139,42 @@ def test_gemv_argument_errors():
     assert call(K=16384) == E.MOE_ERR_UNSUPPORTED
     assert call(B=8, K=8192) == E.MOE_ERR_UNSUPPORTED          # x no longer fits LDS
     assert call(y=A + 64) == E.MOE_ERR_INVALID_ARG             # y overlaps x
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_fused_neighbour_argument_errors(prefill):
+    """Every call here fails a check before any launch (none may pass them all:
+    the pointers are fake)."""
+    E = moe
+    S = moe.shape()
+    R = moe.experts_struct(_FakeExperts(A + 0x4000000))
+    Sh = moe.experts_struct(_FakeExperts(A + 0x5000000))
+    fn = moe.lib().moe_prefill_forward_ex if prefill else moe.lib().moe_decode_forward_ex
+    X, OUT, WS = A, A + 0x2000000, A + 0x3000000
+    NW, RES, XN = A + 0x50000000, A + 0x51000000, A + 0x52000000   # past the workspace
+
+    def call(B=2, **f):
+        F = moe.Fuse(f.get("norm_w"), f.get("eps", 1e-6), f.get("residual"), f.get("xn_out"))
+        return fn(ctypes.byref(S), X, B, ctypes.byref(F), A + 0x1000000, ctypes.byref(R),
+                  ctypes.byref(Sh), OUT, None, None, WS, WS_BIG, 0)
+    assert call(norm_w=NW + 2) == E.MOE_ERR_MISALIGNED
+    assert call(norm_w=NW, eps=0.0) == E.MOE_ERR_INVALID_ARG
+    assert call(norm_w=NW, eps=-1.0) == E.MOE_ERR_INVALID_ARG
+    assert call(norm_w=NW, eps=float("nan")) == E.MOE_ERR_INVALID_ARG
+    assert call(norm_w=NW, eps=float("inf")) == E.MOE_ERR_INVALID_ARG
+    assert call(norm_w=OUT + 64) == E.MOE_ERR_INVALID_ARG        # weight inside out
+    assert call(residual=RES + 8) == E.MOE_ERR_MISALIGNED
+    assert call(residual=OUT + 4096) == E.MOE_ERR_INVALID_ARG    # partly overlaps out
+    assert call(residual=WS + 1024) == E.MOE_ERR_INVALID_ARG     # inside the workspace
+    assert call(xn_out=XN) == E.MOE_ERR_INVALID_ARG              # needs the norm
+    assert call(norm_w=NW, xn_out=XN + 4) == E.MOE_ERR_MISALIGNED
+    assert call(norm_w=NW, xn_out=X + 16) == E.MOE_ERR_INVALID_ARG
+    assert call(norm_w=NW, xn_out=OUT) == E.MOE_ERR_INVALID_ARG
+    assert call(norm_w=NW, residual=RES, xn_out=RES + 4096) == E.MOE_ERR_INVALID_ARG
+    # the layer's own checks still come first
+    assert call(B=0, norm_w=NW) == E.MOE_ERR_INVALID_ARG
+    if not prefill:
+        assert call(B=9, norm_w=NW) == E.MOE_ERR_UNSUPPORTED
 
 
 def test_decode_batch_limit_is_unsupported_not_invalid():

@@ -1,0 +1,229 @@
+"""GPU parity of the layer with its neighbours fused in: the pre-MoE RMSNorm
+on the input and the residual add on the output ("Day-0 Support for Flint on
+vLLM", Optimization section, low-latency path: norm and combine fused into
+the adjacent GEMVs), decode and prefill, through the C ABI.
+
+Inputs: the seeded synthetic Flint-shaped layer; x ~ N(0, 1) bf16 with token t
+scaled by 2^(t mod 5 - 2) so that the norm does real work; norm weight and
+residual ~ N(0, 1) bf16; eps = 1e-5.
+
+Protocol.  The normalised input is bf16, and an fp32 computation of it can
+land on the other side of a bf16 rounding midpoint than the fp64 one (about
+3e-4 of the elements, 1 ulp each).  Routing is a decision taken on that
+input, so the oracle evaluates the layer on the GPU's normalised input
+(returned through xn_out), after that input has been checked against the
+oracle's own RMSNorm: equal, or 1 ulp apart on at most 0.2% of the elements.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import testgen
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+moe = pytest.importorskip("moe_decode_sigmoid_amd")
+
+EPS = float(np.float32(1e-5))
+H = 2048
+
+
+@functools.lru_cache(maxsize=None)
+def host_layer(seed: int, fmt: str = "nvfp4"):
+    return testgen.make_layer(seed, 0, fmt)
+
+
+_DEV = {}
+
+
+def dev_layer(seed: int, fmt: str = "nvfp4"):
+    key = (seed, fmt)
+    if key not in _DEV:
+        if len(_DEV) >= 2:
+            _DEV.pop(next(iter(_DEV)))
+        _DEV[key] = moe.DeviceLayer.from_host(host_layer(seed, fmt))
+    return _DEV[key]
+
+
+def scaled_x(seed: int, T: int) -> np.ndarray:
+    """x ~ N(0, 1) bf16, token t times 2^(t mod 5 - 2) (exact in bf16)."""
+    x = testgen.make_x(seed, T)
+    f = (x.astype(np.uint32) << 16).view(np.float32)
+    f = f * (2.0 ** (np.arange(T) % 5 - 2))[:, None].astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def dev(a):
+    return moe.device.to_device_bf16(np.ascontiguousarray(a))
+
+
+def check_xn(xn_gpu: np.ndarray, x: np.ndarray, nw: np.ndarray):
+    want = oracle.rmsnorm_bf16(x, nw, EPS)
+    diff = xn_gpu != want
+    n = int(diff.sum())
+    assert n <= 2e-3 * x.size, f"{n} of {x.size} normalised elements differ"
+    if n:
+        a = xn_gpu[diff].astype(np.int32)
+        b = want[diff].astype(np.int32)
+        assert np.all((a ^ b) < 0x8000) and np.all(np.abs(a - b) == 1), "more than 1 ulp apart"
+    return n
+
+
+def oracle_fused(x, HL, ids_gpu, residual, xn):
+    """Oracle outputs on the GPU's normalised input, near-ties re-evaluated on
+    the GPU's ids (gap below the near-tie threshold only)."""
+    y, ids, w, gap, _ = oracle.forward_fused(x, HL, residual=residual, xn=xn)
+    log = []
+    for t in range(x.shape[0]):
+        if set(ids_gpu[t].tolist()) == set(ids[t].tolist()):
+            continue
+        assert gap[t] < parity.NEAR_TIE, (t, float(gap[t]))
+        log.append((t, float(gap[t])))
+        y[t] = oracle.forward_fused(x[t:t + 1], HL,
+                                    residual=None if residual is None else residual[t:t + 1],
+                                    xn=xn[t:t + 1], forced_ids=ids_gpu[t:t + 1].copy())[0][0]
+    return y, ids, w, gap, log
+
+
+def run_decode(seed, x, nw=None, res=None, fmt="nvfp4", xn_out=True, inplace=False):
+    L = dev_layer(seed, fmt)
+    B = x.shape[0]
+    xd = dev(x)
+    rd = dev(res) if res is not None else None
+    out = rd if inplace else torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+    xn = torch.empty((B, H), dtype=torch.bfloat16, device="cuda") if (xn_out and nw is not None) else None
+    ids = torch.empty((B, 6), dtype=torch.int32, device="cuda")
+    w = torch.empty((B, 6), dtype=torch.float32, device="cuda")
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(B, fmt=fmt))
+    moe.moe_decode_forward_ex(xd, L.router, L.routed, L.shared, out, ws,
+                              norm_w=dev(nw) if nw is not None else None, eps=EPS,
+                              residual=rd, xn_out=xn, ids_out=ids, w_out=w, fmt=fmt)
+    torch.cuda.synchronize()
+    xn_h = None if xn is None else xn.view(torch.int16).cpu().numpy().view(np.uint16)
+    return parity.bf16_out_to_f64(out), ids.cpu().numpy(), w.cpu().numpy(), xn_h
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "bf16"])
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_decode_norm_matches_oracle(B, fmt):
+    """RMSNorm fused, no residual: the layer's output at full tolerance."""
+    seed = 1 if fmt == "nvfp4" else 2
+    x = scaled_x(10 + B, B)
+    nw = testgen.make_x(20, 1)[0]
+    y, ids, w, xn = run_decode(seed, x, nw=nw, fmt=fmt)
+    check_xn(xn, x, nw)
+    y_ref, ids_or, w_or, gap, log = oracle_fused(x, host_layer(seed, fmt), ids, None, xn)
+    parity.check_weights(ids, w, ids_or, w_or, gap)
+    parity.check_output(y, y_ref, f"decode norm B {B} {fmt}")
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_decode_norm_and_residual_match_oracle(B):
+    x = scaled_x(30 + B, B)
+    nw = testgen.make_x(21, 1)[0]
+    res = testgen.make_x(22, B)
+    y, ids, w, xn = run_decode(3, x, nw=nw, res=res)
+    check_xn(xn, x, nw)
+    y_ref, ids_or, w_or, gap, _ = oracle_fused(x, host_layer(3), ids, res, xn)
+    parity.check_output(y, y_ref, f"decode norm + residual B {B}")
+
+
+def test_decode_residual_only_matches_oracle():
+    B = 4
+    x = testgen.make_x(40, B)
+    res = testgen.make_x(41, B)
+    y, ids, w, _ = run_decode(1, x, res=res)
+    y_ref, *_ = oracle_fused(x, host_layer(1), ids, res, x)
+    parity.check_output(y, y_ref, "decode residual only")
+
+
+def test_decode_without_fusion_equals_plain_forward_bitwise():
+    B = 5
+    x = testgen.make_x(42, B)
+    L = dev_layer(1)
+    xd = dev(x)
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(B))
+    a = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    moe.moe_decode_forward(xd, L.router, L.routed, L.shared, a, ws)
+    moe.moe_decode_forward_ex(xd, L.router, L.routed, L.shared, b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_in_place_residual_and_optional_xn_give_the_same_bits():
+    B = 6
+    x = scaled_x(43, B)
+    nw = testgen.make_x(23, 1)[0]
+    res = testgen.make_x(24, B)
+    y1, ids1, _, _ = run_decode(1, x, nw=nw, res=res)
+    y2, ids2, _, _ = run_decode(1, x, nw=nw, res=res, xn_out=False, inplace=True)
+    assert np.array_equal(ids1, ids2)
+    assert np.array_equal(y1, y2)
+
+
+# ----------------------------------------------------------------- prefill
+def run_prefill(seed, x, nw=None, res=None, fmt="nvfp4", xn_out=True):
+    L = dev_layer(seed, fmt)
+    T = x.shape[0]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    xn = torch.empty((T, H), dtype=torch.bfloat16, device="cuda") if (xn_out and nw is not None) else None
+    ids = torch.empty((T, 6), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 6), dtype=torch.float32, device="cuda")
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(T, prefill=True, fmt=fmt))
+    moe.moe_prefill_forward_ex(dev(x), L.router, L.routed, L.shared, out, ws,
+                               norm_w=dev(nw) if nw is not None else None, eps=EPS,
+                               residual=dev(res) if res is not None else None, xn_out=xn,
+                               ids_out=ids, w_out=w, fmt=fmt)
+    torch.cuda.synchronize()
+    xn_h = None if xn is None else xn.view(torch.int16).cpu().numpy().view(np.uint16)
+    return parity.bf16_out_to_f64(out), ids.cpu().numpy(), w.cpu().numpy(), xn_h
+
+
+@pytest.mark.parametrize("T", [1, 77, 300])
+def test_prefill_norm_and_residual_match_oracle(T):
+    x = scaled_x(50 + T, T)
+    nw = testgen.make_x(25, 1)[0]
+    res = testgen.make_x(26, T)
+    y, ids, w, xn = run_prefill(1, x, nw=nw, res=res)
+    check_xn(xn, x, nw)
+    y_ref, ids_or, w_or, gap, _ = oracle_fused(x, host_layer(1), ids, res, xn)
+    parity.check_weights(ids, w, ids_or, w_or, gap)
+    parity.check_output(y, y_ref, f"prefill norm + residual T {T}")
+
+
+def test_prefill_norm_matches_oracle_at_full_tolerance():
+    T = 160
+    x = scaled_x(60, T)
+    nw = testgen.make_x(27, 1)[0]
+    y, ids, w, xn = run_prefill(1, x, nw=nw)
+    check_xn(xn, x, nw)
+    y_ref, *_ = oracle_fused(x, host_layer(1), ids, None, xn)
+    parity.check_output(y, y_ref, "prefill norm")
+
+
+def test_prefill_and_decode_normalise_a_token_identically():
+    """Same partial sums in the same order on both paths: bit-equal xn."""
+    x = scaled_x(61, 8)
+    nw = testgen.make_x(28, 1)[0]
+    _, _, _, xn_d = run_decode(1, x, nw=nw)
+    _, _, _, xn_p = run_prefill(1, x, nw=nw)
+    assert np.array_equal(xn_d, xn_p)
+
+
+def test_prefill_without_fusion_equals_plain_prefill_bitwise():
+    T = 96
+    x = testgen.make_x(62, T)
+    L = dev_layer(1)
+    xd = dev(x)
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(T, prefill=True))
+    a = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    moe.moe_prefill_forward(xd, L.router, L.routed, L.shared, a, ws)
+    moe.moe_prefill_forward_ex(xd, L.router, L.routed, L.shared, b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
