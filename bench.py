@@ -83,7 +83,7 @@ def write_traffic_record(dec_fetch: str, dec_write: str, copy_fetch: str, copy_w
         assert vals, f"no {counter} rows for {kernel_part} in {path}"
         return sum(vals.values()) / len(vals), len(vals)
 
-    kname = "k_decode_fused<1, 0>"
+    kname = "k_decode_fused<1, 0, false, false>"
     f_dec, nf = mean_kib(dec_fetch, kname, "FETCH_SIZE")
     w_dec, nw = mean_kib(dec_write, kname, "WRITE_SIZE")
     f_cp, _ = mean_kib(copy_fetch, "copyBuffer", "FETCH_SIZE")
