@@ -41,6 +41,8 @@ def lib() -> ctypes.CDLL:
         L.or_e2m1.argtypes = [ctypes.c_uint8]
         L.or_e4m3.restype = d
         L.or_e4m3.argtypes = [ctypes.c_uint8]
+        L.or_e8m0.restype = d
+        L.or_e8m0.argtypes = [ctypes.c_uint8]
         L.or_bf16.restype = d
         L.or_bf16.argtypes = [ctypes.c_uint16]
         L.or_sigmoid.restype = d
@@ -74,10 +76,13 @@ def _p(a) -> int:
 
 
 def _experts(X) -> _Experts:
-    """X: an object with fmt ('nvfp4' | 'bf16'), w13, w2 and, for nvfp4,
-    w13_scale, w2_scale, glob (the input generator's Experts)."""
+    """X: an object with fmt ('nvfp4' | 'bf16' | 'mxfp8'), w13, w2 and, for
+    nvfp4, w13_scale, w2_scale, glob; for mxfp8, w13_scale, w2_scale (the
+    input generator's Experts)."""
     if X.fmt == "nvfp4":
         return _Experts(_p(X.w13), _p(X.w13_scale), _p(X.w2), _p(X.w2_scale), _p(X.glob), 0)
+    if X.fmt == "mxfp8":
+        return _Experts(_p(X.w13), _p(X.w13_scale), _p(X.w2), _p(X.w2_scale), None, 2)
     return _Experts(_p(X.w13), None, _p(X.w2), None, None, 1)
 
 
@@ -92,6 +97,10 @@ def e2m1(nibble: int) -> float:
 
 def e4m3(byte: int) -> float:
     return float(lib().or_e4m3(byte))
+
+
+def e8m0(byte: int) -> float:
+    return float(lib().or_e8m0(byte))
 
 
 def bf16(bits: int) -> float:
@@ -181,7 +190,7 @@ def forward(x: np.ndarray, router: np.ndarray, routed, shared, k: int, I: int,
     if forced_ids is not None:
         forced = np.ascontiguousarray(forced_ids, np.int32)
         assert forced.shape == (B, k)
-    S = _shape(H, I, E, k, 1 if shared is not None else 0)
+    S = _shape(H, I, E, k, shared.n if shared is not None else 0)
     R = _experts(routed)
     Sh = _experts(shared) if shared is not None else _experts(routed)
     lib().or_forward(ctypes.byref(S), _p(x), B, _p(router), ctypes.byref(R), ctypes.byref(Sh),
@@ -195,7 +204,7 @@ def forward_dense(x: np.ndarray, router: np.ndarray, routed, shared, k: int, I: 
     B, H = x.shape
     E = router.shape[0]
     y = np.empty((B, H), np.float64)
-    S = _shape(H, I, E, k, 1 if shared is not None else 0)
+    S = _shape(H, I, E, k, shared.n if shared is not None else 0)
     R = _experts(routed)
     Sh = _experts(shared) if shared is not None else _experts(routed)
     lib().or_forward_dense(ctypes.byref(S), _p(x), B, _p(router), ctypes.byref(R),

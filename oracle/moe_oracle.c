@@ -74,6 +74,13 @@ double or_e4m3(uint8_t byte) {
   return sign ? -mag : mag;
 }
 
+/* E8M0 (OCP Microscaling Formats v1.0, the shared block scale of the MX
+ * formats): an unsigned biased exponent, 2^(b - 127); 0xFF is NaN. */
+double or_e8m0(uint8_t byte) {
+  if (byte == 0xFF) return NAN;
+  return ldexp(1.0, (int)byte - 127);
+}
+
 double or_bf16(uint16_t h) {
   uint32_t u = (uint32_t)h << 16;
   float f;
@@ -98,11 +105,15 @@ static void or_tables(void) {
 
 /* ------------------------------------------------------------ weight access */
 
-enum { OR_NVFP4 = 0, OR_BF16 = 1 };
+enum { OR_NVFP4 = 0, OR_BF16 = 1, OR_MXFP8 = 2 };
 
 /* One expert set (n experts).  NVFP4: w13 u8 [n][2][I][H/2], w13s u8
  * [n][2][I][H/16], w2 u8 [n][H][I/2], w2s u8 [n][H][I/16], glob f32 [n][3].
- * BF16: w13 u16 [n][2][I][H], w2 u16 [n][H][I]; w13s, w2s, glob unused. */
+ * BF16: w13 u16 [n][2][I][H], w2 u16 [n][H][I]; w13s, w2s, glob unused.
+ * MXFP8 (OCP MX, the expert format of the Inkling-2-Small article's last 8
+ * layers, 48-layer MoE section): E4M3 elements w13 u8 [n][2][I][H], w2 u8
+ * [n][H][I], one E8M0 scale per 32 consecutive inputs w13s u8 [n][2][I][H/32],
+ * w2s u8 [n][H][I/32]; no tensor scale (glob unused). */
 typedef struct {
   const void* w13;
   const uint8_t* w13s;
@@ -126,6 +137,15 @@ static void or_row(const or_experts* X, int64_t e, int t, int64_t r, int64_t H, 
     const uint16_t* base = t < 2 ? (const uint16_t*)X->w13 + ((e * 2 + t) * rows) * cols
                                  : (const uint16_t*)X->w2 + (e * rows) * cols;
     for (int64_t c = 0; c < cols; ++c) out[c] = or_bf16(base[r * cols + c]);
+    return;
+  }
+  if (X->fmt == OR_MXFP8) {
+    const uint8_t* el = t < 2 ? (const uint8_t*)X->w13 + ((e * 2 + t) * rows) * cols
+                              : (const uint8_t*)X->w2 + (e * rows) * cols;
+    const uint8_t* sc = t < 2 ? X->w13s + ((e * 2 + t) * rows) * (cols / 32)
+                              : X->w2s + (e * rows) * (cols / 32);
+    for (int64_t c = 0; c < cols; ++c)
+      out[c] = g_e4m3[el[r * cols + c]] * or_e8m0(sc[r * (cols / 32) + c / 32]);
     return;
   }
   const uint8_t* codes = t < 2 ? (const uint8_t*)X->w13 + ((e * 2 + t) * rows) * (cols / 2)
@@ -269,7 +289,10 @@ static int or_cmp_i32(const void* a, const void* b) {
   return (x > y) - (x < y);
 }
 
-/* One token of the layer: y = sum_j w_j d_{e_j} (ascending expert id) + d_shared. */
+/* One token of the layer: y = sum_j w_j d_{e_j} (ascending expert id), then
+ * + d_s of each shared expert s = 0 .. n_shared - 1 in turn (weight 1; the
+ * Flint page has one shared expert, the Inkling article's earlier model two,
+ * Inkling-2-Small none). */
 static void or_forward_token(const or_shape* S, const uint16_t* xb, const uint16_t* router,
                              const or_experts* routed, const or_experts* shared,
                              const int32_t* forced, double* y, int32_t* ids, double* w,
@@ -290,8 +313,8 @@ static void or_forward_token(const or_shape* S, const uint16_t* xb, const uint16
     or_expert(S, routed, sorted[s], x, d);
     for (int64_t c = 0; c < H; ++c) y[c] += wj * d[c];
   }
-  if (shared && S->n_shared > 0) {
-    or_expert(S, shared, 0, x, d);
+  for (int32_t s = 0; shared && s < S->n_shared; ++s) {
+    or_expert(S, shared, s, x, d);
     for (int64_t c = 0; c < H; ++c) y[c] += d[c];
   }
   free(x);
@@ -337,8 +360,8 @@ void or_forward_dense(const or_shape* S, const uint16_t* xb, int32_t B, const ui
       or_expert(S, routed, e, x, d);
       for (int64_t c = 0; c < H; ++c) yt[c] += m[e] * d[c];
     }
-    if (shared && S->n_shared > 0) {
-      or_expert(S, shared, 0, x, d);
+    for (int32_t s = 0; shared && s < S->n_shared; ++s) {
+      or_expert(S, shared, s, x, d);
       for (int64_t c = 0; c < H; ++c) yt[c] += d[c];
     }
   }

@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.tg_quantize_nvfp4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.tg_make_experts_nvfp4.argtypes = [u64, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]
         L.tg_make_experts_bf16.argtypes = [u64, i32, i32, i32, i32, i32, f32, vp, vp]
+        L.tg_quantize_mxfp8.argtypes = [vp, i64, i64, vp, vp]
+        L.tg_make_experts_mxfp8.argtypes = [u64, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp]
         L.tg_make_router.argtypes = [u64, i32, i32, i32, f32, vp]
         L.tg_make_x.argtypes = [u64, i32, i32, vp]
         L.tg_num_threads.restype = ctypes.c_int
@@ -133,6 +135,8 @@ def make_dense(seed: int, layer: int, which: int, N: int, K: int, sigma: float =
 class Experts:
     """One expert set.  fmt 'nvfp4': w13 u8 [n,2,I,H/2], w13_scale u8 [n,2,I,H/16],
     w2 u8 [n,H,I/2], w2_scale u8 [n,H,I/16], glob f32 [n,3].
+    fmt 'mxfp8': w13 u8 [n,2,I,H] (E4M3), w13_scale u8 [n,2,I,H/32] (E8M0),
+    w2 u8 [n,H,I], w2_scale u8 [n,H,I/32] (glob None).
     fmt 'bf16': w13 u16 [n,2,I,H], w2 u16 [n,H,I] (scales and glob None)."""
     fmt: str
     n: int
@@ -154,6 +158,14 @@ def make_experts(seed: int, layer: int, e0: int, n: int, H: int = HIDDEN, I: int
         lib().tg_make_experts_nvfp4(seed, layer, e0, n, H, I, sigma, _p(w13), _p(w13s), _p(w2),
                                     _p(w2s), _p(g))
         return Experts("nvfp4", n, w13, w2, w13s, w2s, g)
+    if fmt == "mxfp8":
+        w13 = np.empty((n, 2, I, H), np.uint8)
+        w13s = np.empty((n, 2, I, H // 32), np.uint8)
+        w2 = np.empty((n, H, I), np.uint8)
+        w2s = np.empty((n, H, I // 32), np.uint8)
+        lib().tg_make_experts_mxfp8(seed, layer, e0, n, H, I, sigma, _p(w13), _p(w13s), _p(w2),
+                                    _p(w2s))
+        return Experts("mxfp8", n, w13, w2, w13s, w2s, None)
     if fmt == "bf16":
         w13 = np.empty((n, 2, I, H), np.uint16)
         w2 = np.empty((n, H, I), np.uint16)
@@ -170,15 +182,29 @@ class Layer:
     K: int
     router: np.ndarray          # u16 [E, H]
     routed: Experts             # n = E
-    shared: Experts             # n = 1 (stream expert id E)
+    shared: Experts | None      # n = n_shared (stream expert ids E ..), None if none
 
 
 def make_layer(seed: int, layer: int = 0, fmt: str = "nvfp4", H: int = HIDDEN, I: int = INTER,
-               E: int = N_EXPERTS, K: int = TOP_K, sigma: float = SIGMA_W) -> Layer:
+               E: int = N_EXPERTS, K: int = TOP_K, sigma: float = SIGMA_W,
+               n_shared: int = 1) -> Layer:
+    """Shared experts take expert ids E .. E + n_shared - 1 of the stream key
+    (none when n_shared is 0: then `shared` is None)."""
     router = make_router(seed, layer, E, H, sigma)
     routed = make_experts(seed, layer, 0, E, H, I, fmt, sigma)
-    shared = make_experts(seed, layer, E, 1, H, I, fmt, sigma)
+    shared = make_experts(seed, layer, E, n_shared, H, I, fmt, sigma) if n_shared > 0 else None
     return Layer(H, I, E, K, router, routed, shared)
+
+
+def quantize_mxfp8(w_bf16: np.ndarray):
+    """Pack a bf16 [rows, cols] tensor to MXFP8: (E4M3 u8 [rows, cols], E8M0 u8 [rows, cols/32])."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    rows, cols = w.shape
+    assert cols % 32 == 0
+    el = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows, cols // 32), np.uint8)
+    lib().tg_quantize_mxfp8(_p(w), rows, cols, _p(el), _p(sc))
+    return el, sc
 
 
 def num_threads() -> int:

@@ -226,6 +226,70 @@ void tg_make_experts_bf16(uint64_t seed, int32_t layer, int32_t e0, int32_t n, i
   }
 }
 
+/*
+ * MXFP8 packing (OCP Microscaling Formats v1.0, conversion to an MX format):
+ * per block of 32 consecutive values, shared exponent
+ *   X = 2^(floor(log2(amax)) - 8)      (8 = exponent of E4M3's largest normal)
+ * clamped to the E8M0 range [-127, 127], stored as the byte 127 + log2 X; each
+ * element is v / X rounded to E4M3FN (nearest-even, saturating at +-448).  An
+ * all-zero block gets the byte 0 and zero elements.
+ */
+static uint8_t tg_e4m3_signed(float v) {
+  float q;
+  uint8_t b = tg_e4m3_encode(fabsf(v), &q);
+  return (uint8_t)(b | (signbit(v) ? 0x80 : 0));
+}
+
+void tg_quantize_mxfp8(const uint16_t* w, int64_t rows, int64_t cols, uint8_t* el,
+                       uint8_t* scales) {
+  int64_t nb = cols / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint16_t* blk = w + r * cols + b * 32;
+      uint8_t* eb = el + r * cols + b * 32;
+      float amax = 0.0f;
+      for (int j = 0; j < 32; ++j) {
+        float a = fabsf(tg_bf16_to_float(blk[j]));
+        if (a > amax) amax = a;
+      }
+      if (amax == 0.0f) {
+        scales[r * nb + b] = 0;
+        memset(eb, 0, 32);
+        continue;
+      }
+      int k;
+      (void)frexpf(amax, &k);                   /* amax in [2^(k-1), 2^k) */
+      int xe = (k - 1) - 8;
+      if (xe < -127) xe = -127;
+      if (xe > 127) xe = 127;
+      scales[r * nb + b] = (uint8_t)(xe + 127);
+      for (int j = 0; j < 32; ++j) eb[j] = tg_e4m3_signed(ldexpf(tg_bf16_to_float(blk[j]), -xe));
+    }
+}
+
+/* Expert set in MXFP8: w13 u8 [n][2][I][H], w13s u8 [n][2][I][H/32],
+ * w2 u8 [n][H][I], w2s u8 [n][H][I/32]. */
+void tg_make_experts_mxfp8(uint64_t seed, int32_t layer, int32_t e0, int32_t n, int32_t H,
+                           int32_t I, float sigma, uint8_t* w13, uint8_t* w13s, uint8_t* w2,
+                           uint8_t* w2s) {
+  int64_t mat = (int64_t)H * I;
+  #pragma omp parallel
+  {
+    uint16_t* tmp = (uint16_t*)malloc((size_t)mat * sizeof(uint16_t));
+    #pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < (int64_t)n * 3; ++task) {
+      int64_t e = task / 3;
+      int t = (int)(task % 3);
+      tg_normal_bf16(seed, layer, e0 + (int32_t)e, 1 + t, sigma, mat, tmp);
+      if (t < 2)
+        tg_quantize_mxfp8(tmp, I, H, w13 + (e * 2 + t) * mat, w13s + (e * 2 + t) * (mat / 32));
+      else
+        tg_quantize_mxfp8(tmp, H, I, w2 + e * mat, w2s + e * (mat / 32));
+    }
+    free(tmp);
+  }
+}
+
 /* Router [E][H] bf16, split over rows with OpenMP (row r uses elements r*H..). */
 void tg_make_router(uint64_t seed, int32_t layer, int32_t E, int32_t H, float sigma,
                     uint16_t* out) {

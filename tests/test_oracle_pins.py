@@ -8,6 +8,7 @@ a plausible slip in the oracle: a dropped or extra term, a wrong sign, a
 swapped gate/up, a transposed matrix, a wrong tie order or expert index.
 """
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -441,3 +442,108 @@ def test_fused_layer_normalises_before_routing():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     assert not np.array_equal(oracle.forward_layer(x, L)[0],
                               oracle.forward_layer(x + np.uint16(2 << 7), L)[0])
+
+
+# ----------------------------------------------------------------- MXFP8, shared-expert count
+def test_e8m0_spec_values():
+    """OCP MX v1.0 E8M0: bias 127, 2^-127 .. 2^127, 0xFF is NaN."""
+    assert oracle.e8m0(127) == 1.0
+    assert oracle.e8m0(128) == 2.0 and oracle.e8m0(126) == 0.5
+    assert oracle.e8m0(0) == 2.0 ** -127 and oracle.e8m0(254) == 2.0 ** 127
+    assert math.isnan(oracle.e8m0(255))
+
+
+def _mx_tensor(rng, n, rows, cols):
+    """Random MXFP8 bytes (finite E4M3 elements from the hand-written table,
+    scales 2^-8 .. 2^-3) and their values decoded in the test."""
+    e4 = load_table("e4m3_values.txt")
+    ok = np.array(sorted(b for b, v in e4.items() if v == v), np.uint8)
+    el = rng.choice(ok, size=(n, rows, cols)).astype(np.uint8)
+    sc = rng.integers(119, 125, (n, rows, cols // 32), dtype=np.uint8)
+    lut = np.array([e4.get(b, np.nan) for b in range(256)])
+    vals = lut[el] * np.repeat(2.0 ** (sc.astype(np.float64) - 127), 32, -1)
+    return el, sc, vals
+
+
+def test_mxfp8_layer_equals_bf16_layer_on_grid_weights():
+    """MXFP8 values (E4M3 element x power-of-two scale) are bf16-exact here; a
+    bf16 copy built from the hand-written E4M3 table, not from the oracle's
+    decoder, must give the identical layer (routed and 2 shared experts)."""
+    rng = np.random.default_rng(8)
+    HH, II = 64, 32
+    e13, s13, v13 = _mx_tensor(rng, E + 2, 2 * II, HH)
+    e2, s2, v2 = _mx_tensor(rng, E + 2, HH, II)
+
+    def mx(sl):
+        n = len(range(*sl.indices(E + 2)))
+        return testgen.Experts("mxfp8", n, e13[sl].reshape(-1, 2, II, HH).copy(), e2[sl].copy(),
+                               s13[sl].reshape(-1, 2, II, HH // 32).copy(), s2[sl].copy(), None)
+
+    def bf(sl):
+        return _bf16_experts(v13[sl].reshape(-1, 2, II, HH).astype(np.float32),
+                             v2[sl].astype(np.float32))
+
+    R = testgen.make_router(5, 0, E, HH, 0.5)
+    x = testgen.make_x(14, 3, HH)
+    y_mx, ids_mx, _, _ = oracle.forward(x, R, mx(slice(0, E)), mx(slice(E, E + 2)), K, II)
+    y_bf, ids_bf, _, _ = oracle.forward(x, R, bf(slice(0, E)), bf(slice(E, E + 2)), K, II)
+    np.testing.assert_array_equal(ids_mx, ids_bf)
+    np.testing.assert_array_equal(y_mx, y_bf)
+
+
+def test_mxfp8_packer_follows_the_mx_conversion_rule():
+    """Per 32-block: scale 2^(floor(log2 amax) - 8); amax maps into [256, 512)
+    (saturating to 448 above the last tie at 464); grid values come back exactly;
+    an all-zero block is byte 0 with zero elements."""
+    e4 = {b: oracle.e4m3(b) for b in range(256)}      # pinned against the spec table
+    vals = np.zeros((3, 32), np.float32)
+    vals[0] = 2.0 ** -4 * np.array([1, -1.5, 0.25, 3, 0.5, 1.75] * 5 + [0, 1], np.float32)
+    vals[1, 0], vals[1, 1] = 1.9375, 1.0                     # amax 1.9375 -> 496 -> 448
+    w = f32_to_bf16_bits_exact(vals)
+    el, sc = testgen.quantize_mxfp8(w)
+    # amax 3 * 2^-4 lies in [2^-3, 2^-2): exponent -3; amax 1.9375 in [1, 2): exponent 0
+    assert sc[0, 0] == 127 + (-3 - 8) and sc[1, 0] == 127 + (0 - 8) and sc[2, 0] == 0
+    dec = np.array([[e4[int(b)] for b in row] for row in el]) * \
+        np.repeat(2.0 ** (sc.astype(np.float64) - 127), 32, -1)
+    dec[2] = 0.0
+    np.testing.assert_array_equal(dec[0], vals[0])
+    assert dec[1, 0] == 448 * 2.0 ** -8 and dec[1, 1] == 1.0
+    assert not el[2].any()
+
+
+def test_mxfp8_round_trip_error_is_within_half_an_e4m3_step():
+    w = testgen.make_x(15, 64, 256)
+    el, sc = testgen.quantize_mxfp8(w)
+    lut = np.array([oracle.e4m3(b) for b in range(256)])
+    dec = lut[el] * np.repeat(2.0 ** (sc.astype(np.float64) - 127), 32, -1)
+    v = f64(w)
+    # half the relative step 2^-3 of a normal E4M3 value; subnormals have step
+    # 2^-9 * scale; values above 448 * scale (only the top of [256, 512) that
+    # the block maximum maps into) saturate to 448 * scale
+    scale = np.repeat(2.0 ** (sc.astype(np.float64) - 127), 32, -1)
+    sat = np.abs(v) > 448 * scale
+    bound = np.where(sat, np.abs(v) - 448 * scale,
+                     np.maximum(np.abs(v) * 2.0 ** -4, scale * 2.0 ** -10))
+    assert np.all(np.abs(dec - v) <= bound)
+    assert np.all(np.abs(v) / scale < 512)
+
+
+def test_every_shared_expert_is_added_with_weight_one():
+    L = testgen.make_layer(3, 0, "nvfp4", H, I, E, K, 0.5, n_shared=2)
+    x = testgen.make_x(16, 2, H)
+    y, ids, _, _ = oracle.forward_layer(x, L)
+    y0, ids0, _, _ = oracle.forward(x, L.router, L.routed, None, K, I)
+    np.testing.assert_array_equal(ids, ids0)
+    for t in range(2):
+        d = oracle.expert(L.shared, 0, f64(x[t]), H, I) + oracle.expert(L.shared, 1, f64(x[t]), H, I)
+        np.testing.assert_allclose(y[t] - y0[t], d, rtol=1e-12, atol=1e-14)
+    # two identical shared experts count twice
+    L1 = testgen.make_layer(3, 0, "nvfp4", H, I, E, K, 0.5, n_shared=1)
+    sh2 = testgen.Experts("nvfp4", 2, np.concatenate([L1.shared.w13] * 2),
+                          np.concatenate([L1.shared.w2] * 2),
+                          np.concatenate([L1.shared.w13_scale] * 2),
+                          np.concatenate([L1.shared.w2_scale] * 2),
+                          np.concatenate([L1.shared.glob] * 2))
+    y1 = oracle.forward(x, L1.router, L1.routed, L1.shared, K, I)[0]
+    y2 = oracle.forward(x, L1.router, L1.routed, sh2, K, I)[0]
+    np.testing.assert_allclose(y2 - y0, 2 * (y1 - y0), rtol=1e-12, atol=1e-13)
