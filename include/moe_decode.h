@@ -31,7 +31,8 @@
  *    workspace must be ordered (same stream, or events).
  *  - No C++ exception crosses this boundary.
  *
- * Tensor layouts (E experts in a set; H = hidden = 2048, I = inter = 512)
+ * Tensor layouts (E experts in a set; H = hidden, I = inter: 2048 and 512
+ * for Flint)
  *  x, out         bf16 [T][H], token-major.
  *  router_w       bf16 [E_routed][H] (row e gives logit e).
  *  NVFP4 expert set (16-element blocks along the input dimension):
@@ -47,7 +48,17 @@
  *    weight value = e2m1(code) * e4m3(block scale) * global.
  *  BF16 expert set: w13 bf16 [E][2][I][H], w2 bf16 [E][H][I]; the scale and
  *    global pointers must be NULL.
- *  The shared expert is an expert set with E = 1 in the same format.
+ *  MXFP8 expert set (OCP Microscaling: 32-element blocks along the input
+ *  dimension; the expert format of the last 8 layers of Inkling-2-Small in
+ *  the AREX article on vLLM's Day-0 support for it, 48-layer MoE section):
+ *    w13          u8  [E][2][I][H]     E4M3FN elements of gate and up.
+ *    w13_scale    u8  [E][2][I][H/32]  E8M0 block scales (2^(b - 127)).
+ *    w2           u8  [E][H][I]        E4M3FN elements of down.
+ *    w2_scale     u8  [E][H][I/32]     E8M0 block scales.
+ *    global       NULL (the MX formats have no tensor scale).
+ *    weight value = e4m3(element) * 2^(scale - 127).
+ *  The shared experts are one expert set of E = n_shared experts in the same
+ *  format (NULL when n_shared is 0); each is added with weight 1.
  */
 #ifndef MOE_DECODE_H
 #define MOE_DECODE_H
@@ -68,11 +79,21 @@ typedef enum {
   MOE_ERR_HIP = -5          /* a HIP launch failed                           */
 } moe_status;
 
-typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1 } moe_wformat;
+typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1, MOE_W_MXFP8 = 2 } moe_wformat;
 
-/* Layer shape.  This library serves {2048, 512, 256, 6, 1, NVFP4 | BF16}
- * (Model architecture section: hidden 2048, 256 experts, sigmoid top-6, one
- * shared expert); anything else returns MOE_ERR_UNSUPPORTED. */
+/* Layer shape.  Every entry point serves the Flint layer {2048, 512, 256, 6,
+ * 1, NVFP4 | BF16} (Model architecture section: hidden 2048, 256 experts,
+ * sigmoid top-6, one shared expert) on its fast paths.  The decode entry
+ * points (moe_decode_route, moe_decode_forward, moe_decode_forward_timed)
+ * also serve the other MoE shapes the pages name, and more, on a general
+ * path: Inkling's 256 experts with top-6 and 2 shared experts,
+ * Inkling-2-Small's 384 experts with top-8 and none (the AREX article,
+ * 48-layer MoE section), in NVFP4, BF16 or MXFP8; its limits are
+ * 32 <= H <= 8192 and 32 <= I <= 4096, both multiples of 32;
+ * 1 <= top_k <= 8; top_k <= n_experts <= 512; 0 <= n_shared <= 2.  The
+ * prefill and fused-neighbour entry points and the dequant probe return
+ * MOE_ERR_UNSUPPORTED for any shape but Flint's, and so does any entry point
+ * for a shape outside these limits. */
 typedef struct {
   int32_t hidden;    /* H */
   int32_t inter;     /* I, per expert */

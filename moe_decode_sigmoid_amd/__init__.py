@@ -16,7 +16,7 @@ LIB_PATH = HERE / "libmoe_decode.so"
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED = 0, -1, -2
 MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = -3, -4, -5
-MOE_W_NVFP4, MOE_W_BF16 = 0, 1
+MOE_W_NVFP4, MOE_W_BF16, MOE_W_MXFP8 = 0, 1, 2
 HIDDEN, INTER, N_EXPERTS, TOP_K, N_SHARED = 2048, 512, 256, 6, 1
 MAX_DECODE_BATCH = 8
 
@@ -96,7 +96,7 @@ def shape(fmt: int = MOE_W_NVFP4, hidden=HIDDEN, inter=INTER, n_experts=N_EXPERT
 
 def _fmt(fmt) -> int:
     if isinstance(fmt, str):
-        return {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16}[fmt]
+        return {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16, "mxfp8": MOE_W_MXFP8}[fmt]
     return int(fmt)
 
 
@@ -117,13 +117,20 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
+def _ref(st):
+    return None if st is None else ctypes.byref(st)
+
+
 def _check(status: int, where: str) -> None:
     if status != MOE_OK:
         raise MoeError(status, where)
 
 
-def experts_struct(ex) -> Experts:
-    """ex: object with w13, w2 and (NVFP4) w13_scale, w2_scale, glob device tensors."""
+def experts_struct(ex) -> Experts | None:
+    """ex: object with w13, w2 and (NVFP4) w13_scale, w2_scale, glob device
+    tensors, (MXFP8) w13_scale, w2_scale; None (no shared expert) -> None."""
+    if ex is None:
+        return None
     return Experts(_ptr(ex.w13), _ptr(getattr(ex, "w13_scale", None)), _ptr(ex.w2),
                    _ptr(getattr(ex, "w2_scale", None)), _ptr(getattr(ex, "glob", None)))
 
@@ -132,8 +139,9 @@ def abi_version() -> int:
     return int(lib().moe_abi_version())
 
 
-def moe_workspace_bytes(tokens: int, prefill: bool = False, fmt=MOE_W_NVFP4) -> int:
-    S = shape(_fmt(fmt))
+def moe_workspace_bytes(tokens: int, prefill: bool = False, fmt=MOE_W_NVFP4,
+                        S: Shape | None = None) -> int:
+    S = S or shape(_fmt(fmt))
     return int(lib().moe_workspace_bytes(ctypes.byref(S), tokens, 1 if prefill else 0))
 
 
@@ -153,7 +161,7 @@ def moe_decode_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_out
     B = x.shape[0] if B is None else B
     R, Sh = experts_struct(routed), experts_struct(shared)
     st = lib().moe_decode_forward(ctypes.byref(S), _ptr(x), B, _ptr(router_w), ctypes.byref(R),
-                                  ctypes.byref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
+                                  _ref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_decode_forward")
 
@@ -172,7 +180,7 @@ def moe_decode_forward_timed(x, router_w, routed, shared, out, ws, ev_start, ev_
         if not ev.cuda_event:           # torch creates its events at their first record
             ev.record(torch.cuda.current_stream())
     st = lib().moe_decode_forward_timed(ctypes.byref(S), _ptr(x), B, _ptr(router_w),
-                                        ctypes.byref(R), ctypes.byref(Sh), _ptr(out),
+                                        ctypes.byref(R), _ref(Sh), _ptr(out),
                                         _ptr(ids_out), _ptr(w_out), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream),
                                         ctypes.c_void_p(ev_start.cuda_event),
@@ -198,7 +206,7 @@ def moe_prefill_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_ou
     T = x.shape[0] if T is None else T
     R, Sh = experts_struct(routed), experts_struct(shared)
     st = lib().moe_prefill_forward(ctypes.byref(S), _ptr(x), T, _ptr(router_w), ctypes.byref(R),
-                                   ctypes.byref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
+                                   _ref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_prefill_forward")
 
@@ -218,7 +226,7 @@ def moe_decode_forward_ex(x, router_w, routed, shared, out, ws, norm_w=None, eps
     R, Sh = experts_struct(routed), experts_struct(shared)
     F = fuse_struct(norm_w, eps, residual, xn_out)
     st = lib().moe_decode_forward_ex(ctypes.byref(S), _ptr(x), B, ctypes.byref(F),
-                                     _ptr(router_w), ctypes.byref(R), ctypes.byref(Sh),
+                                     _ptr(router_w), ctypes.byref(R), _ref(Sh),
                                      _ptr(out), _ptr(ids_out), _ptr(w_out), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_decode_forward_ex")
@@ -234,7 +242,7 @@ def moe_prefill_forward_ex(x, router_w, routed, shared, out, ws, norm_w=None, ep
     R, Sh = experts_struct(routed), experts_struct(shared)
     F = fuse_struct(norm_w, eps, residual, xn_out)
     st = lib().moe_prefill_forward_ex(ctypes.byref(S), _ptr(x), T, ctypes.byref(F),
-                                      _ptr(router_w), ctypes.byref(R), ctypes.byref(Sh),
+                                      _ptr(router_w), ctypes.byref(R), _ref(Sh),
                                       _ptr(out), _ptr(ids_out), _ptr(w_out), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_prefill_forward_ex")

@@ -10,7 +10,8 @@ HERE = pathlib.Path(__file__).resolve().parent
 CSRC = HERE / "csrc"
 OBJ = HERE / "_build"
 LIB = HERE / "libmoe_decode.so"
-SOURCES = ["capi.hip", "decode.hip", "decode_fused.hip", "prefill.hip", "gemv.hip"]
+SOURCES = ["capi.hip", "decode.hip", "decode_fused.hip", "decode_general.hip", "prefill.hip",
+           "gemv.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -17,6 +17,7 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The Flint layer (every entry point; the fused kernels).
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_INVALID_ARG;
   if (s->wfmt != MOE_W_NVFP4 && s->wfmt != MOE_W_BF16) return MOE_ERR_UNSUPPORTED;
@@ -24,6 +25,34 @@ moe_status check_shape(const moe_shape* s) {
       s->top_k != moe::kK || s->n_shared != 1)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// A shape the general decode path serves (any other than Flint's fast path).
+bool general_shape(const moe_shape* s, moe::GenShape* g) {
+  if (!s) return false;
+  if (s->wfmt != MOE_W_NVFP4 && s->wfmt != MOE_W_BF16 && s->wfmt != MOE_W_MXFP8) return false;
+  const bool ok = s->hidden >= 32 && s->hidden <= 8192 && s->hidden % 32 == 0 &&
+                  s->inter >= 32 && s->inter <= 4096 && s->inter % 32 == 0 && s->top_k >= 1 &&
+                  s->top_k <= moe::kGenMaxK && s->n_experts >= s->top_k &&
+                  s->n_experts <= moe::kGenMaxE && s->n_shared >= 0 &&
+                  s->n_shared <= moe::kGenMaxNS;
+  if (ok && g) *g = moe::GenShape{s->hidden, s->inter, s->n_experts, s->top_k, s->n_shared};
+  return ok;
+}
+
+// Decode entry points: the Flint layer, or a shape of the general path.
+moe_status check_shape_decode(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (check_shape(s) == MOE_OK || general_shape(s, nullptr)) return MOE_OK;
+  return MOE_ERR_UNSUPPORTED;
+}
+bool fast_path(const moe_shape* s) { return check_shape(s) == MOE_OK; }
+
+// Workspace bytes of the decode entry points for a checked shape.
+size_t decode_ws_need(const moe_shape* s) {
+  if (fast_path(s)) return moe::kDecodeWsBytes;
+  moe::GenShape g;
+  return general_shape(s, &g) ? moe::gen_ws_bytes(g) : 0;
 }
 
 moe_status check_ptr(const void* p, uintptr_t a = 16) {
@@ -41,6 +70,10 @@ moe_status check_experts(const moe_experts* X, int fmt) {
     if ((st = check_ptr(X->w13_scale)) != MOE_OK) return st;
     if ((st = check_ptr(X->w2_scale)) != MOE_OK) return st;
     if ((st = check_ptr(X->global)) != MOE_OK) return st;
+  } else if (fmt == MOE_W_MXFP8) {
+    if ((st = check_ptr(X->w13_scale)) != MOE_OK) return st;
+    if ((st = check_ptr(X->w2_scale)) != MOE_OK) return st;
+    if (X->global) return MOE_ERR_INVALID_ARG;
   } else if (X->w13_scale || X->w2_scale || X->global) {
     return MOE_ERR_INVALID_ARG;
   }
@@ -48,6 +81,7 @@ moe_status check_experts(const moe_experts* X, int fmt) {
 }
 
 ExpertsDev to_dev(const moe_experts* X) {
+  if (!X) return ExpertsDev{};
   return ExpertsDev{static_cast<const uint8_t*>(X->w13), static_cast<const uint8_t*>(X->w13_scale),
                     static_cast<const uint8_t*>(X->w2), static_cast<const uint8_t*>(X->w2_scale),
                     X->global};
@@ -58,24 +92,26 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
-// Checks common to moe_decode_forward and moe_prefill_forward.
+// Checks common to moe_decode_forward and moe_prefill_forward (decode: the
+// general shapes are served too).  The shared set may be NULL only when the
+// shape has no shared expert.
 moe_status check_forward(const moe_shape* shape, const void* x, int32_t T, const void* router_w,
                          const moe_experts* routed, const moe_experts* shared, const void* out,
                          const int32_t* ids_out, const float* w_out, const void* ws,
-                         size_t ws_bytes, size_t ws_need) {
+                         size_t ws_bytes, size_t ws_need, bool decode = false) {
   moe_status st;
-  if ((st = check_shape(shape)) != MOE_OK) return st;
+  if ((st = decode ? check_shape_decode(shape) : check_shape(shape)) != MOE_OK) return st;
   if (T < 1) return MOE_ERR_INVALID_ARG;
   if ((st = check_ptr(x)) != MOE_OK) return st;
   if ((st = check_ptr(router_w)) != MOE_OK) return st;
   if ((st = check_ptr(out)) != MOE_OK) return st;
   if ((st = check_experts(routed, shape->wfmt)) != MOE_OK) return st;
-  if ((st = check_experts(shared, shape->wfmt)) != MOE_OK) return st;
+  if (shape->n_shared > 0 && (st = check_experts(shared, shape->wfmt)) != MOE_OK) return st;
   if (ids_out && !aligned(ids_out, 4)) return MOE_ERR_MISALIGNED;
   if (w_out && !aligned(w_out, 4)) return MOE_ERR_MISALIGNED;
   if (!ws || ws_need == 0 || ws_bytes < ws_need) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_MISALIGNED;
-  const size_t xb = (size_t)T * moe::kH * 2;
+  const size_t xb = (size_t)T * shape->hidden * 2;
   if (overlap(out, xb, x, xb)) return MOE_ERR_INVALID_ARG;
   if (overlap(out, xb, ws, ws_bytes)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
@@ -142,23 +178,31 @@ const char* moe_status_string(moe_status s) {
 }
 
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens, int32_t prefill) {
-  if (check_shape(shape) != MOE_OK || tokens < 1) return 0;
-  if (!prefill) return tokens <= moe::kMaxB ? moe::kDecodeWsBytes : 0;
+  if (tokens < 1) return 0;
+  if (!prefill) return tokens <= moe::kMaxB ? decode_ws_need(shape) : 0;
+  if (check_shape(shape) != MOE_OK) return 0;
   return moe::prefill_ws_bytes(tokens);
 }
 
 moe_status moe_decode_route(const moe_shape* shape, const void* x, int32_t B, const void* router_w,
                             int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
   moe_status st;
-  if ((st = check_shape(shape)) != MOE_OK) return st;
+  if ((st = check_shape_decode(shape)) != MOE_OK) return st;
   if (B < 1) return MOE_ERR_INVALID_ARG;
   if (B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
   if ((st = check_ptr(x)) != MOE_OK) return st;
   if ((st = check_ptr(router_w)) != MOE_OK) return st;
   if (!ids || !w) return MOE_ERR_INVALID_ARG;
   if (!aligned(ids, 4) || !aligned(w, 4)) return MOE_ERR_MISALIGNED;
-  if (!ws || ws_bytes < moe::kDecodeWsBytes) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < decode_ws_need(shape)) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_MISALIGNED;
+  moe::GenShape g;
+  if (!fast_path(shape) && general_shape(shape, &g)) {
+    const hipError_t e = moe::launch_route_general(
+        B, g, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), ids, w,
+        static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   const ExpertsDev none{};
   hipError_t e = moe::launch_decode(B, shape->wfmt, true, static_cast<const uint16_t*>(x),
                                     static_cast<const uint16_t*>(router_w), none, none, nullptr,
@@ -171,12 +215,20 @@ moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
                               const void* router_w, const moe_experts* routed,
                               const moe_experts* shared, void* out, int32_t* ids_out,
                               float* w_out, void* ws, size_t ws_bytes, void* stream) {
-  if (shape && check_shape(shape) == MOE_OK && B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
+  if (shape && check_shape_decode(shape) == MOE_OK && B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
   moe_status st = check_forward(shape, x, B, router_w, routed, shared, out, ids_out, w_out, ws,
-                                ws_bytes, moe::kDecodeWsBytes);
+                                ws_bytes, decode_ws_need(shape), true);
   if (st != MOE_OK) return st;
-  const bool fused = moe::fused_supported() && !split_path_forced();
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::GenShape g;
+  if (!fast_path(shape) && general_shape(shape, &g)) {
+    const hipError_t e = moe::launch_decode_general(
+        B, shape->wfmt, g, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w),
+        to_dev(routed), to_dev(shape->n_shared > 0 ? shared : nullptr),
+        static_cast<uint16_t*>(out), ids_out, w_out, static_cast<uint8_t*>(ws), s);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
+  const bool fused = moe::fused_supported() && !split_path_forced();
   const hipError_t e =
       fused ? moe::launch_decode_fused(B, shape->wfmt, static_cast<const uint16_t*>(x),
                                        static_cast<const uint16_t*>(router_w), to_dev(routed),
@@ -195,14 +247,24 @@ moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32
                                     float* w_out, void* ws, size_t ws_bytes, void* stream,
                                     void* ev_start, void* ev_stop) {
   if (!ev_start || !ev_stop) return MOE_ERR_INVALID_ARG;
-  if (shape && check_shape(shape) == MOE_OK && B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
+  if (shape && check_shape_decode(shape) == MOE_OK && B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
   moe_status st = check_forward(shape, x, B, router_w, routed, shared, out, ids_out, w_out, ws,
-                                ws_bytes, moe::kDecodeWsBytes);
+                                ws_bytes, decode_ws_need(shape), true);
   if (st != MOE_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   hipError_t e;
-  if (moe::fused_supported() && !split_path_forced()) {
+  moe::GenShape g;
+  if (!fast_path(shape) && general_shape(shape, &g)) {
+    e = hipEventRecord(e0, s);
+    if (e == hipSuccess)
+      e = moe::launch_decode_general(
+          B, shape->wfmt, g, static_cast<const uint16_t*>(x),
+          static_cast<const uint16_t*>(router_w), to_dev(routed),
+          to_dev(shape->n_shared > 0 ? shared : nullptr), static_cast<uint16_t*>(out), ids_out,
+          w_out, static_cast<uint8_t*>(ws), s);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+  } else if (moe::fused_supported() && !split_path_forced()) {
     e = moe::launch_decode_fused(B, shape->wfmt, static_cast<const uint16_t*>(x),
                                  static_cast<const uint16_t*>(router_w), to_dev(routed),
                                  to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
@@ -243,7 +305,7 @@ moe_status moe_decode_forward_ex(const moe_shape* shape, const void* x, int32_t 
   if (shape && check_shape(shape) == MOE_OK && B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
   moe_status st = check_forward(shape, x, B, router_w, routed, shared, out, ids_out, w_out, ws,
                                 ws_bytes, moe::kDecodeWsBytes);
-  if (st != MOE_OK) return st;
+  if (st != MOE_OK) return st;   // shapes other than Flint's: MOE_ERR_UNSUPPORTED
   moe::FuseDev fz;
   if ((st = check_fuse(fuse, B, x, out, ws, ws_bytes, &fz)) != MOE_OK) return st;
   if (!moe::fused_supported()) return MOE_ERR_UNSUPPORTED;

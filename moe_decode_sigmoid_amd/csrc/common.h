@@ -30,7 +30,46 @@ struct ExpertsDev {
   const float* glob;     // NVFP4 f32 [n][3]
 };
 
-enum { FMT_NVFP4 = 0, FMT_BF16 = 1 };
+enum { FMT_NVFP4 = 0, FMT_BF16 = 1, FMT_MXFP8 = 2 };
+
+// ------------------------------------------------------------ general shapes
+// Layer shape of the general decode path (any served H, I, E, top-k, shared
+// count; see decode_general.hip for the limits).
+struct GenShape {
+  int H, I, E, K, NS;
+};
+constexpr int kGenMaxE = 512;
+constexpr int kGenMaxK = 8;
+constexpr int kGenMaxNS = 2;
+constexpr int kGenMaxEntries = kMaxB * kGenMaxK + kGenMaxNS;
+
+// Dispatch of one call: the touched experts in ascending id, then the shared
+// experts (entry value E + s), each with its token mask and weights.
+struct GenCtl {
+  int n_entries;
+  int entry[kGenMaxEntries];
+  unsigned amask[kGenMaxEntries];
+  float wt[kGenMaxEntries][kMaxB];
+};
+
+// Workspace of the general path: logits f32 [kMaxB][E], the dispatch, and h
+// bf16 [entry][kMaxB][I].
+struct GenLayout {
+  size_t logits, ctl, h, total;
+};
+__host__ __device__ inline GenLayout gen_layout(const GenShape& S) {
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  GenLayout L;
+  L.logits = 0;
+  L.ctl = al(sizeof(float) * kMaxB * (size_t)S.E);
+  L.h = al(L.ctl + sizeof(GenCtl));
+  L.total = al(L.h + 2 * (size_t)kGenMaxEntries * kMaxB * S.I);
+  return L;
+}
+// upper bound of the entries of a call of B tokens
+__host__ __device__ inline int gen_max_entries(const GenShape& S, int B) {
+  return (S.E < B * S.K ? S.E : B * S.K) + S.NS;
+}
 
 // ---------------------------------------------------------------- workspace
 // Decode workspace, all offsets in bytes from a 256-byte-aligned base.

@@ -1,0 +1,455 @@
+// General-shape decode path (B <= 8 tokens): the same layer for the other MoE
+// shapes the pages name and the MXFP8 expert format.
+//
+// The pages describe, besides Flint's 256 experts / top-6 / one shared expert
+// ("Day-0 Support for Flint on vLLM", Model architecture section), the earlier
+// Inkling with 256 experts, top-6 and two shared experts, and Inkling-2-Small
+// with 384 experts, top-8 and none, whose last 8 layers hold their experts in
+// MXFP8 (the AREX article on vLLM's Day-0 support for Inkling-2-Small,
+// 48-layer MoE section).  The Flint layer runs on the single-launch kernel;
+// every other shape within the limits below runs here, as four launches:
+//
+//   route    one wave per router row: logits [B][E] (fp32 accumulate)
+//   select   one workgroup: per token the top-k logits (ties to the lower
+//            index), sigmoid, w = s / sum s; the touched experts become
+//            entries in ascending id, then the shared experts (weight 1)
+//   gate/up  workgroup (entry, 4 rows): per wave one gate/up row pair over
+//            the tokens of the entry: h = SiLU(g) * u, bf16, to the workspace
+//   down     per wave 64 / L output rows (L lanes per row): the weighted sum
+//            over the entries in order, rounded once to bf16
+//
+// Limits: H and I multiples of 32 (one 32-element chunk per lane step: 16
+// code bytes + 2 E4M3 scales in NVFP4, 32 E4M3 bytes + 1 E8M0 scale in MXFP8,
+// 64 bytes in BF16), H <= 8192, I <= 4096, top_k <= 8, n_experts <= 512,
+// n_shared <= 2.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kGenThreads = 256;
+
+// ------------------------------------------------------------------ weights
+// One 32-element chunk of a weight row: dot(xw) is sum_k w_k v_k over the
+// chunk before the tensor scale (v: 32 bf16 values as 16 pairs).
+template <int FMT>
+struct GChunk;
+
+template <>
+struct GChunk<FMT_NVFP4> {
+  uint4 c;
+  uint32_t s;
+  // row of `cols` inputs starting at element row * cols of tensor (codes, scales)
+  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, size_t row,
+                                       int cols, int ch) {
+    c = *reinterpret_cast<const uint4*>(codes + row * (cols / 2) + 16 * ch);
+    s = *reinterpret_cast<const uint16_t*>(scales + row * (cols / 16) + 2 * ch);
+  }
+  __device__ __forceinline__ float dot(const uint32_t (&xw)[16]) const {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      b0 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), xw[4 * d + 0], b0);
+      b0 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), xw[4 * d + 1], b0);
+      b0 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), xw[4 * d + 2], b0);
+      b0 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b0);
+    }
+#pragma unroll
+    for (int d = 2; d < 4; ++d) {
+      b1 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), xw[4 * d + 0], b1);
+      b1 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), xw[4 * d + 1], b1);
+      b1 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), xw[4 * d + 2], b1);
+      b1 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b1);
+    }
+    return b0 * e4m3_to_f32<0>(s) + b1 * e4m3_to_f32<1>(s);
+  }
+};
+
+template <>
+struct GChunk<FMT_BF16> {
+  uint4 w[4];
+  __device__ __forceinline__ void load(const uint8_t* el, const uint8_t*, size_t row, int cols,
+                                       int ch) {
+    const uint4* p = reinterpret_cast<const uint4*>(el + (row * cols + 32 * ch) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = p[i];
+  }
+  __device__ __forceinline__ float dot(const uint32_t (&xw)[16]) const {
+    float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      b0 = dot2_bf16(w[i].x, xw[4 * i + 0], b0);
+      b0 = dot2_bf16(w[i].y, xw[4 * i + 1], b0);
+      b0 = dot2_bf16(w[i].z, xw[4 * i + 2], b0);
+      b0 = dot2_bf16(w[i].w, xw[4 * i + 3], b0);
+    }
+#pragma unroll
+    for (int i = 2; i < 4; ++i) {
+      b1 = dot2_bf16(w[i].x, xw[4 * i + 0], b1);
+      b1 = dot2_bf16(w[i].y, xw[4 * i + 1], b1);
+      b1 = dot2_bf16(w[i].z, xw[4 * i + 2], b1);
+      b1 = dot2_bf16(w[i].w, xw[4 * i + 3], b1);
+    }
+    return b0 + b1;
+  }
+};
+
+// MXFP8: 32 E4M3 bytes converted pairwise to exact bf16 with gfx950's
+// scaled FP8 convert (scale 1), dot2 against x, then times the block's E8M0
+// scale 2^(b - 127), built as an fp32 bit pattern (b = 0 is the subnormal
+// 2^-127).
+template <>
+struct GChunk<FMT_MXFP8> {
+  uint4 c[2];
+  uint32_t s;
+  __device__ __forceinline__ void load(const uint8_t* el, const uint8_t* scales, size_t row,
+                                       int cols, int ch) {
+    const uint4* p = reinterpret_cast<const uint4*>(el + row * cols + 32 * ch);
+    c[0] = p[0];
+    c[1] = p[1];
+    s = scales[row * (cols / 32) + ch];
+  }
+  __device__ __forceinline__ float dot(const uint32_t (&xw)[16]) const {
+    const uint32_t w[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
+    float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], 1.0f, false);
+      const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], 1.0f, true);
+      if (d & 1) {
+        b1 = dot2_bf16(lo, xw[2 * d], b1);
+        b1 = dot2_bf16(hi, xw[2 * d + 1], b1);
+      } else {
+        b0 = dot2_bf16(lo, xw[2 * d], b0);
+        b0 = dot2_bf16(hi, xw[2 * d + 1], b0);
+      }
+    }
+    const float sc = __builtin_bit_cast(float, s == 0u ? 0x00400000u : s << 23);
+    return (b0 + b1) * sc;
+  }
+};
+
+// tensor scale of matrix m (0 gate, 1 up, 2 down) of expert ee
+template <int FMT>
+__device__ __forceinline__ float gen_gscale(const ExpertsDev& X, size_t ee, int m) {
+  if constexpr (FMT == FMT_NVFP4) return X.glob[ee * 3 + m];
+  return 1.0f;
+}
+
+// x chunk ch of token t (32 bf16 values as 16 pairs)
+__device__ __forceinline__ void load_x32(const uint16_t* x, int H, int t, int ch,
+                                         uint32_t (&xw)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H + 32 * ch);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = p[i];
+    xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+  }
+}
+
+// ------------------------------------------------------------------ route
+// One wave per router row e: logits[t][e] = sum_k W_r[e][k] x[t][k].
+__global__ __launch_bounds__(kGenThreads) void k_gen_route(const uint16_t* __restrict__ x, int B,
+                                                           const uint16_t* __restrict__ rw,
+                                                           GenShape S, uint8_t* __restrict__ ws) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (kGenThreads / 64) + (threadIdx.x >> 6);
+  if (e >= S.E) return;
+  float* logits = reinterpret_cast<float*>(ws + gen_layout(S).logits);
+  float acc[kMaxB];
+#pragma unroll
+  for (int t = 0; t < kMaxB; ++t) acc[t] = 0.0f;
+  const uint4* wrow = reinterpret_cast<const uint4*>(rw + (size_t)e * S.H);
+  for (int c = lane; c < S.H / 8; c += 64) {
+    const uint4 w = wrow[c];
+#pragma unroll
+    for (int t = 0; t < kMaxB; ++t) {
+      if (t < B) {
+        const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)t * S.H)[c];
+        float a = dot2_bf16(w.x, v.x, acc[t]);
+        a = dot2_bf16(w.y, v.y, a);
+        a = dot2_bf16(w.z, v.z, a);
+        acc[t] = dot2_bf16(w.w, v.w, a);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMaxB; ++t) {
+    if (t < B) {
+      const float z = wave_sum(acc[t]);
+      if (lane == 0) logits[t * S.E + e] = z;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ select
+// Top-k of E <= 512 logits held 8 per lane (expert lane + 64 q in v[q]) under
+// (value descending, index ascending): each round takes the wave maximum and
+// the lowest index holding it.
+__device__ __forceinline__ void wave_topk512(float (&v)[8], int lane, int K,
+                                             int (&ids)[kGenMaxK], float (&vals)[kGenMaxK]) {
+#pragma unroll
+  for (int j = 0; j < kGenMaxK; ++j) {
+    if (j >= K) break;
+    float lm = v[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) lm = fmaxf(lm, v[q]);
+    const float m = wave_max(lm);
+    int idx = -1;
+#pragma unroll
+    for (int q = 7; q >= 0; --q) {
+      const uint64_t bal = __ballot(v[q] == m);
+      if (bal) idx = 64 * q + __builtin_ctzll(bal);
+    }
+    if (idx < 0) idx = j;   // only when every value is NaN (outside the contract)
+    ids[j] = idx;
+    vals[j] = m;
+    if ((idx & 63) == lane) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if ((idx >> 6) == q) v[q] = -INFINITY;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kGenThreads) void k_gen_select(int B, GenShape S,
+                                                            int32_t* __restrict__ ids_out,
+                                                            float* __restrict__ w_out,
+                                                            uint8_t* __restrict__ ws) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const GenLayout L = gen_layout(S);
+  const float* logits = reinterpret_cast<const float*>(ws + L.logits);
+  GenCtl* ctl = reinterpret_cast<GenCtl*>(ws + L.ctl);
+  __shared__ int s_ids[kMaxB][kGenMaxK];
+  __shared__ float s_w[kMaxB][kGenMaxK];
+  __shared__ unsigned s_mask[kGenMaxE];
+  __shared__ float s_wt[kGenMaxE][kMaxB];
+  for (int t = wave; t < B; t += 4) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = e < S.E ? logits[t * S.E + e] : -INFINITY;
+    }
+    int sel_i[kGenMaxK];
+    float sel_l[kGenMaxK];
+    wave_topk512(v, lane, S.K, sel_i, sel_l);
+    if (lane == 0) {
+      float s[kGenMaxK], sum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kGenMaxK; ++j) {
+        s[j] = j < S.K ? 1.0f / (1.0f + expf(-sel_l[j])) : 0.0f;
+        sum += s[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kGenMaxK; ++j) {
+        if (j < S.K) {
+          s_ids[t][j] = sel_i[j];
+          s_w[t][j] = s[j] / sum;
+        }
+      }
+    }
+  }
+  for (int e = tid; e < S.E; e += kGenThreads) {
+    s_mask[e] = 0u;
+#pragma unroll
+    for (int t = 0; t < kMaxB; ++t) s_wt[e][t] = 0.0f;
+  }
+  __syncthreads();
+  if (tid < B * S.K) {
+    const int t = tid / S.K, j = tid % S.K;
+    const int e = s_ids[t][j];
+    atomicOr(&s_mask[e], 1u << t);
+    s_wt[e][t] = s_w[t][j];
+    if (ids_out) ids_out[t * S.K + j] = e;
+    if (w_out) w_out[t * S.K + j] = s_w[t][j];
+  }
+  __syncthreads();
+  if (wave == 0) {   // the touched experts in ascending id, then the shared ones
+    int base = 0;
+    for (int q = 0; q < kGenMaxE / 64; ++q) {
+      const int e = 64 * q + lane;
+      const unsigned m = e < S.E ? s_mask[e] : 0u;
+      const uint64_t bal = __ballot(m != 0u);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (m != 0u) {
+        ctl->entry[pos] = e;
+        ctl->amask[pos] = m;
+#pragma unroll
+        for (int t = 0; t < kMaxB; ++t) ctl->wt[pos][t] = s_wt[e][t];
+      }
+      base += __popcll(bal);
+    }
+    if (lane < S.NS) {
+      ctl->entry[base + lane] = S.E + lane;
+      ctl->amask[base + lane] = (1u << B) - 1u;
+#pragma unroll
+      for (int t = 0; t < kMaxB; ++t) ctl->wt[base + lane][t] = t < B ? 1.0f : 0.0f;
+    }
+    if (lane == 0) ctl->n_entries = base + S.NS;
+  }
+}
+
+// ------------------------------------------------------------------ gate/up
+// Workgroup (entry a, rows 4 blockIdx.y + wave): h[a][t][r] = SiLU(g) * u for
+// the entry's tokens, bf16.
+template <int FMT>
+__global__ __launch_bounds__(kGenThreads) void k_gen_gateup(const uint16_t* __restrict__ x, int B,
+                                                            GenShape S, ExpertsDev routed,
+                                                            ExpertsDev shared,
+                                                            uint8_t* __restrict__ ws) {
+  const int lane = threadIdx.x & 63;
+  const int a = blockIdx.x;
+  const int r = blockIdx.y * (kGenThreads / 64) + (threadIdx.x >> 6);
+  const GenLayout L = gen_layout(S);
+  const GenCtl* ctl = reinterpret_cast<const GenCtl*>(ws + L.ctl);
+  if (a >= ctl->n_entries || r >= S.I) return;
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.h);
+  const int e = ctl->entry[a];
+  const unsigned mask = ctl->amask[a];
+  const bool sh = e >= S.E;
+  const ExpertsDev& X = sh ? shared : routed;
+  const size_t ee = sh ? (size_t)(e - S.E) : (size_t)e;
+  const size_t rg = (ee * 2 + 0) * S.I + r, ru = (ee * 2 + 1) * S.I + r;
+  float ag[kMaxB], au[kMaxB];
+#pragma unroll
+  for (int t = 0; t < kMaxB; ++t) ag[t] = au[t] = 0.0f;
+  for (int ch = lane; ch < S.H / 32; ch += 64) {
+    GChunk<FMT> cg, cu;
+    cg.load(X.w13, X.w13s, rg, S.H, ch);
+    cu.load(X.w13, X.w13s, ru, S.H, ch);
+#pragma unroll
+    for (int t = 0; t < kMaxB; ++t) {
+      if ((mask >> t) & 1u) {
+        uint32_t xw[16];
+        load_x32(x, S.H, t, ch, xw);
+        ag[t] += cg.dot(xw);
+        au[t] += cu.dot(xw);
+      }
+    }
+  }
+  const float sg = gen_gscale<FMT>(X, ee, 0), su = gen_gscale<FMT>(X, ee, 1);
+#pragma unroll
+  for (int t = 0; t < kMaxB; ++t) {
+    if ((mask >> t) & 1u) {
+      const float g = wave_sum(ag[t]) * sg, u = wave_sum(au[t]) * su;
+      if (lane == 0) hbuf[((size_t)a * kMaxB + t) * S.I + r] = f32_to_bf16_rne(silu_mul(g, u));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ down + combine
+// A wave covers 64 / LPR output rows, LPR lanes each (LPR = 16, 32 or 64 by
+// the chunk count of I); the entries are added in their order (routed
+// experts by ascending id, then the shared ones), each with its weight.
+template <int FMT, int LPR>
+__global__ __launch_bounds__(kGenThreads) void k_gen_down(int B, GenShape S, ExpertsDev routed,
+                                                          ExpertsDev shared,
+                                                          uint8_t* __restrict__ ws,
+                                                          uint16_t* __restrict__ out) {
+  constexpr int kRowsPerWave = 64 / LPR;
+  const int lane = threadIdx.x & 63, sub = lane % LPR;
+  const int j = (blockIdx.x * (kGenThreads / 64) + (threadIdx.x >> 6)) * kRowsPerWave + lane / LPR;
+  const GenLayout L = gen_layout(S);
+  const GenCtl* ctl = reinterpret_cast<const GenCtl*>(ws + L.ctl);
+  const uint16_t* hbuf = reinterpret_cast<const uint16_t*>(ws + L.h);
+  const bool live = j < S.H;
+  const int na = ctl->n_entries;
+  float acc[kMaxB];
+#pragma unroll
+  for (int t = 0; t < kMaxB; ++t) acc[t] = 0.0f;
+  for (int a = 0; a < na; ++a) {
+    const int e = ctl->entry[a];
+    const unsigned mask = ctl->amask[a];
+    const bool sh = e >= S.E;
+    const ExpertsDev& X = sh ? shared : routed;
+    const size_t ee = sh ? (size_t)(e - S.E) : (size_t)e;
+    float part[kMaxB];
+#pragma unroll
+    for (int t = 0; t < kMaxB; ++t) part[t] = 0.0f;
+    if (live) {
+      for (int ch = sub; ch < S.I / 32; ch += LPR) {
+        GChunk<FMT> cd;
+        cd.load(X.w2, X.w2s, ee * S.H + j, S.I, ch);
+#pragma unroll
+        for (int t = 0; t < kMaxB; ++t) {
+          if ((mask >> t) & 1u) {
+            uint32_t hw[16];
+            const uint4* p = reinterpret_cast<const uint4*>(hbuf + ((size_t)a * kMaxB + t) * S.I +
+                                                            32 * ch);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint4 v = p[i];
+              hw[4 * i] = v.x; hw[4 * i + 1] = v.y; hw[4 * i + 2] = v.z; hw[4 * i + 3] = v.w;
+            }
+            part[t] += cd.dot(hw);
+          }
+        }
+      }
+    }
+    const float sd = live ? gen_gscale<FMT>(X, ee, 2) : 0.0f;
+#pragma unroll
+    for (int t = 0; t < kMaxB; ++t) {
+      if ((mask >> t) & 1u) {
+        float z = part[t];
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) z += __shfl_xor(z, o, 64);
+        acc[t] += ctl->wt[a][t] * (z * sd);
+      }
+    }
+  }
+  if (live && sub == 0) {
+    for (int t = 0; t < B; ++t) out[(size_t)t * S.H + j] = f32_to_bf16_rne(acc[t]);
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+size_t gen_ws_bytes(const GenShape& S) { return gen_layout(S).total; }
+
+hipError_t launch_route_general(int B, const GenShape& S, const uint16_t* x, const uint16_t* rw,
+                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st) {
+  hipLaunchKernelGGL(k_gen_route, dim3((S.E + 3) / 4), dim3(kGenThreads), 0, st, x, B, rw, S, ws);
+  hipLaunchKernelGGL(k_gen_select, dim3(1), dim3(kGenThreads), 0, st, B, S, ids, w, ws);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static void launch_experts_general(int B, const GenShape& S, const uint16_t* x,
+                                   const ExpertsDev& routed, const ExpertsDev& shared,
+                                   uint16_t* out, uint8_t* ws, hipStream_t st) {
+  const int maxa = gen_max_entries(S, B);
+  hipLaunchKernelGGL(k_gen_gateup<FMT>, dim3(maxa, (S.I + 3) / 4), dim3(kGenThreads), 0, st, x, B,
+                     S, routed, shared, ws);
+  const int nch = S.I / 32;
+  if (nch <= 16) {
+    const int rows = kGenThreads / 64 * 4;
+    hipLaunchKernelGGL((k_gen_down<FMT, 16>), dim3((S.H + rows - 1) / rows), dim3(kGenThreads), 0,
+                       st, B, S, routed, shared, ws, out);
+  } else if (nch <= 32) {
+    const int rows = kGenThreads / 64 * 2;
+    hipLaunchKernelGGL((k_gen_down<FMT, 32>), dim3((S.H + rows - 1) / rows), dim3(kGenThreads), 0,
+                       st, B, S, routed, shared, ws, out);
+  } else {
+    const int rows = kGenThreads / 64;
+    hipLaunchKernelGGL((k_gen_down<FMT, 64>), dim3((S.H + rows - 1) / rows), dim3(kGenThreads), 0,
+                       st, B, S, routed, shared, ws, out);
+  }
+}
+
+hipError_t launch_decode_general(int B, int fmt, const GenShape& S, const uint16_t* x,
+                                 const uint16_t* rw, const ExpertsDev& routed,
+                                 const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
+                                 uint8_t* ws, hipStream_t st) {
+  hipError_t e = launch_route_general(B, S, x, rw, ids, w, ws, st);
+  if (e != hipSuccess) return e;
+  if (fmt == FMT_NVFP4)
+    launch_experts_general<FMT_NVFP4>(B, S, x, routed, shared, out, ws, st);
+  else if (fmt == FMT_BF16)
+    launch_experts_general<FMT_BF16>(B, S, x, routed, shared, out, ws, st);
+  else
+    launch_experts_general<FMT_MXFP8>(B, S, x, routed, shared, out, ws, st);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -42,6 +42,16 @@ hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
                           int32_t* ids, float* w, uint8_t* ws, hipStream_t st,
                           const FuseDev& fuse = FuseDev{});
 
+// General-shape decode path, B = 1..8 (any served shape and format,
+// including MXFP8): four launches.  The route-only entry runs its first two.
+size_t gen_ws_bytes(const GenShape& S);
+hipError_t launch_route_general(int B, const GenShape& S, const uint16_t* x, const uint16_t* rw,
+                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
+hipError_t launch_decode_general(int B, int fmt, const GenShape& S, const uint16_t* x,
+                                 const uint16_t* rw, const ExpertsDev& routed,
+                                 const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
+                                 uint8_t* ws, hipStream_t st);
+
 // Workspace bytes of the prefill path for T tokens (0 = not served).
 size_t prefill_ws_bytes(int T);
 

@@ -23,7 +23,8 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 class DeviceExperts:
     """An expert set resident in HBM.  NVFP4: w13 u8 [n,2,I,H/2], w13_scale u8
     [n,2,I,H/16], w2 u8 [n,H,I/2], w2_scale u8 [n,H,I/16], glob f32 [n,3].
-    BF16: w13 bf16 [n,2,I,H], w2 bf16 [n,H,I]."""
+    BF16: w13 bf16 [n,2,I,H], w2 bf16 [n,H,I].  MXFP8: w13 u8 [n,2,I,H],
+    w13_scale u8 [n,2,I,H/32], w2 u8 [n,H,I], w2_scale u8 [n,H,I/32]."""
     fmt: str
     n: int
     w13: torch.Tensor
@@ -39,12 +40,17 @@ class DeviceExperts:
             return cls("nvfp4", ex.n, _dev(ex.w13, device), _dev(ex.w2, device),
                        _dev(ex.w13_scale, device), _dev(ex.w2_scale, device),
                        _dev(ex.glob, device))
+        if ex.fmt == "mxfp8":
+            return cls("mxfp8", ex.n, _dev(ex.w13, device), _dev(ex.w2, device),
+                       _dev(ex.w13_scale, device), _dev(ex.w2_scale, device))
         return cls("bf16", ex.n, _dev(ex.w13, device), _dev(ex.w2, device))
 
     def nbytes_per_expert(self) -> int:
         tot = self.w13.numel() * self.w13.element_size() + self.w2.numel() * self.w2.element_size()
+        if self.fmt in ("nvfp4", "mxfp8"):
+            tot += self.w13_scale.numel() + self.w2_scale.numel()
         if self.fmt == "nvfp4":
-            tot += self.w13_scale.numel() + self.w2_scale.numel() + self.glob.numel() * 4
+            tot += self.glob.numel() * 4
         return tot // self.n
 
 
@@ -53,14 +59,14 @@ class DeviceLayer:
     fmt: str
     router: torch.Tensor          # bf16 [E, H]
     routed: DeviceExperts
-    shared: DeviceExperts
+    shared: DeviceExperts | None      # None when the layer has no shared expert
 
     @classmethod
     def from_host(cls, layer, device="cuda") -> "DeviceLayer":
         """layer: host layer with router (u16 [E, H]), routed and shared expert sets."""
         return cls(layer.routed.fmt, _dev(layer.router, device),
                    DeviceExperts.from_host(layer.routed, device),
-                   DeviceExperts.from_host(layer.shared, device))
+                   None if layer.shared is None else DeviceExperts.from_host(layer.shared, device))
 
 
 def to_device_bf16(a: np.ndarray, device="cuda") -> torch.Tensor:

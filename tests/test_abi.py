@@ -44,8 +44,10 @@ def test_workspace_sizes():
         assert moe.moe_workspace_bytes(B) > 0
     assert moe.moe_workspace_bytes(9) == 0
     assert moe.moe_workspace_bytes(0) == 0
-    S = moe.shape(moe.MOE_W_NVFP4, hidden=4096)
+    S = moe.shape(moe.MOE_W_NVFP4, hidden=4100)
     assert moe.lib().moe_workspace_bytes(ctypes.byref(S), 1, 0) == 0
+    S = moe.shape(moe.MOE_W_NVFP4, hidden=4096)                  # general decode path
+    assert moe.lib().moe_workspace_bytes(ctypes.byref(S), 1, 0) > 0
 
 
 # Fake, never-dereferenced device addresses: every call below must be refused
@@ -96,9 +98,16 @@ def test_forward_argument_errors(prefill):
     bf = _FakeExperts(A + 0x4000000)                     # BF16 sets carry no scales
     assert _forward(S=moe.shape(moe.MOE_W_BF16), routed=bf, prefill=prefill) == E.MOE_ERR_INVALID_ARG
     assert _forward(ids=A + 2, prefill=prefill) == E.MOE_ERR_MISALIGNED
+    # shapes the general decode path serves: prefill refuses them; decode accepts
+    # them and still checks the rest first (here: a workspace that is too small)
     for kw in [dict(hidden=4096), dict(inter=1024), dict(n_experts=384), dict(top_k=8),
-               dict(n_shared=2)]:
-        assert _forward(S=moe.shape(**kw), prefill=prefill) == E.MOE_ERR_UNSUPPORTED
+               dict(n_shared=2), dict(n_experts=384, top_k=8, n_shared=0)]:
+        got = _forward(S=moe.shape(**kw), prefill=prefill, ws_bytes=1024)
+        assert got == (E.MOE_ERR_UNSUPPORTED if prefill else E.MOE_ERR_WORKSPACE), kw
+    # outside every path
+    for kw in [dict(hidden=4100), dict(inter=48), dict(n_experts=1024), dict(top_k=9),
+               dict(n_shared=3), dict(n_experts=4, top_k=6), dict(hidden=16384)]:
+        assert _forward(S=moe.shape(**kw), prefill=prefill) == E.MOE_ERR_UNSUPPORTED, kw
     assert _forward(S=moe.shape(7), prefill=prefill) == E.MOE_ERR_UNSUPPORTED
 
 
@@ -175,6 +184,45 @@ def test_fused_neighbour_argument_errors(prefill):
     assert call(B=0, norm_w=NW) == E.MOE_ERR_INVALID_ARG
     if not prefill:
         assert call(B=9, norm_w=NW) == E.MOE_ERR_UNSUPPORTED
+
+
+def test_general_shapes_workspace_and_expert_checks():
+    """General decode shapes: workspace sizes, MXFP8 sets (scales, no global),
+    a missing shared set only when the shape has none.  Every call below
+    fails a check (fake pointers must never reach a launch)."""
+    S = moe.shape(moe.MOE_W_MXFP8, n_experts=384, top_k=8, n_shared=0)
+    L = moe.lib()
+    need = L.moe_workspace_bytes(ctypes.byref(S), 8, 0)
+    assert need > 0 and L.moe_workspace_bytes(ctypes.byref(S), 9, 0) == 0
+    assert L.moe_workspace_bytes(ctypes.byref(S), 8, 1) == 0          # no general prefill
+    assert moe.moe_workspace_bytes(1) == moe.moe_workspace_bytes(8)   # Flint: one size
+
+    class MX:
+        def __init__(self, base, glob=None):
+            self.w13, self.w2 = base, base + 0x100000
+            self.w13_scale, self.w2_scale, self.glob = base + 0x200000, base + 0x300000, glob
+    R = moe.experts_struct(MX(A + 0x4000000))
+    fn = L.moe_decode_forward
+
+    def call(S=S, routed=R, shared=None, ws_bytes=need - 256, out=A + 0x2000000):
+        return fn(ctypes.byref(S), A, 2, A + 0x1000000, ctypes.byref(routed),
+                  None if shared is None else ctypes.byref(shared), out, None, None,
+                  A + 0x3000000, ws_bytes, 0)
+    assert call() == moe.MOE_ERR_WORKSPACE                 # shared NULL is fine with none
+    assert call(routed=moe.experts_struct(MX(A + 0x4000000, glob=A))) == moe.MOE_ERR_INVALID_ARG
+    bad = MX(A + 0x4000000)
+    bad.w2_scale = None
+    assert call(routed=moe.experts_struct(bad)) == moe.MOE_ERR_INVALID_ARG
+    S2 = moe.shape(moe.MOE_W_MXFP8, n_shared=2)
+    assert call(S=S2) == moe.MOE_ERR_INVALID_ARG            # two shared experts, set missing
+    assert call(S=S2, shared=R, ws_bytes=1024) == moe.MOE_ERR_WORKSPACE
+    # the fused-neighbour entry and the dequant probe stay Flint-only
+    F = moe.Fuse(None, 1e-6, None, None)
+    assert L.moe_decode_forward_ex(ctypes.byref(S), A, 2, ctypes.byref(F), A + 0x1000000,
+                                   ctypes.byref(R), None, A + 0x2000000, None, None,
+                                   A + 0x3000000, WS_BIG, 0) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_nvfp4_dequant(ctypes.byref(S), ctypes.byref(R), 0, 0, A, 0) == \
+        moe.MOE_ERR_UNSUPPORTED
 
 
 def test_decode_batch_limit_is_unsupported_not_invalid():
