@@ -157,6 +157,80 @@ def run_dense(args, moe, testgen, torch, dev) -> dict:
     return out
 
 
+# other MoE shapes of the pages (the general decode path); hidden and expert
+# intermediate sizes are Flint's (the pages give none for these models)
+GENERAL_SHAPES = {
+    "inkling2small_384x8_mxfp8": (2048, 512, 384, 8, 0, "mxfp8"),
+    "inkling_256x6_2shared_nvfp4": (2048, 512, 256, 6, 2, "nvfp4"),
+}
+
+
+def expert_bytes(H: int, I: int, fmt: str) -> int:
+    """Bytes of one expert (gate, up, down) as the kernels read them."""
+    m = H * I
+    if fmt == "nvfp4":
+        return 3 * (m // 2 + m // 16 + 4)
+    if fmt == "mxfp8":
+        return 3 * (m + m // 32)
+    return 3 * 2 * m
+
+
+def run_general(args, moe, testgen, torch, dev, copies: int = 16) -> dict:
+    """Each shape at batch 1 and 8: one host layer, `copies` device copies (a
+    pass touches more than the last-level cache), one graph of `copies`
+    launches per step, HIP events around the replays."""
+    out = {}
+    for name, (H, I, E, K, NS, fmt) in GENERAL_SHAPES.items():
+        host = testgen.make_layer(args.seed, 0, fmt, H, I, E, K, n_shared=NS)
+        d0 = moe.DeviceLayer.from_host(host, dev)
+        del host
+
+        def clone(dx):
+            if dx is None:
+                return None
+            return moe.device.DeviceExperts(
+                dx.fmt, dx.n, dx.w13.clone(), dx.w2.clone(),
+                None if dx.w13_scale is None else dx.w13_scale.clone(),
+                None if dx.w2_scale is None else dx.w2_scale.clone(),
+                None if dx.glob is None else dx.glob.clone())
+        ls = [d0] + [moe.device.DeviceLayer(d0.fmt, d0.router.clone(), clone(d0.routed),
+                                            clone(d0.shared)) for _ in range(copies - 1)]
+        S = moe.shape(moe._fmt(fmt), hidden=H, inter=I, n_experts=E, top_k=K, n_shared=NS)
+        for B in (1, 8):
+            x = moe.device.to_device_bf16(testgen.make_x(args.seed, B, H), dev)
+            y = torch.empty((copies, B, H), dtype=torch.bfloat16, device=dev)
+            ids = torch.empty((B, K), dtype=torch.int32, device=dev)
+            ws = moe.alloc_workspace(moe.moe_workspace_bytes(B, S=S), dev)
+            moe.moe_decode_forward(x, ls[0].router, ls[0].routed, ls[0].shared, y[0], ws, ids,
+                                   S=S)
+            torch.cuda.synchronize()
+            n_read = len(set(ids.cpu().numpy().ravel().tolist())) + NS
+            nb = n_read * expert_bytes(H, I, fmt) + E * H * 2 + 2 * 2 * B * H
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for l, d in enumerate(ls):
+                    moe.moe_decode_forward(x, d.router, d.routed, d.shared, y[l], ws, S=S)
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000 / (args.steps * copies)
+            out[f"{name}_b{B}"] = dict(H=H, I=I, E=E, top_k=K, n_shared=NS, fmt=fmt, B=B,
+                                       experts_read=n_read, bytes_per_call=nb,
+                                       us_per_layer=round(us, 3),
+                                       gbps=round(nb / (us * 1e-6) / 1e9, 1))
+            log(f"general {name} B={B}: {us:.2f} us/layer, {nb / (us * 1e-6) / 1e9:.0f} GB/s")
+            del g
+        del ls, d0
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,9 +243,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate host time spent on the oracle baseline (0 = skip)")
     ap.add_argument("--workload", default="all",
-                    choices=["all", "decode", "prefill", "dense", "copy"],
+                    choices=["all", "decode", "prefill", "dense", "general", "copy"],
                     help="decode = the 47-layer stack only; prefill = the 8192-token layer only; "
                          "dense = the NVFP4 attention-projection GEMVs only; "
+                         "general = the other MoE shapes (general decode path) only; "
                          "copy = a plain 1 GiB device copy (reference for the traffic counters)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--traffic-record", nargs=4, metavar="CSV",
@@ -208,6 +283,10 @@ def main() -> int:
     fmt = args.fmt
     if args.workload == "dense":
         print(json.dumps({"dense_gemv": run_dense(args, moe, testgen, torch, dev)}), flush=True)
+        return 0
+    if args.workload == "general":
+        print(json.dumps({"general_shapes": run_general(args, moe, testgen, torch, dev)}),
+              flush=True)
         return 0
     L = 1 if args.workload == "prefill" else args.layers
 
@@ -346,8 +425,10 @@ def main() -> int:
         rp = run_prefill()
         log(f"prefill {rp['tokens']} tokens: {rp['ms_per_layer']:.3f} ms/layer, "
             f"{rp['tflops']:.0f} TFLOP/s ({100 * rp['mfma_util']:.1f}% of bf16 peak)")
+    rg = None
     if args.workload == "all":
         rd = run_dense(args, moe, testgen, torch, dev)
+        rg = run_general(args, moe, testgen, torch, dev)
     if r1 is None:
         print(json.dumps({"prefill": rp}), flush=True)
         return 0
@@ -398,6 +479,7 @@ def main() -> int:
                    "layers": L, "batch": 1, "weight_format": fmt,
                    "resident_weight_bytes": int(resident)},
         "batch1": r1, "batch8": r8, "batch1_fused_norm_residual": rf, "prefill": rp, "dense_gemv": rd,
+        "general_shapes": rg,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -15,8 +15,9 @@
 //            entries in ascending id, then the shared experts (weight 1)
 //   gate/up  workgroup (entry, 4 rows): per wave one gate/up row pair over
 //            the tokens of the entry: h = SiLU(g) * u, bf16, to the workspace
-//   down     per wave 64 / L output rows (L lanes per row): the weighted sum
-//            over the entries in order, rounded once to bf16
+//   down     per workgroup 64 / L output rows (L lanes per row), its waves
+//            splitting the entries by expert id: the weighted sum over the
+//            entries, rounded once to bf16
 //
 // Limits: H and I multiples of 32 (one 32-element chunk per lane step: 16
 // code bytes + 2 E4M3 scales in NVFP4, 32 E4M3 bytes + 1 E8M0 scale in MXFP8,
@@ -340,27 +341,34 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_gateup(const uint16_t* __re
 }
 
 // ------------------------------------------------------------------ down + combine
-// A wave covers 64 / LPR output rows, LPR lanes each (LPR = 16, 32 or 64 by
-// the chunk count of I); the entries are added in their order (routed
-// experts by ascending id, then the shared ones), each with its weight.
+// A workgroup covers 64 / LPR output rows (LPR lanes per row; LPR = 16, 32 or
+// 64 by the chunk count of I).  Its 4 waves split the entries by expert id
+// (wave w: routed experts in [w E / 4, (w + 1) E / 4), the shared experts in
+// wave 3), each walking its entries in order, and the 4 partial sums are added
+// in wave order: a token's sum depends only on its own experts, never on the
+// rest of the batch.
 template <int FMT, int LPR>
 __global__ __launch_bounds__(kGenThreads) void k_gen_down(int B, GenShape S, ExpertsDev routed,
                                                           ExpertsDev shared,
                                                           uint8_t* __restrict__ ws,
                                                           uint16_t* __restrict__ out) {
-  constexpr int kRowsPerWave = 64 / LPR;
-  const int lane = threadIdx.x & 63, sub = lane % LPR;
-  const int j = (blockIdx.x * (kGenThreads / 64) + (threadIdx.x >> 6)) * kRowsPerWave + lane / LPR;
+  constexpr int kRows = 64 / LPR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane % LPR;
+  const int q = lane / LPR;
+  const int j = blockIdx.x * kRows + q;
   const GenLayout L = gen_layout(S);
   const GenCtl* ctl = reinterpret_cast<const GenCtl*>(ws + L.ctl);
   const uint16_t* hbuf = reinterpret_cast<const uint16_t*>(ws + L.h);
+  __shared__ float s_red[4][kRows][kMaxB];
   const bool live = j < S.H;
   const int na = ctl->n_entries;
+  const int e_lo = (wave * S.E) / 4, e_hi = wave == 3 ? S.E + S.NS : ((wave + 1) * S.E) / 4;
   float acc[kMaxB];
 #pragma unroll
   for (int t = 0; t < kMaxB; ++t) acc[t] = 0.0f;
   for (int a = 0; a < na; ++a) {
     const int e = ctl->entry[a];
+    if (e < e_lo || e >= e_hi) continue;
     const unsigned mask = ctl->amask[a];
     const bool sh = e >= S.E;
     const ExpertsDev& X = sh ? shared : routed;
@@ -399,8 +407,17 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_down(int B, GenShape S, Exp
       }
     }
   }
-  if (live && sub == 0) {
-    for (int t = 0; t < B; ++t) out[(size_t)t * S.H + j] = f32_to_bf16_rne(acc[t]);
+  if (sub == 0) {
+#pragma unroll
+    for (int t = 0; t < kMaxB; ++t) s_red[wave][q][t] = acc[t];
+  }
+  __syncthreads();
+  if (tid < kRows * kMaxB) {
+    const int rq = tid / kMaxB, t = tid % kMaxB, jj = blockIdx.x * kRows + rq;
+    if (jj < S.H && t < B) {
+      const float y = ((s_red[0][rq][t] + s_red[1][rq][t]) + s_red[2][rq][t]) + s_red[3][rq][t];
+      out[(size_t)t * S.H + jj] = f32_to_bf16_rne(y);
+    }
   }
 }
 
@@ -422,19 +439,15 @@ static void launch_experts_general(int B, const GenShape& S, const uint16_t* x,
   hipLaunchKernelGGL(k_gen_gateup<FMT>, dim3(maxa, (S.I + 3) / 4), dim3(kGenThreads), 0, st, x, B,
                      S, routed, shared, ws);
   const int nch = S.I / 32;
-  if (nch <= 16) {
-    const int rows = kGenThreads / 64 * 4;
-    hipLaunchKernelGGL((k_gen_down<FMT, 16>), dim3((S.H + rows - 1) / rows), dim3(kGenThreads), 0,
-                       st, B, S, routed, shared, ws, out);
-  } else if (nch <= 32) {
-    const int rows = kGenThreads / 64 * 2;
-    hipLaunchKernelGGL((k_gen_down<FMT, 32>), dim3((S.H + rows - 1) / rows), dim3(kGenThreads), 0,
-                       st, B, S, routed, shared, ws, out);
-  } else {
-    const int rows = kGenThreads / 64;
-    hipLaunchKernelGGL((k_gen_down<FMT, 64>), dim3((S.H + rows - 1) / rows), dim3(kGenThreads), 0,
-                       st, B, S, routed, shared, ws, out);
-  }
+  if (nch <= 16)
+    hipLaunchKernelGGL((k_gen_down<FMT, 16>), dim3((S.H + 3) / 4), dim3(kGenThreads), 0, st, B, S,
+                       routed, shared, ws, out);
+  else if (nch <= 32)
+    hipLaunchKernelGGL((k_gen_down<FMT, 32>), dim3((S.H + 1) / 2), dim3(kGenThreads), 0, st, B, S,
+                       routed, shared, ws, out);
+  else
+    hipLaunchKernelGGL((k_gen_down<FMT, 64>), dim3(S.H), dim3(kGenThreads), 0, st, B, S, routed,
+                       shared, ws, out);
 }
 
 hipError_t launch_decode_general(int B, int fmt, const GenShape& S, const uint16_t* x,
