@@ -367,6 +367,29 @@ def main() -> int:
         g.replay()
         torch.cuda.synchronize()
         same = bool(torch.equal(ref, outs))
+        stack = None
+        if not fused:
+            # the same L layers as ONE launch (moe_decode_stack_forward), in a graph
+            table = moe.layer_table(layers, dev)
+            outs.zero_()
+            moe.moe_decode_stack_forward(xd, table, outs, ws, S=S, B=B)
+            torch.cuda.synchronize()
+            stack_same = bool(torch.equal(ref, outs))
+            gs = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gs):
+                moe.moe_decode_stack_forward(xd, table, outs, ws, S=S, B=B)
+            for _ in range(args.warmup):
+                gs.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                gs.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms_s = e0.elapsed_time(e1) / args.steps
+            stack = dict(ms_per_pass=ms_s, us_per_layer=ms_s * 1000 / L,
+                         gbps=pass_bytes / (ms_s * 1e-3) / 1e9, equals_per_layer_calls=stack_same)
+            del gs
         if fused:
             return dict(B=B, ms_per_pass=ms, us_per_layer=ms * 1000 / L, pass_bytes=pass_bytes,
                         gbps=pass_bytes / (ms * 1e-3) / 1e9, graph_matches_eager=same,
@@ -376,7 +399,7 @@ def main() -> int:
                     kernel_us_mean=float(np.mean(call_ms)) * 1000,
                     kernel_gbps=float(np.mean([layer_bytes(n, B, fmt) / (c * 1e-3) / 1e9
                                                for n, c in zip(n_read, call_ms)])),
-                    graph_matches_eager=same)
+                    graph_matches_eager=same, stack_one_launch=stack)
 
     def run_prefill() -> dict:
         T = PREFILL_T
@@ -416,11 +439,17 @@ def main() -> int:
     if args.workload in ("all", "decode"):
         r1 = run_batch(1)
         log(f"B=1: {r1['us_per_layer']:.2f} us/layer, {r1['gbps']:.0f} GB/s")
+        st1 = r1["stack_one_launch"]
+        log(f"B=1 stack in one launch: {st1['us_per_layer']:.2f} us/layer, {st1['gbps']:.0f} GB/s "
+            f"(equal to per-layer calls: {st1['equals_per_layer_calls']})")
         rf = run_batch(1, fused=True)
         log(f"B=1 with RMSNorm + residual fused: {rf['us_per_layer']:.2f} us/layer")
         if not args.no_batch8:
             r8 = run_batch(8)
             log(f"B=8: {r8['us_per_layer']:.2f} us/layer, {r8['gbps']:.0f} GB/s")
+            st8 = r8["stack_one_launch"]
+            log(f"B=8 stack in one launch: {st8['us_per_layer']:.2f} us/layer, "
+                f"{st8['gbps']:.0f} GB/s")
     if args.workload in ("all", "prefill"):
         rp = run_prefill()
         log(f"prefill {rp['tokens']} tokens: {rp['ms_per_layer']:.3f} ms/layer, "

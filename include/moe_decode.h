@@ -190,6 +190,33 @@ moe_status moe_prefill_forward(const moe_shape* shape, const void* x, int32_t T,
                                const moe_experts* shared, void* out, int32_t* ids_out,
                                float* w_out, void* ws, size_t ws_bytes, void* stream);
 
+/* One layer of a stack for moe_decode_stack_forward: its router and expert
+ * sets, with the same meaning and rules as moe_decode_forward's arguments.
+ * The layout (11 pointers, 88 bytes) is part of the ABI. */
+typedef struct {
+  const void* router_w;
+  moe_experts routed;
+  moe_experts shared;
+} moe_layer;
+
+/* A stack of n_layers independent Flint layers that all read the same x
+ * (B = 1..8 tokens), in ONE launch: out[l] = layer_l(x).  Every workgroup
+ * runs layer l + 1 as soon as its part of layer l is done, so there is no
+ * launch gap between layers (the pages hide that gap with programmatic
+ * dependent launch: Optimization section, low-latency path and Fig. 3).
+ * Each layer computes exactly what moe_decode_forward computes (the same
+ * kernel code, bit for bit).
+ *   layers   DEVICE array of n_layers moe_layer, 8-byte aligned; its
+ *            contents cannot be checked on the host: every pointer in it
+ *            must follow moe_decode_forward's rules for the shape.
+ *   out      bf16 [n_layers][B][H] (written; must not overlap x or ws)
+ *   ids_out  int32 [n_layers][B][top_k] or NULL: the routing of each layer.
+ * Flint's shape only (NVFP4 or BF16); the workspace is moe_decode_forward's.
+ * Where the single-launch kernel cannot run: MOE_ERR_UNSUPPORTED. */
+moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t n_layers,
+                                    const moe_layer* layers, const void* x, int32_t B, void* out,
+                                    int32_t* ids_out, void* ws, size_t ws_bytes, void* stream);
+
 /* The layer's neighbours, fused into it (Optimization section, low-latency
  * path: the norm and the combine fused into the adjacent GEMV kernels; the
  * norm kernels are one of the Fig. 2 steps).  Each part is optional.

@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.moe_prefill_forward_ex.restype = ctypes.c_int
         L.moe_prefill_forward_ex.argtypes = [P(Shape), vp, i32, P(Fuse), vp, P(Experts),
                                              P(Experts), vp, vp, vp, vp, sz, vp]
+        L.moe_decode_stack_forward.restype = ctypes.c_int
+        L.moe_decode_stack_forward.argtypes = [P(Shape), i32, vp, vp, i32, vp, vp, vp, sz, vp]
         L.moe_nvfp4_dequant.restype = ctypes.c_int
         L.moe_nvfp4_dequant.argtypes = [P(Shape), P(Experts), i32, i32, vp, vp]
         _LIB = L
@@ -246,6 +248,33 @@ def moe_prefill_forward_ex(x, router_w, routed, shared, out, ws, norm_w=None, ep
                                       _ptr(out), _ptr(ids_out), _ptr(w_out), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_prefill_forward_ex")
+
+
+def layer_table(device_layers, device="cuda"):
+    """A device array of moe_layer records (int64 [L, 11]: router, then the
+    routed and shared sets' w13, w13_scale, w2, w2_scale, global) for
+    moe_decode_stack_forward; the tensors it points to must stay alive."""
+    import torch
+    rows = []
+    for d in device_layers:
+        r = experts_struct(d.routed)
+        sh = experts_struct(d.shared)
+        rows.append([_ptr(d.router) or 0] +
+                    [v or 0 for v in (r.w13, r.w13_scale, r.w2, r.w2_scale, r.global_)] +
+                    [v or 0 for v in (sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, sh.global_)])
+    return torch.tensor(rows, dtype=torch.int64).to(device)
+
+
+def moe_decode_stack_forward(x, table, out, ws, ids_out=None, fmt=MOE_W_NVFP4, stream=None,
+                             S: Shape | None = None, B: int | None = None):
+    """n_layers = table.shape[0] independent layers on the same x bf16 [B, H],
+    one launch: out bf16 [L, B, H] (ids_out int32 [L, B, k] optional)."""
+    S = S or shape(_fmt(fmt))
+    B = x.shape[0] if B is None else B
+    st = lib().moe_decode_stack_forward(ctypes.byref(S), table.shape[0], _ptr(table), _ptr(x), B,
+                                        _ptr(out), _ptr(ids_out), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_decode_stack_forward")
 
 
 def moe_nvfp4_dequant(expert_set, expert: int, tensor: int, out, stream=None):

@@ -336,6 +336,34 @@ moe_status moe_prefill_forward_ex(const moe_shape* shape, const void* x, int32_t
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+static_assert(sizeof(moe_layer) == sizeof(moe::LayerDev), "moe_layer is the device layer record");
+static_assert(sizeof(moe_experts) == sizeof(moe::ExpertsDev), "moe_experts is the device set");
+
+moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t n_layers,
+                                    const moe_layer* layers, const void* x, int32_t B, void* out,
+                                    int32_t* ids_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
+  if ((st = check_shape(shape)) != MOE_OK) return st;
+  if (B < 1 || n_layers < 1) return MOE_ERR_INVALID_ARG;
+  if (B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
+  if (!layers) return MOE_ERR_INVALID_ARG;
+  if (!aligned(layers, 8)) return MOE_ERR_MISALIGNED;
+  if ((st = check_ptr(x)) != MOE_OK) return st;
+  if ((st = check_ptr(out)) != MOE_OK) return st;
+  if (ids_out && !aligned(ids_out, 4)) return MOE_ERR_MISALIGNED;
+  if (!ws || ws_bytes < moe::kDecodeWsBytes) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_MISALIGNED;
+  const size_t xb = (size_t)B * moe::kH * 2, ob = xb * (size_t)n_layers;
+  if (overlap(out, ob, x, xb) || overlap(out, ob, ws, ws_bytes)) return MOE_ERR_INVALID_ARG;
+  if (overlap(layers, sizeof(moe_layer) * (size_t)n_layers, out, ob)) return MOE_ERR_INVALID_ARG;
+  if (!moe::fused_supported()) return MOE_ERR_UNSUPPORTED;
+  const hipError_t e = moe::launch_decode_stack(
+      B, shape->wfmt, static_cast<const uint16_t*>(x),
+      reinterpret_cast<const moe::LayerDev*>(layers), n_layers, static_cast<uint16_t*>(out),
+      ids_out, static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 moe_status moe_nvfp4_dequant(const moe_shape* shape, const moe_experts* set, int32_t expert,
                              int32_t tensor, float* out, void* stream) {
   moe_status st;

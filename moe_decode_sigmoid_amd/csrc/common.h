@@ -32,6 +32,13 @@ struct ExpertsDev {
 
 enum { FMT_NVFP4 = 0, FMT_BF16 = 1, FMT_MXFP8 = 2 };
 
+// One layer of a stack as the stacked decode kernel reads it (device memory).
+struct LayerDev {
+  const uint16_t* rw;    // router bf16 [E][H]
+  ExpertsDev routed;
+  ExpertsDev shared;
+};
+
 // ------------------------------------------------------------ general shapes
 // Layer shape of the general decode path (any served H, I, E, top-k, shared
 // count; see decode_general.hip for the limits).

@@ -410,12 +410,49 @@ __device__ __forceinline__ uint32_t* hready_bank(uint8_t* ws, int r, int k) {
                                      ((size_t)kFusedGrid + (size_t)r * kHBanks + k) * kFlagStride);
 }
 
+// The loads of a layer that depend on neither x nor the routing: router row
+// g (wave w covers columns [512 w, 512 w + 512), 8 per lane); the shared
+// expert's gate/up row 2g + (w & 1) for the tokens of parity w >> 1 (at B = 1
+// waves 0 and 1 only); its down rows of this workgroup's 8 outputs.
+template <int FMT>
+struct StepAPre {
+  uint4 wr;
+  Chunk<FMT> scg, scu, dsh[2];
+};
+
+template <int B>
+__device__ __forceinline__ unsigned shared_token_mask(int wave) {
+  return ((1u << B) - 1u) & ((wave >> 1) ? 0xAAAAAAAAu : 0x55555555u);
+}
+
+template <int B, int FMT>
+__device__ __forceinline__ void load_pre_gateup(StepAPre<FMT>& p, const uint16_t* rw,
+                                                const ExpertsDev& shared, int g, int wave,
+                                                int lane) {
+  p.wr = *reinterpret_cast<const uint4*>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
+  if (shared_token_mask<B>(wave)) {
+    p.scg.load_gu(shared, 0, 0, 2 * g + (wave & 1), lane);
+    p.scu.load_gu(shared, 0, 1, 2 * g + (wave & 1), lane);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_pre_down(StepAPre<FMT>& p, const ExpertsDev& shared, int g,
+                                              int lane) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    p.dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * (lane >> 4) + r, lane & 15);
+}
+
 // ------------------------------------------------------------------ kernel
+// One layer, as one workgroup of the 256 runs it (the body of both kernels
+// below).
 template <int B, int FMT, bool NORM, bool RESID>
-__global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, ExpertsDev routed,
-    ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, uint8_t* __restrict__ ws, FuseDev fz) {
+__device__ __forceinline__ void decode_layer(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, const ExpertsDev& routed,
+    const ExpertsDev& shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz) {
+  StepAPre<FMT> pre;
   constexpr int kTB = FMT == FMT_NVFP4 ? 4 : 2;      // gate/up row pairs per batch
   constexpr int kDepthC = FMT == FMT_NVFP4 ? 4 : 1;  // entries of down rows in flight
   constexpr int kPairs = (kK + 1) * B;               // h pairs: 6 B routed + B shared
@@ -444,17 +481,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
 
   trace_stamp(ws, 0);
   // ---------------------------------------------------------------- step A
-  // router row g: wave w covers columns [512 w, 512 w + 512), 8 per lane
-  const uint4 wr = *reinterpret_cast<const uint4*>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
-  // shared expert gate/up: row 2g + (w & 1) in wave w, for the tokens of
-  // parity w >> 1 (at B = 1 waves 0 and 1 only)
-  const int srow = 2 * g + (wave & 1);
-  const unsigned smask = ((1u << B) - 1u) & ((wave >> 1) ? 0xAAAAAAAAu : 0x55555555u);
-  Chunk<FMT> scg, scu;
-  if (smask) {
-    scg.load_gu(shared, 0, 0, srow, lane);
-    scu.load_gu(shared, 0, 1, srow, lane);
-  }
+  const unsigned smask = shared_token_mask<B>(wave);
+  load_pre_gateup<B, FMT>(pre, rw, shared, g, wave, lane);
   // Every load of step A goes out before any of them is used (loads return
   // in issue order, so a wait for one is a wait for all before it): x, piece
   // tid of each token; the norm weight and the residual of this workgroup's
@@ -482,9 +510,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   }
   const float sh_sg = Chunk<FMT>::gscale(shared, 0, 0), sh_su = Chunk<FMT>::gscale(shared, 0, 1),
               sh_sd = Chunk<FMT>::gscale(shared, 0, 2);
-  Chunk<FMT> dsh[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * grp4 + r, c16);
+  load_pre_down<FMT>(pre, shared, g, lane);
   const float resid = __builtin_bit_cast(float, (uint32_t)rv << 16);
   // x to LDS as is, or through the fused RMSNorm.  A row's mean square is
   // summed by one wave holding the row 32 elements per lane (the same order
@@ -547,10 +573,10 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
 #pragma unroll
     for (int t = 0; t < B; ++t) {
       const uint4 xv = s_x[t * (kH / 8) + 64 * wave + lane];
-      float a = dot2_bf16(wr.x, xv.x, 0.0f);
-      a = dot2_bf16(wr.y, xv.y, a);
-      a = dot2_bf16(wr.z, xv.z, a);
-      a = dot2_bf16(wr.w, xv.w, a);
+      float a = dot2_bf16(pre.wr.x, xv.x, 0.0f);
+      a = dot2_bf16(pre.wr.y, xv.y, a);
+      a = dot2_bf16(pre.wr.z, xv.z, a);
+      a = dot2_bf16(pre.wr.w, xv.w, a);
       acc[t] = wave_sum(a);
     }
     if (lane == 0) {
@@ -572,7 +598,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   }
   trace_stamp(ws, 2);
   if (smask)
-    gateup_compute<B, FMT>(scg, scu, sh_sg, sh_su, smask, s_x, x0, lane,
+    gateup_compute<B, FMT>(pre.scg, pre.scu, sh_sg, sh_su, smask, s_x, x0, lane,
                            &s_hsh[wave & 1][0]);
   trace_stamp(ws, 3);
 
@@ -847,8 +873,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
       if (t < B) {
         uint32_t h[16];
         load_h(s_h, kK * B + t, c16, h);
-        accs[0][j] = __builtin_fmaf(gl, dsh[0].dot_x(h), accs[0][j]);
-        accs[1][j] = __builtin_fmaf(gl, dsh[1].dot_x(h), accs[1][j]);
+        accs[0][j] = __builtin_fmaf(gl, pre.dsh[0].dot_x(h), accs[0][j]);
+        accs[1][j] = __builtin_fmaf(gl, pre.dsh[1].dot_x(h), accs[1][j]);
       }
     }
   }
@@ -906,6 +932,39 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   trace_flush(ws);
 }
 
+template <int B, int FMT, bool NORM, bool RESID>
+__global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, ExpertsDev routed,
+    ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out, uint8_t* __restrict__ ws, FuseDev fz) {
+  decode_layer<B, FMT, NORM, RESID>(x, rw, routed, shared, out, ids_out, w_out, ws, fz);
+}
+
+// A stack of L layers in one launch, one after another: every workgroup
+// runs layer l + 1 as soon as it has finished its part of layer l (the
+// layers read the same x), so its first loads of layer l + 1 overlap the
+// other workgroups' tail of layer l.  (Issuing layer l + 1's router and
+// shared-expert rows inside layer l's step C was measured slower: 12.6
+// against 11.9 us per layer.)  The hand-over protocol already orders
+// consecutive layers: a workgroup can only publish layer l + 1's logits after
+// it has read all of layer l's, and only write layer l + 1's h after every
+// workgroup has published layer l + 1's logits, i.e. after each has copied
+// layer l's h.  So the per-layer epochs are all the kernel needs, and the
+// launch gap between layers disappears (the pages hide it with programmatic
+// dependent launch).
+template <int B, int FMT>
+__global__ __launch_bounds__(kFusedThreads, 1) void k_decode_stack(
+    const uint16_t* __restrict__ x, const LayerDev* __restrict__ layers, int L,
+    uint16_t* __restrict__ out, int32_t* __restrict__ ids_out, uint8_t* __restrict__ ws) {
+  for (int l = 0; l < L; ++l) {
+    const LayerDev d = layers[l];
+    if (l) __syncthreads();
+    decode_layer<B, FMT, false, false>(x, d.rw, d.routed, d.shared, out + (size_t)l * B * kH,
+                                       ids_out ? ids_out + (size_t)l * B * kK : nullptr, nullptr,
+                                       ws, FuseDev{});
+  }
+}
+
 // ------------------------------------------------------------------ launcher
 static int g_fused_ok[64];   // per device: 0 unknown, 1 usable, -1 not
 
@@ -913,7 +972,7 @@ bool fused_supported() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   if (g_fused_ok[dev] == 0) {
-    int cus = 0, occ_nv = 0, occ_bf = 0, occ_nn = 0, occ_bn = 0;
+    int cus = 0, occ_nv = 0, occ_bf = 0, occ_nn = 0, occ_bn = 0, occ_sn = 0, occ_sb = 0;
     const bool ok =
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -923,9 +982,13 @@ bool fused_supported() {
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &occ_nn, k_decode_fused<8, FMT_NVFP4, true, true>, kFusedThreads, 0) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ_bn, k_decode_fused<8, FMT_BF16, true, true>, kFusedThreads, 0) == hipSuccess;
+            &occ_bn, k_decode_fused<8, FMT_BF16, true, true>, kFusedThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ_sn, k_decode_stack<8, FMT_NVFP4>, kFusedThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ_sb, k_decode_stack<8, FMT_BF16>, kFusedThreads, 0) == hipSuccess;
     g_fused_ok[dev] = (ok && cus >= kFusedGrid && occ_nv >= 1 && occ_bf >= 1 && occ_nn >= 1 &&
-                       occ_bn >= 1) ? 1 : -1;
+                       occ_bn >= 1 && occ_sn >= 1 && occ_sb >= 1) ? 1 : -1;
   }
   return g_fused_ok[dev] == 1;
 }
@@ -950,6 +1013,29 @@ static void launch_fused_b(int fmt, const uint16_t* x, const uint16_t* rw, const
   else
     hipLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, x, rw, routed, shared, out,
                        ids, w, ws, fz);
+}
+
+template <int B>
+static void launch_stack_b(int fmt, const uint16_t* x, const LayerDev* layers, int L,
+                           uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st) {
+  auto k = fmt == FMT_NVFP4 ? k_decode_stack<B, FMT_NVFP4> : k_decode_stack<B, FMT_BF16>;
+  hipLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, x, layers, L, out, ids, ws);
+}
+
+hipError_t launch_decode_stack(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
+                               uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st) {
+  switch (B) {
+    case 1: launch_stack_b<1>(fmt, x, layers, L, out, ids, ws, st); break;
+    case 2: launch_stack_b<2>(fmt, x, layers, L, out, ids, ws, st); break;
+    case 3: launch_stack_b<3>(fmt, x, layers, L, out, ids, ws, st); break;
+    case 4: launch_stack_b<4>(fmt, x, layers, L, out, ids, ws, st); break;
+    case 5: launch_stack_b<5>(fmt, x, layers, L, out, ids, ws, st); break;
+    case 6: launch_stack_b<6>(fmt, x, layers, L, out, ids, ws, st); break;
+    case 7: launch_stack_b<7>(fmt, x, layers, L, out, ids, ws, st); break;
+    case 8: launch_stack_b<8>(fmt, x, layers, L, out, ids, ws, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t* rw,

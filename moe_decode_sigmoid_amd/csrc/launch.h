@@ -25,6 +25,10 @@ hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
                                const FuseDev& fuse = FuseDev{});
 
+// A stack of L layers (same x) in one launch of the fused kernel's body.
+hipError_t launch_decode_stack(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
+                               uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st);
+
 // Dense NVFP4 GEMV, B = 1..8, K % 32 == 0, K <= 8192, B * K <= 32768.
 constexpr int kGemvMaxK = 8192;
 constexpr int kGemvMaxBK = 32768;                  // x staged in LDS: B * K * 2 bytes <= 64 KiB

@@ -20,7 +20,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["moe_decode_route", "moe_decode_forward", "moe_decode_forward_timed",
               "moe_prefill_forward", "moe_nvfp4_gemv", "moe_decode_forward_ex",
-              "moe_prefill_forward_ex",
+              "moe_prefill_forward_ex", "moe_decode_stack_forward",
               "moe_nvfp4_dequant", "moe_workspace_bytes", "moe_status_string",
               "moe_abi_version"]:
         assert n in names
@@ -222,6 +222,29 @@ def test_general_shapes_workspace_and_expert_checks():
                                    ctypes.byref(R), None, A + 0x2000000, None, None,
                                    A + 0x3000000, WS_BIG, 0) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_nvfp4_dequant(ctypes.byref(S), ctypes.byref(R), 0, 0, A, 0) == \
+        moe.MOE_ERR_UNSUPPORTED
+
+
+def test_stack_argument_errors():
+    """Every call fails a host-side check (the layer table is a fake device
+    address and must never be read)."""
+    L = moe.lib()
+    S = moe.shape()
+    T = A + 0x6000000
+
+    def call(S=S, n=4, layers=T, x=A, B=2, out=A + 0x2000000, ids=None, ws=A + 0x3000000,
+             wsb=1024):
+        return L.moe_decode_stack_forward(ctypes.byref(S), n, layers, x, B, out, ids, ws, wsb, 0)
+    assert call() == moe.MOE_ERR_WORKSPACE
+    assert call(n=0, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG
+    assert call(layers=None, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG
+    assert call(layers=T + 4, wsb=WS_BIG) == moe.MOE_ERR_MISALIGNED
+    assert call(B=9, wsb=WS_BIG) == moe.MOE_ERR_UNSUPPORTED
+    assert call(B=0, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG
+    assert call(x=A + 8) == moe.MOE_ERR_MISALIGNED
+    assert call(ids=A + 2) == moe.MOE_ERR_MISALIGNED
+    assert call(out=A + 4096, ws=A + 0x50000000, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG  # x
+    assert call(S=moe.shape(n_experts=384, top_k=8, n_shared=0), wsb=WS_BIG) == \
         moe.MOE_ERR_UNSUPPORTED
 
 

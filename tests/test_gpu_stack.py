@@ -1,0 +1,86 @@
+"""GPU tests of the stacked decode entry (a stack of independent layers in one
+launch): each layer of the stack must equal moe_decode_forward on that layer
+bit for bit (same kernel code), and the oracle within tolerance; a HIP graph
+of the stack replays to the same bits.  Inputs: the seeded synthetic
+Flint-shaped layers of the decode tests."""
+import numpy as np
+import pytest
+
+import oracle
+import testgen
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+moe = pytest.importorskip("moe_decode_sigmoid_amd")
+
+_CACHE = {}
+
+
+def stack(fmt: str, L: int = 5, seed: int = 11):
+    key = (fmt, L, seed)
+    if key not in _CACHE:
+        _CACHE.clear()
+        hosts = [testgen.make_layer(seed, l, fmt) for l in range(L)]
+        devs = [moe.DeviceLayer.from_host(h) for h in hosts]
+        _CACHE[key] = (hosts, devs, moe.layer_table(devs))
+    return _CACHE[key]
+
+
+def run_both(fmt, B, L=5):
+    hosts, devs, table = stack(fmt, L)
+    x = testgen.make_x(50 + B, B)
+    xd = moe.device.to_device_bf16(x)
+    S = moe.shape(moe._fmt(fmt))
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(B, fmt=fmt))
+    out_s = torch.empty((L, B, 2048), dtype=torch.bfloat16, device="cuda")
+    ids_s = torch.empty((L, B, 6), dtype=torch.int32, device="cuda")
+    moe.moe_decode_stack_forward(xd, table, out_s, ws, ids_s, S=S)
+    out_1 = torch.empty_like(out_s)
+    ids_1 = torch.empty_like(ids_s)
+    for l, d in enumerate(devs):
+        moe.moe_decode_forward(xd, d.router, d.routed, d.shared, out_1[l], ws, ids_1[l], S=S)
+    torch.cuda.synchronize()
+    return hosts, x, out_s, ids_s, out_1, ids_1
+
+
+@pytest.mark.parametrize("fmt,B", [("nvfp4", 1), ("nvfp4", 3), ("nvfp4", 8), ("bf16", 2)])
+def test_stack_equals_per_layer_calls_bitwise(fmt, B):
+    hosts, x, out_s, ids_s, out_1, ids_1 = run_both(fmt, B)
+    assert torch.equal(ids_s, ids_1)
+    for l in range(out_s.shape[0]):
+        assert torch.equal(out_s[l], out_1[l]), l
+
+
+def test_stack_layers_match_the_oracle():
+    hosts, x, out_s, ids_s, _, _ = run_both("nvfp4", 2)
+    for l in (0, 4):
+        y_or, ids_or, w_or, gap = oracle.forward_layer(x, hosts[l])
+        log = []
+        ids = ids_s[l].cpu().numpy()
+        y_ref = parity.resolve_near_ties(x, hosts[l], ids, y_or, ids_or, w_or, gap, log)
+        parity.check_output(parity.bf16_out_to_f64(out_s[l]), y_ref, f"stack layer {l}")
+
+
+def test_stack_in_a_hip_graph_replays_to_the_same_bits():
+    hosts, devs, table = stack("nvfp4")
+    B = 1
+    xd = moe.device.to_device_bf16(testgen.make_x(60, B))
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(B))
+    out = torch.empty((len(devs), B, 2048), dtype=torch.bfloat16, device="cuda")
+    moe.moe_decode_stack_forward(xd, table, out, ws)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    out.zero_()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_decode_stack_forward(xd, table, out, ws)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        # eager work between replays
+        moe.moe_decode_forward(xd, devs[0].router, devs[0].routed, devs[0].shared, out[0], ws)
+        torch.cuda.synchronize()
