@@ -44,13 +44,16 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic() -> float | None:
-    """HBM bytes per launch of the fused batch-1 decode kernel from the
-    committed rocprofv3 counter summary, if that kernel's sources are
-    unchanged since the counters were taken (else None)."""
+def measured_traffic(record: str, layers: int | None = None) -> float | None:
+    """HBM bytes per launch of a batch-1 decode kernel from a committed
+    rocprofv3 counter record (profiles/<record>.json), if that kernel's
+    sources are unchanged since the counters were taken and (stack) the
+    record covers the same number of layers; else None."""
     try:
-        rec = json.load(open(os.path.join(ROOT, "profiles", "k_decode_fused_b1_traffic.json")))
+        rec = json.load(open(os.path.join(ROOT, "profiles", record + ".json")))
         if source_hash() != rec.get("source_sha256_16"):
+            return None
+        if layers is not None and rec.get("layers") != layers:
             return None
     except OSError:
         return None
@@ -70,9 +73,12 @@ def source_hash() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def write_traffic_record(dec_fetch: str, dec_write: str, copy_fetch: str, copy_write: str) -> int:
-    """Per-launch HBM bytes of the batch-1 fused decode kernel from counter runs,
-    each counter scaled by what it reads for a plain 1 GiB copy."""
+def write_traffic_record(dec_fetch: str, dec_write: str, copy_fetch: str, copy_write: str,
+                         layers: int) -> int:
+    """Per-launch HBM bytes of the batch-1 decode kernels (one layer per launch,
+    and the stack of `layers` layers in one launch) from counter runs of
+    `bench.py --workload decode --layers <layers>`, each counter scaled by what
+    it reads for a plain 1 GiB copy."""
     import csv
 
     def mean_kib(path, kernel_part, counter):
@@ -83,22 +89,26 @@ def write_traffic_record(dec_fetch: str, dec_write: str, copy_fetch: str, copy_w
         assert vals, f"no {counter} rows for {kernel_part} in {path}"
         return sum(vals.values()) / len(vals), len(vals)
 
-    kname = "k_decode_fused<1, 0, false, false>"
-    f_dec, nf = mean_kib(dec_fetch, kname, "FETCH_SIZE")
-    w_dec, nw = mean_kib(dec_write, kname, "WRITE_SIZE")
     f_cp, _ = mean_kib(copy_fetch, "copyBuffer", "FETCH_SIZE")
     w_cp, _ = mean_kib(copy_write, "copyBuffer", "WRITE_SIZE")
     gib_kib = float(1 << 20)
     fs, wsc = gib_kib / f_cp, gib_kib / w_cp
-    rec = {"kernel": "k_decode_fused<1, nvfp4>", "source_sha256_16": source_hash(),
-           "fetch_kib_per_launch": f_dec, "write_kib_per_launch": w_dec,
-           "dispatches_sampled": [nf, nw], "copy_fetch_kib_per_gib": f_cp,
-           "copy_write_kib_per_gib": w_cp, "fetch_scale": fs, "write_scale": wsc,
-           "traffic_bytes_per_launch": (f_dec * fs + w_dec * wsc) * 1024,
-           "algorithmic_bytes_per_launch": layer_bytes(7, 1, "nvfp4")}
-    with open(os.path.join(ROOT, "profiles", "k_decode_fused_b1_traffic.json"), "w") as fh:
-        json.dump(rec, fh, indent=1)
-    print(json.dumps(rec))
+    for kname, label, record, n in [
+            ("k_decode_fused<1, 0, false, false>", "k_decode_fused<1, nvfp4>",
+             "k_decode_fused_b1_traffic", 1),
+            ("k_decode_stack<1, 0>", f"k_decode_stack<1, nvfp4> ({layers} layers)",
+             "k_decode_stack_b1_traffic", layers)]:
+        f_dec, nf = mean_kib(dec_fetch, kname, "FETCH_SIZE")
+        w_dec, nw = mean_kib(dec_write, kname, "WRITE_SIZE")
+        rec = {"kernel": label, "source_sha256_16": source_hash(), "layers": n,
+               "fetch_kib_per_launch": f_dec, "write_kib_per_launch": w_dec,
+               "dispatches_sampled": [nf, nw], "copy_fetch_kib_per_gib": f_cp,
+               "copy_write_kib_per_gib": w_cp, "fetch_scale": fs, "write_scale": wsc,
+               "traffic_bytes_per_launch": (f_dec * fs + w_dec * wsc) * 1024,
+               "algorithmic_bytes_per_launch": n * layer_bytes(7, 1, "nvfp4")}
+        with open(os.path.join(ROOT, "profiles", record + ".json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
     return 0
 
 
@@ -252,10 +262,12 @@ def main() -> int:
     ap.add_argument("--traffic-record", nargs=4, metavar="CSV",
                     help="no GPU work: read four rocprofv3 counter_collection.csv files "
                          "(decode FETCH_SIZE, decode WRITE_SIZE, copy FETCH_SIZE, copy "
-                         "WRITE_SIZE) and write profiles/k_decode_fused_b1_traffic.json")
+                         "WRITE_SIZE; the decode runs with the same --layers) and write "
+                         "profiles/k_decode_fused_b1_traffic.json and "
+                         "profiles/k_decode_stack_b1_traffic.json")
     args = ap.parse_args()
     if args.traffic_record:
-        return write_traffic_record(*args.traffic_record)
+        return write_traffic_record(*args.traffic_record, args.layers)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -484,26 +496,35 @@ def main() -> int:
                          f"{time.time() - t_start:.1f} s on {nthreads} OpenMP threads"}
         log(f"oracle: {per_layer * 1e6:.0f} us/layer on {nthreads} threads")
 
-    # the timed region is one graph of L back-to-back launches per step: its
-    # HIP-event time per launch is the kernel's average launch duration there
-    roof = {"bound": "hbm", "kernel": "k_decode_fused<1, nvfp4> (one launch per layer)",
-            "achieved": r1["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": r1["gbps"] / PEAK_HBM_GBS,
-            "traffic": measured_traffic() if fmt == "nvfp4" else None,
-            "per_launch_bytes": r1["pass_bytes"] / L, "launch_us": r1["us_per_layer"],
-            "timing": f"HIP events around {args.steps} graph replays of {L} launches, per launch; "
+    # The timed region is one HIP-graph replay per step holding the whole L-layer
+    # pass as ONE launch of the stacked kernel (moe_decode_stack_forward): the
+    # HIP-event time per replay is that kernel's average launch duration.  The
+    # same layers as L single-layer launches per replay are reported in batch1.
+    st1 = r1["stack_one_launch"]
+    roof = {"bound": "hbm",
+            "kernel": f"k_decode_stack<1, nvfp4> (one launch per {L}-layer pass)",
+            "achieved": st1["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": st1["gbps"] / PEAK_HBM_GBS,
+            "traffic": (measured_traffic("k_decode_stack_b1_traffic", L)
+                        if fmt == "nvfp4" else None),
+            "per_launch_bytes": r1["pass_bytes"], "launch_us": st1["ms_per_pass"] * 1000,
+            "timing": f"HIP events around {args.steps} graph replays of one launch each; "
+                      f"per-layer launches instead: {r1['us_per_layer']:.2f} us per layer "
+                      f"(traffic {measured_traffic('k_decode_fused_b1_traffic')} B per launch), "
                       f"single eager launches timed by their own start/end events: "
                       f"{r1['kernel_us_mean']:.2f} us"}
     res = {
         "metric": "MoE-layer decode µs/layer + achieved HBM GB/s (W4A16, batch 1 and 8)",
-        "value": round(r1["gbps"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(r1["ms_per_pass"], 4),
-        "us_per_layer": round(r1["us_per_layer"], 3),
+        "value": round(st1["gbps"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(st1["ms_per_pass"], 4),
+        "us_per_layer": round(st1["us_per_layer"], 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "nvfp4-w/bf16-a, fp32 accumulate" if fmt == "nvfp4" else "bf16, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights packed to NVFP4)",
         "config": {"workload": f"{L}-layer Flint-shaped MoE decode stack, batch 1, {fmt}, "
-                               f"one HIP graph per pass, weights cold (pass > last-level cache)",
+                               f"independent layers on the same x, one HIP graph per pass "
+                               f"holding one stacked launch, weights cold (pass > last-level "
+                               f"cache)",
                    "hidden": H, "inter": I, "experts": E, "top_k": K, "shared": 1,
                    "layers": L, "batch": 1, "weight_format": fmt,
                    "resident_weight_bytes": int(resident)},
