@@ -59,24 +59,6 @@ struct GenCtl {
   float wt[kGenMaxEntries][kMaxB];
 };
 
-// Workspace of the general path: logits f32 [kMaxB][E], the dispatch, and h
-// bf16 [entry][kMaxB][I].
-struct GenLayout {
-  size_t logits, ctl, h, total;
-};
-__host__ __device__ inline GenLayout gen_layout(const GenShape& S) {
-  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  GenLayout L;
-  L.logits = 0;
-  L.ctl = al(sizeof(float) * kMaxB * (size_t)S.E);
-  L.h = al(L.ctl + sizeof(GenCtl));
-  L.total = al(L.h + 2 * (size_t)kGenMaxEntries * kMaxB * S.I);
-  return L;
-}
-// upper bound of the entries of a call of B tokens
-__host__ __device__ inline int gen_max_entries(const GenShape& S, int B) {
-  return (S.E < B * S.K ? S.E : B * S.K) + S.NS;
-}
 
 // ---------------------------------------------------------------- workspace
 // Decode workspace, all offsets in bytes from a 256-byte-aligned base.
@@ -107,6 +89,28 @@ constexpr size_t kSlotLogitOff = kHOff + sizeof(float) * kMaxActive * kMaxB * kI
 constexpr size_t kFlagOff = kSlotLogitOff + kSlotLogitRep * kLogitReps;
 constexpr size_t kFlagStride = 128;
 constexpr size_t kDecodeWsBytes = kFlagOff + (256 + 64 * kBankReps) * kFlagStride;
+constexpr size_t kGenBase = kDecodeWsBytes;
+
+// Workspace of the general path: logits f32 [kMaxB][E], the dispatch, and h
+// bf16 [entry][kMaxB][I], after the Flint paths' region (kGenBase bytes), so
+// that one workspace can serve both without either touching the other's
+// counters.
+struct GenLayout {
+  size_t logits, ctl, h, total;
+};
+__host__ __device__ inline GenLayout gen_layout(const GenShape& S) {
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  GenLayout L;
+  L.logits = al(kGenBase);
+  L.ctl = al(L.logits + sizeof(float) * kMaxB * (size_t)S.E);
+  L.h = al(L.ctl + sizeof(GenCtl));
+  L.total = al(L.h + 2 * (size_t)kGenMaxEntries * kMaxB * S.I);
+  return L;
+}
+// upper bound of the entries of a call of B tokens
+__host__ __device__ inline int gen_max_entries(const GenShape& S, int B) {
+  return (S.E < B * S.K ? S.E : B * S.K) + S.NS;
+}
 constexpr int kShSlot = kMaxActive - 1;  // h entry of the shared expert in the fused kernel
 
 // ---------------------------------------------------------------- numerics

@@ -151,3 +151,33 @@ def test_timed_entry_on_a_general_shape():
     moe.moe_decode_forward_timed(x, dl.router, dl.routed, dl.shared, b, ws, e0, e1, S=S)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and e0.elapsed_time(e1) > 0
+
+
+def test_one_workspace_serves_the_general_and_the_flint_path():
+    """The general path keeps to its own part of the workspace: Flint-shape
+    and general-shape calls alternating on one workspace give the results of
+    separate workspaces, bit for bit."""
+    name = "inkling2small_mxfp8"
+    H = SHAPES[name][0]
+    _, dl = layers(name, 2)
+    S = S_of(name)
+    flint = moe.DeviceLayer.from_host(testgen.make_layer(1, 0, "nvfp4"))
+    x = moe.device.to_device_bf16(testgen.make_x(93, 3, H))
+    nbytes = max(moe.moe_workspace_bytes(3, S=S), moe.moe_workspace_bytes(3))
+    shared_ws = moe.alloc_workspace(nbytes)
+
+    def gen(ws):
+        o = torch.empty((3, H), dtype=torch.bfloat16, device="cuda")
+        moe.moe_decode_forward(x, dl.router, dl.routed, dl.shared, o, ws, S=S)
+        return o
+
+    def fl(ws):
+        o = torch.empty((3, H), dtype=torch.bfloat16, device="cuda")
+        moe.moe_decode_forward(x, flint.router, flint.routed, flint.shared, o, ws)
+        return o
+    ref_g = gen(moe.alloc_workspace(nbytes))
+    ref_f = fl(moe.alloc_workspace(nbytes))
+    outs = [fl(shared_ws), gen(shared_ws), fl(shared_ws), gen(shared_ws), fl(shared_ws)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, ref_f if i % 2 == 0 else ref_g), i
