@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.or_bf16_rne.argtypes = [d]
         L.or_bf16_rne_array.argtypes = [vp, i64, vp]
         L.or_rmsnorm_bf16.argtypes = [vp, i32, i32, vp, d, vp]
+        L.or_quant_fp4_46.argtypes = [vp, i64, vp, vp, vp, vp]
+        L.or_forward_w4a4.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp, ctypes.POINTER(_Experts),
+                                      ctypes.POINTER(_Experts), vp, vp, vp, vp, vp, vp, vp]
         L.or_num_threads.restype = ctypes.c_int
         L.or_set_num_threads.argtypes = [ctypes.c_int]
         _LIB = L
@@ -266,6 +269,45 @@ def forward_fused(x: np.ndarray, layer, norm_w=None, eps: float = 0.0, residual=
         r = np.ascontiguousarray(residual, np.uint16).astype(np.uint32) << 16
         y = y + r.view(np.float32).astype(np.float64)
     return y, ids, w, gap, xn
+
+
+# ----------------------------------------------------------------- W4A4 (Four Over Six)
+def quant_fp4_46(v) -> tuple:
+    """One vector (float32, length a multiple of 16) -> (codes u8 [n], scales
+    u8 [n/16], global float, exact values f64 [n])."""
+    v = np.ascontiguousarray(np.asarray(v, np.float32))
+    n = v.size
+    codes = np.empty(n, np.uint8)
+    scales = np.empty(n // 16, np.uint8)
+    g = np.zeros(1, np.float32)
+    out = np.empty(n, np.float64)
+    lib().or_quant_fp4_46(_p(v), n, _p(codes), _p(scales), _p(g), _p(out))
+    return codes, scales, float(g[0]), out
+
+
+def forward_w4a4(x: np.ndarray, layer, forced_ids=None, h_in=None):
+    """The W4A4 layer (NVFP4 weights, Four-Over-Six NVFP4 activations) for x
+    u16 [B, H].  h_in: u16 [B, k + n_shared, I] (routed ids ascending, then
+    shared) replacing the oracle's bf16 h before its quantisation.
+    Returns (y f64 [B, H], ids, w, gap, h u16 [B, k + n_shared, I])."""
+    x = np.ascontiguousarray(x, np.uint16)
+    B, H = x.shape
+    k, I = layer.K, layer.I
+    ns = layer.shared.n if layer.shared is not None else 0
+    y = np.empty((B, H), np.float64)
+    ids = np.empty((B, k), np.int32)
+    w = np.empty((B, k), np.float64)
+    gap = np.empty(B, np.float64)
+    h_out = np.empty((B, k + ns, I), np.uint16)
+    forced = None if forced_ids is None else np.ascontiguousarray(forced_ids, np.int32)
+    hin = None if h_in is None else np.ascontiguousarray(h_in, np.uint16)
+    S = _shape(H, I, layer.router.shape[0], k, ns)
+    R = _experts(layer.routed)
+    Sh = _experts(layer.shared) if layer.shared is not None else _experts(layer.routed)
+    lib().or_forward_w4a4(ctypes.byref(S), _p(x), B, _p(layer.router), ctypes.byref(R),
+                          ctypes.byref(Sh), _p(forced), _p(hin), _p(y), _p(ids), _p(w), _p(gap),
+                          _p(h_out))
+    return y, ids, w, gap, h_out
 
 
 def num_threads() -> int:

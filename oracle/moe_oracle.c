@@ -446,6 +446,185 @@ void or_rmsnorm_bf16(const uint16_t* x, int32_t T, int32_t H, const uint16_t* w,
   }
 }
 
+/* ------------------------------------------------------------------ W4A4 */
+
+/* NVFP4 activations with the Four Over Six block scale (the AREX article on
+ * vLLM's Day-0 support for Inkling-2-Small, 48-layer MoE section: a
+ * per-token global scale, and for each 16-element block the scale that maps
+ * the block maximum to 6 or the one that maps it to 4, whichever leaves the
+ * smaller reconstruction error, MAE).  Readings (the article gives no
+ * formula): the global is amax / (6 * 448) like the weights'; a candidate's
+ * scale is fp32(fp32(bmax / M) / g) rounded to E4M3 (nearest-even,
+ * saturating at 448); codes are v / fp32(e4m3 * g) rounded to E2M1; the MAE
+ * is summed in fp32 in element order over |v - fp32(e2m1 * q)|; a tie keeps
+ * the max->6 candidate.  Every step is an fp32 operation in the order
+ * written, so that another implementation can take the same decisions. */
+
+/* nearest-even onto the E4M3FN grid of a finite s >= 0, saturating at 448 */
+static uint8_t or_e4m3_rne(float s) {
+  if (!(s > 0.0f)) return 0;
+  if (s >= 448.0f) return 0x7E;
+  if (s < 0.015625f) {                          /* subnormal: multiples of 2^-9 */
+    const float m = rintf(ldexpf(s, 9));
+    return m >= 8.0f ? 0x08 : (uint8_t)m;
+  }
+  int k;
+  (void)frexpf(s, &k);                          /* s in [2^(k-1), 2^k) */
+  int e = k - 1;
+  float m = rintf((ldexpf(s, -e) - 1.0f) * 8.0f);
+  if (m >= 8.0f) { m = 0.0f; e += 1; }
+  if (e > 8 || (e == 8 && m > 6.0f)) return 0x7E;
+  return (uint8_t)(((e + 7) << 3) | (int)m);
+}
+
+/* nearest-even onto the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating:
+ * the 4-bit code (bit 3 = sign).  Midpoints go to the neighbour with the even
+ * mantissa bit: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+ * 3.5 -> 4, 5 -> 4. */
+static uint8_t or_e2m1_rne(float v) {
+  static const float grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  const float a = fabsf(v);
+  int best = 0;
+  for (int i = 1; i < 8; ++i) {
+    const float dn = a - grid[best], di = fabsf(a - grid[i]);
+    if (di < fabsf(dn) || (di == fabsf(dn) && (i & 1) == 0)) best = i;
+  }
+  return (uint8_t)((signbit(v) ? 8 : 0) | best);
+}
+
+/* One 16-block with scale candidate M: the E4M3 byte, the codes and the MAE. */
+static float or_fp4_candidate(const float* v, float bmax, float g, float M, uint8_t* sbyte,
+                              uint8_t* codes) {
+  *sbyte = or_e4m3_rne((bmax / M) / g);
+  const float q = (float)or_e4m3(*sbyte) * g;
+  float mae = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    codes[i] = q > 0.0f ? or_e2m1_rne(v[i] / q) : 0;
+    const float d = (float)or_e2m1(codes[i]) * q;
+    mae += fabsf(v[i] - d);
+  }
+  return mae;
+}
+
+/* Quantise v[n] (n a multiple of 16, one token's vector): codes u8 [n] (one
+ * 4-bit code per byte), scales u8 [n / 16], *g_out the global, out[n] the
+ * exact fp64 values e2m1 * e4m3 * g. */
+void or_quant_fp4_46(const float* v, int64_t n, uint8_t* codes, uint8_t* scales, float* g_out,
+                     double* out) {
+  or_tables();
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const float g = amax / 2688.0f;
+  *g_out = g;
+  for (int64_t b = 0; b < n / 16; ++b) {
+    const float* vb = v + 16 * b;
+    uint8_t* cb = codes + 16 * b;
+    float bmax = 0.0f;
+    for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(vb[i]));
+    if (g == 0.0f || bmax == 0.0f) {
+      scales[b] = 0;
+      memset(cb, 0, 16);
+    } else {
+      uint8_t s6, s4, c6[16], c4[16];
+      const float m6 = or_fp4_candidate(vb, bmax, g, 6.0f, &s6, c6);
+      const float m4 = or_fp4_candidate(vb, bmax, g, 4.0f, &s4, c4);
+      const int four = m4 < m6;
+      scales[b] = four ? s4 : s6;
+      memcpy(cb, four ? c4 : c6, 16);
+    }
+    for (int i = 0; i < 16; ++i)
+      out[16 * b + i] = g_e2m1[cb[i]] * g_e4m3[scales[b]] * (double)g;
+  }
+}
+
+/* h = SiLU(G_e x) * (U_e x) of one expert for an fp64 input (I values). */
+static void or_expert_h(const or_shape* S, const or_experts* X, int32_t e, const double* x,
+                        double* h) {
+  int64_t H = S->hidden, I = S->inter;
+  double* row = (double*)malloc(sizeof(double) * (size_t)H);
+  for (int64_t i = 0; i < I; ++i) {
+    double gg = 0.0, u = 0.0;
+    or_row(X, e, 0, i, H, I, row);
+    for (int64_t k = 0; k < H; ++k) gg += row[k] * x[k];
+    or_row(X, e, 1, i, H, I, row);
+    for (int64_t k = 0; k < H; ++k) u += row[k] * x[k];
+    h[i] = gg * or_sigmoid(gg) * u;
+  }
+  free(row);
+}
+
+/* d = D_e h (H values). */
+static void or_expert_down(const or_shape* S, const or_experts* X, int32_t e, const double* h,
+                           double* d) {
+  int64_t H = S->hidden, I = S->inter;
+  double* row = (double*)malloc(sizeof(double) * (size_t)I);
+  for (int64_t j = 0; j < H; ++j) {
+    double acc = 0.0;
+    or_row(X, e, 2, j, H, I, row);
+    for (int64_t i = 0; i < I; ++i) acc += row[i] * h[i];
+    d[j] = acc;
+  }
+  free(row);
+}
+
+/* The W4A4 layer for B tokens: routing on x itself (the router stays in high
+ * precision); each expert's input is the Four-Over-Six quantisation of x,
+ * its h = SiLU(g) * u is rounded to bf16 (the activation type between the
+ * GEMVs) and quantised the same way before the down GEMV; combine as
+ * or_forward.  h slots [B][k + n_shared][I] bf16, in the order routed ids
+ * ascending then shared: h_out (nullable) receives this oracle's, and h_in
+ * (nullable) replaces them, so that the second quantisation can be taken on
+ * another implementation's h. */
+void or_forward_w4a4(const or_shape* S, const uint16_t* x, int32_t B, const uint16_t* router,
+                     const or_experts* routed, const or_experts* shared, const int32_t* forced,
+                     const uint16_t* h_in, double* y, int32_t* ids, double* w, double* gap,
+                     uint16_t* h_out) {
+  or_tables();
+  const int64_t H = S->hidden, I = S->inter;
+  const int32_t k = S->top_k, ns = S->n_shared, nslot = k + ns;
+  #pragma omp parallel for schedule(dynamic, 1) if (B > 1)
+  for (int32_t t = 0; t < B; ++t) {
+    const uint16_t* xb = x + t * H;
+    int32_t* it = ids + (int64_t)t * k;
+    double* wt = w + (int64_t)t * k;
+    or_route_token(S, xb, router, forced ? forced + (int64_t)t * k : NULL, it, wt, gap + t, NULL);
+    float* xf = (float*)malloc(sizeof(float) * (size_t)(H > I ? H : I));
+    double* xq = (double*)malloc(sizeof(double) * (size_t)H);
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    double* hq = (double*)malloc(sizeof(double) * (size_t)I);
+    double* d = (double*)malloc(sizeof(double) * (size_t)H);
+    uint8_t* codes = (uint8_t*)malloc((size_t)(H > I ? H : I));
+    uint8_t* sc = (uint8_t*)malloc((size_t)(H > I ? H : I) / 16);
+    float gq;
+    for (int64_t c = 0; c < H; ++c) xf[c] = (float)or_bf16(xb[c]);
+    or_quant_fp4_46(xf, H, codes, sc, &gq, xq);
+    int32_t sorted[16];
+    memcpy(sorted, it, sizeof(int32_t) * (size_t)k);
+    qsort(sorted, (size_t)k, sizeof(int32_t), or_cmp_i32);
+    double* yt = y + t * H;
+    for (int64_t c = 0; c < H; ++c) yt[c] = 0.0;
+    for (int32_t sl = 0; sl < nslot; ++sl) {
+      const int is_sh = sl >= k;
+      const or_experts* X = is_sh ? shared : routed;
+      const int32_t e = is_sh ? sl - k : sorted[sl];
+      double wj = 1.0;
+      if (!is_sh)
+        for (int32_t j = 0; j < k; ++j) if (it[j] == e) wj = wt[j];
+      const int64_t off = ((int64_t)t * nslot + sl) * I;
+      or_expert_h(S, X, e, xq, h);
+      for (int64_t i = 0; i < I; ++i) {
+        const uint16_t hb = or_bf16_rne(h[i]);
+        if (h_out) h_out[off + i] = hb;
+        xf[i] = (float)or_bf16(h_in ? h_in[off + i] : hb);
+      }
+      or_quant_fp4_46(xf, I, codes, sc, &gq, hq);
+      or_expert_down(S, X, e, hq, d);
+      for (int64_t c = 0; c < H; ++c) yt[c] += wj * d[c];
+    }
+    free(xf); free(xq); free(h); free(hq); free(d); free(codes); free(sc);
+  }
+}
+
 int or_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -547,3 +547,87 @@ def test_every_shared_expert_is_added_with_weight_one():
     y1 = oracle.forward(x, L1.router, L1.routed, L1.shared, K, I)[0]
     y2 = oracle.forward(x, L1.router, L1.routed, sh2, K, I)[0]
     np.testing.assert_allclose(y2 - y0, 2 * (y1 - y0), rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------- Four Over Six (W4A4)
+G0 = 2.0 ** -10          # global of a vector whose maximum is 2688 * 2^-10 = 2.625
+E2 = np.array([6, 4, 3, 2, 1.5, 1, .5, 0, -6, -4, -3, -2, -1.5, -1, -.5, 0.0])
+
+
+def _vec(*blocks):
+    """A vector fixing the global at 2^-10 (first block holds 2.625) followed by the blocks."""
+    first = np.zeros(16)
+    first[0] = 2688 * G0
+    return np.concatenate([first, *blocks]).astype(np.float32)
+
+
+def test_fp4_46_exact_block_keeps_the_max_to_6_scale():
+    blk = E2 * 16 * G0                               # scale 16 = 2^4: E4M3 byte 0x58
+    codes, scales, g, vals = oracle.quant_fp4_46(_vec(blk))
+    assert g == G0
+    assert scales.tolist() == [0x7E, 0x58]          # 448 for 2.625 = 6 * 448 * 2^-10
+    np.testing.assert_array_equal(vals, _vec(blk).astype(np.float64))
+
+
+def test_fp4_46_takes_max_to_4_when_it_reconstructs_better():
+    blk = np.array([4, 3, 2, 1.5, 1, .5, 0, -4, -3, -2, -1.5, -1, -.5, 0, 2, 1]) * 16 * G0
+    # max -> 6 needs scale 10.67 (E4M3 rounds it to 11: 64/11 is not on the grid);
+    # max -> 4 needs exactly 16
+    codes, scales, g, vals = oracle.quant_fp4_46(_vec(blk))
+    assert scales[1] == 0x58
+    np.testing.assert_array_equal(vals[16:], blk)
+
+
+def test_fp4_46_tie_keeps_the_max_to_6_scale():
+    blk = np.full(16, 96 * G0)                       # 6 * 16 g and 4 * 24 g: both exact
+    _, scales, _, vals = oracle.quant_fp4_46(_vec(blk))
+    assert scales[1] == 0x58                         # 16, not 24 (0x5C)
+    np.testing.assert_array_equal(vals[16:], blk)
+
+
+def test_fp4_46_zero_and_power_of_two_scaling():
+    c, s, g, v = oracle.quant_fp4_46(np.zeros(32, np.float32))
+    assert g == 0.0 and not s.any() and not v.any()
+    x = f64(testgen.make_x(30, 1, 256)[0]).astype(np.float32)
+    c1, s1, g1, v1 = oracle.quant_fp4_46(x)
+    c2, s2, g2, v2 = oracle.quant_fp4_46(x * np.float32(8))
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    assert g2 == 8 * g1 and np.array_equal(v2, 8 * v1)
+
+
+def test_fp4_46_departs_from_the_max_to_6_packer_only_to_reconstruct_better():
+    """The input generator's NVFP4 packer is the max->6 rule with the same
+    global (amax / 2688); the oracle's choice equals it block by block, or has
+    a smaller MAE (and does somewhere)."""
+    w = testgen.make_x(31, 1, 4096)
+    c6p, s6, g6 = testgen.quantize_nvfp4(w)
+    c6 = np.stack([c6p[0] & 15, c6p[0] >> 4], -1).reshape(-1)
+    v = f64(w[0])
+    codes, scales, g, vals = oracle.quant_fp4_46(v.astype(np.float32))
+    assert np.float32(g) == np.float32(g6)
+    e2 = np.array([oracle.e2m1(i) for i in range(16)])
+    e4 = np.array([oracle.e4m3(b) for b in range(256)])
+    v6 = e2[c6] * np.repeat(e4[s6[0]], 16) * g6
+    n_four = 0
+    for b in range(v.size // 16):
+        sl = slice(16 * b, 16 * b + 16)
+        if scales[b] == s6[0, b] and np.array_equal(codes[sl], c6[sl]):
+            continue
+        n_four += 1
+        assert np.abs(vals[sl] - v[sl]).sum() < np.abs(v6[sl] - v[sl]).sum() * (1 + 1e-6)
+    assert 0 < n_four < v.size // 16
+
+
+def test_w4a4_layer_override_and_token_independence():
+    L = tiny_layer(seed=7)
+    x = testgen.make_x(32, 3, H)
+    y, ids, w, gap, h = oracle.forward_w4a4(x, L)
+    y2, ids2, _, _, h2 = oracle.forward_w4a4(x, L, h_in=h)
+    assert np.array_equal(y, y2) and np.array_equal(h, h2)
+    y1, ids1, _, _, h1 = oracle.forward_w4a4(x[1:2].copy(), L)
+    assert np.array_equal(y1[0], y[1]) and np.array_equal(h1[0], h[1])
+    # the routing is the plain layer's (the router stays in high precision)
+    assert np.array_equal(ids, oracle.forward_layer(x, L)[1])
+    # an h overridden with zeros leaves no expert output
+    y0 = oracle.forward_w4a4(x, L, h_in=np.zeros_like(h))[0]
+    assert not y0.any()
