@@ -79,7 +79,22 @@ typedef enum {
   MOE_ERR_HIP = -5          /* a HIP launch failed                           */
 } moe_status;
 
-typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1, MOE_W_MXFP8 = 2 } moe_wformat;
+/* MOE_W_NVFP4_A4: NVFP4 weights and NVFP4 activations (W4A4).  The experts'
+ * inputs x and h are quantised on the fly with the Four Over Six block
+ * scale (the AREX article on vLLM's Day-0 support for Inkling-2-Small,
+ * 48-layer MoE section): per vector (a token's x; one (expert, token) h of
+ * I values) a global amax / 2688, and per 16-block the E4M3 scale mapping
+ * the block maximum to 6 or to 4, whichever reconstructs with the smaller
+ * mean absolute error (a tie keeps 6), every step an fp32 operation in a
+ * stated order (the library's general decode path).  The router
+ * uses x itself.  Decode entry points only (general path); weights as
+ * MOE_W_NVFP4. */
+typedef enum {
+  MOE_W_NVFP4 = 0,
+  MOE_W_BF16 = 1,
+  MOE_W_MXFP8 = 2,
+  MOE_W_NVFP4_A4 = 3
+} moe_wformat;
 
 /* Layer shape.  Every entry point serves the Flint layer {2048, 512, 256, 6,
  * 1, NVFP4 | BF16} (Model architecture section: hidden 2048, 256 experts,
@@ -88,7 +103,8 @@ typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1, MOE_W_MXFP8 = 2 } moe_wformat;
  * also serve the other MoE shapes the pages name, and more, on a general
  * path: Inkling's 256 experts with top-6 and 2 shared experts,
  * Inkling-2-Small's 384 experts with top-8 and none (the AREX article,
- * 48-layer MoE section), in NVFP4, BF16 or MXFP8; its limits are
+ * 48-layer MoE section), in NVFP4, BF16, MXFP8 or NVFP4 with NVFP4
+ * activations (MOE_W_NVFP4_A4, also for Flint's shape); its limits are
  * 32 <= H <= 8192 and 32 <= I <= 4096, both multiples of 32;
  * 1 <= top_k <= 8; top_k <= n_experts <= 512; 0 <= n_shared <= 2.  The
  * prefill and fused-neighbour entry points and the dequant probe return
@@ -260,6 +276,19 @@ moe_status moe_prefill_forward_ex(const moe_shape* shape, const void* x, int32_t
                                   const moe_experts* routed, const moe_experts* shared, void* out,
                                   int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/* Diagnostics for tests of the general decode path: byte offsets, in its
+ * workspace for `shape`, of
+ *   [0] the entry count (int32);   [1] the entries (int32 [66]: a routed
+ *   expert id, or n_experts + s for shared expert s), routed ones in
+ *   ascending id first;   [2] their token masks (uint32 [66]);
+ *   [3] h before any quantisation (bf16 [66][8][inter], entry-major);
+ *   W4A4 only: [4] the quantised x as e2m1 * e4m3 (bf16 [8][hidden]),
+ *   [5] the x globals (f32 [8]), [6] the quantised h as e2m1 * e4m3 (bf16
+ *   [66][8][inter]), [7] the h globals (f32 [66][8]).
+ * Valid after a decode call on that workspace; MOE_ERR_UNSUPPORTED for
+ * shapes the general path does not serve. */
+moe_status moe_general_workspace_layout(const moe_shape* shape, size_t offsets[8]);
 
 /* Parity probe of the in-register NVFP4 decode: writes tensor `tensor`
  * (0 gate, 1 up, 2 down) of expert `expert` of an NVFP4 set as fp32,

@@ -16,7 +16,7 @@ LIB_PATH = HERE / "libmoe_decode.so"
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED = 0, -1, -2
 MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = -3, -4, -5
-MOE_W_NVFP4, MOE_W_BF16, MOE_W_MXFP8 = 0, 1, 2
+MOE_W_NVFP4, MOE_W_BF16, MOE_W_MXFP8, MOE_W_NVFP4_A4 = 0, 1, 2, 3
 HIDDEN, INTER, N_EXPERTS, TOP_K, N_SHARED = 2048, 512, 256, 6, 1
 MAX_DECODE_BATCH = 8
 
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
                                              P(Experts), vp, vp, vp, vp, sz, vp]
         L.moe_decode_stack_forward.restype = ctypes.c_int
         L.moe_decode_stack_forward.argtypes = [P(Shape), i32, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_general_workspace_layout.restype = ctypes.c_int
+        L.moe_general_workspace_layout.argtypes = [P(Shape), P(sz)]
         L.moe_nvfp4_dequant.restype = ctypes.c_int
         L.moe_nvfp4_dequant.argtypes = [P(Shape), P(Experts), i32, i32, vp, vp]
         _LIB = L
@@ -98,7 +100,8 @@ def shape(fmt: int = MOE_W_NVFP4, hidden=HIDDEN, inter=INTER, n_experts=N_EXPERT
 
 def _fmt(fmt) -> int:
     if isinstance(fmt, str):
-        return {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16, "mxfp8": MOE_W_MXFP8}[fmt]
+        return {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16, "mxfp8": MOE_W_MXFP8,
+                "nvfp4_a4": MOE_W_NVFP4_A4}[fmt]
     return int(fmt)
 
 
@@ -248,6 +251,14 @@ def moe_prefill_forward_ex(x, router_w, routed, shared, out, ws, norm_w=None, ep
                                       _ptr(out), _ptr(ids_out), _ptr(w_out), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_prefill_forward_ex")
+
+
+def general_workspace_layout(S: Shape) -> dict:
+    """Byte offsets of the general decode path's workspace regions (diagnostics)."""
+    off = (ctypes.c_size_t * 8)()
+    _check(lib().moe_general_workspace_layout(ctypes.byref(S), off), "moe_general_workspace_layout")
+    keys = ["n_entries", "entry", "amask", "h", "xq", "gx", "hq", "gh"]
+    return {k: int(v) for k, v in zip(keys, off)}
 
 
 def layer_table(device_layers, device="cuda"):

@@ -2,6 +2,7 @@
 // launches on the caller's stream.  Declarations and the contract of each
 // entry point are in include/moe_decode.h.
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -30,7 +31,9 @@ moe_status check_shape(const moe_shape* s) {
 // A shape the general decode path serves (any other than Flint's fast path).
 bool general_shape(const moe_shape* s, moe::GenShape* g) {
   if (!s) return false;
-  if (s->wfmt != MOE_W_NVFP4 && s->wfmt != MOE_W_BF16 && s->wfmt != MOE_W_MXFP8) return false;
+  if (s->wfmt != MOE_W_NVFP4 && s->wfmt != MOE_W_BF16 && s->wfmt != MOE_W_MXFP8 &&
+      s->wfmt != MOE_W_NVFP4_A4)
+    return false;
   const bool ok = s->hidden >= 32 && s->hidden <= 8192 && s->hidden % 32 == 0 &&
                   s->inter >= 32 && s->inter <= 4096 && s->inter % 32 == 0 && s->top_k >= 1 &&
                   s->top_k <= moe::kGenMaxK && s->n_experts >= s->top_k &&
@@ -66,7 +69,7 @@ moe_status check_experts(const moe_experts* X, int fmt) {
   moe_status st;
   if ((st = check_ptr(X->w13)) != MOE_OK) return st;
   if ((st = check_ptr(X->w2)) != MOE_OK) return st;
-  if (fmt == MOE_W_NVFP4) {
+  if (fmt == MOE_W_NVFP4 || fmt == MOE_W_NVFP4_A4) {
     if ((st = check_ptr(X->w13_scale)) != MOE_OK) return st;
     if ((st = check_ptr(X->w2_scale)) != MOE_OK) return st;
     if ((st = check_ptr(X->global)) != MOE_OK) return st;
@@ -362,6 +365,23 @@ moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t n_layers,
       reinterpret_cast<const moe::LayerDev*>(layers), n_layers, static_cast<uint16_t*>(out),
       ids_out, static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_general_workspace_layout(const moe_shape* shape, size_t offsets[8]) {
+  moe::GenShape g;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  if (fast_path(shape) || !general_shape(shape, &g)) return MOE_ERR_UNSUPPORTED;
+  static_assert(moe::kGenMaxEntries == 66 && moe::kMaxB == 8, "layout documented in the header");
+  const moe::GenLayout L = moe::gen_layout(g);
+  offsets[0] = L.ctl + offsetof(moe::GenCtl, n_entries);
+  offsets[1] = L.ctl + offsetof(moe::GenCtl, entry);
+  offsets[2] = L.ctl + offsetof(moe::GenCtl, amask);
+  offsets[3] = L.h;
+  offsets[4] = L.xq;
+  offsets[5] = L.gx;
+  offsets[6] = L.hq;
+  offsets[7] = L.gh;
+  return MOE_OK;
 }
 
 moe_status moe_nvfp4_dequant(const moe_shape* shape, const moe_experts* set, int32_t expert,

@@ -30,7 +30,7 @@ struct ExpertsDev {
   const float* glob;     // NVFP4 f32 [n][3]
 };
 
-enum { FMT_NVFP4 = 0, FMT_BF16 = 1, FMT_MXFP8 = 2 };
+enum { FMT_NVFP4 = 0, FMT_BF16 = 1, FMT_MXFP8 = 2, FMT_NVFP4_A4 = 3 };
 
 // One layer of a stack as the stacked decode kernel reads it (device memory).
 struct LayerDev {
@@ -91,12 +91,12 @@ constexpr size_t kFlagStride = 128;
 constexpr size_t kDecodeWsBytes = kFlagOff + (256 + 64 * kBankReps) * kFlagStride;
 constexpr size_t kGenBase = kDecodeWsBytes;
 
-// Workspace of the general path: logits f32 [kMaxB][E], the dispatch, and h
-// bf16 [entry][kMaxB][I], after the Flint paths' region (kGenBase bytes), so
+// Workspace of the general path: logits f32 [kMaxB][E], the dispatch, h
+// bf16 [entry][kMaxB][I] (and for W4A4 the quantised x and h), after the Flint paths' region (kGenBase bytes), so
 // that one workspace can serve both without either touching the other's
 // counters.
 struct GenLayout {
-  size_t logits, ctl, h, total;
+  size_t logits, ctl, h, xq, gx, hq, gh, total;
 };
 __host__ __device__ inline GenLayout gen_layout(const GenShape& S) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
@@ -104,7 +104,13 @@ __host__ __device__ inline GenLayout gen_layout(const GenShape& S) {
   L.logits = al(kGenBase);
   L.ctl = al(L.logits + sizeof(float) * kMaxB * (size_t)S.E);
   L.h = al(L.ctl + sizeof(GenCtl));
-  L.total = al(L.h + 2 * (size_t)kGenMaxEntries * kMaxB * S.I);
+  // W4A4 only: the quantised x and h (bf16 e2m1 * e4m3, exact) and their
+  // per-vector global scales
+  L.xq = al(L.h + 2 * (size_t)kGenMaxEntries * kMaxB * S.I);
+  L.gx = al(L.xq + 2 * (size_t)kMaxB * S.H);
+  L.hq = al(L.gx + sizeof(float) * kMaxB);
+  L.gh = al(L.hq + 2 * (size_t)kGenMaxEntries * kMaxB * S.I);
+  L.total = al(L.gh + sizeof(float) * kGenMaxEntries * kMaxB);
   return L;
 }
 // upper bound of the entries of a call of B tokens

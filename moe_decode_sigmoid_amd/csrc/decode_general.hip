@@ -149,6 +149,96 @@ __device__ __forceinline__ void load_x32(const uint16_t* x, int H, int t, int ch
   }
 }
 
+// ------------------------------------------------------------------ W4A4 quantiser
+// Four Over Six NVFP4 quantisation of activations (the AREX article on vLLM's
+// Day-0 support for Inkling-2-Small, 48-layer MoE section: per-token global
+// scale, per-16-block scale mapping the block maximum to 6 or to 4, whichever
+// reconstructs with the smaller mean absolute error; a tie keeps 6).  Every
+// operation is an explicitly rounded fp32 one in a fixed order (global =
+// amax / 2688; candidate scale E4M3(bmax / M / g), nearest-even, saturating
+// at 448; q = e4m3 * g; code E2M1(v / q), nearest-even, saturating at 6; MAE
+// summed in element order over |v - e2m1 * q|), so every workgroup, and any
+// other implementation of these steps, takes the same decisions.
+
+// nearest-even onto the E4M3FN grid of a finite s >= 0, saturating at 448
+__device__ __forceinline__ uint32_t a4_e4m3_rne(float s) {
+  if (!(s > 0.0f)) return 0u;
+  if (s >= 448.0f) return 0x7Eu;
+  if (s < 0.015625f) {                                  // subnormal: multiples of 2^-9
+    const float m = __builtin_rintf(__builtin_ldexpf(s, 9));
+    return m >= 8.0f ? 0x08u : (uint32_t)m;
+  }
+  int e = (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFF) - 127;   // s normal here
+  float m = __builtin_rintf(__fmul_rn(__fsub_rn(__builtin_ldexpf(s, -e), 1.0f), 8.0f));
+  if (m >= 8.0f) { m = 0.0f; e += 1; }
+  if (e > 8 || (e == 8 && m > 6.0f)) return 0x7Eu;
+  return (uint32_t)(((e + 7) << 3) | (int)m);
+}
+
+__constant__ float kA4Grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+// nearest-even onto the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6} (saturating):
+// the signed value (midpoints go to the even-mantissa neighbour)
+__device__ __forceinline__ float a4_e2m1_rne(float v) {
+  const float a = fabsf(v);
+  int best = 0;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    const float dn = fabsf(__fsub_rn(a, kA4Grid[best])), di = fabsf(__fsub_rn(a, kA4Grid[i]));
+    if (di < dn || (di == dn && (i & 1) == 0)) best = i;
+  }
+  return __builtin_copysignf(kA4Grid[best], v);
+}
+
+__device__ __forceinline__ float a4_e4m3_value(uint32_t b) { return e4m3_to_f32<0>(b); }
+
+// one candidate for a 16-block held in v: the scale byte and the MAE
+__device__ __forceinline__ float a4_candidate(const float (&v)[16], float bmax, float g, float M,
+                                              uint32_t& sbyte) {
+  sbyte = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bmax, M), g));
+  const float q = __fmul_rn(a4_e4m3_value(sbyte), g);
+  float mae = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float c = q > 0.0f ? a4_e2m1_rne(__fdiv_rn(v[i], q)) : 0.0f;
+    mae = __fadd_rn(mae, fabsf(__fsub_rn(v[i], __fmul_rn(c, q))));
+  }
+  return mae;
+}
+
+// Quantise one 16-block v (global g): the 16 values e2m1 * e4m3 as bf16
+// (exact: at most 6 significant bits), two per word, into out[8].
+__device__ __forceinline__ void a4_block(const float (&v)[16], float g, uint32_t (&out)[8]) {
+  float bmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[i]));
+  if (g == 0.0f || bmax == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = 0u;
+    return;
+  }
+  uint32_t s6, s4;
+  const float m6 = a4_candidate(v, bmax, g, 6.0f, s6);
+  const float m4 = a4_candidate(v, bmax, g, 4.0f, s4);
+  const uint32_t sb = m4 < m6 ? s4 : s6;
+  const float sv = a4_e4m3_value(sb), q = __fmul_rn(sv, g);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c0 = q > 0.0f ? a4_e2m1_rne(__fdiv_rn(v[2 * i], q)) : 0.0f;
+    const float c1 = q > 0.0f ? a4_e2m1_rne(__fdiv_rn(v[2 * i + 1], q)) : 0.0f;
+    out[i] = (uint32_t)f32_to_bf16_rne(c0 * sv) | ((uint32_t)f32_to_bf16_rne(c1 * sv) << 16);
+  }
+}
+
+// 16 bf16 values (8 words) to fp32
+__device__ __forceinline__ void a4_unpack16(const uint32_t (&w)[8], float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = bf16_lo(w[i]);
+    v[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
 // ------------------------------------------------------------------ route
 // One wave per router row e: logits[t][e] = sum_k W_r[e][k] x[t][k].
 __global__ __launch_bounds__(kGenThreads) void k_gen_route(const uint16_t* __restrict__ x, int B,
@@ -217,7 +307,9 @@ __device__ __forceinline__ void wave_topk512(float (&v)[8], int lane, int K,
 __global__ __launch_bounds__(kGenThreads) void k_gen_select(int B, GenShape S,
                                                             int32_t* __restrict__ ids_out,
                                                             float* __restrict__ w_out,
-                                                            uint8_t* __restrict__ ws) {
+                                                            uint8_t* __restrict__ ws,
+                                                            const uint16_t* __restrict__ x,
+                                                            int a4) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const GenLayout L = gen_layout(S);
   const float* logits = reinterpret_cast<const float*>(ws + L.logits);
@@ -290,12 +382,82 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_select(int B, GenShape S,
     }
     if (lane == 0) ctl->n_entries = base + S.NS;
   }
+  if (!a4) return;
+  // W4A4: the experts' input is the Four-Over-Six quantisation of x (the
+  // router above used x itself); per token the global from its maximum, then
+  // one 16-block per thread
+  __shared__ float s_amax[kMaxB][4];
+  uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq);
+  float* gx = reinterpret_cast<float*>(ws + L.gx);
+  for (int t = 0; t < B; ++t) {
+    float m = 0.0f;
+    for (int i = tid; i < S.H / 8; i += kGenThreads) {
+      const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)t * S.H)[i];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[k])), fabsf(bf16_hi(u[k]))));
+    }
+    m = wave_max(m);
+    if (lane == 0) s_amax[t][wave] = m;
+  }
+  __syncthreads();
+  const int nb = S.H / 16;
+  for (int idx = tid; idx < B * nb; idx += kGenThreads) {
+    const int t = idx / nb, b = idx - t * nb;
+    const float g = __fdiv_rn(fmaxf(fmaxf(s_amax[t][0], s_amax[t][1]),
+                                    fmaxf(s_amax[t][2], s_amax[t][3])), 2688.0f);
+    if (b == 0) gx[t] = g;
+    const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * S.H + 16 * b);
+    const uint4 v0 = p[0], v1 = p[1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float v[16];
+    a4_unpack16(w, v);
+    uint32_t o[8];
+    a4_block(v, g, o);
+    uint4* q = reinterpret_cast<uint4*>(xq + (size_t)t * S.H + 16 * b);
+    q[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    q[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// W4A4: h of each (entry, token) pair quantised like x (its own global from
+// the pair's maximum over I), one wave per pair.  The pages quantise inside
+// the SiLU kernel; here a pair's h is spread over several workgroups of the
+// gate/up launch, so its maximum needs this separate pass.
+__global__ __launch_bounds__(64) void k_gen_quant_h(GenShape S, uint8_t* __restrict__ ws) {
+  const int lane = threadIdx.x, a = blockIdx.x, t = blockIdx.y;
+  const GenLayout L = gen_layout(S);
+  const GenCtl* ctl = reinterpret_cast<const GenCtl*>(ws + L.ctl);
+  if (a >= ctl->n_entries || !((ctl->amask[a] >> t) & 1u)) return;
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(ws + L.h) + ((size_t)a * kMaxB + t) * S.I;
+  uint16_t* hq = reinterpret_cast<uint16_t*>(ws + L.hq) + ((size_t)a * kMaxB + t) * S.I;
+  float m = 0.0f;
+  for (int i = lane; i < S.I / 8; i += 64) {
+    const uint4 v = reinterpret_cast<const uint4*>(h)[i];
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[k])), fabsf(bf16_hi(u[k]))));
+  }
+  const float g = __fdiv_rn(wave_max(m), 2688.0f);
+  if (lane == 0) reinterpret_cast<float*>(ws + L.gh)[(size_t)a * kMaxB + t] = g;
+  for (int b = lane; b < S.I / 16; b += 64) {
+    const uint4* p = reinterpret_cast<const uint4*>(h + 16 * b);
+    const uint4 v0 = p[0], v1 = p[1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float v[16];
+    a4_unpack16(w, v);
+    uint32_t o[8];
+    a4_block(v, g, o);
+    uint4* q = reinterpret_cast<uint4*>(hq + 16 * b);
+    q[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    q[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
 }
 
 // ------------------------------------------------------------------ gate/up
 // Workgroup (entry a, rows 4 blockIdx.y + wave): h[a][t][r] = SiLU(g) * u for
 // the entry's tokens, bf16.
-template <int FMT>
+template <int FMT, bool A4>
 __global__ __launch_bounds__(kGenThreads) void k_gen_gateup(const uint16_t* __restrict__ x, int B,
                                                             GenShape S, ExpertsDev routed,
                                                             ExpertsDev shared,
@@ -307,6 +469,7 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_gateup(const uint16_t* __re
   const GenCtl* ctl = reinterpret_cast<const GenCtl*>(ws + L.ctl);
   if (a >= ctl->n_entries || r >= S.I) return;
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.h);
+  if constexpr (A4) x = reinterpret_cast<const uint16_t*>(ws + L.xq);   // e2m1 * e4m3, x global apart
   const int e = ctl->entry[a];
   const unsigned mask = ctl->amask[a];
   const bool sh = e >= S.E;
@@ -334,7 +497,8 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_gateup(const uint16_t* __re
 #pragma unroll
   for (int t = 0; t < kMaxB; ++t) {
     if ((mask >> t) & 1u) {
-      const float g = wave_sum(ag[t]) * sg, u = wave_sum(au[t]) * su;
+      const float gxt = A4 ? reinterpret_cast<const float*>(ws + L.gx)[t] : 1.0f;
+      const float g = wave_sum(ag[t]) * sg * gxt, u = wave_sum(au[t]) * su * gxt;
       if (lane == 0) hbuf[((size_t)a * kMaxB + t) * S.I + r] = f32_to_bf16_rne(silu_mul(g, u));
     }
   }
@@ -347,7 +511,7 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_gateup(const uint16_t* __re
 // wave 3), each walking its entries in order, and the 4 partial sums are added
 // in wave order: a token's sum depends only on its own experts, never on the
 // rest of the batch.
-template <int FMT, int LPR>
+template <int FMT, int LPR, bool A4>
 __global__ __launch_bounds__(kGenThreads) void k_gen_down(int B, GenShape S, ExpertsDev routed,
                                                           ExpertsDev shared,
                                                           uint8_t* __restrict__ ws,
@@ -358,7 +522,7 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_down(int B, GenShape S, Exp
   const int j = blockIdx.x * kRows + q;
   const GenLayout L = gen_layout(S);
   const GenCtl* ctl = reinterpret_cast<const GenCtl*>(ws + L.ctl);
-  const uint16_t* hbuf = reinterpret_cast<const uint16_t*>(ws + L.h);
+  const uint16_t* hbuf = reinterpret_cast<const uint16_t*>(ws + (A4 ? L.hq : L.h));
   __shared__ float s_red[4][kRows][kMaxB];
   const bool live = j < S.H;
   const int na = ctl->n_entries;
@@ -403,6 +567,7 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_down(int B, GenShape S, Exp
         float z = part[t];
 #pragma unroll
         for (int o = 1; o < LPR; o <<= 1) z += __shfl_xor(z, o, 64);
+        if constexpr (A4) z *= reinterpret_cast<const float*>(ws + L.gh)[(size_t)a * kMaxB + t];
         acc[t] += ctl->wt[a][t] * (z * sd);
       }
     }
@@ -425,38 +590,42 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_down(int B, GenShape S, Exp
 size_t gen_ws_bytes(const GenShape& S) { return gen_layout(S).total; }
 
 hipError_t launch_route_general(int B, const GenShape& S, const uint16_t* x, const uint16_t* rw,
-                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st) {
+                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st, int a4) {
   hipLaunchKernelGGL(k_gen_route, dim3((S.E + 3) / 4), dim3(kGenThreads), 0, st, x, B, rw, S, ws);
-  hipLaunchKernelGGL(k_gen_select, dim3(1), dim3(kGenThreads), 0, st, B, S, ids, w, ws);
+  hipLaunchKernelGGL(k_gen_select, dim3(1), dim3(kGenThreads), 0, st, B, S, ids, w, ws, x, a4);
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool A4 = false>
 static void launch_experts_general(int B, const GenShape& S, const uint16_t* x,
                                    const ExpertsDev& routed, const ExpertsDev& shared,
                                    uint16_t* out, uint8_t* ws, hipStream_t st) {
   const int maxa = gen_max_entries(S, B);
-  hipLaunchKernelGGL(k_gen_gateup<FMT>, dim3(maxa, (S.I + 3) / 4), dim3(kGenThreads), 0, st, x, B,
-                     S, routed, shared, ws);
+  hipLaunchKernelGGL((k_gen_gateup<FMT, A4>), dim3(maxa, (S.I + 3) / 4), dim3(kGenThreads), 0, st,
+                     x, B, S, routed, shared, ws);
+  if constexpr (A4)
+    hipLaunchKernelGGL(k_gen_quant_h, dim3(maxa, B), dim3(64), 0, st, S, ws);
   const int nch = S.I / 32;
   if (nch <= 16)
-    hipLaunchKernelGGL((k_gen_down<FMT, 16>), dim3((S.H + 3) / 4), dim3(kGenThreads), 0, st, B, S,
-                       routed, shared, ws, out);
+    hipLaunchKernelGGL((k_gen_down<FMT, 16, A4>), dim3((S.H + 3) / 4), dim3(kGenThreads), 0, st, B,
+                       S, routed, shared, ws, out);
   else if (nch <= 32)
-    hipLaunchKernelGGL((k_gen_down<FMT, 32>), dim3((S.H + 1) / 2), dim3(kGenThreads), 0, st, B, S,
-                       routed, shared, ws, out);
+    hipLaunchKernelGGL((k_gen_down<FMT, 32, A4>), dim3((S.H + 1) / 2), dim3(kGenThreads), 0, st, B,
+                       S, routed, shared, ws, out);
   else
-    hipLaunchKernelGGL((k_gen_down<FMT, 64>), dim3(S.H), dim3(kGenThreads), 0, st, B, S, routed,
-                       shared, ws, out);
+    hipLaunchKernelGGL((k_gen_down<FMT, 64, A4>), dim3(S.H), dim3(kGenThreads), 0, st, B, S,
+                       routed, shared, ws, out);
 }
 
 hipError_t launch_decode_general(int B, int fmt, const GenShape& S, const uint16_t* x,
                                  const uint16_t* rw, const ExpertsDev& routed,
                                  const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
                                  uint8_t* ws, hipStream_t st) {
-  hipError_t e = launch_route_general(B, S, x, rw, ids, w, ws, st);
+  hipError_t e = launch_route_general(B, S, x, rw, ids, w, ws, st, fmt == FMT_NVFP4_A4);
   if (e != hipSuccess) return e;
-  if (fmt == FMT_NVFP4)
+  if (fmt == FMT_NVFP4_A4)
+    launch_experts_general<FMT_NVFP4, true>(B, S, x, routed, shared, out, ws, st);
+  else if (fmt == FMT_NVFP4)
     launch_experts_general<FMT_NVFP4>(B, S, x, routed, shared, out, ws, st);
   else if (fmt == FMT_BF16)
     launch_experts_general<FMT_BF16>(B, S, x, routed, shared, out, ws, st);

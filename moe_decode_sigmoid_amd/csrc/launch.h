@@ -50,7 +50,7 @@ hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
 // including MXFP8): four launches.  The route-only entry runs its first two.
 size_t gen_ws_bytes(const GenShape& S);
 hipError_t launch_route_general(int B, const GenShape& S, const uint16_t* x, const uint16_t* rw,
-                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st);
+                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st, int a4 = 0);
 hipError_t launch_decode_general(int B, int fmt, const GenShape& S, const uint16_t* x,
                                  const uint16_t* rw, const ExpertsDev& routed,
                                  const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,

@@ -21,6 +21,7 @@ def test_header_declares_the_entry_points():
     for n in ["moe_decode_route", "moe_decode_forward", "moe_decode_forward_timed",
               "moe_prefill_forward", "moe_nvfp4_gemv", "moe_decode_forward_ex",
               "moe_prefill_forward_ex", "moe_decode_stack_forward",
+              "moe_general_workspace_layout",
               "moe_nvfp4_dequant", "moe_workspace_bytes", "moe_status_string",
               "moe_abi_version"]:
         assert n in names
@@ -246,6 +247,23 @@ def test_stack_argument_errors():
     assert call(out=A + 4096, ws=A + 0x50000000, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG  # x
     assert call(S=moe.shape(n_experts=384, top_k=8, n_shared=0), wsb=WS_BIG) == \
         moe.MOE_ERR_UNSUPPORTED
+
+
+def test_general_workspace_layout():
+    S = moe.shape(moe.MOE_W_NVFP4_A4)                    # Flint's shape, W4A4: general path
+    off = moe.general_workspace_layout(S)
+    need = moe.moe_workspace_bytes(8, S=S)
+    assert off["n_entries"] >= moe.moe_workspace_bytes(8)   # after the Flint paths' region
+    assert sorted(off.values()) == [off[k] for k in ["n_entries", "entry", "amask", "h", "xq",
+                                                      "gx", "hq", "gh"]]
+    assert off["gh"] + 4 * 66 * 8 <= need
+    with pytest.raises(moe.MoeError):
+        moe.general_workspace_layout(moe.shape())        # Flint NVFP4: the fused path
+    # W4A4 needs the NVFP4 scales and global (no launch: workspace too small)
+    assert _forward(S=S, ws_bytes=1024) == moe.MOE_ERR_WORKSPACE
+    bf = _FakeExperts(A + 0x4000000, fmt="bf16")
+    assert _forward(S=S, routed=bf) == moe.MOE_ERR_INVALID_ARG
+    assert _forward(S=S, prefill=True) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_decode_batch_limit_is_unsupported_not_invalid():
