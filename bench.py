@@ -172,13 +172,14 @@ def run_dense(args, moe, testgen, torch, dev) -> dict:
 GENERAL_SHAPES = {
     "inkling2small_384x8_mxfp8": (2048, 512, 384, 8, 0, "mxfp8"),
     "inkling_256x6_2shared_nvfp4": (2048, 512, 256, 6, 2, "nvfp4"),
+    "flint_w4a4_four_over_six": (2048, 512, 256, 6, 1, "nvfp4_a4"),
 }
 
 
 def expert_bytes(H: int, I: int, fmt: str) -> int:
     """Bytes of one expert (gate, up, down) as the kernels read them."""
     m = H * I
-    if fmt == "nvfp4":
+    if fmt in ("nvfp4", "nvfp4_a4"):
         return 3 * (m // 2 + m // 16 + 4)
     if fmt == "mxfp8":
         return 3 * (m + m // 32)
@@ -191,7 +192,8 @@ def run_general(args, moe, testgen, torch, dev, copies: int = 16) -> dict:
     launches per step, HIP events around the replays."""
     out = {}
     for name, (H, I, E, K, NS, fmt) in GENERAL_SHAPES.items():
-        host = testgen.make_layer(args.seed, 0, fmt, H, I, E, K, n_shared=NS)
+        host = testgen.make_layer(args.seed, 0, "nvfp4" if fmt == "nvfp4_a4" else fmt, H, I, E, K,
+                                  n_shared=NS)
         d0 = moe.DeviceLayer.from_host(host, dev)
         del host
 

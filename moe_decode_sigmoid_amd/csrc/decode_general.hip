@@ -9,7 +9,8 @@
 // 48-layer MoE section).  The Flint layer runs on the single-launch kernel;
 // every other shape within the limits below runs here, as four launches:
 //
-//   route    one wave per router row: logits [B][E] (fp32 accumulate)
+//   route    one wave per router row: logits [B][E] (fp32 accumulate); W4A4:
+//            also the experts' quantised x
 //   select   one workgroup: per token the top-k logits (ties to the lower
 //            index), sigmoid, w = s / sum s; the touched experts become
 //            entries in ascending id, then the shared experts (weight 1)
@@ -175,103 +176,131 @@ __device__ __forceinline__ uint32_t a4_e4m3_rne(float s) {
   return (uint32_t)(((e + 7) << 3) | (int)m);
 }
 
-__constant__ float kA4Grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-
-// nearest-even onto the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6} (saturating):
-// the signed value (midpoints go to the even-mantissa neighbour)
+// nearest-even onto the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at
+// 6, as a signed value: midpoints go to the neighbour with the even mantissa
+// bit (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4)
 __device__ __forceinline__ float a4_e2m1_rne(float v) {
   const float a = fabsf(v);
-  int best = 0;
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    const float dn = fabsf(__fsub_rn(a, kA4Grid[best])), di = fabsf(__fsub_rn(a, kA4Grid[i]));
-    if (di < dn || (di == dn && (i & 1) == 0)) best = i;
-  }
-  return __builtin_copysignf(kA4Grid[best], v);
+  const float r = a <= 0.25f ? 0.0f : a < 0.75f ? 0.5f : a <= 1.25f ? 1.0f : a < 1.75f ? 1.5f
+                : a <= 2.5f ? 2.0f : a < 3.5f ? 3.0f : a <= 5.0f ? 4.0f : 6.0f;
+  return __builtin_copysignf(r, v);
 }
 
 __device__ __forceinline__ float a4_e4m3_value(uint32_t b) { return e4m3_to_f32<0>(b); }
 
-// one candidate for a 16-block held in v: the scale byte and the MAE
-__device__ __forceinline__ float a4_candidate(const float (&v)[16], float bmax, float g, float M,
-                                              uint32_t& sbyte) {
-  sbyte = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bmax, M), g));
-  const float q = __fmul_rn(a4_e4m3_value(sbyte), g);
-  float mae = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float c = q > 0.0f ? a4_e2m1_rne(__fdiv_rn(v[i], q)) : 0.0f;
-    mae = __fadd_rn(mae, fabsf(__fsub_rn(v[i], __fmul_rn(c, q))));
-  }
-  return mae;
+// max over each aligned group of 16 lanes (a DPP row)
+__device__ __forceinline__ float group16_max(float v) {
+  v = fmaxf(v, dpp_f32<0x128>(v));
+  v = fmaxf(v, dpp_f32<0x124>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  return v;
 }
 
-// Quantise one 16-block v (global g): the 16 values e2m1 * e4m3 as bf16
-// (exact: at most 6 significant bits), two per word, into out[8].
-__device__ __forceinline__ void a4_block(const float (&v)[16], float g, uint32_t (&out)[8]) {
-  float bmax = 0.0f;
+// sum of the 16 values of a lane group in lane order (each lane gets it),
+// through the wave's 64-float LDS area (a wave's LDS accesses are ordered)
+__device__ __forceinline__ float group16_sum_in_order(float v, int lane, float* lds) {
+  lds[lane] = v;
+  const float4* p = reinterpret_cast<const float4*>(lds + (lane & ~15));
+  float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[i]));
-  if (g == 0.0f || bmax == 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = 0u;
-    return;
+  for (int i = 0; i < 4; ++i) {
+    const float4 q = p[i];
+    s = __fadd_rn(__fadd_rn(__fadd_rn(__fadd_rn(s, q.x), q.y), q.z), q.w);
   }
-  uint32_t s6, s4;
-  const float m6 = a4_candidate(v, bmax, g, 6.0f, s6);
-  const float m4 = a4_candidate(v, bmax, g, 4.0f, s4);
-  const uint32_t sb = m4 < m6 ? s4 : s6;
-  const float sv = a4_e4m3_value(sb), q = __fmul_rn(sv, g);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float c0 = q > 0.0f ? a4_e2m1_rne(__fdiv_rn(v[2 * i], q)) : 0.0f;
-    const float c1 = q > 0.0f ? a4_e2m1_rne(__fdiv_rn(v[2 * i + 1], q)) : 0.0f;
-    out[i] = (uint32_t)f32_to_bf16_rne(c0 * sv) | ((uint32_t)f32_to_bf16_rne(c1 * sv) << 16);
-  }
+  return s;
 }
 
-// 16 bf16 values (8 words) to fp32
-__device__ __forceinline__ void a4_unpack16(const uint32_t (&w)[8], float (&v)[16]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = bf16_lo(w[i]);
-    v[2 * i + 1] = bf16_hi(w[i]);
+// One 16-block held by a group of 16 lanes (lane l: element l & 15, value v),
+// global g: this lane's quantised value e2m1 * e4m3 (the global apart; exact
+// in bf16).  Both candidates are evaluated element-wise and their errors
+// summed in element order.
+__device__ __forceinline__ float a4_quant_elem(float v, float g, int lane, float* lds) {
+  const float bmax = group16_max(fabsf(v));
+  if (g == 0.0f || bmax == 0.0f) return 0.0f;
+  const uint32_t s6 = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bmax, 6.0f), g));
+  const uint32_t s4 = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bmax, 4.0f), g));
+  const float v6 = a4_e4m3_value(s6), v4 = a4_e4m3_value(s4);
+  const float q6 = __fmul_rn(v6, g), q4 = __fmul_rn(v4, g);
+  const float c6 = q6 > 0.0f ? a4_e2m1_rne(__fdiv_rn(v, q6)) : 0.0f;
+  const float c4 = q4 > 0.0f ? a4_e2m1_rne(__fdiv_rn(v, q4)) : 0.0f;
+  const float m6 = group16_sum_in_order(fabsf(__fsub_rn(v, __fmul_rn(c6, q6))), lane, lds);
+  const float m4 = group16_sum_in_order(fabsf(__fsub_rn(v, __fmul_rn(c4, q4))), lane, lds + 64);
+  return m4 < m6 ? c4 * v4 : c6 * v6;
+}
+
+// Quantise n bf16 values (a multiple of 16) at src into dst (bf16 e2m1 *
+// e4m3) with global g, by the threads [0, nthreads) of the caller, 16 per
+// block; lds: 128 floats per wave of the caller.
+__device__ __forceinline__ void a4_quant_vector(const uint16_t* src, uint16_t* dst, int n, float g,
+                                                int tid, int nthreads, float* lds) {
+  const int lane = tid & 63;
+  float* wl = lds + 128 * (tid >> 6);
+  for (int i0 = 0; i0 < n; i0 += nthreads) {          // uniform trip count per wave
+    const int i = i0 + tid;
+    const float v = i < n ? __builtin_bit_cast(float, (uint32_t)src[i] << 16) : 0.0f;
+    const float q = a4_quant_elem(v, g, lane, wl);
+    if (i < n) dst[i] = f32_to_bf16_rne(q);
   }
 }
 
 // ------------------------------------------------------------------ route
-// One wave per router row e: logits[t][e] = sum_k W_r[e][k] x[t][k].
+// One wave per router row e: logits[t][e] = sum_k W_r[e][k] x[t][k].  W4A4:
+// workgroup t < B also quantises token t's x for the experts (the router
+// itself reads x), after its router rows.
 __global__ __launch_bounds__(kGenThreads) void k_gen_route(const uint16_t* __restrict__ x, int B,
                                                            const uint16_t* __restrict__ rw,
-                                                           GenShape S, uint8_t* __restrict__ ws) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * (kGenThreads / 64) + (threadIdx.x >> 6);
-  if (e >= S.E) return;
-  float* logits = reinterpret_cast<float*>(ws + gen_layout(S).logits);
-  float acc[kMaxB];
+                                                           GenShape S, uint8_t* __restrict__ ws,
+                                                           int a4) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x * (kGenThreads / 64) + wave;
+  const GenLayout L = gen_layout(S);
+  if (e < S.E) {
+    float* logits = reinterpret_cast<float*>(ws + L.logits);
+    float acc[kMaxB];
 #pragma unroll
-  for (int t = 0; t < kMaxB; ++t) acc[t] = 0.0f;
-  const uint4* wrow = reinterpret_cast<const uint4*>(rw + (size_t)e * S.H);
-  for (int c = lane; c < S.H / 8; c += 64) {
-    const uint4 w = wrow[c];
+    for (int t = 0; t < kMaxB; ++t) acc[t] = 0.0f;
+    const uint4* wrow = reinterpret_cast<const uint4*>(rw + (size_t)e * S.H);
+    for (int c = lane; c < S.H / 8; c += 64) {
+      const uint4 w = wrow[c];
+#pragma unroll
+      for (int t = 0; t < kMaxB; ++t) {
+        if (t < B) {
+          const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)t * S.H)[c];
+          float a = dot2_bf16(w.x, v.x, acc[t]);
+          a = dot2_bf16(w.y, v.y, a);
+          a = dot2_bf16(w.z, v.z, a);
+          acc[t] = dot2_bf16(w.w, v.w, a);
+        }
+      }
+    }
 #pragma unroll
     for (int t = 0; t < kMaxB; ++t) {
       if (t < B) {
-        const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)t * S.H)[c];
-        float a = dot2_bf16(w.x, v.x, acc[t]);
-        a = dot2_bf16(w.y, v.y, a);
-        a = dot2_bf16(w.z, v.z, a);
-        acc[t] = dot2_bf16(w.w, v.w, a);
+        const float z = wave_sum(acc[t]);
+        if (lane == 0) logits[t * S.E + e] = z;
       }
     }
   }
+  if (!a4 || (int)blockIdx.x >= B) return;
+  const int t = blockIdx.x;
+  __shared__ float s_amax[4];
+  float m = 0.0f;
+  for (int i = tid; i < S.H / 8; i += kGenThreads) {
+    const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)t * S.H)[i];
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int t = 0; t < kMaxB; ++t) {
-    if (t < B) {
-      const float z = wave_sum(acc[t]);
-      if (lane == 0) logits[t * S.E + e] = z;
-    }
+    for (int k = 0; k < 4; ++k) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[k])), fabsf(bf16_hi(u[k]))));
   }
+  m = wave_max(m);
+  if (lane == 0) s_amax[wave] = m;
+  __syncthreads();
+  const float g =
+      __fdiv_rn(fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3])), 2688.0f);
+  if (tid == 0) reinterpret_cast<float*>(ws + L.gx)[t] = g;
+  __shared__ float s_q[kGenThreads / 64 * 128];
+  a4_quant_vector(x + (size_t)t * S.H, reinterpret_cast<uint16_t*>(ws + L.xq) + (size_t)t * S.H,
+                  S.H, g, tid, kGenThreads, s_q);
 }
 
 // ------------------------------------------------------------------ select
@@ -307,9 +336,7 @@ __device__ __forceinline__ void wave_topk512(float (&v)[8], int lane, int K,
 __global__ __launch_bounds__(kGenThreads) void k_gen_select(int B, GenShape S,
                                                             int32_t* __restrict__ ids_out,
                                                             float* __restrict__ w_out,
-                                                            uint8_t* __restrict__ ws,
-                                                            const uint16_t* __restrict__ x,
-                                                            int a4) {
+                                                            uint8_t* __restrict__ ws) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const GenLayout L = gen_layout(S);
   const float* logits = reinterpret_cast<const float*>(ws + L.logits);
@@ -382,76 +409,35 @@ __global__ __launch_bounds__(kGenThreads) void k_gen_select(int B, GenShape S,
     }
     if (lane == 0) ctl->n_entries = base + S.NS;
   }
-  if (!a4) return;
-  // W4A4: the experts' input is the Four-Over-Six quantisation of x (the
-  // router above used x itself); per token the global from its maximum, then
-  // one 16-block per thread
-  __shared__ float s_amax[kMaxB][4];
-  uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq);
-  float* gx = reinterpret_cast<float*>(ws + L.gx);
-  for (int t = 0; t < B; ++t) {
-    float m = 0.0f;
-    for (int i = tid; i < S.H / 8; i += kGenThreads) {
-      const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)t * S.H)[i];
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[k])), fabsf(bf16_hi(u[k]))));
-    }
-    m = wave_max(m);
-    if (lane == 0) s_amax[t][wave] = m;
-  }
-  __syncthreads();
-  const int nb = S.H / 16;
-  for (int idx = tid; idx < B * nb; idx += kGenThreads) {
-    const int t = idx / nb, b = idx - t * nb;
-    const float g = __fdiv_rn(fmaxf(fmaxf(s_amax[t][0], s_amax[t][1]),
-                                    fmaxf(s_amax[t][2], s_amax[t][3])), 2688.0f);
-    if (b == 0) gx[t] = g;
-    const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * S.H + 16 * b);
-    const uint4 v0 = p[0], v1 = p[1];
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    float v[16];
-    a4_unpack16(w, v);
-    uint32_t o[8];
-    a4_block(v, g, o);
-    uint4* q = reinterpret_cast<uint4*>(xq + (size_t)t * S.H + 16 * b);
-    q[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    q[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  }
 }
 
 // W4A4: h of each (entry, token) pair quantised like x (its own global from
-// the pair's maximum over I), one wave per pair.  The pages quantise inside
+// the pair's maximum over I), one workgroup per pair.  The pages quantise inside
 // the SiLU kernel; here a pair's h is spread over several workgroups of the
 // gate/up launch, so its maximum needs this separate pass.
-__global__ __launch_bounds__(64) void k_gen_quant_h(GenShape S, uint8_t* __restrict__ ws) {
-  const int lane = threadIdx.x, a = blockIdx.x, t = blockIdx.y;
+__global__ __launch_bounds__(kGenThreads) void k_gen_quant_h(GenShape S, uint8_t* __restrict__ ws) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, a = blockIdx.x, t = blockIdx.y;
   const GenLayout L = gen_layout(S);
   const GenCtl* ctl = reinterpret_cast<const GenCtl*>(ws + L.ctl);
   if (a >= ctl->n_entries || !((ctl->amask[a] >> t) & 1u)) return;
   const uint16_t* h = reinterpret_cast<const uint16_t*>(ws + L.h) + ((size_t)a * kMaxB + t) * S.I;
   uint16_t* hq = reinterpret_cast<uint16_t*>(ws + L.hq) + ((size_t)a * kMaxB + t) * S.I;
+  __shared__ float s_amax[kGenThreads / 64];
+  __shared__ float s_q[kGenThreads / 64 * 128];
   float m = 0.0f;
-  for (int i = lane; i < S.I / 8; i += 64) {
+  for (int i = tid; i < S.I / 8; i += kGenThreads) {
     const uint4 v = reinterpret_cast<const uint4*>(h)[i];
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[k])), fabsf(bf16_hi(u[k]))));
   }
-  const float g = __fdiv_rn(wave_max(m), 2688.0f);
-  if (lane == 0) reinterpret_cast<float*>(ws + L.gh)[(size_t)a * kMaxB + t] = g;
-  for (int b = lane; b < S.I / 16; b += 64) {
-    const uint4* p = reinterpret_cast<const uint4*>(h + 16 * b);
-    const uint4 v0 = p[0], v1 = p[1];
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    float v[16];
-    a4_unpack16(w, v);
-    uint32_t o[8];
-    a4_block(v, g, o);
-    uint4* q = reinterpret_cast<uint4*>(hq + 16 * b);
-    q[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    q[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  }
+  m = wave_max(m);
+  if (lane == 0) s_amax[wave] = m;
+  __syncthreads();
+  const float g =
+      __fdiv_rn(fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3])), 2688.0f);
+  if (tid == 0) reinterpret_cast<float*>(ws + L.gh)[(size_t)a * kMaxB + t] = g;
+  a4_quant_vector(h, hq, S.I, g, tid, kGenThreads, s_q);
 }
 
 // ------------------------------------------------------------------ gate/up
@@ -591,8 +577,10 @@ size_t gen_ws_bytes(const GenShape& S) { return gen_layout(S).total; }
 
 hipError_t launch_route_general(int B, const GenShape& S, const uint16_t* x, const uint16_t* rw,
                                 int32_t* ids, float* w, uint8_t* ws, hipStream_t st, int a4) {
-  hipLaunchKernelGGL(k_gen_route, dim3((S.E + 3) / 4), dim3(kGenThreads), 0, st, x, B, rw, S, ws);
-  hipLaunchKernelGGL(k_gen_select, dim3(1), dim3(kGenThreads), 0, st, B, S, ids, w, ws, x, a4);
+  const int nwg = (S.E + 3) / 4;
+  hipLaunchKernelGGL(k_gen_route, dim3(a4 && nwg < B ? B : nwg), dim3(kGenThreads), 0, st, x, B, rw,
+                     S, ws, a4);
+  hipLaunchKernelGGL(k_gen_select, dim3(1), dim3(kGenThreads), 0, st, B, S, ids, w, ws);
   return hipGetLastError();
 }
 
@@ -604,7 +592,7 @@ static void launch_experts_general(int B, const GenShape& S, const uint16_t* x,
   hipLaunchKernelGGL((k_gen_gateup<FMT, A4>), dim3(maxa, (S.I + 3) / 4), dim3(kGenThreads), 0, st,
                      x, B, S, routed, shared, ws);
   if constexpr (A4)
-    hipLaunchKernelGGL(k_gen_quant_h, dim3(maxa, B), dim3(64), 0, st, S, ws);
+    hipLaunchKernelGGL(k_gen_quant_h, dim3(maxa, B), dim3(kGenThreads), 0, st, S, ws);
   const int nch = S.I / 32;
   if (nch <= 16)
     hipLaunchKernelGGL((k_gen_down<FMT, 16, A4>), dim3((S.H + 3) / 4), dim3(kGenThreads), 0, st, B,
