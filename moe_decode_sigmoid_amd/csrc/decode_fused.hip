@@ -52,6 +52,8 @@
 // on data).
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -65,6 +67,24 @@ constexpr int kMaxRange = (kMaxB * kK * kI + kFusedGrid - 1) / kFusedGrid;  // r
 constexpr int kSpinLimit = 1 << 18;
 
 // ------------------------------------------------------------------ row chunks
+// Weight loads through global-address-space pointers.  The stacked launch
+// reads its weight pointers from the layer table in memory, which the
+// compiler cannot place, and a flat load also counts against the LDS wait
+// counter: every LDS wait and barrier would then wait for the weights in
+// flight.
+// (HIP's uint4 is a struct, whose copy drops the address space: its loads
+// go through a native vector type.)
+template <typename T>
+__device__ __forceinline__ T gld(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <>
+__device__ __forceinline__ uint4 gld<uint4>(const void* p) {
+  const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // A lane's 32 consecutive elements of one weight row.
 template <int FMT>
 struct Chunk;
@@ -75,13 +95,13 @@ struct Chunk<FMT_NVFP4> {
   uint32_t s;
   __device__ __forceinline__ void load_gu(const ExpertsDev& X, size_t ee, int m, int row, int ch) {
     const size_t r = (ee * 2 + m) * kI + row;
-    c = *reinterpret_cast<const uint4*>(X.w13 + r * (kH / 2) + 16 * ch);
-    s = *reinterpret_cast<const uint16_t*>(X.w13s + r * (kH / 16) + 2 * ch);
+    c = gld<uint4>(X.w13 + r * (kH / 2) + 16 * ch);
+    s = gld<uint16_t>(X.w13s + r * (kH / 16) + 2 * ch);
   }
   __device__ __forceinline__ void load_dn(const ExpertsDev& X, size_t ee, int row, int ch) {
     const size_t r = ee * kH + row;
-    c = *reinterpret_cast<const uint4*>(X.w2 + r * (kI / 2) + 16 * ch);
-    s = *reinterpret_cast<const uint16_t*>(X.w2s + r * (kI / 16) + 2 * ch);
+    c = gld<uint4>(X.w2 + r * (kI / 2) + 16 * ch);
+    s = gld<uint16_t>(X.w2s + r * (kI / 16) + 2 * ch);
   }
   // sum_k w_k v_k over the chunk (v: 32 bf16 values in pairs), without the
   // tensor scale; v is x for gate/up rows and h for down rows
@@ -105,7 +125,7 @@ struct Chunk<FMT_NVFP4> {
     return b0 * e4m3_to_f32<0>(s) + b1 * e4m3_to_f32<1>(s);
   }
   __device__ __forceinline__ static float gscale(const ExpertsDev& X, size_t ee, int m) {
-    return X.glob[ee * 3 + m];
+    return gld<float>(X.glob + ee * 3 + m);
   }
 };
 
@@ -113,14 +133,14 @@ template <>
 struct Chunk<FMT_BF16> {
   uint4 w[4];
   __device__ __forceinline__ void load_gu(const ExpertsDev& X, size_t ee, int m, int row, int ch) {
-    const uint4* p = reinterpret_cast<const uint4*>(X.w13 + (((ee * 2 + m) * kI + row) * kH + 32 * ch) * 2);
+    const uint8_t* p = X.w13 + (((ee * 2 + m) * kI + row) * kH + 32 * ch) * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = p[i];
+    for (int i = 0; i < 4; ++i) w[i] = gld<uint4>(p + 16 * i);
   }
   __device__ __forceinline__ void load_dn(const ExpertsDev& X, size_t ee, int row, int ch) {
-    const uint4* p = reinterpret_cast<const uint4*>(X.w2 + ((ee * kH + row) * kI + 32 * ch) * 2);
+    const uint8_t* p = X.w2 + ((ee * kH + row) * kI + 32 * ch) * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = p[i];
+    for (int i = 0; i < 4; ++i) w[i] = gld<uint4>(p + 16 * i);
   }
   __device__ __forceinline__ float dot_x(const uint32_t (&xw)[16]) const {
     float b0 = 0.0f, b1 = 0.0f;
@@ -429,7 +449,7 @@ template <int B, int FMT>
 __device__ __forceinline__ void load_pre_gateup(StepAPre<FMT>& p, const uint16_t* rw,
                                                 const ExpertsDev& shared, int g, int wave,
                                                 int lane) {
-  p.wr = *reinterpret_cast<const uint4*>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
+  p.wr = gld<uint4>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
   if (shared_token_mask<B>(wave)) {
     p.scg.load_gu(shared, 0, 0, 2 * g + (wave & 1), lane);
     p.scu.load_gu(shared, 0, 1, 2 * g + (wave & 1), lane);
@@ -444,17 +464,33 @@ __device__ __forceinline__ void load_pre_down(StepAPre<FMT>& p, const ExpertsDev
     p.dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * (lane >> 4) + r, lane & 15);
 }
 
+// A stacked launch prefetches the next layer's step-A rows only when this
+// layer issues no load after its h copy: each wave's routed entries (at most
+// 6 B / 4 of them) all fit in the two down-row sets issued before the
+// h-ready wait.  Otherwise the later down loads would queue behind them.
+template <int FMT>
+constexpr int kDownDepth = FMT == FMT_NVFP4 ? 4 : 1;   // routed entries per down-row set
+template <int B, int FMT>
+constexpr bool kPrefetchNext = kK * B <= 4 * 2 * kDownDepth<FMT>;
+
 // ------------------------------------------------------------------ kernel
 // One layer, as one workgroup of the 256 runs it (the body of both kernels
 // below).
-template <int B, int FMT, bool NORM, bool RESID>
+// pre: the step-A loads of this layer.  PF (layers of a stacked launch when
+// kPrefetchNext holds): 0 none; 1 this layer issues its own step-A loads and,
+// once nothing of its own is left to load, those of `next`; 2 as 1, but this
+// layer's were issued by the previous layer.  PF is static so that the
+// compiler counts the loads in flight exactly (a load under a runtime branch
+// makes it wait for all of them).
+template <int B, int FMT, bool NORM, bool RESID, int PF>
 __device__ __forceinline__ void decode_layer(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, const ExpertsDev& routed,
     const ExpertsDev& shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz) {
-  StepAPre<FMT> pre;
+    float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz, StepAPre<FMT>& pre,
+    const LayerDev& next) {
+  static_assert(PF == 0 || kPrefetchNext<B, FMT>, "prefetch needs every down row in flight");
   constexpr int kTB = FMT == FMT_NVFP4 ? 4 : 2;      // gate/up row pairs per batch
-  constexpr int kDepthC = FMT == FMT_NVFP4 ? 4 : 1;  // entries of down rows in flight
+  constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
   constexpr int kPairs = (kK + 1) * B;               // h pairs: 6 B routed + B shared
   const int g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -482,7 +518,7 @@ __device__ __forceinline__ void decode_layer(
   trace_stamp(ws, 0);
   // ---------------------------------------------------------------- step A
   const unsigned smask = shared_token_mask<B>(wave);
-  load_pre_gateup<B, FMT>(pre, rw, shared, g, wave, lane);
+  if constexpr (PF != 2) load_pre_gateup<B, FMT>(pre, rw, shared, g, wave, lane);
   // Every load of step A goes out before any of them is used (loads return
   // in issue order, so a wait for one is a wait for all before it): x, piece
   // tid of each token; the norm weight and the residual of this workgroup's
@@ -510,7 +546,7 @@ __device__ __forceinline__ void decode_layer(
   }
   const float sh_sg = Chunk<FMT>::gscale(shared, 0, 0), sh_su = Chunk<FMT>::gscale(shared, 0, 1),
               sh_sd = Chunk<FMT>::gscale(shared, 0, 2);
-  load_pre_down<FMT>(pre, shared, g, lane);
+  if constexpr (PF != 2) load_pre_down<FMT>(pre, shared, g, lane);
   const float resid = __builtin_bit_cast(float, (uint32_t)rv << 16);
   // x to LDS as is, or through the fused RMSNorm.  A row's mean square is
   // summed by one wave holding the row 32 elements per lane (the same order
@@ -857,6 +893,11 @@ __device__ __forceinline__ void decode_layer(
   }
   __syncthreads();
   trace_stamp(ws, 10);
+  // The next layer's router row and shared gate/up rows (registers free
+  // since step A): no load of this layer is issued after this point when
+  // every routed entry's down rows are already in flight, so these wait
+  // behind nothing and arrive while this layer finishes.
+  if constexpr (PF != 0) load_pre_gateup<B, FMT>(pre, next.rw, next.shared, g, wave, lane);
 
   float acc[2][B], accs[2][2];
 #pragma unroll
@@ -878,6 +919,7 @@ __device__ __forceinline__ void decode_layer(
       }
     }
   }
+  if constexpr (PF != 0) load_pre_down<FMT>(pre, next.shared, g, lane);  // the next layer's
   // routed entries of this wave in order, two sets of kDepthC in flight
   const int n_mine = nr > wsel ? (nr - wsel + 3) >> 2 : 0;
   auto run_set = [&](const Chunk<FMT> (&buf)[kDepthC][2], int k0) {
@@ -891,13 +933,18 @@ __device__ __forceinline__ void decode_layer(
       }
     }
   };
-  for (int k0 = 0; k0 < n_mine; k0 += 2 * kDepthC) {
-    run_set(dbuf, k0);
+  if constexpr (kPrefetchNext<B, FMT>) {   // every entry of this wave is in the two sets
+    run_set(dbuf, 0);
+    run_set(dbuf2, kDepthC);
+  } else {
+    for (int k0 = 0; k0 < n_mine; k0 += 2 * kDepthC) {
+      run_set(dbuf, k0);
 #pragma unroll
-    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * (k0 + 2 * kDepthC + q));
-    run_set(dbuf2, k0 + kDepthC);
+      for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * (k0 + 2 * kDepthC + q));
+      run_set(dbuf2, k0 + kDepthC);
 #pragma unroll
-    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf2[q], wsel + 4 * (k0 + 3 * kDepthC + q));
+      for (int q = 0; q < kDepthC; ++q) load_entry(dbuf2[q], wsel + 4 * (k0 + 3 * kDepthC + q));
+    }
   }
   trace_stamp(ws, 11);
   // reduce over the 16 lanes of each row group, then over the waves in a
@@ -937,7 +984,9 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, ExpertsDev routed,
     ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, uint8_t* __restrict__ ws, FuseDev fz) {
-  decode_layer<B, FMT, NORM, RESID>(x, rw, routed, shared, out, ids_out, w_out, ws, fz);
+  StepAPre<FMT> pre;
+  decode_layer<B, FMT, NORM, RESID, 0>(x, rw, routed, shared, out, ids_out, w_out, ws, fz, pre,
+                                       LayerDev{});
 }
 
 // A stack of L layers in one launch, one after another: every workgroup
@@ -956,12 +1005,20 @@ template <int B, int FMT>
 __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_stack(
     const uint16_t* __restrict__ x, const LayerDev* __restrict__ layers, int L,
     uint16_t* __restrict__ out, int32_t* __restrict__ ids_out, uint8_t* __restrict__ ws) {
-  for (int l = 0; l < L; ++l) {
-    const LayerDev d = layers[l];
-    if (l) __syncthreads();
-    decode_layer<B, FMT, false, false>(x, d.rw, d.routed, d.shared, out + (size_t)l * B * kH,
-                                       ids_out ? ids_out + (size_t)l * B * kK : nullptr, nullptr,
-                                       ws, FuseDev{});
+  StepAPre<FMT> pre;
+  constexpr bool kPF = kPrefetchNext<B, FMT>;
+  // the last layer "prefetches" its own rows again (cache hits, unused), so
+  // that every layer body has the same static load count
+  auto layer = [&](auto pf, int l) __attribute__((always_inline)) {
+    const LayerDev d = layers[l], dn = layers[l + 1 < L ? l + 1 : l];
+    decode_layer<B, FMT, false, false, decltype(pf)::value>(
+        x, d.rw, d.routed, d.shared, out + (size_t)l * B * kH,
+        ids_out ? ids_out + (size_t)l * B * kK : nullptr, nullptr, ws, FuseDev{}, pre, dn);
+  };
+  layer(std::integral_constant<int, kPF ? 1 : 0>{}, 0);
+  for (int l = 1; l < L; ++l) {
+    __syncthreads();
+    layer(std::integral_constant<int, kPF ? 2 : 0>{}, l);
   }
 }
 
