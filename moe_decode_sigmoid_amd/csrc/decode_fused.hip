@@ -481,13 +481,14 @@ constexpr bool kPrefetchNext = kK * B <= 4 * 2 * kDownDepth<FMT>;
 // once nothing of its own is left to load, those of `next`; 2 as 1, but this
 // layer's were issued by the previous layer.  PF is static so that the
 // compiler counts the loads in flight exactly (a load under a runtime branch
-// makes it wait for all of them).
-template <int B, int FMT, bool NORM, bool RESID, int PF>
+// makes it wait for all of them).  epoch_reg: this layer's epoch on return;
+// on entry, when EPREG, the previous layer's (stacked launches).
+template <int B, int FMT, bool NORM, bool RESID, int PF, bool EPREG>
 __device__ __forceinline__ void decode_layer(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, const ExpertsDev& routed,
     const ExpertsDev& shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz, StepAPre<FMT>& pre,
-    const LayerDev& next) {
+    const LayerDev& next, uint32_t& epoch_reg) {
   static_assert(PF == 0 || kPrefetchNext<B, FMT>, "prefetch needs every down row in flight");
   constexpr int kTB = FMT == FMT_NVFP4 ? 4 : 2;      // gate/up row pairs per batch
   constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
@@ -579,14 +580,18 @@ __device__ __forceinline__ void decode_layer(
     for (int k = 0; k < B; ++k) s_x[k * (kH / 8) + tid] = xr[k];
   }
   s_mask[tid] = 0u;
-  if (tid == 0) {                                    // this call's epoch
+  // this call's epoch: the workgroup's counter + 1; layer l > 0 of a stacked
+  // launch knows it already (the previous layer's + 1), which saves a memory
+  // round trip at the start of each layer
+  if (tid == 0) {
     uint32_t* ctr = epoch_ptr(ws, g);
-    const uint32_t e = load_flag(ctr) + 1u;
+    const uint32_t e = (EPREG ? epoch_reg : load_flag(ctr)) + 1u;
     store_flag(ctr, e);
     s_epoch = e;
   }
   __syncthreads();
   const uint32_t epoch = s_epoch;
+  epoch_reg = epoch;
   if constexpr (NORM && B == 1) {          // x0 again, normalised
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -985,8 +990,9 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, uint8_t* __restrict__ ws, FuseDev fz) {
   StepAPre<FMT> pre;
-  decode_layer<B, FMT, NORM, RESID, 0>(x, rw, routed, shared, out, ids_out, w_out, ws, fz, pre,
-                                       LayerDev{});
+  uint32_t epoch = 0;
+  decode_layer<B, FMT, NORM, RESID, 0, false>(x, rw, routed, shared, out, ids_out, w_out, ws, fz,
+                                              pre, LayerDev{}, epoch);
 }
 
 // A stack of L layers in one launch, one after another: every workgroup
@@ -1009,16 +1015,17 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_stack(
   constexpr bool kPF = kPrefetchNext<B, FMT>;
   // the last layer "prefetches" its own rows again (cache hits, unused), so
   // that every layer body has the same static load count
-  auto layer = [&](auto pf, int l) __attribute__((always_inline)) {
+  uint32_t epoch = 0;
+  auto layer = [&](auto pf, auto epreg, int l) __attribute__((always_inline)) {
     const LayerDev d = layers[l], dn = layers[l + 1 < L ? l + 1 : l];
-    decode_layer<B, FMT, false, false, decltype(pf)::value>(
+    decode_layer<B, FMT, false, false, decltype(pf)::value, decltype(epreg)::value>(
         x, d.rw, d.routed, d.shared, out + (size_t)l * B * kH,
-        ids_out ? ids_out + (size_t)l * B * kK : nullptr, nullptr, ws, FuseDev{}, pre, dn);
+        ids_out ? ids_out + (size_t)l * B * kK : nullptr, nullptr, ws, FuseDev{}, pre, dn, epoch);
   };
-  layer(std::integral_constant<int, kPF ? 1 : 0>{}, 0);
+  layer(std::integral_constant<int, kPF ? 1 : 0>{}, std::false_type{}, 0);
   for (int l = 1; l < L; ++l) {
     __syncthreads();
-    layer(std::integral_constant<int, kPF ? 2 : 0>{}, l);
+    layer(std::integral_constant<int, kPF ? 2 : 0>{}, std::true_type{}, l);
   }
 }
 
