@@ -579,7 +579,7 @@ __device__ __forceinline__ void decode_layer(
 #pragma unroll
     for (int k = 0; k < B; ++k) s_x[k * (kH / 8) + tid] = xr[k];
   }
-  s_mask[tid] = 0u;
+  if constexpr (B > 1) s_mask[tid] = 0u;
   // this call's epoch: the workgroup's counter + 1; layer l > 0 of a stacked
   // launch knows it already (the previous layer's + 1), which saves a memory
   // round trip at the start of each layer
@@ -646,6 +646,45 @@ __device__ __forceinline__ void decode_layer(
   // ---------------------------------------------------------------- step B
   // top-6 per token (wave t % 4 takes token t), repeated identically in every
   // workgroup; sigmoid scores of the chosen six renormalised to sum to 1
+  if constexpr (B == 1) {
+    // one token: its six experts are the routed entries, each with one h
+    // pair, so wave 0 orders them by id (rank by counting) and writes the
+    // entry tables itself, with no token masks and no barrier in between
+    if (wave == 0) {
+      float v[4];
+      wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane, 64, epoch, v,
+                    &ctl->err);
+      trace_stamp(ws, 4);
+      int my_id;
+      float my_l;
+      wave_top6(v, lane, my_id, my_l);
+      const float s = 1.0f / (1.0f + expf(-my_l));
+      float sum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kK; ++j) sum += readlane_f32(s, j);
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < kK; ++j) rank += __builtin_amdgcn_readlane(my_id, j) < my_id ? 1 : 0;
+      if (lane < kK) {
+        const float wgt = s / sum;
+        s_wfull[my_id][0] = wgt;
+        s_act[rank] = my_id;
+        s_amask[rank] = 1u;
+        s_pair0[rank] = rank;
+        if (g == 0) {
+          if (ids_out) ids_out[lane] = my_id;
+          if (w_out) w_out[lane] = wgt;
+        }
+      }
+      if (lane == 0) {
+        s_nr = kK;
+        s_act[kK] = 0;
+        s_amask[kK] = 1u;
+        s_pair0[kK] = kK;
+      }
+    }
+    trace_stamp(ws, 5);
+  } else {
   for (int t = wave; t < B; t += 4) {
     float v[4];
     wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + t * kE + lane, 64, epoch, v,
@@ -703,6 +742,7 @@ __device__ __forceinline__ void decode_layer(
       s_amask[base] = (1u << B) - 1u;
       s_pair0[base] = kK * B;
     }
+  }
   }
   __syncthreads();
   const int nr = s_nr;
