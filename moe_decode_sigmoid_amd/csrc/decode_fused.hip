@@ -492,6 +492,9 @@ __device__ __forceinline__ void decode_layer(
   static_assert(PF == 0 || kPrefetchNext<B, FMT>, "prefetch needs every down row in flight");
   constexpr int kTB = FMT == FMT_NVFP4 ? 4 : 2;      // gate/up row pairs per batch
   constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
+  // batch 1 issues its routed down rows after publishing h instead of behind
+  // the gate/up rows: the gate/up burst then carries only gate/up rows
+  constexpr bool kLateDown = B == 1;
   constexpr int kPairs = (kK + 1) * B;               // h pairs: 6 B routed + B shared
   const int g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -842,8 +845,12 @@ __device__ __forceinline__ void decode_layer(
     if (gs_mine) gsv = Chunk<FMT>::gscale(routed, (size_t)s_act[tid / 3], tid % 3);
     load_batch(cg[0], cu[0], 0);
     // the first kDepthC entries' down rows of step C, behind the first batch
+    // (at B = 1 after the h publish: the wait for the tensor scales below
+    // waits for every load before it)
+    if constexpr (!kLateDown) {
 #pragma unroll
-    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
+      for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
+    }
     if (gs_mine) s_gs[tid / 3][tid % 3] = gsv;
     __syncthreads();
     for (int j0 = 0; T0 + wave + 4 * j0 < T1; j0 += 2 * kTB) {
@@ -893,6 +900,10 @@ __device__ __forceinline__ void decode_layer(
 #pragma unroll
     for (int q = 0; q < kDepthC; ++q) load_entry(dbuf2[q], wsel + 4 * (kDepthC + q));
   };
+  if constexpr (kLateDown) {   // HBM is idle while the h-ready counters fill
+#pragma unroll
+    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
+  }
   if (wave != 3) prefetch();
   if (wave == 3) {
     const uint32_t want = (uint32_t)(kFusedGrid / kHBanks) * epoch;
