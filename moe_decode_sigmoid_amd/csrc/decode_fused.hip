@@ -490,7 +490,8 @@ __device__ __forceinline__ void decode_layer(
     float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz, StepAPre<FMT>& pre,
     const LayerDev& next, uint32_t& epoch_reg) {
   static_assert(PF == 0 || kPrefetchNext<B, FMT>, "prefetch needs every down row in flight");
-  constexpr int kTB = FMT == FMT_NVFP4 ? 4 : 2;      // gate/up row pairs per batch
+  // gate/up row pairs per batch (at B = 1 a wave has exactly 3: 12 per workgroup)
+  constexpr int kTB = FMT == FMT_NVFP4 ? (B == 1 ? 3 : 4) : 2;
   constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
   // batch 1 issues its routed down rows after publishing h instead of behind
   // the gate/up rows: the gate/up burst then carries only gate/up rows
@@ -770,15 +771,17 @@ __device__ __forceinline__ void decode_layer(
   Chunk<FMT> dbuf[kDepthC][2];
   {
     Chunk<FMT> cg[2][kTB], cu[2][kTB];
+    // Loads are unconditional: a slot past the range reads the range's last
+    // row again (a cache hit; run_batch drops its sums).  A load under a
+    // branch would leave the compiler unsure how many loads are in flight,
+    // and it would then wait for all of them before the next batch goes out.
     auto load_batch = [&](Chunk<FMT> (&bg)[kTB], Chunk<FMT> (&bu)[kTB], int j0) {
 #pragma unroll
       for (int q = 0; q < kTB; ++q) {
-        const int s = T0 + wave + 4 * (j0 + q);
-        if (s < T1) {
-          const size_t ee = (size_t)s_act[s / kI];
-          bg[q].load_gu(routed, ee, 0, s % kI, lane);
-          bu[q].load_gu(routed, ee, 1, s % kI, lane);
-        }
+        const int s0 = T0 + wave + 4 * (j0 + q), s = s0 < T1 ? s0 : T1 - 1;
+        const size_t ee = (size_t)s_act[s / kI];
+        bg[q].load_gu(routed, ee, 0, s % kI, lane);
+        bu[q].load_gu(routed, ee, 1, s % kI, lane);
       }
     };
     // a batch for each token any of its row pairs uses: the 2 kTB gate and up
@@ -853,11 +856,22 @@ __device__ __forceinline__ void decode_layer(
     }
     if (gs_mine) s_gs[tid / 3][tid % 3] = gsv;
     __syncthreads();
-    for (int j0 = 0; T0 + wave + 4 * j0 < T1; j0 += 2 * kTB) {
+    // this wave's row pairs T0 + wave + 4 j, j < nj; the loop runs while a
+    // batch after the two in hand exists, the last one or two are peeled
+    const int nj = T1 - T0 > wave ? (T1 - T0 - wave + 3) >> 2 : 0;
+    int j0 = 0;
+    for (; j0 + 2 * kTB < nj; j0 += 2 * kTB) {
       load_batch(cg[1], cu[1], j0 + kTB);
       run_batch(cg[0], cu[0], j0);
       load_batch(cg[0], cu[0], j0 + 2 * kTB);
       run_batch(cg[1], cu[1], j0 + kTB);
+    }
+    if (j0 + kTB < nj) {
+      load_batch(cg[1], cu[1], j0 + kTB);
+      run_batch(cg[0], cu[0], j0);
+      run_batch(cg[1], cu[1], j0 + kTB);
+    } else {
+      run_batch(cg[0], cu[0], j0);
     }
   }
   trace_stamp(ws, 7);
@@ -993,14 +1007,26 @@ __device__ __forceinline__ void decode_layer(
     run_set(dbuf, 0);
     run_set(dbuf2, kDepthC);
   } else {
-    for (int k0 = 0; k0 < n_mine; k0 += 2 * kDepthC) {
+    // loads in the loop are unconditional (as in the gate/up loop): an entry
+    // past this wave's last reads the last one's rows again
+    auto load_set = [&](Chunk<FMT> (&buf)[kDepthC][2], int k) {
+#pragma unroll
+      for (int q = 0; q < kDepthC; ++q) {
+        const int kk = k + q < n_mine ? k + q : n_mine - 1;
+        const size_t ee = (size_t)s_act[wsel + 4 * kk];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) buf[q][r].load_dn(routed, ee, g * kRowsPerWg + 2 * grp4 + r, c16);
+      }
+    };
+    int k0 = 0;
+    for (; k0 + 2 * kDepthC < n_mine; k0 += 2 * kDepthC) {
       run_set(dbuf, k0);
-#pragma unroll
-      for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * (k0 + 2 * kDepthC + q));
+      load_set(dbuf, k0 + 2 * kDepthC);
       run_set(dbuf2, k0 + kDepthC);
-#pragma unroll
-      for (int q = 0; q < kDepthC; ++q) load_entry(dbuf2[q], wsel + 4 * (k0 + 3 * kDepthC + q));
+      load_set(dbuf2, k0 + 3 * kDepthC);
     }
+    run_set(dbuf, k0);
+    run_set(dbuf2, k0 + kDepthC);
   }
   trace_stamp(ws, 11);
   // reduce over the 16 lanes of each row group, then over the waves in a
