@@ -92,7 +92,7 @@ struct Chunk;
 template <>
 struct Chunk<FMT_NVFP4> {
   uint4 c;
-  uint32_t s;
+  uint16_t s;   // the two E4M3 block scales, as loaded (a 16-bit register value)
   __device__ __forceinline__ void load_gu(const ExpertsDev& X, size_t ee, int m, int row, int ch) {
     const size_t r = (ee * 2 + m) * kI + row;
     c = gld<uint4>(X.w13 + r * (kH / 2) + 16 * ch);
@@ -491,7 +491,7 @@ __device__ __forceinline__ void decode_layer(
     const LayerDev& next, uint32_t& epoch_reg) {
   static_assert(PF == 0 || kPrefetchNext<B, FMT>, "prefetch needs every down row in flight");
   // gate/up row pairs per batch (at B = 1 a wave has exactly 3: 12 per workgroup)
-  constexpr int kTB = FMT == FMT_NVFP4 ? (B == 1 ? 3 : 4) : 2;
+  constexpr int kTB = FMT == FMT_NVFP4 ? 3 : 2;
   constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
   // batch 1 issues its routed down rows after publishing h instead of behind
   // the gate/up rows: the gate/up burst then carries only gate/up rows
