@@ -37,6 +37,8 @@
 // and B[k 8(l/32)..+7][col l%32]; result element i of lane l is
 // C[(i%4) + 8(i/4) + 4(l/32)][l%32].  The weight matrices are stored
 // output-major with K contiguous, so B rows come straight from memory.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -186,29 +188,50 @@ __device__ __forceinline__ void dequant_to_lds(__bf16* dst, const uint4 (&c)[E /
 // K pipeline over NK stages: register ring of D stages in flight, two LDS
 // buffers.  gload(slot, kt) issues stage kt's global loads into a ring slot;
 // sstore(slot, buf) writes a slot to LDS buffer buf; mma(buf) consumes it.
-// Slot of stage s is s % D; the loop is unrolled by D so slots are static.
+// Slot of stage s is s % D.  Every load is unconditional: the main loop
+// (unrolled by D, so slots are static) runs the blocks whose refills all
+// exist, and the last blocks are unrolled with static conditions.  A load
+// under a runtime branch would leave the compiler unsure how many loads are
+// in flight, and it would then drain the ring at every block.
+// f(integral_constant<int, J0>), ..., f(integral_constant<int, J0 + N - 1>)
+template <int J0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    f(std::integral_constant<int, J0>{});
+    static_for<J0 + 1, N - 1>(f);
+  }
+}
+
 template <int D, int NK, typename Slot, typename GL, typename SS, typename MM>
 __device__ __forceinline__ void kpipeline(Slot (&ring)[D], GL gload, SS sstore, MM mma) {
+  static_assert(D % 2 == 0, "a block of D stages starts on LDS buffer 0");
+  // stage kt held in slot Q = kt % D (LDS buffer kt & 1 = Q & 1): consume it,
+  // stage the next one into LDS and refill its slot (LOAD), if any (NEXT)
+  auto stage = [&](auto Q, int kt, auto LOAD, auto NEXT) __attribute__((always_inline)) {
+    constexpr int q = decltype(Q)::value;
+    mma(q & 1);
+    if constexpr (decltype(NEXT)::value) {
+      sstore(ring[(q + 1) % D], (q + 1) & 1);
+      if constexpr (decltype(LOAD)::value) gload(ring[(q + 1) % D], kt + 1 + D);
+    }
+    __syncthreads();
+  };
 #pragma unroll
   for (int q = 0; q < D; ++q)
     if (q < NK) gload(ring[q], q);
   sstore(ring[0], 0);
-  if (D < NK) gload(ring[0], D);
+  if constexpr (D < NK) gload(ring[0], D);
   __syncthreads();
-  for (int kt0 = 0; kt0 < NK; kt0 += D) {
-#pragma unroll
-    for (int q = 0; q < D; ++q) {
-      const int kt = kt0 + q;
-      if (kt < NK) {
-        mma(kt & 1);
-        if (kt + 1 < NK) {
-          sstore(ring[(q + 1) % D], (kt + 1) & 1);
-          if (kt + 1 + D < NK) gload(ring[(q + 1) % D], kt + 1 + D);
-        }
-        __syncthreads();
-      }
-    }
-  }
+  constexpr int kMain = NK > 2 * D ? (NK - 2 * D) / D * D : 0;   // blocks with every refill
+  for (int kt0 = 0; kt0 < kMain; kt0 += D)
+    static_for<0, D>([&](auto Q) __attribute__((always_inline)) {
+      stage(Q, kt0 + decltype(Q)::value, std::true_type{}, std::true_type{});
+    });
+  static_for<0, NK - kMain>([&](auto J) __attribute__((always_inline)) {
+    constexpr int kt = kMain + decltype(J)::value;
+    stage(std::integral_constant<int, kt % D>{}, kt, std::bool_constant<(kt + 1 + D < NK)>{},
+          std::bool_constant<(kt + 1 < NK)>{});
+  });
 }
 
 // ------------------------------------------------------------------ P1 router + top-6
@@ -414,7 +437,9 @@ struct GSlot;
 template <int EA, int EB>
 struct GSlot<FMT_NVFP4, EA, EB> {
   uint4 a[EA / 8], c[EB / 32];
-  uint32_t s;
+  // the block scales as loaded (kept at their width: a widened copy is
+  // re-masked at the loop back-edge, which waits for the load)
+  std::conditional_t<EB == 64, uint32_t, uint16_t> s;
 };
 template <int EA, int EB>
 struct GSlot<FMT_BF16, EA, EB> {
