@@ -405,13 +405,9 @@ template <int B, int FMT>
 __device__ __forceinline__ void down_entry(const Chunk<FMT> (&rows)[2], float gl, unsigned mask,
                                            const float* wt /* by token */, const uint4* s_h,
                                            int p0, int c16, float (&acc)[2][B]) {
-  int p = p0;
-#pragma unroll 1
-  for (int t = 0; t < B; ++t) {
-    if (!((mask >> t) & 1u)) continue;
+  auto token = [&](int t, int p) __attribute__((always_inline)) {
     uint32_t h[16];
     load_h(s_h, p, c16, h);
-    ++p;
     const float sc = wt[t] * gl;
     const float d0 = rows[0].dot_x(h), d1 = rows[1].dot_x(h);
 #pragma unroll
@@ -420,6 +416,14 @@ __device__ __forceinline__ void down_entry(const Chunk<FMT> (&rows)[2], float gl
         acc[0][tt] = __builtin_fmaf(sc, d0, acc[0][tt]);
         acc[1][tt] = __builtin_fmaf(sc, d1, acc[1][tt]);
       }
+  };
+  if constexpr (B == 1) {                // the one token (mask 1): a static index
+    token(0, p0);
+  } else {
+    // the entry's tokens only: set bits in ascending order, as its h pairs
+    int p = p0;
+#pragma unroll 1
+    for (unsigned m = mask; m != 0u; m &= m - 1u) token(__builtin_ctz(m), p++);
   }
 }
 
