@@ -468,10 +468,11 @@ __device__ __forceinline__ void load_pre_down(StepAPre<FMT>& p, const ExpertsDev
     p.dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * (lane >> 4) + r, lane & 15);
 }
 
-// A stacked launch prefetches the next layer's step-A rows only when this
-// layer issues no load after its h copy: each wave's routed entries (at most
-// 6 B / 4 of them) all fit in the two down-row sets issued before the
-// h-ready wait.  Otherwise the later down loads would queue behind them.
+// A stacked launch prefetches the next layer's step-A rows right after the
+// h copy when this layer issues no load after it: each wave's routed
+// entries (at most 6 B / 4 of them) all fit in the two down-row sets issued
+// before the h-ready wait.  Otherwise the prefetch goes out behind the last
+// down-row loads, so that none of them queues behind it.
 template <int FMT>
 constexpr int kDownDepth = FMT == FMT_NVFP4 ? 4 : 1;   // routed entries per down-row set
 template <int B, int FMT>
@@ -480,10 +481,10 @@ constexpr bool kPrefetchNext = kK * B <= 4 * 2 * kDownDepth<FMT>;
 // ------------------------------------------------------------------ kernel
 // One layer, as one workgroup of the 256 runs it (the body of both kernels
 // below).
-// pre: the step-A loads of this layer.  PF (layers of a stacked launch when
-// kPrefetchNext holds): 0 none; 1 this layer issues its own step-A loads and,
-// once nothing of its own is left to load, those of `next`; 2 as 1, but this
-// layer's were issued by the previous layer.  PF is static so that the
+// pre: the step-A loads of this layer.  PF: 0 none (one layer per launch);
+// in a stacked launch 1 this layer issues its own step-A loads and, once
+// nothing of its own queues behind them, those of `next` (see
+// kPrefetchNext); 2 as 1, but this layer's were issued by the previous layer.  PF is static so that the
 // compiler counts the loads in flight exactly (a load under a runtime branch
 // makes it wait for all of them).  epoch_reg: this layer's epoch on return;
 // on entry, when EPREG, the previous layer's (stacked launches).
@@ -493,7 +494,10 @@ __device__ __forceinline__ void decode_layer(
     const ExpertsDev& shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz, StepAPre<FMT>& pre,
     const LayerDev& next, uint32_t& epoch_reg) {
-  static_assert(PF == 0 || kPrefetchNext<B, FMT>, "prefetch needs every down row in flight");
+  // early: after the h copy (every routed down row is already in flight);
+  // late: behind step C's last down-row loads
+  constexpr bool kPfEarly = PF != 0 && kPrefetchNext<B, FMT>;
+  constexpr bool kPfLate = PF != 0 && !kPrefetchNext<B, FMT>;
   // gate/up row pairs per batch (at B = 1 a wave has exactly 3: 12 per workgroup)
   constexpr int kTB = FMT == FMT_NVFP4 ? 3 : 2;
   constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
@@ -971,7 +975,7 @@ __device__ __forceinline__ void decode_layer(
   // since step A): no load of this layer is issued after this point when
   // every routed entry's down rows are already in flight, so these wait
   // behind nothing and arrive while this layer finishes.
-  if constexpr (PF != 0) load_pre_gateup<B, FMT>(pre, next.rw, next.shared, g, wave, lane);
+  if constexpr (kPfEarly) load_pre_gateup<B, FMT>(pre, next.rw, next.shared, g, wave, lane);
 
   float acc[2][B], accs[2][2];
 #pragma unroll
@@ -993,7 +997,7 @@ __device__ __forceinline__ void decode_layer(
       }
     }
   }
-  if constexpr (PF != 0) load_pre_down<FMT>(pre, next.shared, g, lane);  // the next layer's
+  if constexpr (kPfEarly) load_pre_down<FMT>(pre, next.shared, g, lane);  // the next layer's
   // routed entries of this wave in order, two sets of kDepthC in flight
   const int n_mine = nr > wsel ? (nr - wsel + 3) >> 2 : 0;
   auto run_set = [&](const Chunk<FMT> (&buf)[kDepthC][2], int k0) {
@@ -1028,6 +1032,10 @@ __device__ __forceinline__ void decode_layer(
       load_set(dbuf, k0 + 2 * kDepthC);
       run_set(dbuf2, k0 + kDepthC);
       load_set(dbuf2, k0 + 3 * kDepthC);
+    }
+    if constexpr (kPfLate) {     // the next layer's step-A rows, behind these
+      load_pre_gateup<B, FMT>(pre, next.rw, next.shared, g, wave, lane);
+      load_pre_down<FMT>(pre, next.shared, g, lane);
     }
     run_set(dbuf, k0);
     run_set(dbuf2, k0 + kDepthC);
@@ -1093,7 +1101,6 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_stack(
     const uint16_t* __restrict__ x, const LayerDev* __restrict__ layers, int L,
     uint16_t* __restrict__ out, int32_t* __restrict__ ids_out, uint8_t* __restrict__ ws) {
   StepAPre<FMT> pre;
-  constexpr bool kPF = kPrefetchNext<B, FMT>;
   // the last layer "prefetches" its own rows again (cache hits, unused), so
   // that every layer body has the same static load count
   uint32_t epoch = 0;
@@ -1103,10 +1110,10 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_stack(
         x, d.rw, d.routed, d.shared, out + (size_t)l * B * kH,
         ids_out ? ids_out + (size_t)l * B * kK : nullptr, nullptr, ws, FuseDev{}, pre, dn, epoch);
   };
-  layer(std::integral_constant<int, kPF ? 1 : 0>{}, std::false_type{}, 0);
+  layer(std::integral_constant<int, 1>{}, std::false_type{}, 0);
   for (int l = 1; l < L; ++l) {
     __syncthreads();
-    layer(std::integral_constant<int, kPF ? 2 : 0>{}, std::true_type{}, l);
+    layer(std::integral_constant<int, 2>{}, std::true_type{}, l);
   }
 }
 
