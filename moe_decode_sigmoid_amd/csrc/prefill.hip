@@ -247,21 +247,24 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_route(const uint16_t* __r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ __align__(16) __bf16 sA[2][kPTile * kRLdsRow];
   __shared__ __align__(16) __bf16 sB[2][kE * kRLdsRow];
-  // A: 32 rows x 128 B -> one uint4 per thread; B: router row tid, 8 uint4
+  // A: 32 rows x 128 B -> one uint4 per thread; B: 256 router rows x 128 B,
+  // thread tid takes rows 32 i + tid / 8, segment tid % 8, so that 8
+  // consecutive lanes read one row's 128 B (a load touches 8 cache lines,
+  // not 64)
   const int ar = tid >> 3, aseg = tid & 7;
   const uint4* ap = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + ar, T - 1) * kH) + aseg;
-  const uint4* bp = reinterpret_cast<const uint4*>(rw + (size_t)tid * kH);
+  const uint4* bp = reinterpret_cast<const uint4*>(rw + (size_t)ar * kH) + aseg;
   struct Slot { uint4 a, b[8]; };
   Slot ring[2];
   auto gload = [&](Slot& sl, int kt) {
     sl.a = ap[kt * 8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sl.b[i] = bp[kt * 8 + i];
+    for (int i = 0; i < 8; ++i) sl.b[i] = bp[(size_t)i * 32 * (kH / 8) + kt * 8];
   };
   auto sstore = [&](const Slot& sl, int buf) {
     st_lds16(&sA[buf][ar * kRLdsRow + aseg * 8], sl.a);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st_lds16(&sB[buf][tid * kRLdsRow + i * 8], sl.b[i]);
+    for (int i = 0; i < 8; ++i) st_lds16(&sB[buf][(32 * i + ar) * kRLdsRow + aseg * 8], sl.b[i]);
   };
   Acc acc;
   acc.zero();
