@@ -249,13 +249,17 @@ __device__ __forceinline__ float key_logit(int k) {
   return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF));
 }
 
+// The wave's maximum in every lane: within 16-lane rows by DPP, then across
+// rows with gfx950's 16- and 32-lane half swaps (all vector instructions).
 __device__ __forceinline__ int wave_max_i32(int v) {
   v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));
   v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));
   v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
   v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
-  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  const auto r16 = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = max((int)r16[0], (int)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return max((int)r32[0], (int)r32[1]);
 }
 
 __device__ __forceinline__ int wave_min_i32(int v) {
