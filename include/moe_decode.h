@@ -27,8 +27,18 @@
  *    caller should fall back to a generic implementation, the convention the
  *    Flint pages describe for configurations outside their kernels
  *    (Usage notes section).
- *  - Calls on distinct workspaces may run concurrently; calls sharing a
- *    workspace must be ordered (same stream, or events).
+ *  - Calls sharing a workspace must be ordered (same stream, or events).
+ *    The single-launch decode entry points (moe_decode_forward and
+ *    moe_decode_forward_timed on Flint's shape, moe_decode_forward_ex,
+ *    moe_decode_stack_forward, moe_decode_chain_forward) run 256
+ *    workgroups that hand data to each other inside the launch, so all 256
+ *    must be resident at once: such a call needs the device to itself, with
+ *    no other kernel (another such call included, on any workspace) running
+ *    beside it.  If compute units are taken by other work, workgroups wait
+ *    for data that does not come; every wait is bounded, so the kernel still
+ *    ends, but the output is invalid and the workspace's wait-status word
+ *    records it (moe_workspace_status).  The other entry points have no
+ *    such requirement and calls on distinct workspaces may overlap.
  *  - No C++ exception crosses this boundary.
  *
  * Tensor layouts (E experts in a set; H = hidden, I = inter: 2048 and 512
@@ -136,8 +146,15 @@ const char* moe_status_string(moe_status status);
 /* Workspace bytes needed for `tokens` tokens: prefill = 0 for the decode
  * entry points (tokens 1..8), 1 for moe_prefill_forward.  Returns 0 when the
  * shape or token count is not served.  The workspace must be zero-filled
- * once before its first use (e.g. allocated with torch.zeros); every call
- * leaves its internal counters at zero again when its kernels finish. */
+ * once before its first use (e.g. allocated with torch.zeros).  After that
+ * it carries state from call to call that the caller must leave alone: the
+ * single-launch decode kernels keep per-workgroup call counters (epochs) and
+ * epoch-tagged hand-over slots in its first region, and every call advances
+ * them consistently.  One workspace may serve every entry point (decode,
+ * stacks, prefill, the general shapes), as long as it is large enough for
+ * each: the other paths write only past that first region.  After a call
+ * whose wait status is nonzero (moe_workspace_status), zero-fill the
+ * workspace again before using it. */
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens, int32_t prefill);
 
 /* Router GEMV + sigmoid + top-k + renormalisation for B = 1..8 tokens
@@ -232,6 +249,46 @@ typedef struct {
 moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t n_layers,
                                     const moe_layer* layers, const void* x, int32_t B, void* out,
                                     int32_t* ids_out, void* ws, size_t ws_bytes, void* stream);
+
+/* A chained residual stack of n_layers Flint layers in ONE launch: the
+ * residual stream of a pre-norm decoder ("Day-0 Support for Flint on vLLM",
+ * Model architecture: 49 layers, 47 of them MoE), MoE layers only:
+ *   x_0 = x,   x_{l+1} = bf16(x_l + layer_l(norm_l(x_l))),   out[l] = x_{l+1},
+ * where norm_l is the pre-MoE RMSNorm of moe_fuse with weight norm_w[l] (or
+ * the identity when norm_w is NULL).  Layer l equals
+ * moe_decode_forward_ex(x_l, {norm_w[l], norm_eps, residual = x_l}) bit for
+ * bit.  Layer l + 1 starts from all of x_{l+1}: only its weight loads that
+ * depend on neither its input nor its routing (router row, shared expert)
+ * are issued early, during layer l (the pages load the next kernel's
+ * weights early under programmatic dependent launch: Optimization section,
+ * low-latency path and Fig. 3).
+ *   layers   DEVICE array of n_layers moe_layer (as moe_decode_stack_forward)
+ *   x        bf16 [B][H], B = 1..8 (B > 8: MOE_ERR_UNSUPPORTED)
+ *   norm_w   bf16 [n_layers][H] or NULL; norm_eps > 0 and finite when set
+ *   out      bf16 [n_layers][B][H] (written; must not overlap x, norm_w, the
+ *            layer table or ws)
+ *   ids_out  int32 [n_layers][B][top_k] or NULL: the routing of each layer.
+ * Flint's shape only (NVFP4 or BF16); the workspace is moe_decode_forward's.
+ * Where the single-launch kernel cannot run: MOE_ERR_UNSUPPORTED. */
+moe_status moe_decode_chain_forward(const moe_shape* shape, int32_t n_layers,
+                                    const moe_layer* layers, const void* x, int32_t B,
+                                    const void* norm_w, float norm_eps, void* out,
+                                    int32_t* ids_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Wait status of a workspace: copies its status word to *status (DEVICE
+ * int32, 4-byte aligned) and clears the word, in one kernel on `stream`, so
+ * it can be captured in a HIP graph with the calls it checks.  The word
+ * collects, since the last status call, the waits of the single-launch
+ * decode kernels that gave up because their data never arrived (see the
+ * concurrency rule above): bit 0 the router-logit exchange, bit 1 the h
+ * hand-over between the GEMVs, bit 2 the residual-stream hand-over of a
+ * chained stack.  Zero: every call since the last status call completed
+ * its hand-overs; nonzero: those calls' outputs are invalid and the
+ * workspace must be zero-filled before its next use (a caller can then fall
+ * back, the convention of the Usage notes section).
+ *   ws     the workspace (256-byte aligned, ws_bytes >= 256)
+ *   status int32 [1] (device; must not overlap ws) */
+moe_status moe_workspace_status(void* ws, size_t ws_bytes, int32_t* status, void* stream);
 
 /* The layer's neighbours, fused into it (Optimization section, low-latency
  * path: the norm and the combine fused into the adjacent GEMV kernels; the

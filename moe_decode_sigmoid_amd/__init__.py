@@ -81,6 +81,11 @@ def lib() -> ctypes.CDLL:
                                              P(Experts), vp, vp, vp, vp, sz, vp]
         L.moe_decode_stack_forward.restype = ctypes.c_int
         L.moe_decode_stack_forward.argtypes = [P(Shape), i32, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_decode_chain_forward.restype = ctypes.c_int
+        L.moe_decode_chain_forward.argtypes = [P(Shape), i32, vp, vp, i32, vp, ctypes.c_float, vp,
+                                               vp, vp, sz, vp]
+        L.moe_workspace_status.restype = ctypes.c_int
+        L.moe_workspace_status.argtypes = [vp, sz, vp, vp]
         L.moe_general_workspace_layout.restype = ctypes.c_int
         L.moe_general_workspace_layout.argtypes = [P(Shape), P(sz)]
         L.moe_nvfp4_dequant.restype = ctypes.c_int
@@ -286,6 +291,29 @@ def moe_decode_stack_forward(x, table, out, ws, ids_out=None, fmt=MOE_W_NVFP4, s
                                         _ptr(out), _ptr(ids_out), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_decode_stack_forward")
+
+
+def moe_decode_chain_forward(x, table, out, ws, norm_w=None, eps: float = 1e-6, ids_out=None,
+                             fmt=MOE_W_NVFP4, stream=None, S: Shape | None = None,
+                             B: int | None = None):
+    """A chained residual stack of n_layers = table.shape[0] layers in one launch:
+    x_0 = x bf16 [B, H], x_{l+1} = x_l + layer_l(rmsnorm_l(x_l)) into out bf16
+    [L, B, H] (norm_w bf16 [L, H] or None; ids_out int32 [L, B, k] optional)."""
+    S = S or shape(_fmt(fmt))
+    B = x.shape[0] if B is None else B
+    st = lib().moe_decode_chain_forward(ctypes.byref(S), table.shape[0], _ptr(table), _ptr(x), B,
+                                        _ptr(norm_w), float(eps), _ptr(out), _ptr(ids_out),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_decode_chain_forward")
+
+
+def moe_workspace_status(ws, status, stream=None):
+    """Enqueue the copy of the workspace's wait-status word into status (device
+    int32 [1]) and clear the word; nonzero after a synchronize means a bounded
+    wait of a single-launch decode call gave up and its output is invalid."""
+    st = lib().moe_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), _ptr(status),
+                                    _stream(stream))
+    _check(st, "moe_workspace_status")
 
 
 def moe_nvfp4_dequant(expert_set, expert: int, tensor: int, out, stream=None):

@@ -1,6 +1,7 @@
 """Compile the gfx950 HIP library (libmoe_decode.so) in place with hipcc:
-each source to an object in parallel (the decode kernel file alone holds 64
-kernel instances), then one link."""
+each source to an object in parallel (the single-launch decode kernels'
+instances are spread over several sources, one weight format each), then
+one link."""
 import concurrent.futures
 import os
 import pathlib
@@ -10,8 +11,9 @@ HERE = pathlib.Path(__file__).resolve().parent
 CSRC = HERE / "csrc"
 OBJ = HERE / "_build"
 LIB = HERE / "libmoe_decode.so"
-SOURCES = ["capi.hip", "decode.hip", "decode_fused.hip", "decode_general.hip", "prefill.hip",
-           "gemv.hip"]
+SOURCES = ["capi.hip", "decode.hip", "decode_fused.hip", "decode_fused_nv.hip",
+           "decode_fused_bf.hip", "decode_stack.hip", "decode_chain_nv.hip", "decode_chain_bf.hip",
+           "decode_general.hip", "prefill.hip", "gemv.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -367,6 +367,51 @@ moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t n_layers,
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+moe_status moe_decode_chain_forward(const moe_shape* shape, int32_t n_layers,
+                                    const moe_layer* layers, const void* x, int32_t B,
+                                    const void* norm_w, float norm_eps, void* out,
+                                    int32_t* ids_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
+  if ((st = check_shape(shape)) != MOE_OK) return st;
+  if (B < 1 || n_layers < 1) return MOE_ERR_INVALID_ARG;
+  if (B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;
+  if (!layers) return MOE_ERR_INVALID_ARG;
+  if (!aligned(layers, 8)) return MOE_ERR_MISALIGNED;
+  if ((st = check_ptr(x)) != MOE_OK) return st;
+  if ((st = check_ptr(out)) != MOE_OK) return st;
+  if (norm_w) {
+    if ((st = check_ptr(norm_w)) != MOE_OK) return st;
+    if (!(norm_eps > 0.0f) || !(norm_eps < INFINITY)) return MOE_ERR_INVALID_ARG;
+  }
+  if (ids_out && !aligned(ids_out, 4)) return MOE_ERR_MISALIGNED;
+  if (!ws || ws_bytes < moe::kDecodeWsBytes) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_MISALIGNED;
+  const size_t xb = (size_t)B * moe::kH * 2, ob = xb * (size_t)n_layers;
+  const size_t nb = (size_t)n_layers * moe::kH * 2;
+  if (overlap(out, ob, x, xb) || overlap(out, ob, ws, ws_bytes)) return MOE_ERR_INVALID_ARG;
+  if (overlap(layers, sizeof(moe_layer) * (size_t)n_layers, out, ob)) return MOE_ERR_INVALID_ARG;
+  if (norm_w && (overlap(norm_w, nb, out, ob) || overlap(norm_w, nb, ws, ws_bytes)))
+    return MOE_ERR_INVALID_ARG;
+  if (!moe::fused_supported()) return MOE_ERR_UNSUPPORTED;
+  const hipError_t e = moe::launch_decode_chain(
+      B, shape->wfmt, static_cast<const uint16_t*>(x),
+      reinterpret_cast<const moe::LayerDev*>(layers), n_layers,
+      static_cast<const uint16_t*>(norm_w), norm_eps, static_cast<uint16_t*>(out), ids_out,
+      static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_workspace_status(void* ws, size_t ws_bytes, int32_t* status, void* stream) {
+  if (!ws || ws_bytes < moe::kCtlBytes) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_MISALIGNED;
+  if (!status) return MOE_ERR_INVALID_ARG;
+  if (!aligned(status, 4)) return MOE_ERR_MISALIGNED;
+  if (overlap(status, 4, ws, ws_bytes)) return MOE_ERR_INVALID_ARG;
+  const hipError_t e = moe::launch_ws_status(static_cast<uint8_t*>(ws), status,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 moe_status moe_general_workspace_layout(const moe_shape* shape, size_t offsets[8]) {
   moe::GenShape g;
   if (!offsets) return MOE_ERR_INVALID_ARG;

@@ -65,16 +65,20 @@ struct GenCtl {
 struct DecodeCtl {
   unsigned ticket;                       // 0: route kernel arrival counter (self-resetting)
   int n_active;                          // 4: dispatch entries of the split path (shared last)
-  unsigned err;                          // 8: nonzero when a device-side wait timed out
-  unsigned pad0;                         // 12
-  unsigned long long arrive[2];          // 16: grid barrier counters of the fused kernel
-  int pad1[56];
+  unsigned err;                          // 8: kErr* bits of device-side waits that timed out
+  unsigned pad0[61];                     // 12
   int active_expert[64];                 // expert id; kE marks the shared expert
   unsigned active_mask[64];              // bit t set when token t uses the entry
   float wtab[64][kMaxB];                 // routing weight of token t for the entry
   int ids[kMaxB][kK];                    // routing of the call (descending score)
   float w[kMaxB][kK];
 };
+// Bits of DecodeCtl::err: a bounded wait of the single-launch decode kernels
+// gave up (its data never arrived), so the call's output is not valid.  The
+// word is sticky until moe_workspace_status reads and clears it.
+constexpr unsigned kErrLogits = 1u;   // the router logits exchange
+constexpr unsigned kErrHReady = 2u;   // the h hand-over between the GEMVs
+constexpr unsigned kErrXReady = 4u;   // the residual stream hand-over of a chained stack
 constexpr size_t kCtlBytes = (sizeof(DecodeCtl) + 255) / 256 * 256;
 constexpr size_t kLogitsOff = kCtlBytes;                          // f32 [kMaxB][kE]
 constexpr size_t kHOff = kLogitsOff + sizeof(float) * kMaxB * kE; // f32 [kMaxActive][kMaxB][kI]
@@ -88,7 +92,15 @@ constexpr size_t kSlotLogitRep = 8 * kMaxB * kE;                                
 constexpr size_t kSlotLogitOff = kHOff + sizeof(float) * kMaxActive * kMaxB * kI;
 constexpr size_t kFlagOff = kSlotLogitOff + kSlotLogitRep * kLogitReps;
 constexpr size_t kFlagStride = 128;
-constexpr size_t kDecodeWsBytes = kFlagOff + (256 + 64 * kBankReps) * kFlagStride;
+// Chained stack: the residual stream x_{l+1} as tagged 8-byte slots {two
+// bf16 elements, epoch of layer l}, [kMaxB][kH / 2] per copy, kXReps copies.
+constexpr int kXReps = 4;
+constexpr size_t kSlotXRep = 8 * kMaxB * (kH / 2);
+constexpr size_t kSlotXOff = kFlagOff + (256 + 64 * kBankReps) * kFlagStride;
+// Everything below kDecodeWsBytes is the single-launch decode kernels'; the
+// epoch counters, h-ready counters and tagged slots keep their values from
+// call to call, so no other path writes below this offset.
+constexpr size_t kDecodeWsBytes = kSlotXOff + kSlotXRep * kXReps;
 constexpr size_t kGenBase = kDecodeWsBytes;
 
 // Workspace of the general path: logits f32 [kMaxB][E], the dispatch, h

@@ -386,7 +386,18 @@ __global__ __launch_bounds__(256) void k_down(ExpertsDev routed, ExpertsDev shar
 }
 
 // ------------------------------------------------------------------ dequant probe
-// out[r][c] = fp32(e2m1 * e4m3) * global; one thread per 8 codes.
+// out[r][c] = fp32(e2m1 * e4m3) * global; one thread per 8 codes.  The codes
+// go through both FP4 converts the layer kernels use, with their nibble
+// order: FP4 pair -> bf16 pair (fp4x2_to_bf16, the decode kernels) and FP4
+// pair -> fp32 pair (fp4x2_to_f32, the prefill and split-path kernels).  An
+// E2M1 value is exact in either type and its product with the E4M3 scale is
+// exact in fp32, so the only rounding is the one by the tensor scale.  Where
+// the two converts disagree the probe writes NaN, which no expected value
+// equals, so one bit-exact comparison checks both.
+__device__ __forceinline__ float probe_value(float a, float b, float s, float g) {
+  return a == b ? (a * s) * g : __builtin_nanf("");
+}
+
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scales,
                                                  const float* __restrict__ glob, int rows,
@@ -399,11 +410,15 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   const float s = e4m3_to_f32<0>(scales[(size_t)r * (cols / 16) + d / 2]);
   const float g = *glob;
   float* o = out + (size_t)r * cols + 8 * d;
-  f32x2 p;
-  p = fp4x2_to_f32<0>(w); o[0] = (p.x * s) * g; o[1] = (p.y * s) * g;
-  p = fp4x2_to_f32<1>(w); o[2] = (p.x * s) * g; o[3] = (p.y * s) * g;
-  p = fp4x2_to_f32<2>(w); o[4] = (p.x * s) * g; o[5] = (p.y * s) * g;
-  p = fp4x2_to_f32<3>(w); o[6] = (p.x * s) * g; o[7] = (p.y * s) * g;
+  const bf16x2 b[4] = {fp4x2_to_bf16<0>(w), fp4x2_to_bf16<1>(w), fp4x2_to_bf16<2>(w),
+                       fp4x2_to_bf16<3>(w)};
+  const f32x2 f[4] = {fp4x2_to_f32<0>(w), fp4x2_to_f32<1>(w), fp4x2_to_f32<2>(w),
+                      fp4x2_to_f32<3>(w)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = probe_value((float)b[i].x, f[i].x, s, g);
+    o[2 * i + 1] = probe_value((float)b[i].y, f[i].y, s, g);
+  }
 }
 
 // ------------------------------------------------------------------ launchers

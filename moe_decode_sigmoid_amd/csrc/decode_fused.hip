@@ -1,1215 +1,77 @@
-// Fused low-latency decode kernel (B <= 8 tokens) of the Flint-style MoE layer
-// on gfx950: the whole layer in ONE launch.
+// Host side of the single-launch decode kernels (layer body in decode_layer.h,
+// instances in decode_fused_*.hip, decode_stack.hip, decode_chain_*.hip):
+// whether the device can run them, the dispatch by weight format, and the
+// workspace's wait-status read-back.
 //
-// The pages describe a low-latency path for up to 8 requests in which routing
-// and the expert combine are fused into the neighbouring GEMV kernels and each
-// kernel starts loading its weights while the previous one still runs
-// ("Day-0 Support for Flint on vLLM", Optimization section and Fig. 3).
-// MI355X has no programmatic dependent launch, so the dependent steps live
-// inside one kernel of 256 workgroups (one per CU, all resident) that hand
-// data to each other through the workspace, and every workgroup issues the
-// weight loads of a later step as soon as it knows their addresses:
-//
-//   A  router GEMV, one expert row per workgroup (the 4 waves split the 2048
-//      columns) -> logit slots; the shared expert's gate/up rows 2g, 2g+1
-//      (routing-independent) -> h; the shared expert's down rows of the
-//      workgroup's 8 outputs are fetched.
-//   B  every workgroup waits for the 256 x B logits and repeats the sigmoid /
-//      top-6 / renormalisation / dispatch itself (identical result everywhere,
-//      no extra round trip): touched experts become entries in ascending id,
-//      and each (entry, token) pair a slot of a compact h array (routed
-//      pairs first, then the shared expert's).  The routed gate/up row pairs,
-//      cut into 256 contiguous ranges, give SiLU(g) * u per token; the
-//      workgroup writes its h once, as bf16, then counts in on an h-ready
-//      counter.
-//   C  once all h is in: the 7 B h pairs are copied to LDS, then the down GEMV
-//      of the workgroup's 8 output rows over every entry (wave w takes routed
-//      entries a = w - 1 mod 4 and the shared expert's tokens w, w + 4),
-//      weighted by the routing, summed in a fixed order, rounded once to bf16.
-//
-// The layer's neighbours can be fused in (template parameters NORM, RESID;
-// the same section's low-latency path fuses norm and combine into the
-// adjacent GEMVs): the pre-MoE RMSNorm of x at the start of step A (every
-// workgroup normalises the same x, so no exchange is needed), and the
-// residual add before the output rounding of step C.
-//
-// Hand-over between workgroups uses only device-coherent accesses (relaxed
-// agent-scope atomics: no cache write-back or invalidation):
-//  - call epoch: workgroup g keeps a private counter in the workspace; every
-//    call adds one, so all counters agree (the workspace starts zeroed).
-//  - logits: 8-byte slots {fp32 value, epoch} in kLogitReps copies; readers
-//    poll copy g % kLogitReps until the epochs match.
-//  - h: coherent stores; after waiting for them a workgroup adds 1 to
-//    h-ready counter g % 64 of each of kBankReps copies (one 128-byte line
-//    each); readers poll the 64 counters of copy g % kBankReps until each
-//    holds 4 * epoch.
-// A wave's loads and stores complete in issue order, so the kernel keeps
-// stores out of the way of loads it waits for: h is staged in LDS and stored
-// in one go, and the polling wave issues its prefetches after its wait.
-// Every wait is bounded (tens of ms); on time-out the workgroup sets the
-// workspace error word and carries on, so the kernel always terminates.
-// Results are reproducible bit for bit (fixed summation orders, no atomics
-// on data).
-#include <hip/hip_ext.h>
-
-#include <type_traits>
-
-#include "common.h"
-#include "launch.h"
+// The kernels need all 256 workgroups resident at the same time (they hand
+// data to each other inside the launch, with bounded waits).  A device with
+// fewer compute units cannot run them (fused_supported() is false and the
+// entry points fall back or return MOE_ERR_UNSUPPORTED); on a device that has
+// them, other work occupying compute units during a call can leave
+// workgroups undispatched while the others wait, the waits give up and the
+// call's output is invalid: the error word records it and
+// moe_workspace_status reads it back.
+#include "decode_layer.h"
 
 namespace moe {
 
-constexpr int kFusedGrid = 256;             // workgroups (one per CU)
-constexpr int kFusedThreads = 256;          // 4 waves, 16 groups of 16 lanes
-constexpr int kRowsPerWg = kH / kFusedGrid; // 8 output rows per workgroup
-constexpr int kHBanks = 64;                 // h-ready counters, one 128-byte line each
-constexpr int kMaxRange = (kMaxB * kK * kI + kFusedGrid - 1) / kFusedGrid;  // routed rows per workgroup
-constexpr int kSpinLimit = 1 << 18;
-
-// ------------------------------------------------------------------ row chunks
-// Weight loads through global-address-space pointers.  The stacked launch
-// reads its weight pointers from the layer table in memory, which the
-// compiler cannot place, and a flat load also counts against the LDS wait
-// counter: every LDS wait and barrier would then wait for the weights in
-// flight.
-// (HIP's uint4 is a struct, whose copy drops the address space: its loads
-// go through a native vector type.)
-template <typename T>
-__device__ __forceinline__ T gld(const void* p) {
-  return *(const __attribute__((address_space(1))) T*)p;
-}
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-template <>
-__device__ __forceinline__ uint4 gld<uint4>(const void* p) {
-  const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)p;
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// A lane's 32 consecutive elements of one weight row.
-template <int FMT>
-struct Chunk;
-
-template <>
-struct Chunk<FMT_NVFP4> {
-  uint4 c;
-  uint16_t s;   // the two E4M3 block scales, as loaded (a 16-bit register value)
-  __device__ __forceinline__ void load_gu(const ExpertsDev& X, size_t ee, int m, int row, int ch) {
-    const size_t r = (ee * 2 + m) * kI + row;
-    c = gld<uint4>(X.w13 + r * (kH / 2) + 16 * ch);
-    s = gld<uint16_t>(X.w13s + r * (kH / 16) + 2 * ch);
-  }
-  __device__ __forceinline__ void load_dn(const ExpertsDev& X, size_t ee, int row, int ch) {
-    const size_t r = ee * kH + row;
-    c = gld<uint4>(X.w2 + r * (kI / 2) + 16 * ch);
-    s = gld<uint16_t>(X.w2s + r * (kI / 16) + 2 * ch);
-  }
-  // sum_k w_k v_k over the chunk (v: 32 bf16 values in pairs), without the
-  // tensor scale; v is x for gate/up rows and h for down rows
-  __device__ __forceinline__ float dot_x(const uint32_t (&xw)[16]) const {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float b0 = 0.0f, b1 = 0.0f;
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      b0 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), xw[4 * d + 0], b0);
-      b0 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), xw[4 * d + 1], b0);
-      b0 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), xw[4 * d + 2], b0);
-      b0 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b0);
-    }
-#pragma unroll
-    for (int d = 2; d < 4; ++d) {
-      b1 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), xw[4 * d + 0], b1);
-      b1 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), xw[4 * d + 1], b1);
-      b1 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), xw[4 * d + 2], b1);
-      b1 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b1);
-    }
-    return b0 * e4m3_to_f32<0>(s) + b1 * e4m3_to_f32<1>(s);
-  }
-  __device__ __forceinline__ static float gscale(const ExpertsDev& X, size_t ee, int m) {
-    return gld<float>(X.glob + ee * 3 + m);
-  }
-};
-
-template <>
-struct Chunk<FMT_BF16> {
-  uint4 w[4];
-  __device__ __forceinline__ void load_gu(const ExpertsDev& X, size_t ee, int m, int row, int ch) {
-    const uint8_t* p = X.w13 + (((ee * 2 + m) * kI + row) * kH + 32 * ch) * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = gld<uint4>(p + 16 * i);
-  }
-  __device__ __forceinline__ void load_dn(const ExpertsDev& X, size_t ee, int row, int ch) {
-    const uint8_t* p = X.w2 + ((ee * kH + row) * kI + 32 * ch) * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = gld<uint4>(p + 16 * i);
-  }
-  __device__ __forceinline__ float dot_x(const uint32_t (&xw)[16]) const {
-    float b0 = 0.0f, b1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      b0 = dot2_bf16(w[i].x, xw[4 * i + 0], b0);
-      b0 = dot2_bf16(w[i].y, xw[4 * i + 1], b0);
-      b0 = dot2_bf16(w[i].z, xw[4 * i + 2], b0);
-      b0 = dot2_bf16(w[i].w, xw[4 * i + 3], b0);
-    }
-#pragma unroll
-    for (int i = 2; i < 4; ++i) {
-      b1 = dot2_bf16(w[i].x, xw[4 * i + 0], b1);
-      b1 = dot2_bf16(w[i].y, xw[4 * i + 1], b1);
-      b1 = dot2_bf16(w[i].z, xw[4 * i + 2], b1);
-      b1 = dot2_bf16(w[i].w, xw[4 * i + 3], b1);
-    }
-    return b0 + b1;
-  }
-  __device__ __forceinline__ static float gscale(const ExpertsDev&, size_t, int) { return 1.0f; }
-};
-
-// ------------------------------------------------------------------ helpers
-// Phase timestamps of a traced build (-DMOE_PHASE_TRACE): kept in LDS and
-// written after the kernel's last step, so they add no stores to the
-// memory queue of the phases they time.
-#ifdef MOE_PHASE_TRACE
-__shared__ unsigned long long s_trace[16];
-#endif
-__device__ __forceinline__ void trace_stamp(uint8_t* ws, int k) {
-#ifdef MOE_PHASE_TRACE
-  if (threadIdx.x == 0) s_trace[k] = __builtin_amdgcn_s_memrealtime();
-#else
-  (void)ws;
-  (void)k;
-#endif
-}
-__device__ __forceinline__ void trace_flush(uint8_t* ws) {
-#ifdef MOE_PHASE_TRACE
-  __syncthreads();
-  if (threadIdx.x < 16)
-    reinterpret_cast<unsigned long long*>(ws + kDecodeWsBytes)[blockIdx.x * 16 + threadIdx.x] =
-        s_trace[threadIdx.x];
-#else
-  (void)ws;
-#endif
-}
-
-__device__ __forceinline__ void put_slot(uint64_t* p, float v, uint32_t epoch) {
-  const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, v) | ((uint64_t)epoch << 32);
-  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint64_t get_slot(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint32_t load_flag(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_flag(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Per-workgroup epoch counter in the workspace, one 128-byte line each.
-__device__ __forceinline__ uint32_t* epoch_ptr(uint8_t* ws, int wg) {
-  return reinterpret_cast<uint32_t*>(ws + kFlagOff + (size_t)wg * kFlagStride);
-}
-
-// Reads N slots per lane (p[k * stride], k < N) into out[], polling until all
-// of the active lanes' slots carry `epoch`.  Bounded.
-template <int N>
-__device__ __forceinline__ void wait_slots(const uint64_t* p, int stride, uint32_t epoch,
-                                           float (&out)[N], unsigned* err) {
-  uint32_t pending = (1u << N) - 1u;
-  for (int spin = 0;; ++spin) {
-    uint64_t w[N];
-#pragma unroll
-    for (int k = 0; k < N; ++k)
-      if (pending & (1u << k)) w[k] = get_slot(p + k * stride);
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      if ((pending & (1u << k)) && (uint32_t)(w[k] >> 32) == epoch) {
-        out[k] = __builtin_bit_cast(float, (uint32_t)w[k]);
-        pending &= ~(1u << k);
-      }
-    }
-    if (__ballot(pending != 0u) == 0) break;
-    if (spin > kSpinLimit) {
-      __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
+// The workspace's wait status: the error word, copied to the caller and
+// cleared in one atomic exchange (a kernel, so that it can be captured).
+__global__ __launch_bounds__(64) void k_ws_status(uint8_t* __restrict__ ws,
+                                                 int32_t* __restrict__ status) {
+  if (threadIdx.x == 0) {
+    DecodeCtl* ctl = reinterpret_cast<DecodeCtl*>(ws);
+    const unsigned v =
+        __hip_atomic_exchange(&ctl->err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *status = (int32_t)v;
   }
 }
 
-// Sortable integer key of a logit: order-preserving over all non-NaN floats,
-// with -0 taken as +0 so that equal values compare equal.
-__device__ __forceinline__ int logit_key(float f) {
-  int b = __builtin_bit_cast(int, f);
-  b = b == (int)0x80000000 ? 0 : b;
-  return b ^ ((b >> 31) & 0x7FFFFFFF);
-}
-__device__ __forceinline__ float key_logit(int k) {
-  return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF));
+hipError_t launch_ws_status(uint8_t* ws, int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(k_ws_status, dim3(1), dim3(64), 0, st, ws, status);
+  return hipGetLastError();
 }
 
-// The wave's maximum in every lane: within 16-lane rows by DPP, then across
-// rows with gfx950's 16- and 32-lane half swaps (all vector instructions).
-__device__ __forceinline__ int wave_max_i32(int v) {
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
-  const auto r16 = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
-  v = max((int)r16[0], (int)r16[1]);
-  const auto r32 = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
-  return max((int)r32[0], (int)r32[1]);
-}
-
-__device__ __forceinline__ int wave_min_i32(int v) {
-  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));
-  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));
-  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
-  v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
-  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-
-// Positions i, i + 1 of a lane's list, descending by key; a swap needs a
-// strictly larger key, so equal keys keep their order (lower expert first).
-__device__ __forceinline__ void cmpx(int (&k)[4], int (&q)[4], int i) {
-  const bool sw = k[i + 1] > k[i];
-  const int ka = k[i], qa = q[i];
-  k[i] = sw ? k[i + 1] : ka;
-  q[i] = sw ? q[i + 1] : qa;
-  k[i + 1] = sw ? ka : k[i + 1];
-  q[i + 1] = sw ? qa : q[i + 1];
-}
-
-// Top-6 of one token's 256 router logits (v[q] = logit of expert 64 q + lane)
-// under the order (logit descending, expert ascending), as the pages' router
-// selects ("Day-0 Support for Flint on vLLM", Model architecture).  Each lane
-// first sorts its 4 logits (odd-even transposition, stable); each round takes
-// the maximum of the lane heads and pops it.  Lane j < 6 returns choice j.
-__device__ __forceinline__ void wave_top6(const float (&v)[4], int lane, int& my_id, float& my_l) {
-  int k[4], q[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    k[i] = logit_key(v[i]);
-    q[i] = i;
-  }
-  cmpx(k, q, 0); cmpx(k, q, 2); cmpx(k, q, 1);
-  cmpx(k, q, 0); cmpx(k, q, 2); cmpx(k, q, 1);
-  int myk = 0;
-  my_id = 0;
-#pragma unroll
-  for (int j = 0; j < kK; ++j) {
-    const int m = wave_max_i32(k[0]);
-    const uint64_t bal = __ballot(k[0] == m);
-    int sel;
-    if (__popcll(bal) == 1) {
-      sel = __builtin_ctzll(bal);
-    } else {               // equal heads: the lowest expert id among them
-      sel = wave_min_i32(k[0] == m ? 64 * q[0] + lane : 0x7FFFFFFF) & 63;
-    }
-    const int e = 64 * __builtin_amdgcn_readlane(q[0], sel) + sel;
-    if (lane == j) {
-      my_id = e;
-      myk = m;
-    }
-    if (lane == sel) {
-      k[0] = k[1]; k[1] = k[2]; k[2] = k[3]; k[3] = (int)0x80000000;
-      q[0] = q[1]; q[1] = q[2]; q[2] = q[3];
-    }
-  }
-  my_l = key_logit(myk);
-}
-
-// One gate/up row pair of an entry for the tokens in `mask`; the wave's lanes
-// cover the 2048 columns; lane 0 puts h = SiLU(g) * u of token t in hdst[t]
-// (LDS: the workgroup writes its h to the workspace in one go, so that no
-// store sits in front of the next weight loads in the wave's memory queue).
-template <int B, int FMT>
-__device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk<FMT>& cu, float sg,
-                                               float su, unsigned mask, const uint4* s_x,
-                                               const uint32_t (&x0)[16], int lane, float* hdst) {
-#pragma unroll
-  for (int t = 0; t < B; ++t) {
-    if (!((mask >> t) & 1u)) continue;
-    uint32_t xw[16];
-    if constexpr (B == 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xw[i] = x0[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = s_x[t * (kH / 8) + 4 * lane + i];
-        xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
-      }
-    }
-    const float g = wave_sum(cg.dot_x(xw)) * sg;
-    const float u = wave_sum(cu.dot_x(xw)) * su;
-    if (lane == 0) hdst[t] = silu_mul(g, u);
-  }
-}
-
-// 32-lane and 16-lane half swaps of gfx950 (v_permlane32_swap: a keeps lanes
-// 0-31 and takes b's 0-31 as its 32-63, b gets a's 32-63 and its own 32-63;
-// v_permlane16_swap does the same within each 32-lane half).
-__device__ __forceinline__ void swap32(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
-                                                  __builtin_bit_cast(unsigned, b), false, false);
-  a = __builtin_bit_cast(float, (unsigned)r[0]);
-  b = __builtin_bit_cast(float, (unsigned)r[1]);
-}
-__device__ __forceinline__ void swap16(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
-                                                  __builtin_bit_cast(unsigned, b), false, false);
-  a = __builtin_bit_cast(float, (unsigned)r[0]);
-  b = __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-// Wave totals of 8 per-lane values at once: value j's sum over the 64 lanes
-// ends in lanes 8 j .. 8 j + 7 (halving exchanges across 32 and 16 lanes,
-// then within rows: rotate by 8, half-row mirror, quad swaps).
-__device__ __forceinline__ float wave_sum8(const float (&v)[8], int lane) {
-  float w[4], u[2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float a = v[j], b = v[4 + j];
-    swap32(a, b);
-    w[j] = a + b;
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    float a = w[j], b = w[2 + j];
-    swap16(a, b);
-    u[j] = a + b;
-  }
-  const bool hi = (lane & 8) != 0;
-  float z = (hi ? u[1] : u[0]) + dpp_f32<0x128>(hi ? u[0] : u[1]);
-  z += dpp_f32<0x141>(z);
-  z += dpp_f32<0x4E>(z);
-  z += dpp_f32<0xB1>(z);
-  return z;
-}
-
-// 32 consecutive bf16 h values (chunk c16, as 16 packed pairs) of pair p
-// from LDS.  A pair is 64 uint4s; uint4 (p, 4 c + i) sits at p * 64 + 16 i + c,
-// so the 16 lanes of a row group read consecutive uint4s.
-__device__ __forceinline__ void load_h(const uint4* s_h, int p, int c16, uint32_t (&h)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = s_h[p * 64 + 16 * i + c16];
-    h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
-  }
-}
-
-// Down contribution of one entry to the workgroup's 8 output rows.  Lanes
-// 16 j .. 16 j + 15 of a wave hold rows 2 j and 2 j + 1 (32 columns each);
-// acc[r][t] gathers the lane's unreduced partial sums, scaled by the routing
-// weight of token t and the tensor scale.  The entry's h pairs start at p0.
-template <int B, int FMT>
-__device__ __forceinline__ void down_entry(const Chunk<FMT> (&rows)[2], float gl, unsigned mask,
-                                           const float* wt /* by token */, const uint4* s_h,
-                                           int p0, int c16, float (&acc)[2][B]) {
-  auto token = [&](int t, int p) __attribute__((always_inline)) {
-    uint32_t h[16];
-    load_h(s_h, p, c16, h);
-    const float sc = wt[t] * gl;
-    const float d0 = rows[0].dot_x(h), d1 = rows[1].dot_x(h);
-#pragma unroll
-    for (int tt = 0; tt < B; ++tt)       // static register index for any t
-      if (tt == t) {
-        acc[0][tt] = __builtin_fmaf(sc, d0, acc[0][tt]);
-        acc[1][tt] = __builtin_fmaf(sc, d1, acc[1][tt]);
-      }
-  };
-  if constexpr (B == 1) {                // the one token (mask 1): a static index
-    token(0, p0);
-  } else {
-    // the entry's tokens only: set bits in ascending order, as its h pairs
-    int p = p0;
-#pragma unroll 1
-    for (unsigned m = mask; m != 0u; m &= m - 1u) token(__builtin_ctz(m), p++);
-  }
-}
-
-// h-ready counter k (k < kHBanks) of copy r, one 128-byte line each, after
-// the epoch counters.
-__device__ __forceinline__ uint32_t* hready_bank(uint8_t* ws, int r, int k) {
-  return reinterpret_cast<uint32_t*>(ws + kFlagOff +
-                                     ((size_t)kFusedGrid + (size_t)r * kHBanks + k) * kFlagStride);
-}
-
-// The loads of a layer that depend on neither x nor the routing: router row
-// g (wave w covers columns [512 w, 512 w + 512), 8 per lane); the shared
-// expert's gate/up row 2g + (w & 1) for the tokens of parity w >> 1 (at B = 1
-// waves 0 and 1 only); its down rows of this workgroup's 8 outputs.
-template <int FMT>
-struct StepAPre {
-  uint4 wr;
-  Chunk<FMT> scg, scu, dsh[2];
-};
-
-template <int B>
-__device__ __forceinline__ unsigned shared_token_mask(int wave) {
-  return ((1u << B) - 1u) & ((wave >> 1) ? 0xAAAAAAAAu : 0x55555555u);
-}
-
-template <int B, int FMT>
-__device__ __forceinline__ void load_pre_gateup(StepAPre<FMT>& p, const uint16_t* rw,
-                                                const ExpertsDev& shared, int g, int wave,
-                                                int lane) {
-  p.wr = gld<uint4>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
-  if (shared_token_mask<B>(wave)) {
-    p.scg.load_gu(shared, 0, 0, 2 * g + (wave & 1), lane);
-    p.scu.load_gu(shared, 0, 1, 2 * g + (wave & 1), lane);
-  }
-}
-
-template <int FMT>
-__device__ __forceinline__ void load_pre_down(StepAPre<FMT>& p, const ExpertsDev& shared, int g,
-                                              int lane) {
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-    p.dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * (lane >> 4) + r, lane & 15);
-}
-
-// A stacked launch prefetches the next layer's step-A rows right after the
-// h copy when this layer issues no load after it: each wave's routed
-// entries (at most 6 B / 4 of them) all fit in the two down-row sets issued
-// before the h-ready wait.  Otherwise the prefetch goes out behind the last
-// down-row loads, so that none of them queues behind it.
-template <int FMT>
-constexpr int kDownDepth = FMT == FMT_NVFP4 ? 4 : 1;   // routed entries per down-row set
-template <int B, int FMT>
-constexpr bool kPrefetchNext = kK * B <= 4 * 2 * kDownDepth<FMT>;
-
-// ------------------------------------------------------------------ kernel
-// One layer, as one workgroup of the 256 runs it (the body of both kernels
-// below).
-// pre: the step-A loads of this layer.  PF: 0 none (one layer per launch);
-// in a stacked launch 1 this layer issues its own step-A loads and, once
-// nothing of its own queues behind them, those of `next` (see
-// kPrefetchNext); 2 as 1, but this layer's were issued by the previous layer.  PF is static so that the
-// compiler counts the loads in flight exactly (a load under a runtime branch
-// makes it wait for all of them).  epoch_reg: this layer's epoch on return;
-// on entry, when EPREG, the previous layer's (stacked launches).
-template <int B, int FMT, bool NORM, bool RESID, int PF, bool EPREG>
-__device__ __forceinline__ void decode_layer(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, const ExpertsDev& routed,
-    const ExpertsDev& shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz, StepAPre<FMT>& pre,
-    const LayerDev& next, uint32_t& epoch_reg) {
-  // early: after the h copy (every routed down row is already in flight);
-  // late: behind step C's last down-row loads
-  constexpr bool kPfEarly = PF != 0 && kPrefetchNext<B, FMT>;
-  constexpr bool kPfLate = PF != 0 && !kPrefetchNext<B, FMT>;
-  // gate/up row pairs per batch (at B = 1 a wave has exactly 3: 12 per workgroup)
-  constexpr int kTB = FMT == FMT_NVFP4 ? 3 : 2;
-  constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
-  // batch 1 issues its routed down rows after publishing h instead of behind
-  // the gate/up rows: the gate/up burst then carries only gate/up rows
-  constexpr bool kLateDown = B == 1;
-  constexpr int kPairs = (kK + 1) * B;               // h pairs: 6 B routed + B shared
-  const int g = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp4 = lane >> 4, c16 = lane & 15;
-  DecodeCtl* ctl = reinterpret_cast<DecodeCtl*>(ws);
-  uint64_t* lslots = reinterpret_cast<uint64_t*>(ws + kSlotLogitOff);
-  uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + kHOff);
-
-  // x (bf16 [B][2048]) in steps A and B; the h pairs (bf16 [7 B][512]) in step C
-  __shared__ uint4 s_xh[kPairs * kI * 2 / 16];
-  uint4* s_x = s_xh;
-  const uint4* s_h = s_xh;
-  __shared__ float s_part[4][kMaxB];
-  __shared__ unsigned s_mask[kE];                    // tokens choosing each expert
-  __shared__ float s_wfull[kE][kMaxB];               // routing weight (expert, token)
-  __shared__ int s_act[kMaxActive];                  // entry -> expert (shared last)
-  __shared__ unsigned s_amask[kMaxActive];
-  __shared__ int s_pair0[kMaxActive];                // first h pair of each entry
-  __shared__ float s_gs[kMaxActive][3];              // tensor scales of each routed entry
-  __shared__ int s_nr;
-  __shared__ uint32_t s_epoch;
-  __shared__ float s_hsh[2][kMaxB];                  // this workgroup's shared-expert h
-  __shared__ float s_hout[kMaxRange][kMaxB];         // its routed h, by row of its range
-
-  trace_stamp(ws, 0);
-  // ---------------------------------------------------------------- step A
-  const unsigned smask = shared_token_mask<B>(wave);
-  if constexpr (PF != 2) load_pre_gateup<B, FMT>(pre, rw, shared, g, wave, lane);
-  // Every load of step A goes out before any of them is used (loads return
-  // in issue order, so a wait for one is a wait for all before it): x, piece
-  // tid of each token; the norm weight and the residual of this workgroup's
-  // output elements (row g * 8 + tid / B, token tid % B), read from x when
-  // not fused so that no branch splits the loads; x in registers at B = 1;
-  // the shared expert's down rows of this workgroup (step C).
-  __shared__ float s_rinv[kMaxB];
-  uint4 xr[B], nw = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-  for (int k = 0; k < B; ++k) xr[k] = reinterpret_cast<const uint4*>(x)[k * (kH / 8) + tid];
-  if constexpr (NORM) nw = reinterpret_cast<const uint4*>(fz.norm_w)[tid];
-  uint16_t rv = 0;
-  if constexpr (RESID) {
-    const int ro = tid < kRowsPerWg * B ? (tid % B) * kH + g * kRowsPerWg + tid / B : 0;
-    rv = fz.resid[ro];
-  }
-  uint32_t x0[16];
-  if constexpr (B == 1) {
-    const uint4* p = reinterpret_cast<const uint4*>(x + 32 * lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = p[i];
-      x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
-    }
-  }
-  const float sh_sg = Chunk<FMT>::gscale(shared, 0, 0), sh_su = Chunk<FMT>::gscale(shared, 0, 1),
-              sh_sd = Chunk<FMT>::gscale(shared, 0, 2);
-  if constexpr (PF != 2) load_pre_down<FMT>(pre, shared, g, lane);
-  const float resid = __builtin_bit_cast(float, (uint32_t)rv << 16);
-  // x to LDS as is, or through the fused RMSNorm.  A row's mean square is
-  // summed by one wave holding the row 32 elements per lane (the same order
-  // on every path).  At B = 1 every wave already holds the row in x0, so
-  // each thread normalises its piece before the barrier below and x0 is
-  // reread from LDS after it; at B > 1 wave w sums the rows of tokens w and
-  // w + 4 and the pieces are normalised after the barrier, behind a second
-  // one.
-  if constexpr (NORM) {
-    if constexpr (B == 1) {
-      const float r = row_rms_inv(x0, fz.eps);
-      const uint4 v = rmsnorm8(xr[0], nw, r);
-      s_x[tid] = v;
-      if (fz.xn_out && g == 0) reinterpret_cast<uint4*>(fz.xn_out)[tid] = v;
-    } else {
-      for (int t = wave; t < B; t += 4) {
-        const uint4* q = reinterpret_cast<const uint4*>(x + t * kH + 32 * lane);
-        uint32_t v[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 u = q[i];
-          v[4 * i] = u.x; v[4 * i + 1] = u.y; v[4 * i + 2] = u.z; v[4 * i + 3] = u.w;
-        }
-        const float r = row_rms_inv(v, fz.eps);
-        if (lane == 0) s_rinv[t] = r;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < B; ++k) s_x[k * (kH / 8) + tid] = xr[k];
-  }
-  if constexpr (B > 1) s_mask[tid] = 0u;
-  // this call's epoch: the workgroup's counter + 1; layer l > 0 of a stacked
-  // launch knows it already (the previous layer's + 1), which saves a memory
-  // round trip at the start of each layer
-  if (tid == 0) {
-    uint32_t* ctr = epoch_ptr(ws, g);
-    const uint32_t e = (EPREG ? epoch_reg : load_flag(ctr)) + 1u;
-    store_flag(ctr, e);
-    s_epoch = e;
-  }
-  __syncthreads();
-  const uint32_t epoch = s_epoch;
-  epoch_reg = epoch;
-  if constexpr (NORM && B == 1) {          // x0 again, normalised
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = s_x[4 * lane + i];
-      x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
-    }
-  }
-  if constexpr (NORM && B > 1) {
-#pragma unroll
-    for (int k = 0; k < B; ++k) {
-      const uint4 v = rmsnorm8(xr[k], nw, s_rinv[k]);
-      s_x[k * (kH / 8) + tid] = v;
-      if (fz.xn_out && g == 0) reinterpret_cast<uint4*>(fz.xn_out)[k * (kH / 8) + tid] = v;
-    }
-    __syncthreads();
-  }
-  trace_stamp(ws, 1);
-  {
-    float acc[B];
-#pragma unroll
-    for (int t = 0; t < B; ++t) {
-      const uint4 xv = s_x[t * (kH / 8) + 64 * wave + lane];
-      float a = dot2_bf16(pre.wr.x, xv.x, 0.0f);
-      a = dot2_bf16(pre.wr.y, xv.y, a);
-      a = dot2_bf16(pre.wr.z, xv.z, a);
-      a = dot2_bf16(pre.wr.w, xv.w, a);
-      acc[t] = wave_sum(a);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int t = 0; t < B; ++t) s_part[wave][t] = acc[t];
-    }
-  }
-  __syncthreads();
-  // the last wave stores (wave 0 polls first).  Once every 65536 calls the
-  // slots of tokens t >= B are stamped too, so no slot is ever 2^32 calls old
-  // and a 32-bit tag cannot match a stale value.
-  {
-    const int nt = (epoch & 0xFFFFu) == 0u ? kMaxB : B;
-    const int i = tid - (kFusedThreads - kMaxB * kLogitReps), t = i % kMaxB, r = i / kMaxB;
-    if (i >= 0 && t < nt) {
-      const float v = t < B ? s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t] : 0.0f;
-      put_slot(lslots + r * (kSlotLogitRep / 8) + t * kE + g, v, epoch);
-    }
-  }
-  trace_stamp(ws, 2);
-  if (smask)
-    gateup_compute<B, FMT>(pre.scg, pre.scu, sh_sg, sh_su, smask, s_x, x0, lane,
-                           &s_hsh[wave & 1][0]);
-  trace_stamp(ws, 3);
-
-  // ---------------------------------------------------------------- step B
-  // top-6 per token (wave t % 4 takes token t), repeated identically in every
-  // workgroup; sigmoid scores of the chosen six renormalised to sum to 1
-  if constexpr (B == 1) {
-    // one token: its six experts are the routed entries, each with one h
-    // pair, so wave 0 orders them by id (rank by counting) and writes the
-    // entry tables itself, with no token masks and no barrier in between
-    if (wave == 0) {
-      float v[4];
-      wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane, 64, epoch, v,
-                    &ctl->err);
-      trace_stamp(ws, 4);
-      int my_id;
-      float my_l;
-      wave_top6(v, lane, my_id, my_l);
-      const float s = 1.0f / (1.0f + expf(-my_l));
-      float sum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kK; ++j) sum += readlane_f32(s, j);
-      int rank = 0;
-#pragma unroll
-      for (int j = 0; j < kK; ++j) rank += __builtin_amdgcn_readlane(my_id, j) < my_id ? 1 : 0;
-      if (lane < kK) {
-        const float wgt = s / sum;
-        s_wfull[my_id][0] = wgt;
-        s_act[rank] = my_id;
-        s_amask[rank] = 1u;
-        s_pair0[rank] = rank;
-        if (g == 0) {
-          if (ids_out) ids_out[lane] = my_id;
-          if (w_out) w_out[lane] = wgt;
-        }
-      }
-      if (lane == 0) {
-        s_nr = kK;
-        s_act[kK] = 0;
-        s_amask[kK] = 1u;
-        s_pair0[kK] = kK;
-      }
-    }
-    trace_stamp(ws, 5);
-  } else {
-  for (int t = wave; t < B; t += 4) {
-    float v[4];
-    wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + t * kE + lane, 64, epoch, v,
-                  &ctl->err);
-    trace_stamp(ws, 4);
-    int my_id;
-    float my_l;
-    wave_top6(v, lane, my_id, my_l);
-    const float s = 1.0f / (1.0f + expf(-my_l));
-    float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kK; ++j) sum += readlane_f32(s, j);
-    if (lane < kK) {
-      const float wgt = s / sum;
-      atomicOr(&s_mask[my_id], 1u << t);
-      s_wfull[my_id][t] = wgt;
-      if (g == 0) {
-        if (ids_out) ids_out[t * kK + lane] = my_id;
-        if (w_out) w_out[t * kK + lane] = wgt;
-      }
-    }
-  }
-  trace_stamp(ws, 5);
-  __syncthreads();
-  if (wave == 0) {            // entries: touched experts in ascending id, then the shared one
-    int base = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = 64 * q + lane;
-      const unsigned m = s_mask[e];
-      const uint64_t bal = __ballot(m != 0u);
-      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      if (m != 0u) {
-        s_act[pos] = e;
-        s_amask[pos] = m;
-      }
-      base += __popcll(bal);
-    }
-    // first h pair of each entry: exclusive prefix of the token counts (0..8),
-    // bit by bit over ballots
-    const unsigned ma = lane < base ? s_amask[lane] : 0u;
-    const int cnt = __popc(ma);
-    int excl = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint64_t bb = __ballot((cnt >> b) & 1);
-      excl += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32),
-                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u)) << b;
-    }
-    if (lane < base) s_pair0[lane] = excl;
-    if (lane == 0) {
-      s_nr = base;
-      s_act[base] = 0;
-      s_amask[base] = (1u << B) - 1u;
-      s_pair0[base] = kK * B;
-    }
-  }
-  }
-  __syncthreads();
-  const int nr = s_nr;
-  trace_stamp(ws, 6);
-
-  // routed gate/up: the nr * 512 row pairs are cut into 256 contiguous
-  // ranges, one per workgroup; wave w takes T0 + w, T0 + w + 4, ... in
-  // batches of kTB, the next batch in flight while one computes
-  const int T = nr * kI;
-  const int T0 = (int)(((long long)g * T) >> 8), T1 = (int)(((long long)(g + 1) * T) >> 8);
-  // step-C work of this wave: routed entries a = wsel + 4 k (and the shared
-  // expert's tokens wave, wave + 4); the first kDepthC entries' down rows are
-  // fetched behind the first gate/up batch
-  const int wsel = (wave + 3) & 3;
-  auto load_entry = [&](Chunk<FMT> (&dst)[2], int a) {
-    if (a < nr) {
-      const size_t ee = (size_t)s_act[a];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) dst[r].load_dn(routed, ee, g * kRowsPerWg + 2 * grp4 + r, c16);
-    }
-  };
-  Chunk<FMT> dbuf[kDepthC][2];
-  {
-    Chunk<FMT> cg[2][kTB], cu[2][kTB];
-    // Loads are unconditional: a slot past the range reads the range's last
-    // row again (a cache hit; run_batch drops its sums).  A load under a
-    // branch would leave the compiler unsure how many loads are in flight,
-    // and it would then wait for all of them before the next batch goes out.
-    auto load_batch = [&](Chunk<FMT> (&bg)[kTB], Chunk<FMT> (&bu)[kTB], int j0) {
-#pragma unroll
-      for (int q = 0; q < kTB; ++q) {
-        const int s0 = T0 + wave + 4 * (j0 + q), s = s0 < T1 ? s0 : T1 - 1;
-        const size_t ee = (size_t)s_act[s / kI];
-        bg[q].load_gu(routed, ee, 0, s % kI, lane);
-        bu[q].load_gu(routed, ee, 1, s % kI, lane);
-      }
-    };
-    // a batch for each token any of its row pairs uses: the 2 kTB gate and up
-    // partial sums reduced together; gate/up of pair q land in lanes
-    // 16 q .. 16 q + 7 / 16 q + 8 .. 16 q + 15, lane 16 q writes h
-    auto run_batch = [&](const Chunk<FMT> (&bg)[kTB], const Chunk<FMT> (&bu)[kTB], int j0) {
-      unsigned mq[kTB], um = 0u;
-      float sgq[kTB], suq[kTB];
-#pragma unroll
-      for (int q = 0; q < kTB; ++q) {
-        const int s = T0 + wave + 4 * (j0 + q);
-        mq[q] = 0u;
-        sgq[q] = suq[q] = 0.0f;
-        if (s < T1) {
-          const int a = s / kI;
-          mq[q] = s_amask[a];
-          sgq[q] = s_gs[a][0];
-          suq[q] = s_gs[a][1];
-          um |= mq[q];
-        }
-      }
-      if (um == 0u) return;
-      const int qme = lane >> 4;                     // the row pair this lane may write
-      unsigned mme = 0u;
-      float sgme = 0.0f, sume = 0.0f;
-#pragma unroll
-      for (int q = 0; q < kTB; ++q)
-        if (qme == q) {
-          mme = mq[q];
-          sgme = sgq[q];
-          sume = suq[q];
-        }
-      const int ime = T0 + wave + 4 * (j0 + qme) - T0;
-#pragma unroll
-      for (int t = 0; t < B; ++t) {
-        if (!((um >> t) & 1u)) continue;
-        uint32_t xw[16];
-        if constexpr (B == 1) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xw[i] = x0[i];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 v = s_x[t * (kH / 8) + 4 * lane + i];
-            xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
-          }
-        }
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[2 * q] = q < kTB ? bg[q < kTB ? q : 0].dot_x(xw) : 0.0f;
-          v[2 * q + 1] = q < kTB ? bu[q < kTB ? q : 0].dot_x(xw) : 0.0f;
-        }
-        const float z = wave_sum8(v, lane);
-        const float zu = dpp_f32<0x128>(z);
-        if ((lane & 15) == 0 && ((mme >> t) & 1u))
-          s_hout[ime][t] = silu_mul(z * sgme, zu * sume);
-      }
-    };
-    // the routed entries' tensor scales: one thread each, fetched beside the
-    // first weights and parked in LDS (no wave waits on them in its loop)
-    const bool gs_mine = tid < 3 * nr;
-    float gsv = 1.0f;
-    if (gs_mine) gsv = Chunk<FMT>::gscale(routed, (size_t)s_act[tid / 3], tid % 3);
-    load_batch(cg[0], cu[0], 0);
-    // the first kDepthC entries' down rows of step C, behind the first batch
-    // (at B = 1 after the h publish: the wait for the tensor scales below
-    // waits for every load before it)
-    if constexpr (!kLateDown) {
-#pragma unroll
-      for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
-    }
-    if (gs_mine) s_gs[tid / 3][tid % 3] = gsv;
-    __syncthreads();
-    // this wave's row pairs T0 + wave + 4 j, j < nj; the loop runs while a
-    // batch after the two in hand exists, the last one or two are peeled
-    const int nj = T1 - T0 > wave ? (T1 - T0 - wave + 3) >> 2 : 0;
-    int j0 = 0;
-    for (; j0 + 2 * kTB < nj; j0 += 2 * kTB) {
-      load_batch(cg[1], cu[1], j0 + kTB);
-      run_batch(cg[0], cu[0], j0);
-      load_batch(cg[0], cu[0], j0 + 2 * kTB);
-      run_batch(cg[1], cu[1], j0 + kTB);
-    }
-    if (j0 + kTB < nj) {
-      load_batch(cg[1], cu[1], j0 + kTB);
-      run_batch(cg[0], cu[0], j0);
-      run_batch(cg[1], cu[1], j0 + kTB);
-    } else {
-      run_batch(cg[0], cu[0], j0);
-    }
-  }
-  trace_stamp(ws, 7);
-  // write this workgroup's h to its pairs: shared (6 B + t, rows 2g, 2g + 1),
-  // routed (pair0[a] + rank of t in the entry's tokens, row), consecutive
-  // threads on consecutive rows
-  __syncthreads();
-  if (tid < 2 * B) {
-    const int r = tid / B, t = tid % B;
-    store_coherent_u16(hbuf + (size_t)(kK * B + t) * kI + 2 * g + r, f32_to_bf16_rne(s_hsh[r][t]));
-  }
-  {
-    const int nloc = T1 - T0;
-    for (int idx = tid; idx < nloc * B; idx += kFusedThreads) {
-      const int t = idx / nloc, i = idx - t * nloc;
-      const int s = T0 + i, a = s / kI;
-      const unsigned m = s_amask[a];
-      if ((m >> t) & 1u)
-        store_coherent_u16(hbuf + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kI + (s % kI),
-                           f32_to_bf16_rne(s_hout[i][t]));
-    }
-  }
-  // publish: wait for this workgroup's h stores, then count in on bank g % 64
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid < kBankReps)
-    __hip_atomic_fetch_add(hready_bank(ws, tid, g % kHBanks), 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-  trace_stamp(ws, 8);
-
-  // ---------------------------------------------------------------- step C
-  // The next kDepthC entries' down rows go out now (not earlier: the h
-  // stores above must not wait behind them), so they arrive during the wait.
-  // Wave 3 polls, and issues its rows after the wait (its polls would
-  // otherwise queue behind them).  Every bank of copy g % kBankReps must
-  // reach 4 * epoch (each bank gains 4 per call).
-  Chunk<FMT> dbuf2[kDepthC][2];
-  auto prefetch = [&]() {
-#pragma unroll
-    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf2[q], wsel + 4 * (kDepthC + q));
-  };
-  if constexpr (kLateDown) {   // HBM is idle while the h-ready counters fill
-#pragma unroll
-    for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
-  }
-  if (wave != 3) prefetch();
-  if (wave == 3) {
-    const uint32_t want = (uint32_t)(kFusedGrid / kHBanks) * epoch;
-    for (int spin = 0;; ++spin) {
-      const uint32_t v = load_flag(hready_bank(ws, g % kBankReps, lane));
-      if (__ballot(v != want) == 0) break;
-      if (spin > kSpinLimit) {
-        if (lane == 0)
-          __hip_atomic_fetch_or(&ctl->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    prefetch();
-  }
-  __syncthreads();
-  trace_stamp(ws, 9);
-
-  // all 7 B h pairs of the call into LDS: 16-byte device-coherent loads
-  // (buffer loads with the device-scope bit), 8 in flight per thread
-  {
-    constexpr int kN16 = kPairs * (kI * 2 / 16);
-    const __amdgpu_buffer_rsrc_t hr =
-        __builtin_amdgcn_make_buffer_rsrc(hbuf, 0, (int)(2 * kPairs * kI), 0x00020000);
-#pragma unroll 1
-    for (int i0 = 0; i0 < kN16; i0 += 8 * kFusedThreads) {
-      uint4 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = i0 + kFusedThreads * i + tid;
-        if (idx < kN16) v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hr, idx * 16, 0, 16));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = i0 + kFusedThreads * i + tid;
-        if (idx < kN16) {
-          const int c = idx & 63;
-          s_xh[(idx & ~63) + 16 * (c & 3) + (c >> 2)] = v[i];
-        }
-      }
-    }
-  }
-  __syncthreads();
-  trace_stamp(ws, 10);
-  // The next layer's router row and shared gate/up rows (registers free
-  // since step A): no load of this layer is issued after this point when
-  // every routed entry's down rows are already in flight, so these wait
-  // behind nothing and arrive while this layer finishes.
-  if constexpr (kPfEarly) load_pre_gateup<B, FMT>(pre, next.rw, next.shared, g, wave, lane);
-
-  float acc[2][B], accs[2][2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-#pragma unroll
-    for (int t = 0; t < B; ++t) acc[r][t] = 0.0f;
-    accs[r][0] = accs[r][1] = 0.0f;
-  }
-  {                                                  // shared expert, tokens wave and wave + 4
-    const float gl = sh_sd;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = wave + 4 * j;
-      if (t < B) {
-        uint32_t h[16];
-        load_h(s_h, kK * B + t, c16, h);
-        accs[0][j] = __builtin_fmaf(gl, pre.dsh[0].dot_x(h), accs[0][j]);
-        accs[1][j] = __builtin_fmaf(gl, pre.dsh[1].dot_x(h), accs[1][j]);
-      }
-    }
-  }
-  if constexpr (kPfEarly) load_pre_down<FMT>(pre, next.shared, g, lane);  // the next layer's
-  // routed entries of this wave in order, two sets of kDepthC in flight
-  const int n_mine = nr > wsel ? (nr - wsel + 3) >> 2 : 0;
-  auto run_set = [&](const Chunk<FMT> (&buf)[kDepthC][2], int k0) {
-#pragma unroll
-    for (int q = 0; q < kDepthC; ++q) {
-      if (k0 + q < n_mine) {
-        const int a = wsel + 4 * (k0 + q);
-        const int e = s_act[a];
-        down_entry<B, FMT>(buf[q], s_gs[a][2], s_amask[a],
-                           &s_wfull[e][0], s_h, s_pair0[a], c16, acc);
-      }
-    }
-  };
-  if constexpr (kPrefetchNext<B, FMT>) {   // every entry of this wave is in the two sets
-    run_set(dbuf, 0);
-    run_set(dbuf2, kDepthC);
-  } else {
-    // loads in the loop are unconditional (as in the gate/up loop): an entry
-    // past this wave's last reads the last one's rows again
-    auto load_set = [&](Chunk<FMT> (&buf)[kDepthC][2], int k) {
-#pragma unroll
-      for (int q = 0; q < kDepthC; ++q) {
-        const int kk = k + q < n_mine ? k + q : n_mine - 1;
-        const size_t ee = (size_t)s_act[wsel + 4 * kk];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) buf[q][r].load_dn(routed, ee, g * kRowsPerWg + 2 * grp4 + r, c16);
-      }
-    };
-    int k0 = 0;
-    for (; k0 + 2 * kDepthC < n_mine; k0 += 2 * kDepthC) {
-      run_set(dbuf, k0);
-      load_set(dbuf, k0 + 2 * kDepthC);
-      run_set(dbuf2, k0 + kDepthC);
-      load_set(dbuf2, k0 + 3 * kDepthC);
-    }
-    if constexpr (kPfLate) {     // the next layer's step-A rows, behind these
-      load_pre_gateup<B, FMT>(pre, next.rw, next.shared, g, wave, lane);
-      load_pre_down<FMT>(pre, next.shared, g, lane);
-    }
-    run_set(dbuf, k0);
-    run_set(dbuf2, k0 + kDepthC);
-  }
-  trace_stamp(ws, 11);
-  // reduce over the 16 lanes of each row group, then over the waves in a
-  // fixed order; the shared expert's term of token t comes from wave t % 4
-  __shared__ float s_red[4][kRowsPerWg][kMaxB];
-  __shared__ float s_redsh[4][kRowsPerWg][2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-#pragma unroll
-    for (int t = 0; t < B; ++t) acc[r][t] = group16_sum(acc[r][t]);
-    accs[r][0] = group16_sum(accs[r][0]);
-    accs[r][1] = group16_sum(accs[r][1]);
-  }
-  if (c16 == 0) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-#pragma unroll
-      for (int t = 0; t < B; ++t) s_red[wave][2 * grp4 + r][t] = acc[r][t];
-      s_redsh[wave][2 * grp4 + r][0] = accs[r][0];
-      s_redsh[wave][2 * grp4 + r][1] = accs[r][1];
-    }
-  }
-  __syncthreads();
-  if (tid < kRowsPerWg * B) {
-    const int r8 = tid / B, t = tid % B;
-    float y = (s_red[0][r8][t] + s_red[1][r8][t]) + (s_red[2][r8][t] + s_red[3][r8][t]);
-    y += s_redsh[t & 3][r8][t >> 2];
-    if constexpr (RESID) y += resid;
-    out[(size_t)t * kH + g * kRowsPerWg + r8] = f32_to_bf16_rne(y);
-  }
-  trace_stamp(ws, 12);
-  trace_flush(ws);
-}
-
-template <int B, int FMT, bool NORM, bool RESID>
-__global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, ExpertsDev routed,
-    ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, uint8_t* __restrict__ ws, FuseDev fz) {
-  StepAPre<FMT> pre;
-  uint32_t epoch = 0;
-  decode_layer<B, FMT, NORM, RESID, 0, false>(x, rw, routed, shared, out, ids_out, w_out, ws, fz,
-                                              pre, LayerDev{}, epoch);
-}
-
-// A stack of L layers in one launch, one after another: every workgroup
-// runs layer l + 1 as soon as it has finished its part of layer l (the
-// layers read the same x), so its first loads of layer l + 1 overlap the
-// other workgroups' tail of layer l.  (Issuing layer l + 1's router and
-// shared-expert rows inside layer l's step C was measured slower: 12.6
-// against 11.9 us per layer.)  The hand-over protocol already orders
-// consecutive layers: a workgroup can only publish layer l + 1's logits after
-// it has read all of layer l's, and only write layer l + 1's h after every
-// workgroup has published layer l + 1's logits, i.e. after each has copied
-// layer l's h.  So the per-layer epochs are all the kernel needs, and the
-// launch gap between layers disappears (the pages hide it with programmatic
-// dependent launch).
-template <int B, int FMT>
-__global__ __launch_bounds__(kFusedThreads, 1) void k_decode_stack(
-    const uint16_t* __restrict__ x, const LayerDev* __restrict__ layers, int L,
-    uint16_t* __restrict__ out, int32_t* __restrict__ ids_out, uint8_t* __restrict__ ws) {
-  StepAPre<FMT> pre;
-  // the last layer "prefetches" its own rows again (cache hits, unused), so
-  // that every layer body has the same static load count
-  uint32_t epoch = 0;
-  auto layer = [&](auto pf, auto epreg, int l) __attribute__((always_inline)) {
-    const LayerDev d = layers[l], dn = layers[l + 1 < L ? l + 1 : l];
-    decode_layer<B, FMT, false, false, decltype(pf)::value, decltype(epreg)::value>(
-        x, d.rw, d.routed, d.shared, out + (size_t)l * B * kH,
-        ids_out ? ids_out + (size_t)l * B * kK : nullptr, nullptr, ws, FuseDev{}, pre, dn, epoch);
-  };
-  layer(std::integral_constant<int, 1>{}, std::false_type{}, 0);
-  for (int l = 1; l < L; ++l) {
-    __syncthreads();
-    layer(std::integral_constant<int, 2>{}, std::true_type{}, l);
-  }
-}
-
-// ------------------------------------------------------------------ launcher
 static int g_fused_ok[64];   // per device: 0 unknown, 1 usable, -1 not
 
 bool fused_supported() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   if (g_fused_ok[dev] == 0) {
-    int cus = 0, occ_nv = 0, occ_bf = 0, occ_nn = 0, occ_bn = 0, occ_sn = 0, occ_sb = 0;
+    int cus = 0;
     const bool ok =
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ_nv, k_decode_fused<8, FMT_NVFP4, false, false>, kFusedThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ_bf, k_decode_fused<8, FMT_BF16, false, false>, kFusedThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ_nn, k_decode_fused<8, FMT_NVFP4, true, true>, kFusedThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ_bn, k_decode_fused<8, FMT_BF16, true, true>, kFusedThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ_sn, k_decode_stack<8, FMT_NVFP4>, kFusedThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ_sb, k_decode_stack<8, FMT_BF16>, kFusedThreads, 0) == hipSuccess;
-    g_fused_ok[dev] = (ok && cus >= kFusedGrid && occ_nv >= 1 && occ_bf >= 1 && occ_nn >= 1 &&
-                       occ_bn >= 1 && occ_sn >= 1 && occ_sb >= 1) ? 1 : -1;
+        cus >= kFusedGrid && occupancy_fused_fmt<FMT_NVFP4>() &&
+        occupancy_fused_fmt<FMT_BF16>() && occupancy_stack_fmt<FMT_NVFP4>() &&
+        occupancy_stack_fmt<FMT_BF16>() && occupancy_chain_fmt<FMT_NVFP4>() &&
+        occupancy_chain_fmt<FMT_BF16>();
+    g_fused_ok[dev] = ok ? 1 : -1;
   }
   return g_fused_ok[dev] == 1;
-}
-
-template <int B>
-static void launch_fused_b(int fmt, const uint16_t* x, const uint16_t* rw, const ExpertsDev& routed,
-                           const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
-                           uint8_t* ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1,
-                           const FuseDev& fz) {
-  // one instance per fused combination: without fusion the kernel carries
-  // none of its code (the schedule of the plain layer is left as it is)
-  using K = decltype(&k_decode_fused<B, FMT_NVFP4, false, false>);
-  static const K table[2][2][2] = {
-      {{k_decode_fused<B, FMT_NVFP4, false, false>, k_decode_fused<B, FMT_NVFP4, false, true>},
-       {k_decode_fused<B, FMT_NVFP4, true, false>, k_decode_fused<B, FMT_NVFP4, true, true>}},
-      {{k_decode_fused<B, FMT_BF16, false, false>, k_decode_fused<B, FMT_BF16, false, true>},
-       {k_decode_fused<B, FMT_BF16, true, false>, k_decode_fused<B, FMT_BF16, true, true>}}};
-  const K k = table[fmt == FMT_NVFP4 ? 0 : 1][fz.norm_w ? 1 : 0][fz.resid ? 1 : 0];
-  if (e0 && e1)
-    hipExtLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, e0, e1, 0, x, rw, routed,
-                          shared, out, ids, w, ws, fz);
-  else
-    hipLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, x, rw, routed, shared, out,
-                       ids, w, ws, fz);
-}
-
-template <int B>
-static void launch_stack_b(int fmt, const uint16_t* x, const LayerDev* layers, int L,
-                           uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st) {
-  auto k = fmt == FMT_NVFP4 ? k_decode_stack<B, FMT_NVFP4> : k_decode_stack<B, FMT_BF16>;
-  hipLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, x, layers, L, out, ids, ws);
-}
-
-hipError_t launch_decode_stack(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
-                               uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st) {
-  switch (B) {
-    case 1: launch_stack_b<1>(fmt, x, layers, L, out, ids, ws, st); break;
-    case 2: launch_stack_b<2>(fmt, x, layers, L, out, ids, ws, st); break;
-    case 3: launch_stack_b<3>(fmt, x, layers, L, out, ids, ws, st); break;
-    case 4: launch_stack_b<4>(fmt, x, layers, L, out, ids, ws, st); break;
-    case 5: launch_stack_b<5>(fmt, x, layers, L, out, ids, ws, st); break;
-    case 6: launch_stack_b<6>(fmt, x, layers, L, out, ids, ws, st); break;
-    case 7: launch_stack_b<7>(fmt, x, layers, L, out, ids, ws, st); break;
-    case 8: launch_stack_b<8>(fmt, x, layers, L, out, ids, ws, st); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t* rw,
                                const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st, hipEvent_t e0,
                                hipEvent_t e1, const FuseDev& fz) {
-  switch (B) {
-    case 1: launch_fused_b<1>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
-    case 2: launch_fused_b<2>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
-    case 3: launch_fused_b<3>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
-    case 4: launch_fused_b<4>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
-    case 5: launch_fused_b<5>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
-    case 6: launch_fused_b<6>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
-    case 7: launch_fused_b<7>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
-    case 8: launch_fused_b<8>(fmt, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return fmt == FMT_NVFP4
+             ? launch_fused_fmt<FMT_NVFP4>(B, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz)
+             : launch_fused_fmt<FMT_BF16>(B, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz);
+}
+
+hipError_t launch_decode_stack(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
+                               uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st) {
+  return fmt == FMT_NVFP4 ? launch_stack_fmt<FMT_NVFP4>(B, x, layers, L, out, ids, ws, st)
+                          : launch_stack_fmt<FMT_BF16>(B, x, layers, L, out, ids, ws, st);
+}
+
+hipError_t launch_decode_chain(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
+                               const uint16_t* norm_w, float eps, uint16_t* out, int32_t* ids,
+                               uint8_t* ws, hipStream_t st) {
+  const bool norm = norm_w != nullptr;
+  return fmt == FMT_NVFP4
+             ? launch_chain_fmt<FMT_NVFP4>(B, norm, x, layers, L, norm_w, eps, out, ids, ws, st)
+             : launch_chain_fmt<FMT_BF16>(B, norm, x, layers, L, norm_w, eps, out, ids, ws, st);
 }
 
 }  // namespace moe

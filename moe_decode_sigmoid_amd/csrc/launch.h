@@ -29,6 +29,15 @@ hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t
 hipError_t launch_decode_stack(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
                                uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st);
 
+// A chained residual stack in one launch: x_{l+1} = x_l + layer_l(norm_l(x_l)),
+// out[l] = x_{l+1}; norm_w bf16 [L][H] (nullptr: no norm).
+hipError_t launch_decode_chain(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
+                               const uint16_t* norm_w, float eps, uint16_t* out, int32_t* ids,
+                               uint8_t* ws, hipStream_t st);
+
+// Copy the workspace's wait-status word to *status (device) and clear it.
+hipError_t launch_ws_status(uint8_t* ws, int32_t* status, hipStream_t st);
+
 // Dense NVFP4 GEMV, B = 1..8, K % 32 == 0, K <= 8192, B * K <= 32768.
 constexpr int kGemvMaxK = 8192;
 constexpr int kGemvMaxBK = 32768;                  // x staged in LDS: B * K * 2 bytes <= 64 KiB

@@ -73,7 +73,11 @@ __host__ __device__ inline PrefillLayout prefill_layout(int T) {
   L.T = T;
   L.ntiles = (T + kPTile - 1) / kPTile;
   L.max_items = (T * kK + kGBM - 1) / kGBM + kE + (T + kGBM - 1) / kGBM;
-  size_t o = 0;
+  // after the decode kernels' region: the epoch counters, h-ready counters
+  // and tagged logit slots there persist from call to call, and a byte of
+  // prefill data left in them would desynchronise later decode calls on a
+  // shared workspace
+  size_t o = al256(kDecodeWsBytes);
   L.ids = o;    o = al256(o + sizeof(int) * (size_t)T * kK);
   L.w = o;      o = al256(o + sizeof(float) * (size_t)T * kK);
   L.hist = o;   o = al256(o + sizeof(int) * (size_t)L.ntiles * kE);

@@ -247,6 +247,7 @@ static void or_route_token(const or_shape* S, const uint16_t* x, const uint16_t*
 
 void or_route(const or_shape* S, const uint16_t* x, int32_t B, const uint16_t* router,
               int32_t* ids, double* w, double* gap, double* scores) {
+  #pragma omp parallel for schedule(static) if (B > 1)
   for (int32_t t = 0; t < B; ++t)
     or_route_token(S, x + (int64_t)t * S->hidden, router, NULL, ids + (int64_t)t * S->top_k,
                    w + (int64_t)t * S->top_k, gap + t,

@@ -21,6 +21,7 @@ def test_header_declares_the_entry_points():
     for n in ["moe_decode_route", "moe_decode_forward", "moe_decode_forward_timed",
               "moe_prefill_forward", "moe_nvfp4_gemv", "moe_decode_forward_ex",
               "moe_prefill_forward_ex", "moe_decode_stack_forward",
+              "moe_decode_chain_forward", "moe_workspace_status",
               "moe_general_workspace_layout",
               "moe_nvfp4_dequant", "moe_workspace_bytes", "moe_status_string",
               "moe_abi_version"]:
@@ -247,6 +248,57 @@ def test_stack_argument_errors():
     assert call(out=A + 4096, ws=A + 0x50000000, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG  # x
     assert call(S=moe.shape(n_experts=384, top_k=8, n_shared=0), wsb=WS_BIG) == \
         moe.MOE_ERR_UNSUPPORTED
+
+
+def test_chain_argument_errors():
+    """The chained stack's host-side checks (fake addresses, never read)."""
+    L = moe.lib()
+    S = moe.shape()
+    T = A + 0x6000000
+    NW = A + 0x50000000
+
+    def call(S=S, n=4, layers=T, x=A, B=2, nw=None, eps=1e-6, out=A + 0x2000000, ids=None,
+             ws=A + 0x3000000, wsb=1024):
+        return L.moe_decode_chain_forward(ctypes.byref(S), n, layers, x, B, nw, eps, out, ids, ws,
+                                          wsb, 0)
+    assert call() == moe.MOE_ERR_WORKSPACE
+    assert call(n=0, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG
+    assert call(layers=None, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG
+    assert call(layers=T + 4, wsb=WS_BIG) == moe.MOE_ERR_MISALIGNED
+    assert call(B=9, wsb=WS_BIG) == moe.MOE_ERR_UNSUPPORTED
+    assert call(B=0, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG
+    assert call(x=A + 8) == moe.MOE_ERR_MISALIGNED
+    assert call(nw=NW + 2) == moe.MOE_ERR_MISALIGNED
+    assert call(nw=NW, eps=0.0) == moe.MOE_ERR_INVALID_ARG
+    assert call(nw=NW, eps=float("nan")) == moe.MOE_ERR_INVALID_ARG
+    assert call(ids=A + 2) == moe.MOE_ERR_MISALIGNED
+    assert call(out=A + 4096, ws=A + 0x50000000, wsb=WS_BIG) == moe.MOE_ERR_INVALID_ARG  # x
+    assert call(nw=A + 0x2000000 + 64, ws=A + 0x60000000, wsb=WS_BIG) == \
+        moe.MOE_ERR_INVALID_ARG                                   # norm weights inside out
+    assert call(S=moe.shape(n_experts=384, top_k=8, n_shared=0), wsb=WS_BIG) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert call(S=moe.shape(moe.MOE_W_MXFP8), wsb=WS_BIG) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_status_argument_errors():
+    L = moe.lib()
+    WS = A + 0x3000000
+    assert L.moe_workspace_status(None, WS_BIG, A, 0) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_workspace_status(WS, 64, A, 0) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_workspace_status(WS + 16, WS_BIG, A, 0) == moe.MOE_ERR_MISALIGNED
+    assert L.moe_workspace_status(WS, WS_BIG, None, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_status(WS, WS_BIG, A + 2, 0) == moe.MOE_ERR_MISALIGNED
+    assert L.moe_workspace_status(WS, WS_BIG, WS + 64, 0) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_prefill_workspace_keeps_the_decode_region():
+    """A prefill workspace is larger than the decode one by more than the
+    decode region: its data starts past the region the decode kernels keep
+    their counters in, so one workspace serves both (the GPU test
+    test_one_workspace_serves_prefill_and_decode checks the results)."""
+    d = moe.moe_workspace_bytes(8)
+    for T in (1, 64, 8192):
+        assert moe.moe_workspace_bytes(T, prefill=True) > d
 
 
 def test_general_workspace_layout():

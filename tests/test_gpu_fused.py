@@ -7,12 +7,18 @@ Inputs: the seeded synthetic Flint-shaped layer; x ~ N(0, 1) bf16 with token t
 scaled by 2^(t mod 5 - 2) so that the norm does real work; norm weight and
 residual ~ N(0, 1) bf16; eps = 1e-5.
 
-Protocol.  The normalised input is bf16, and an fp32 computation of it can
-land on the other side of a bf16 rounding midpoint than the fp64 one (about
-3e-4 of the elements, 1 ulp each).  Routing is a decision taken on that
-input, so the oracle evaluates the layer on the GPU's normalised input
-(returned through xn_out), after that input has been checked against the
-oracle's own RMSNorm: equal, or 1 ulp apart on at most 0.2% of the elements.
+Two protocols.
+ - End to end (the *_end_to_end_* tests): the fp64 oracle runs from x alone,
+   with its own RMSNorm, and the GPU output must meet the layer's tolerance
+   (max |err| <= 2e-2, rel L2 <= 5e-3); ids are forced to the GPU's only for
+   a token whose oracle 6th/7th score gap is below 1e-6.
+ - Decomposed (the other tests, diagnostics): the normalised input is bf16,
+   and an fp32 computation of it can land on the other side of a bf16
+   rounding midpoint than the fp64 one (about 3e-4 of the elements, 1 ulp
+   each).  The GPU's normalised input (returned through xn_out) is checked
+   against the oracle's own RMSNorm (equal, or 1 ulp apart on at most 0.2%
+   of the elements), and the oracle then evaluates the layer on it, which
+   isolates the layer from the norm.
 """
 import functools
 
@@ -227,3 +233,48 @@ def test_prefill_without_fusion_equals_plain_prefill_bitwise():
     moe.moe_prefill_forward_ex(xd, L.router, L.routed, L.shared, b, ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------- end to end, unconditioned
+def oracle_own_norm(x, HL, nw, residual, ids_gpu):
+    """The oracle on its own RMSNorm of x (no GPU value enters it); a token's
+    ids are forced to the GPU's only where they differ and the oracle's
+    6th/7th score gap is below the near-tie threshold."""
+    y, ids, w, gap, xn = oracle.forward_fused(x, HL, norm_w=nw, eps=EPS, residual=residual)
+    for t in range(x.shape[0]):
+        if set(ids_gpu[t].tolist()) == set(ids[t].tolist()):
+            continue
+        assert gap[t] < parity.NEAR_TIE, (t, float(gap[t]))
+        print(f"token {t}: near-tie (gap {gap[t]:.2e}), ids forced")
+        y[t] = oracle.forward_fused(x[t:t + 1], HL, norm_w=nw, eps=EPS,
+                                    residual=None if residual is None else residual[t:t + 1],
+                                    forced_ids=ids_gpu[t:t + 1].copy())[0][0]
+    return y, ids, w, gap
+
+
+@pytest.mark.parametrize("fmt,B,resid", [("nvfp4", 1, False), ("nvfp4", 1, True),
+                                         ("nvfp4", 4, True), ("nvfp4", 8, False),
+                                         ("nvfp4", 8, True), ("bf16", 3, True)])
+def test_decode_norm_end_to_end_against_the_oracles_own_norm(fmt, B, resid):
+    """out = residual + layer(rmsnorm(x)) against the fp64 oracle run from x
+    itself: the GPU's normalised input is not used (its 1-ulp departures on
+    rare elements must stay inside the tolerance)."""
+    seed = 1 if fmt == "nvfp4" else 2
+    x = scaled_x(100 + B, B)
+    nw = testgen.make_x(101, 1)[0]
+    res = testgen.make_x(102, B) if resid else None
+    y, ids, w, _ = run_decode(seed, x, nw=nw, res=res, fmt=fmt, xn_out=False)
+    y_ref, ids_or, w_or, gap = oracle_own_norm(x, host_layer(seed, fmt), nw, res, ids)
+    parity.check_weights(ids, w, ids_or, w_or, gap)
+    print(parity.check_output(y, y_ref, f"decode norm e2e B {B} {fmt} resid {resid}"))
+
+
+@pytest.mark.parametrize("T", [77, 300])
+def test_prefill_norm_end_to_end_against_the_oracles_own_norm(T):
+    x = scaled_x(110 + T, T)
+    nw = testgen.make_x(111, 1)[0]
+    res = testgen.make_x(112, T)
+    y, ids, w, _ = run_prefill(1, x, nw=nw, res=res, xn_out=False)
+    y_ref, ids_or, w_or, gap = oracle_own_norm(x, host_layer(1), nw, res, ids)
+    parity.check_weights(ids, w, ids_or, w_or, gap)
+    print(parity.check_output(y, y_ref, f"prefill norm e2e T {T}"))

@@ -9,7 +9,9 @@ quantiser on the same x, the quantised h against the oracle's quantiser on
 the GPU's own h (read from the workspace through the documented diagnostic
 offsets).  The GPU's h before quantisation is compared with the oracle's
 within bf16 rounding, and the output with the oracle evaluated on the GPU's
-h, at the usual tolerance.  Inputs: seeded synthetic NVFP4 layers (weights
+h, at the usual tolerance (a decomposition).  End to end, the output is also
+compared with the oracle run from x alone (its own quantised x, h and
+quantised h) at the same tolerance, ids forced only for near-ties.  Inputs: seeded synthetic NVFP4 layers (weights
 N(0, 0.02) bf16 packed to NVFP4, x ~ N(0, 1) bf16)."""
 import numpy as np
 import pytest
@@ -126,3 +128,22 @@ def test_w4a4_tokens_are_independent():
                                dl.shared, o, ws, S=S)
         torch.cuda.synchronize()
         assert np.array_equal(parity.bf16_out_to_f64(o)[0], y[t]), t
+
+
+@pytest.mark.parametrize("name,B,seed", [("flint", 1, 5), ("flint", 8, 5), ("flint", 4, 6),
+                                         ("inkling2small", 3, 5), ("ragged", 5, 5)])
+def test_w4a4_end_to_end_against_the_oracles_own_h(name, B, seed):
+    """The W4A4 output against the fp64 oracle run from x alone: its own
+    quantised x, its own h, its own quantisation of h (no GPU value enters
+    it).  ids are forced to the GPU's only for a token whose oracle 6th/7th
+    score gap is below the near-tie threshold."""
+    host, x, y, ids, w, _ = run(name, seed, B)
+    y_or, ids_or, w_or, gap, _ = oracle.forward_w4a4(x, host)
+    for t in range(B):
+        if set(ids[t].tolist()) != set(ids_or[t].tolist()):
+            assert gap[t] < parity.NEAR_TIE, (t, gap[t])
+            print(f"token {t}: near-tie (gap {gap[t]:.2e}), ids forced")
+            y_or[t] = oracle.forward_w4a4(x[t:t + 1].copy(), host,
+                                          forced_ids=ids[t:t + 1].copy())[0][0]
+    parity.check_weights(ids, w, ids_or, w_or, gap)
+    print(parity.check_output(y, y_or, f"w4a4 e2e {name} B {B}"))

@@ -631,3 +631,140 @@ def test_w4a4_layer_override_and_token_independence():
     # an h overridden with zeros leaves no expert output
     y0 = oracle.forward_w4a4(x, L, h_in=np.zeros_like(h))[0]
     assert not y0.any()
+
+
+# ------------------------------------------------------- W4A4 layer composition
+# Pins of or_forward_w4a4 against numpy products of weights decoded from the
+# hand-written OCP tables: special cases where the activation quantiser is
+# exact reduce the W4A4 layer to the W4A16 one, and the quantiser (pinned
+# above) is otherwise used only as a step.  A slip in the composition (gate
+# and up fed the unquantised x, the shared expert fed x instead of its
+# quantisation, h quantised without its bf16 rounding, a routing weight
+# dropped or a slot out of order) fails one of them.
+HW, IW = 64, 32
+E4M3_EXACT = [0.25, 0.5, 1.0, 1.5, 2.0, 3.0, 8.0, 14.0, 40.0, 96.0]   # below 448, exact in E4M3
+GRID = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+
+
+def _exact_fp4_vector(rng, n):
+    """A vector the Four-Over-Six quantiser reproduces exactly: amax = 21 * 2^m
+    makes the global amax / 2688 = 2^(m - 7) a power of two, block 0 holds
+    that maximum (E4M3 scale 448), every block is E2M1 values times an E4M3
+    value times the global, with its maximum coded +-6 (scale exact, MAE 0,
+    which the max->4 candidate cannot beat).  Every element has at most six
+    significant bits, so it is exact in bf16."""
+    g = 2.0 ** (int(rng.integers(-3, 3)) - 7)
+    v = np.empty(n)
+    for b in range(n // 16):
+        S = 448.0 if b == 0 else float(rng.choice(E4M3_EXACT))
+        blk = rng.choice(GRID, 16) * rng.choice([-1.0, 1.0], 16)
+        blk[rng.integers(16)] = 6.0 * rng.choice([-1.0, 1.0])
+        v[16 * b:16 * b + 16] = blk * S * g
+    return v
+
+
+def _bf16_rne_np(v):
+    """fp64 -> nearest bf16 value, ties to even (numpy): 8 significant bits,
+    spacing 2^(e - 8) for v = m 2^e (m in [0.5, 1)); below the smallest
+    normal 2^-126 the spacing stays 2^-133 (subnormals, flushing to 0)."""
+    v = np.asarray(v, np.float64)
+    e = np.maximum(np.frexp(v)[1], -125)
+    return np.ldexp(np.rint(np.ldexp(v, 8 - e)), e - 8)
+
+
+def _e4m3_closed_form(b: int) -> float:
+    """OCP E4M3FN: sign bit 7, exponent bits 6-3 (bias 7), mantissa bits 2-0;
+    exponent 0 is subnormal (m / 8 * 2^-6); S.1111.111 is NaN."""
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    if e == 15 and m == 7:
+        return math.nan
+    v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def test_e4m3_closed_form_agrees_with_the_hand_written_table():
+    for b, v in load_table("e4m3_values.txt").items():
+        c = _e4m3_closed_form(b)
+        assert (math.isnan(v) and math.isnan(c)) or c == v, hex(b)
+
+
+def _decode_full(codes, scales, glob):
+    """W [N, K] from the hand-written E2M1 table and the E4M3 closed form."""
+    e2m1 = load_table("e2m1_values.txt")
+    t2 = np.array([e2m1[i] for i in range(16)])
+    t4 = np.array([_e4m3_closed_form(b) for b in range(256)])
+    nib = np.stack([codes & 15, codes >> 4], -1).reshape(codes.shape[0], -1)
+    return t2[nib] * np.repeat(t4[scales], 16, axis=1) * glob
+
+
+def _mats(X, e):
+    """Gate, up, down of expert e of a host NVFP4 set, decoded in the test."""
+    return (_decode_full(X.w13[e, 0], X.w13_scale[e, 0], float(X.glob[e, 0])),
+            _decode_full(X.w13[e, 1], X.w13_scale[e, 1], float(X.glob[e, 1])),
+            _decode_full(X.w2[e], X.w2_scale[e], float(X.glob[e, 2])))
+
+
+def _slots(L, ids_t):
+    """(expert set, index) of each h slot: routed ids ascending, then shared."""
+    return [(L.routed, int(e)) for e in sorted(ids_t.tolist())] + [(L.shared, 0)]
+
+
+def _silu_mul(g, u):
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def test_w4a4_h_equals_the_w4a16_h_when_x_is_on_the_fp4_grid():
+    L = tiny_layer(seed=11, H=HW, I=IW)
+    rng = np.random.default_rng(5)
+    xv = np.stack([_exact_fp4_vector(rng, HW) for _ in range(3)])
+    for t in range(3):                               # the quantiser reproduces x
+        np.testing.assert_array_equal(oracle.quant_fp4_46(xv[t].astype(np.float32))[3], xv[t])
+    x = f32_to_bf16_bits_exact(xv.astype(np.float32))
+    y, ids, w, gap, h = oracle.forward_w4a4(x, L)
+    assert np.array_equal(ids, oracle.forward_layer(x, L)[1])
+    for t in range(3):
+        for s, (X, e) in enumerate(_slots(L, ids[t])):
+            G, U, _ = _mats(X, e)
+            want = _bf16_rne_np(_silu_mul(G @ xv[t], U @ xv[t]))
+            np.testing.assert_array_equal(f64(h[t, s]), want)
+
+
+def test_w4a4_down_and_combine_reduce_to_numpy_when_h_is_on_the_fp4_grid():
+    L = tiny_layer(seed=12, H=HW, I=IW)
+    x = testgen.make_x(33, 3, HW)
+    rng = np.random.default_rng(6)
+    hv = np.stack([np.stack([_exact_fp4_vector(rng, IW) for _ in range(L.K + 1)])
+                   for _ in range(3)])
+    y, ids, w, gap, _ = oracle.forward_w4a4(x, L, h_in=f32_to_bf16_bits_exact(
+        hv.astype(np.float32)))
+    ids_p, w_p, _, _ = oracle.route(x, L.router, L.K)      # the plain layer's routing
+    np.testing.assert_array_equal(ids, ids_p)
+    for t in range(3):
+        wt = dict(zip(ids[t].tolist(), w[t].tolist()))
+        want = np.zeros(HW)
+        for s, (X, e) in enumerate(_slots(L, ids[t])):
+            D = _mats(X, e)[2]
+            want += (wt[e] if X is L.routed else 1.0) * (D @ hv[t, s])
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(sum(wt.values()), 1.0, rtol=1e-12)
+
+
+def test_w4a4_experts_read_the_quantised_x_and_the_bf16_h():
+    """General x: gate and up of every slot (the shared one too) read the
+    quantiser's x, h is SiLU(g) * u rounded to bf16, and the down GEMV reads
+    the quantiser's image of that bf16 h."""
+    L = tiny_layer(seed=13, H=HW, I=IW)
+    x = testgen.make_x(34, 2, HW)
+    y, ids, w, gap, h = oracle.forward_w4a4(x, L)
+    for t in range(2):
+        xq = oracle.quant_fp4_46(f64(x[t]).astype(np.float32))[3]
+        assert not np.array_equal(xq, f64(x[t]))     # the quantisation changes this x
+        wt = dict(zip(ids[t].tolist(), w[t].tolist()))
+        want = np.zeros(HW)
+        for s, (X, e) in enumerate(_slots(L, ids[t])):
+            G, U, D = _mats(X, e)
+            hb = _bf16_rne_np(_silu_mul(G @ xq, U @ xq))
+            np.testing.assert_array_equal(f64(h[t, s]), hb)
+            hq = oracle.quant_fp4_46(hb.astype(np.float32))[3]
+            want += (wt[e] if X is L.routed else 1.0) * (D @ hq)
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-14)
