@@ -196,6 +196,24 @@ moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32
                                     float* w_out, void* ws, size_t ws_bytes, void* stream,
                                     void* ev_start, void* ev_stop);
 
+/* moe_decode_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Flint's shape (NVFP4 or BF16), B =
+ * 1..8; other shapes and B > 8 return MOE_ERR_UNSUPPORTED (they need more
+ * than the library's own workspace holds).  The library keeps that
+ * workspace in a static device array of the decode workspace's size (about
+ * 1.2 MB; moe_workspace_bytes of Flint's decode shape), one per GPU, held
+ * until the process ends; the first call on a GPU looks its address up and
+ * zero-fills it with a kernel on `stream`.  The call allocates nothing.
+ * Every call on one GPU shares that array, which keeps the state of the last
+ * call: calls on one GPU must not overlap (same stream, or ordered by
+ * events); overlapping calls race and give wrong results.  Output, arguments
+ * and errors otherwise as moe_decode_forward, bit for bit. */
+moe_status moe_decode_forward_noalloc(const moe_shape* shape, const void* x, int32_t B,
+                                      const void* router_w, const moe_experts* routed,
+                                      const moe_experts* shared, void* out, int32_t* ids_out,
+                                      float* w_out, void* stream);
+
 /* Small-batch dense GEMV on packed NVFP4 weights, for the non-expert
  * projections and the dense MLP of the first two layers (Optimization
  * section, Fig. 2 change list: a dense GEMV on the packed weights; Model

@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_forward.restype = ctypes.c_int
         L.moe_decode_forward.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts), vp, vp,
                                          vp, vp, sz, vp]
+        L.moe_decode_forward_noalloc.restype = ctypes.c_int
+        L.moe_decode_forward_noalloc.argtypes = [P(Shape), vp, i32, vp, P(Experts), P(Experts),
+                                                 vp, vp, vp, vp]
         L.moe_nvfp4_gemv.restype = ctypes.c_int
         L.moe_nvfp4_gemv.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.moe_decode_forward_timed.restype = ctypes.c_int
@@ -174,6 +177,20 @@ def moe_decode_forward(x, router_w, routed, shared, out, ws, ids_out=None, w_out
                                   _ref(Sh), _ptr(out), _ptr(ids_out), _ptr(w_out),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_decode_forward")
+
+
+def moe_decode_forward_noalloc(x, router_w, routed, shared, out, ids_out=None, w_out=None,
+                               fmt=MOE_W_NVFP4, stream=None, S: Shape | None = None,
+                               B: int | None = None):
+    """moe_decode_forward on the library's own per-GPU workspace (no workspace
+    argument, no allocation); calls on one GPU must not overlap."""
+    S = S or shape(_fmt(fmt))
+    B = x.shape[0] if B is None else B
+    R, Sh = experts_struct(routed), experts_struct(shared)
+    st = lib().moe_decode_forward_noalloc(ctypes.byref(S), _ptr(x), B, _ptr(router_w),
+                                          ctypes.byref(R), _ref(Sh), _ptr(out), _ptr(ids_out),
+                                          _ptr(w_out), _stream(stream))
+    _check(st, "moe_decode_forward_noalloc")
 
 
 def moe_decode_forward_timed(x, router_w, routed, shared, out, ws, ev_start, ev_stop,

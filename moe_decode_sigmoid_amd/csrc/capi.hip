@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe_decode.h"
 #include "common.h"
 #include "launch.h"
@@ -162,6 +164,44 @@ bool split_path_forced() {
   return v && v[0] == '1';
 }
 
+// ------------------------------------------------ the allocation-free variant
+// The workspace of moe_decode_forward_noalloc: one per device (each GPU the
+// library runs on holds its own copy until the process ends), the size of the
+// Flint decode workspace.  In host code `scratch` is only a stand-in for the
+// symbol: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[moe::kDecodeWsBytes];
+
+__global__ __launch_bounds__(256) void k_zero_scratch(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices];   // the device address of `scratch`, per device
+
+// The current device's scratch address, looked up (and the array zero-filled
+// by a kernel on `st`, ahead of the call that needs it) on the first call on
+// that device.  nullptr on failure.
+uint8_t* scratch_for_current_device(hipStream_t st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    // the decode kernels' call counters must start from zero: a fill kernel
+    // (no memset node, so the first call may also be captured in a graph)
+    hipLaunchKernelGGL(k_zero_scratch, dim3(256), dim3(256), 0, st, static_cast<uint4*>(ptr),
+                       moe::kDecodeWsBytes / 16);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  }
+  return g_scratch_ptr[dev];
+}
+static_assert(moe::kDecodeWsBytes % 16 == 0, "scratch is cleared in 16-byte words");
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +281,35 @@ moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
                                        static_cast<const uint16_t*>(router_w), to_dev(routed),
                                        to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
                                        static_cast<uint8_t*>(ws), s);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_decode_forward_noalloc(const moe_shape* shape, const void* x, int32_t B,
+                                      const void* router_w, const moe_experts* routed,
+                                      const moe_experts* shared, void* out, int32_t* ids_out,
+                                      float* w_out, void* stream) {
+  moe_status st;
+  if ((st = check_shape(shape)) != MOE_OK) return st;
+  if (B > moe::kMaxB) return MOE_ERR_UNSUPPORTED;   // beyond what the scratch array holds
+  // the checks of moe_decode_forward; the workspace checks pass trivially (a
+  // 256-byte host stand-in: the device array lies in no caller's allocation)
+  alignas(256) static uint8_t ws_stand_in[256];
+  if ((st = check_forward(shape, x, B, router_w, routed, shared, out, ids_out, w_out,
+                          ws_stand_in, sizeof ws_stand_in, sizeof ws_stand_in, true)) != MOE_OK)
+    return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = scratch_for_current_device(s);
+  if (!ws) return MOE_ERR_HIP;
+  const bool fused = moe::fused_supported() && !split_path_forced();
+  const hipError_t e =
+      fused ? moe::launch_decode_fused(B, shape->wfmt, static_cast<const uint16_t*>(x),
+                                       static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                       to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                       ws, s)
+            : moe::launch_decode_split(B, shape->wfmt, static_cast<const uint16_t*>(x),
+                                       static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                       to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                       ws, s);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
