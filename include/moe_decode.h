@@ -202,7 +202,7 @@ moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32
  * 1..8; other shapes and B > 8 return MOE_ERR_UNSUPPORTED (they need more
  * than the library's own workspace holds).  The library keeps that
  * workspace in a static device array of the decode workspace's size (about
- * 1.2 MB; moe_workspace_bytes of Flint's decode shape), one per GPU, held
+ * 1.3 MB; moe_workspace_bytes of Flint's decode shape), one per GPU, held
  * until the process ends; the first call on a GPU looks its address up and
  * zero-fills it with a kernel on `stream`.  The call allocates nothing.
  * Every call on one GPU shares that array, which keeps the state of the last

@@ -100,7 +100,11 @@ constexpr size_t kSlotXOff = kFlagOff + (256 + 64 * kBankReps) * kFlagStride;
 // Everything below kDecodeWsBytes is the single-launch decode kernels'; the
 // epoch counters, h-ready counters and tagged slots keep their values from
 // call to call, so no other path writes below this offset.
-constexpr size_t kDecodeWsBytes = kSlotXOff + kSlotXRep * kXReps;
+// h as tagged 8-byte slots {two bf16 values, epoch}: [kMaxB * (kK + 1) pairs]
+// [kI / 2 slots] (the small-batch hand-over between the GEMVs).
+constexpr size_t kHSlots = kI / 2;
+constexpr size_t kSlotHOff = kSlotXOff + kSlotXRep * kXReps;
+constexpr size_t kDecodeWsBytes = kSlotHOff + 8 * kMaxB * (kK + 1) * kHSlots;
 constexpr size_t kGenBase = kDecodeWsBytes;
 
 // Workspace of the general path: logits f32 [kMaxB][E], the dispatch, h

@@ -70,6 +70,19 @@ constexpr int kRowsPerWg = kH / kFusedGrid; // 8 output rows per workgroup
 constexpr int kHBanks = 64;                 // h-ready counters, one 128-byte line each
 constexpr int kMaxRange = (kMaxB * kK * kI + kFusedGrid - 1) / kFusedGrid;  // routed rows per workgroup
 constexpr int kSpinLimit = 1 << 18;
+// Batches up to kHTagMaxB hand h over as epoch-tagged slots, which need no
+// wait for the stores' acknowledgement before counting in; larger batches
+// store plain bf16 h (half the bytes for every workgroup to copy) and count in
+// once the stores are acknowledged.  kHDirect: readers of tagged h poll the
+// slots directly instead of waiting for the counters first.
+#ifndef MOE_H_TAG_MAXB
+#define MOE_H_TAG_MAXB 1
+#endif
+#ifndef MOE_H_DIRECT
+#define MOE_H_DIRECT 1
+#endif
+constexpr int kHTagMaxB = MOE_H_TAG_MAXB;
+constexpr bool kHDirect = MOE_H_DIRECT != 0;
 
 // ------------------------------------------------------------------ row chunks
 // Weight loads through global-address-space pointers.  The stacked launch
@@ -560,6 +573,8 @@ __device__ __forceinline__ void decode_layer(
   DecodeCtl* ctl = reinterpret_cast<DecodeCtl*>(ws);
   uint64_t* lslots = reinterpret_cast<uint64_t*>(ws + kSlotLogitOff);
   uint64_t* xslots = reinterpret_cast<uint64_t*>(ws + kSlotXOff);
+  uint64_t* hslots = reinterpret_cast<uint64_t*>(ws + kSlotHOff);
+  constexpr bool kTagH = B <= kHTagMaxB;
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + kHOff);
 
   // x (bf16 [B][2048]) in steps A and B; the h pairs (bf16 [7 B][512]) in step C
@@ -743,10 +758,14 @@ __device__ __forceinline__ void decode_layer(
   // ---------------------------------------------------------------- step B
   // top-6 per token (wave t % 4 takes token t), repeated identically in every
   // workgroup; sigmoid scores of the chosen six renormalised to sum to 1
+  __shared__ float s_sl[kK];                  // B = 1: the six chosen logits, descending
+  __shared__ int s_si[kK];                    //        and their experts
   if constexpr (B == 1) {
     // one token: its six experts are the routed entries, each with one h
     // pair, so wave 0 orders them by id (rank by counting) and writes the
-    // entry tables itself, with no token masks and no barrier in between
+    // entry tables itself, with no token masks and no barrier in between.
+    // The routing weights are computed after the first gate/up loads have
+    // gone out (step C needs them, the loads do not).
     if (wave == 0) {
       float v[4];
       wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane, 64, epoch, v,
@@ -755,23 +774,16 @@ __device__ __forceinline__ void decode_layer(
       int my_id;
       float my_l;
       wave_top6(v, lane, my_id, my_l);
-      const float s = 1.0f / (1.0f + expf(-my_l));
-      float sum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kK; ++j) sum += readlane_f32(s, j);
+      trace_stamp(ws, 15);
       int rank = 0;
 #pragma unroll
       for (int j = 0; j < kK; ++j) rank += __builtin_amdgcn_readlane(my_id, j) < my_id ? 1 : 0;
       if (lane < kK) {
-        const float wgt = s / sum;
-        s_wfull[my_id][0] = wgt;
+        s_sl[lane] = my_l;
+        s_si[lane] = my_id;
         s_act[rank] = my_id;
         s_amask[rank] = 1u;
         s_pair0[rank] = rank;
-        if (g == 0) {
-          if (ids_out) ids_out[lane] = my_id;
-          if (w_out) w_out[lane] = wgt;
-        }
       }
       if (lane == 0) {
         s_nr = kK;
@@ -947,6 +959,18 @@ __device__ __forceinline__ void decode_layer(
 #pragma unroll
       for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
     }
+    if constexpr (B == 1) {
+      // the routing weights of the one token: sigmoid of the six logits in
+      // descending order, renormalised (the same sums as every other path)
+      if (wave == 0) {
+        const float l = s_sl[lane < kK ? lane : 0];
+        const float sc = 1.0f / (1.0f + expf(-l));
+        float sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kK; ++j) sum += readlane_f32(sc, j);
+        if (lane < kK) s_wfull[s_si[lane]][0] = sc / sum;
+      }
+    }
     if (gs_mine) s_gs[tid / 3][tid % 3] = gsv;
     __syncthreads();
     // this wave's row pairs T0 + wave + 4 j, j < nj; the loop runs while a
@@ -972,28 +996,67 @@ __device__ __forceinline__ void decode_layer(
   // routed (pair0[a] + rank of t in the entry's tokens, row), consecutive
   // threads on consecutive rows
   __syncthreads();
-  if (tid < 2 * B) {
-    const int r = tid / B, t = tid % B;
-    store_coherent_u16(hbuf + (size_t)(kK * B + t) * kI + 2 * g + r, f32_to_bf16_rne(s_hsh[r][t]));
+  trace_stamp(ws, 13);
+  // Once every 65536 epochs every h slot not written by this call is stamped
+  // (workgroup g: slot g of each such pair), as the logit slots are, so that
+  // no slot is ever 2^32 epochs old.
+  if ((epoch & 0xFFFFu) == 0u) {
+    for (int p = (kTagH ? kPairs : 0) + tid; p < kMaxB * (kK + 1); p += kFusedThreads)
+      put_slot_u32(hslots + (size_t)p * kHSlots + g, 0u, epoch);
   }
-  {
-    const int nloc = T1 - T0;
-    for (int idx = tid; idx < nloc * B; idx += kFusedThreads) {
-      const int t = idx / nloc, i = idx - t * nloc;
-      const int s = T0 + i, a = s / kI;
+  if constexpr (kTagH) {
+    // h as tagged slots: slot k of a pair holds its rows 2 k, 2 k + 1 (a
+    // workgroup's rows come in pairs: its range starts and ends on even rows)
+    auto pack = [](float a, float b) {
+      return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+    };
+    if (tid < B)
+      put_slot_u32(hslots + (size_t)(kK * B + tid) * kHSlots + g,
+                   pack(s_hsh[0][tid], s_hsh[1][tid]), epoch);
+    const int nloc2 = (T1 - T0) >> 1;
+    for (int idx = tid; idx < nloc2 * B; idx += kFusedThreads) {
+      const int t = idx / nloc2, j = idx - t * nloc2;
+      const int s = T0 + 2 * j, a = s / kI;
       const unsigned m = s_amask[a];
       if ((m >> t) & 1u)
-        store_coherent_u16(hbuf + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kI + (s % kI),
-                           f32_to_bf16_rne(s_hout[i][t]));
+        put_slot_u32(hslots + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kHSlots +
+                         (s % kI) / 2,
+                     pack(s_hout[2 * j][t], s_hout[2 * j + 1][t]), epoch);
     }
+    trace_stamp(ws, 14);
+    // count in at once: the counters only tell the readers when to start
+    // copying, each slot's tag tells them whether it has arrived (the
+    // counters advance in every mode: a later call of another batch size
+    // waits on them)
+    __syncthreads();
+    if (tid < kBankReps)
+      __hip_atomic_fetch_add(hready_bank(ws, tid, g % kHBanks), 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    if (tid < 2 * B) {
+      const int r = tid / B, t = tid % B;
+      store_coherent_u16(hbuf + (size_t)(kK * B + t) * kI + 2 * g + r, f32_to_bf16_rne(s_hsh[r][t]));
+    }
+    {
+      const int nloc = T1 - T0;
+      for (int idx = tid; idx < nloc * B; idx += kFusedThreads) {
+        const int t = idx / nloc, i = idx - t * nloc;
+        const int s = T0 + i, a = s / kI;
+        const unsigned m = s_amask[a];
+        if ((m >> t) & 1u)
+          store_coherent_u16(hbuf + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kI + (s % kI),
+                             f32_to_bf16_rne(s_hout[i][t]));
+      }
+    }
+    // publish: wait for this workgroup's h stores, then count in on bank g % 64
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    trace_stamp(ws, 14);
+    __syncthreads();
+    if (tid < kBankReps)
+      __hip_atomic_fetch_add(hready_bank(ws, tid, g % kHBanks), 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
-  // publish: wait for this workgroup's h stores, then count in on bank g % 64
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid < kBankReps)
-    __hip_atomic_fetch_add(hready_bank(ws, tid, g % kHBanks), 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
   trace_stamp(ws, 8);
 
   // ---------------------------------------------------------------- step C
@@ -1011,8 +1074,9 @@ __device__ __forceinline__ void decode_layer(
 #pragma unroll
     for (int q = 0; q < kDepthC; ++q) load_entry(dbuf[q], wsel + 4 * q);
   }
-  if (wave != 3) prefetch();
-  if (wave == 3) {
+  constexpr bool kPollCounters = !(kTagH && kHDirect);
+  if (!kPollCounters || wave != 3) prefetch();
+  if (kPollCounters && wave == 3) {
     const uint32_t want = (uint32_t)(kFusedGrid / kHBanks) * epoch;
     for (int spin = 0;; ++spin) {
       const uint32_t v = load_flag(hready_bank(ws, g % kBankReps, lane));
@@ -1030,6 +1094,17 @@ __device__ __forceinline__ void decode_layer(
   __syncthreads();
   trace_stamp(ws, 9);
 
+  if constexpr (kTagH) {
+    // all 7 B h pairs into LDS: thread tid reads slot tid of every pair,
+    // polling until each carries this call's epoch, and puts its two values
+    // where load_h expects them (uint4 c of a pair at 16 (c % 4) + c / 4)
+    uint32_t hv[kPairs];
+    wait_slots_u32<kPairs>(hslots + tid, (int)kHSlots, epoch, hv, &ctl->err, kErrHReady);
+    uint32_t* s_h32 = reinterpret_cast<uint32_t*>(s_xh);
+    const int c = tid >> 2, wd = tid & 3;
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) s_h32[4 * (p * 64 + 16 * (c & 3) + (c >> 2)) + wd] = hv[p];
+  } else {
   // all 7 B h pairs of the call into LDS: 16-byte device-coherent loads
   // (buffer loads with the device-scope bit), 8 in flight per thread
   {
@@ -1053,6 +1128,7 @@ __device__ __forceinline__ void decode_layer(
         }
       }
     }
+  }
   }
   __syncthreads();
   trace_stamp(ws, 10);
@@ -1176,8 +1252,14 @@ __device__ __forceinline__ void decode_layer(
                    epoch);
     }
   }
+  if constexpr (B == 1) {
+    // the routing of the call, once nothing of the layer is loaded any more
+    if (g == 0 && tid < kK) {
+      if (ids_out) ids_out[tid] = s_si[tid];
+      if (w_out) w_out[tid] = s_wfull[s_si[tid]][0];
+    }
+  }
   trace_stamp(ws, 12);
-
   trace_flush(ws);
 }
 
