@@ -83,6 +83,14 @@ constexpr int kSpinLimit = 1 << 18;
 #endif
 constexpr int kHTagMaxB = MOE_H_TAG_MAXB;
 constexpr bool kHDirect = MOE_H_DIRECT != 0;
+// Gate/up ranges at B > 1: the row pairs are cut into 256 ranges of equal
+// weight, a row pair of an entry with n tokens weighing kGuWeight + n (its
+// bytes, then one share of arithmetic per token); 0 cuts by row pairs alone.
+#ifndef MOE_GU_WEIGHT
+#define MOE_GU_WEIGHT 1
+#endif
+constexpr int kGuWeight = MOE_GU_WEIGHT;
+static_assert(kGuWeight >= 0 && kGuWeight + kMaxB < 16, "a row pair's weight fits 4 bits");
 
 // ------------------------------------------------------------------ row chunks
 // Weight loads through global-address-space pointers.  The stacked launch
@@ -338,66 +346,53 @@ __device__ __forceinline__ void cmpx(int (&k)[4], int (&q)[4], int i) {
 // selects ("Day-0 Support for Flint on vLLM", Model architecture).  Each lane
 // first sorts its 4 logits (odd-even transposition, stable); each round takes
 // the maximum of the lane heads and pops it.  Lane j < 6 returns choice j.
-__device__ __forceinline__ void wave_top6(const float (&v)[4], int lane, int& my_id, float& my_l) {
-  int k[4], q[4];
+// N tokens at once (a wave with two tokens): their rounds are independent
+// chains, interleaved in one loop so that each hides the other's latency.
+template <int N>
+__device__ __forceinline__ void wave_top6(const float (&v)[N][4], int lane, int (&my_id)[N],
+                                          float (&my_l)[N]) {
+  int k[N][4], q[N][4], myk[N];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    k[i] = logit_key(v[i]);
-    q[i] = i;
+  for (int n = 0; n < N; ++n) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k[n][i] = logit_key(v[n][i]);
+      q[n][i] = i;
+    }
+    cmpx(k[n], q[n], 0); cmpx(k[n], q[n], 2); cmpx(k[n], q[n], 1);
+    cmpx(k[n], q[n], 0); cmpx(k[n], q[n], 2); cmpx(k[n], q[n], 1);
+    myk[n] = 0;
+    my_id[n] = 0;
   }
-  cmpx(k, q, 0); cmpx(k, q, 2); cmpx(k, q, 1);
-  cmpx(k, q, 0); cmpx(k, q, 2); cmpx(k, q, 1);
-  int myk = 0;
-  my_id = 0;
 #pragma unroll
   for (int j = 0; j < kK; ++j) {
-    const int m = wave_max_i32(k[0]);
-    const uint64_t bal = __ballot(k[0] == m);
-    int sel;
-    if (__popcll(bal) == 1) {
-      sel = __builtin_ctzll(bal);
-    } else {               // equal heads: the lowest expert id among them
-      sel = wave_min_i32(k[0] == m ? 64 * q[0] + lane : 0x7FFFFFFF) & 63;
-    }
-    const int e = 64 * __builtin_amdgcn_readlane(q[0], sel) + sel;
-    if (lane == j) {
-      my_id = e;
-      myk = m;
-    }
-    if (lane == sel) {
-      k[0] = k[1]; k[1] = k[2]; k[2] = k[3]; k[3] = (int)0x80000000;
-      q[0] = q[1]; q[1] = q[2]; q[2] = q[3];
-    }
-  }
-  my_l = key_logit(myk);
-}
-
-// One gate/up row pair of an entry for the tokens in `mask`; the wave's lanes
-// cover the 2048 columns; lane 0 puts h = SiLU(g) * u of token t in hdst[t]
-// (LDS: the workgroup writes its h to the workspace in one go, so that no
-// store sits in front of the next weight loads in the wave's memory queue).
-template <int B, int FMT>
-__device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk<FMT>& cu, float sg,
-                                               float su, unsigned mask, const uint4* s_x,
-                                               const uint32_t (&x0)[16], int lane, float* hdst) {
+    int m[N], sel[N];
 #pragma unroll
-  for (int t = 0; t < B; ++t) {
-    if (!((mask >> t) & 1u)) continue;
-    uint32_t xw[16];
-    if constexpr (B == 1) {
+    for (int n = 0; n < N; ++n) m[n] = wave_max_i32(k[n][0]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xw[i] = x0[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = s_x[t * (kH / 8) + 4 * lane + i];
-        xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+    for (int n = 0; n < N; ++n) {
+      const uint64_t bal = __ballot(k[n][0] == m[n]);
+      if (__popcll(bal) == 1) {
+        sel[n] = __builtin_ctzll(bal);
+      } else {             // equal heads: the lowest expert id among them
+        sel[n] = wave_min_i32(k[n][0] == m[n] ? 64 * q[n][0] + lane : 0x7FFFFFFF) & 63;
       }
     }
-    const float g = wave_sum(cg.dot_x(xw)) * sg;
-    const float u = wave_sum(cu.dot_x(xw)) * su;
-    if (lane == 0) hdst[t] = silu_mul(g, u);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int e = 64 * __builtin_amdgcn_readlane(q[n][0], sel[n]) + sel[n];
+      if (lane == j) {
+        my_id[n] = e;
+        myk[n] = m[n];
+      }
+      if (lane == sel[n]) {
+        k[n][0] = k[n][1]; k[n][1] = k[n][2]; k[n][2] = k[n][3]; k[n][3] = (int)0x80000000;
+        q[n][0] = q[n][1]; q[n][1] = q[n][2]; q[n][2] = q[n][3];
+      }
+    }
   }
+#pragma unroll
+  for (int n = 0; n < N; ++n) my_l[n] = key_logit(myk[n]);
 }
 
 // 32-lane and 16-lane half swaps of gfx950 (v_permlane32_swap: a keeps lanes
@@ -439,6 +434,44 @@ __device__ __forceinline__ float wave_sum8(const float (&v)[8], int lane) {
   z += dpp_f32<0x4E>(z);
   z += dpp_f32<0xB1>(z);
   return z;
+}
+
+// One gate/up row pair of an entry for the wave's tokens in `mask` (at most
+// four: the tokens of parity `par`, token t in slot t / 2); the wave's lanes
+// cover the 2048 columns.  The gate and up partial sums of every token are
+// reduced together (wave_sum8: value j's total in lanes 8 j .. 8 j + 7, the
+// same tree for every slot, so a token's h does not depend on its slot), and
+// lane 16 i puts h = SiLU(g) * u of slot i's token t in hdst[t] (LDS: the
+// workgroup writes its h to the workspace in one go, so that no store sits in
+// front of the next weight loads in the wave's memory queue).
+template <int B, int FMT>
+__device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk<FMT>& cu, float sg,
+                                               float su, unsigned mask, int par, const uint4* s_x,
+                                               const uint32_t (&x0)[16], int lane, float* hdst) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < B; ++t) {
+    if (!((mask >> t) & 1u)) continue;
+    uint32_t xw[16];
+    if constexpr (B == 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xw[i] = x0[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u4 = s_x[t * (kH / 8) + 4 * lane + i];
+        xw[4 * i] = u4.x; xw[4 * i + 1] = u4.y; xw[4 * i + 2] = u4.z; xw[4 * i + 3] = u4.w;
+      }
+    }
+    v[2 * (t >> 1)] = cg.dot_x(xw);
+    v[2 * (t >> 1) + 1] = cu.dot_x(xw);
+  }
+  const float z = wave_sum8(v, lane);
+  const float zu = dpp_f32<0x128>(z);
+  const int t = 2 * (lane >> 4) + par;
+  if ((lane & 15) == 0 && t < B && ((mask >> t) & 1u)) hdst[t] = silu_mul(z * sg, zu * su);
 }
 
 // 32 consecutive bf16 h values (chunk c16, as 16 packed pairs) of pair p
@@ -561,7 +594,10 @@ __device__ __forceinline__ void decode_layer(
   constexpr bool kPfEarly = PF != 0 && kPrefetchNext<B, FMT>;
   constexpr bool kPfLate = PF != 0 && !kPrefetchNext<B, FMT>;
   // gate/up row pairs per batch (at B = 1 a wave has exactly 3: 12 per workgroup)
-  constexpr int kTB = FMT == FMT_NVFP4 ? 3 : 2;
+#ifndef MOE_GU_TB
+#define MOE_GU_TB 3
+#endif
+  constexpr int kTB = FMT == FMT_NVFP4 ? (B == 1 ? 3 : MOE_GU_TB) : 2;
   constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
   // batch 1 issues its routed down rows after publishing h instead of behind
   // the gate/up rows: the gate/up burst then carries only gate/up rows
@@ -589,6 +625,7 @@ __device__ __forceinline__ void decode_layer(
   __shared__ int s_pair0[kMaxActive];                // first h pair of each entry
   __shared__ float s_gs[kMaxActive][3];              // tensor scales of each routed entry
   __shared__ int s_nr;
+  __shared__ int s_t01[2];                           // weighted gate/up range (B > 1)
   __shared__ uint32_t s_epoch;
   __shared__ float s_hsh[2][kMaxB];                  // this workgroup's shared-expert h
   __shared__ float s_hout[kMaxRange][kMaxB];         // its routed h, by row of its range
@@ -751,7 +788,7 @@ __device__ __forceinline__ void decode_layer(
   }
   trace_stamp(ws, 2);
   if (smask)
-    gateup_compute<B, FMT>(pre.scg, pre.scu, sh_sg, sh_su, smask, s_x, x0, lane,
+    gateup_compute<B, FMT>(pre.scg, pre.scu, sh_sg, sh_su, smask, wave >> 1, s_x, x0, lane,
                            &s_hsh[wave & 1][0]);
   trace_stamp(ws, 3);
 
@@ -767,13 +804,15 @@ __device__ __forceinline__ void decode_layer(
     // The routing weights are computed after the first gate/up loads have
     // gone out (step C needs them, the loads do not).
     if (wave == 0) {
-      float v[4];
-      wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane, 64, epoch, v,
+      float v[1][4];
+      wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane, 64, epoch, v[0],
                     &ctl->err);
       trace_stamp(ws, 4);
-      int my_id;
-      float my_l;
-      wave_top6(v, lane, my_id, my_l);
+      int my_ids[1];
+      float my_ls[1];
+      wave_top6<1>(v, lane, my_ids, my_ls);
+      const int my_id = my_ids[0];
+      const float my_l = my_ls[0];
       trace_stamp(ws, 15);
       int rank = 0;
 #pragma unroll
@@ -794,14 +833,8 @@ __device__ __forceinline__ void decode_layer(
     }
     trace_stamp(ws, 5);
   } else {
-  for (int t = wave; t < B; t += 4) {
-    float v[4];
-    wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + t * kE + lane, 64, epoch, v,
-                  &ctl->err);
-    trace_stamp(ws, 4);
-    int my_id;
-    float my_l;
-    wave_top6(v, lane, my_id, my_l);
+  // token t's choices: sigmoid scores of the six renormalised to sum to 1
+  auto finish = [&](int t, int my_id, float my_l) __attribute__((always_inline)) {
     const float s = 1.0f / (1.0f + expf(-my_l));
     float sum = 0.0f;
 #pragma unroll
@@ -815,6 +848,26 @@ __device__ __forceinline__ void decode_layer(
         if (w_out) w_out[t * kK + lane] = wgt;
       }
     }
+  };
+  const uint64_t* lrep = lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane;
+  if (wave + 4 < B) {          // two tokens, wave and wave + 4: selected together
+    float v[2][4];
+    wait_slots<4>(lrep + wave * kE, 64, epoch, v[0], &ctl->err);
+    wait_slots<4>(lrep + (wave + 4) * kE, 64, epoch, v[1], &ctl->err);
+    trace_stamp(ws, 4);
+    int my_id[2];
+    float my_l[2];
+    wave_top6<2>(v, lane, my_id, my_l);
+    finish(wave, my_id[0], my_l[0]);
+    finish(wave + 4, my_id[1], my_l[1]);
+  } else if (wave < B) {
+    float v[1][4];
+    wait_slots<4>(lrep + wave * kE, 64, epoch, v[0], &ctl->err);
+    trace_stamp(ws, 4);
+    int my_id[1];
+    float my_l[1];
+    wave_top6<1>(v, lane, my_id, my_l);
+    finish(wave, my_id[0], my_l[0]);
   }
   trace_stamp(ws, 5);
   __syncthreads();
@@ -851,6 +904,35 @@ __device__ __forceinline__ void decode_layer(
       s_amask[base] = (1u << B) - 1u;
       s_pair0[base] = kK * B;
     }
+    if constexpr (kGuWeight > 0) {
+      // this workgroup's range [T0, T1) of the nr * 512 row pairs: entry a
+      // weighs 512 (kGuWeight + n_a); the cuts at g / 256 and (g + 1) / 256
+      // of the total weight, rounded down to an even row
+      const int wr = lane < base ? kGuWeight + cnt : 0;      // weight per row pair (< 16)
+      int excl_r = 0;                                         // weight of the entries before
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint64_t bb = __ballot((wr >> b) & 1);
+        excl_r += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u)) << b;
+      }
+      const int tot = __builtin_amdgcn_readlane(excl_r + wr, 63) * kI;
+      auto cut = [&](int gg) -> int {
+        if (gg >= kFusedGrid) return base * kI;
+        const int tg = (int)(((long long)gg * tot) >> 8);     // weight before the cut
+        const int excl_w = excl_r * kI;
+        const uint64_t bal = __ballot(lane < base && tg >= excl_w && tg < excl_w + wr * kI);
+        if (!bal) return base * kI;
+        const int a = (int)__builtin_ctzll(bal);
+        const int ew = __builtin_amdgcn_readlane(excl_w, a), aw = __builtin_amdgcn_readlane(wr, a);
+        return (a * kI + (tg - ew) / aw) & ~1;
+      };
+      const int c0 = cut(g), c1 = cut(g + 1);
+      if (lane == 0) {
+        s_t01[0] = c0;
+        s_t01[1] = c1;
+      }
+    }
   }
   }
   __syncthreads();
@@ -861,7 +943,9 @@ __device__ __forceinline__ void decode_layer(
   // ranges, one per workgroup; wave w takes T0 + w, T0 + w + 4, ... in
   // batches of kTB, the next batch in flight while one computes
   const int T = nr * kI;
-  const int T0 = (int)(((long long)g * T) >> 8), T1 = (int)(((long long)(g + 1) * T) >> 8);
+  const bool weighted = B > 1 && kGuWeight > 0;
+  const int T0 = weighted ? s_t01[0] : (int)(((long long)g * T) >> 8);
+  const int T1 = weighted ? s_t01[1] : (int)(((long long)(g + 1) * T) >> 8);
   // step-C work of this wave: routed entries a = wsel + 4 k (and the shared
   // expert's tokens wave, wave + 4); the first kDepthC entries' down rows are
   // fetched behind the first gate/up batch
