@@ -282,6 +282,47 @@ __device__ __forceinline__ float wave_max(float v) {
                fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
+// 32-lane and 16-lane half swaps of gfx950 (v_permlane32_swap: a keeps lanes
+// 0-31 and takes b's 0-31 as its 32-63, b gets a's 32-63 and its own 32-63;
+// v_permlane16_swap does the same within each 32-lane half).
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                  __builtin_bit_cast(unsigned, b), false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                  __builtin_bit_cast(unsigned, b), false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Wave totals of 8 per-lane values at once: value j's sum over the 64 lanes
+// ends in lanes 8 j .. 8 j + 7 (halving exchanges across 32 and 16 lanes,
+// then within rows: rotate by 8, half-row mirror, quad swaps).
+__device__ __forceinline__ float wave_sum8(const float (&v)[8], int lane) {
+  float w[4], u[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float a = v[j], b = v[4 + j];
+    swap32(a, b);
+    w[j] = a + b;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float a = w[j], b = w[2 + j];
+    swap16(a, b);
+    u[j] = a + b;
+  }
+  const bool hi = (lane & 8) != 0;
+  float z = (hi ? u[1] : u[0]) + dpp_f32<0x128>(hi ? u[0] : u[1]);
+  z += dpp_f32<0x141>(z);
+  z += dpp_f32<0x4E>(z);
+  z += dpp_f32<0xB1>(z);
+  return z;
+}
+
 // Top-k of 256 scores held 4 per lane (expert e = lane + 64 q in v[q]) under
 // the total order (value descending, index ascending).  Each round takes the
 // wave maximum, then the lowest index holding it (q-major ballots: indices of

@@ -20,41 +20,6 @@ namespace moe {
 
 constexpr int kGvThreads = 256;
 
-__device__ __forceinline__ void gv_swap32(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
-                                                  __builtin_bit_cast(unsigned, b), false, false);
-  a = __builtin_bit_cast(float, (unsigned)r[0]);
-  b = __builtin_bit_cast(float, (unsigned)r[1]);
-}
-__device__ __forceinline__ void gv_swap16(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
-                                                  __builtin_bit_cast(unsigned, b), false, false);
-  a = __builtin_bit_cast(float, (unsigned)r[0]);
-  b = __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-// Wave totals of 8 per-lane values: value j ends in lanes 8 j .. 8 j + 7.
-__device__ __forceinline__ float gv_sum8(const float (&v)[8], int lane) {
-  float w[4], u[2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float a = v[j], b = v[4 + j];
-    gv_swap32(a, b);
-    w[j] = a + b;
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    float a = w[j], b = w[2 + j];
-    gv_swap16(a, b);
-    u[j] = a + b;
-  }
-  const bool hi = (lane & 8) != 0;
-  float z = (hi ? u[1] : u[0]) + dpp_f32<0x128>(hi ? u[0] : u[1]);
-  z += dpp_f32<0x141>(z);
-  z += dpp_f32<0x4E>(z);
-  z += dpp_f32<0xB1>(z);
-  return z;
-}
 
 // sum over one 32-element chunk of w * x (x as 16 packed bf16 pairs), before
 // the tensor scale: two 16-element blocks, each times its E4M3 scale
@@ -154,7 +119,7 @@ __global__ __launch_bounds__(kGvThreads) void k_nvfp4_gemv(const uint16_t* __res
       const int pj = p0 + j;
       v[j] = pj < kPairs ? acc[pj % RW][pj / RW < B ? pj / RW : 0] : 0.0f;
     }
-    const float z = gv_sum8(v, lane);
+    const float z = wave_sum8(v, lane);
     const int pj = p0 + (lane >> 3), q = pj % RW, t = pj / RW;
     if ((lane & 7) == 0 && pj < kPairs && r0 + q < N)
       y[(size_t)t * N + r0 + q] = f32_to_bf16_rne(z * gl);

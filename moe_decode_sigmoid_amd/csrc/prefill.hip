@@ -23,15 +23,15 @@
 //   P6 combine      y[t] = sum over the token's six routed rows (ascending
 //      expert id) + its shared row, fp32, rounded once to bf16.
 //
-// GEMM tiles are 128 x 256 with four waves of 128 x 64 each (8 MFMA blocks
-// per wave, so LDS serves ~380 bytes per MFMA); K advances 32 per stage with
-// two LDS buffers (61 KB, so two workgroups share a CU and one's MFMAs run
-// while the other decodes weights or waits at a barrier), and the global
-// loads of the next kRing stages are held in registers so the HBM / gather
-// latency of one stage hides behind kRing stages of MFMA work.  The router
-// GEMM keeps K = 64 per stage.  Work items are mapped so that the column
-// slices of one item run on one XCD (workgroup b lands on XCD b % 8) and
-// share its L2.
+// GEMM 1 (and GEMM 2 of bf16 experts) tiles are 128 x 256: eight waves of
+// 64 x 64 (2 x 2 MFMA blocks each), A and B staged in LDS as bf16 with K = 64
+// per stage in two LDS buffers (110 KB, one workgroup per CU), NVFP4 decoded
+// to bf16 as it is written to LDS; the global loads of the next kRingDepth
+// stages are held in registers, so the HBM / gather latency of one stage
+// hides behind the MFMA work of the others.  GEMM 2 of NVFP4 experts keeps
+// the weights in registers instead (see its section).  The router GEMM keeps
+// K = 64 per stage.  Work items are mapped so that the column slices of one
+// item run on one XCD (workgroup b lands on XCD b % 8) and share its L2.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  Lane l supplies A[row l%32][k 8(l/32)..+7]
 // and B[k 8(l/32)..+7][col l%32]; result element i of lane l is
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(kGThreads1, 1) void k_prefill_gateup(const uint16_t
     }
 }
 
-// ------------------------------------------------------------------ P5 GEMM 2
+// ------------------------------------------------------------------ P5 GEMM 2, bf16 weights
 // Work item (expert e, row m0) x column slice n (256 of the 2048 outputs):
 // partial[row][col] = w_row * global * (h_row . D_e[col]) as fp16.  512
 // threads as 2 x 4 waves, like GEMM 1.
@@ -637,6 +637,184 @@ __global__ __launch_bounds__(kGThreads2, 1) void k_prefill_down(int T, ExpertsDe
         for (int j = 0; j < Acc::NB; ++j)
           part[(size_t)(rbase + r) * kH + kGBN * n + Acc::col_of(wave, lane, j)] =
               (f16)(acc.c[i][j][k] * wr);
+      }
+    }
+}
+
+// ------------------------------------------------------------------ P5 GEMM 2, NVFP4 weights in registers
+// The down GEMM of NVFP4 experts takes the weight operand straight from
+// memory into the MFMA operand registers (no LDS for it): only the gathered
+// h rows go through LDS.  At K = 512 the LDS-tiled form spends a large share
+// of its time filling and draining the weight tiles; here each weight byte
+// is loaded once, by the wave that multiplies it.  A workgroup is 8 waves (two per SIMD, so one's matrix
+// instructions run while the other waits); each wave owns a 128 x 64 tile
+// of the 128-row item, i.e. 4 x 2 blocks of 32 x 32, so an A fragment read
+// from LDS feeds two products and a dequantised weight fragment four.
+//
+// Weight fragment of v_mfma_f32_32x32x16_bf16: lane l supplies B[k][n] for
+// n = l % 32 and k = 8 (l / 32) .. + 7 of the 16-deep k-step.  A weight row
+// (output column n) keeps K contiguous, so a 64-deep stage of a row is 32
+// code bytes (dwords d = 0..7, dword d holding k 8 d .. 8 d + 7): the lower
+// half-wave needs dwords 0, 2, 4, 6 (one per k-step), the upper half 1, 3,
+// 5, 7.  Lane l loads bytes 16 (l / 32) .. + 15 of its row's stage (dwords
+// 0-3 low, 4-7 high) and two 32-lane swaps hand each half its dwords.  Each
+// k-step lies inside one 16-element block, so one E4M3 scale (byte ks of the
+// stage's scale word) applies to the whole fragment; e2m1 * e4m3 is exact in
+// bf16, so the dequantised operand is exact.
+constexpr int kW2BK = 64;                // K per pipeline stage
+constexpr int kW2Waves = 8;              // waves per workgroup (two per SIMD)
+constexpr int kW2Threads = 64 * kW2Waves;
+constexpr int kW2N = 64 * kW2Waves;      // weight rows (output columns) per workgroup
+constexpr int kW2Slices2 = kH / kW2N;    // column slices of the down GEMM
+constexpr int kW2Ring = 2;               // stages of global loads in flight
+constexpr int kW2TPR = kW2Threads / kGBM;   // threads per A row
+constexpr int kW2EA = kW2BK / kW2TPR;       // A elements per thread per stage
+
+// One stage of a thread's global loads: 16 activation elements of its A row
+// share, and the lane's 16 code bytes and the stage's four block scales of
+// each of its two weight rows.
+struct W2Slot {
+  uint4 a[kW2EA / 8];
+  uint4 c[2];
+  uint32_t s[2];
+};
+// The weight words of the stage being multiplied, after the exchange: d[j][ks]
+// is the dword of row j for k-step ks of this lane's half.
+struct W2Cur {
+  uint32_t d[2][4];
+  uint32_t s[2];
+};
+
+__device__ __forceinline__ void w2_take(const W2Slot& sl, W2Cur& cur) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float r0 = __builtin_bit_cast(float, sl.c[j].x), r1 = __builtin_bit_cast(float, sl.c[j].y);
+    float r2 = __builtin_bit_cast(float, sl.c[j].z), r3 = __builtin_bit_cast(float, sl.c[j].w);
+    swap32(r0, r1);   // r0: dword 0 (low half) / 1 (high half); r1: 4 / 5
+    swap32(r2, r3);   // r2: dword 2 / 3;                        r3: 6 / 7
+    cur.d[j][0] = __builtin_bit_cast(uint32_t, r0);
+    cur.d[j][1] = __builtin_bit_cast(uint32_t, r2);
+    cur.d[j][2] = __builtin_bit_cast(uint32_t, r1);
+    cur.d[j][3] = __builtin_bit_cast(uint32_t, r3);
+    cur.s[j] = sl.s[j];
+  }
+}
+
+// Stage kt of a lane's two weight rows (wrow[j]: the row's first code byte;
+// wsc[j]: its first scale byte).
+__device__ __forceinline__ void w2_load_b(W2Slot& sl, const uint8_t* const (&wrow)[2],
+                                          const uint8_t* const (&wsc)[2], int kt, int half) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    sl.c[j] = *reinterpret_cast<const uint4*>(wrow[j] + (size_t)kt * (kW2BK / 2) + 16 * half);
+    sl.s[j] = *reinterpret_cast<const uint32_t*>(wsc[j] + (size_t)kt * (kW2BK / 16));
+  }
+}
+
+// The wave's 128 x 64 accumulator (4 row blocks x 2 column blocks).
+struct W2Acc {
+  f32x16 c[4][2];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) c[i][j][k] = 0.0f;
+  }
+  // one 64-deep stage: A from LDS (rows of the item, pitch LR), the weight
+  // fragments dequantised from cur one k-step at a time
+  template <int LR>
+  __device__ __forceinline__ void mma(const __bf16* sA, const W2Cur& cur, int lane) {
+    const int r = lane & 31, kh = (lane >> 5) * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(sA + (32 * i + r) * LR + 16 * ks + kh);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = __builtin_bit_cast(bf16x8, dequant8(cur.d[j][ks], e4m3_sel(cur.s[j], ks)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], c[i][j], 0, 0, 0);
+    }
+  }
+  // row (within the item) of accumulator element k of row block i
+  __device__ __forceinline__ static int row_of(int lane, int i, int k) {
+    return 32 * i + (k % 4) + 8 * (k / 4) + 4 * (lane >> 5);
+  }
+};
+
+// P5: work item x slice n: output columns [512 n, 512 n + 512); wave w owns
+// columns 512 n + 64 w + 32 j + l % 32 (j = 0, 1); partial[row][col] =
+// w_row * global * (h_row . D_e[col]) as fp16.
+__global__ __launch_bounds__(kW2Threads, 1) void k_prefill_down_w(int T, ExpertsDev routed,
+                                                                  ExpertsDev shared,
+                                                                  uint8_t* __restrict__ ws) {
+  constexpr int LR = kW2BK + kLdsPad;
+  const PrefillLayout L = prefill_layout(T);
+  int item, n;
+  item_slice<kW2Slices2>(blockIdx.x, item, n);
+  if (item >= wsp<int>(ws, L.nitems)[0]) return;
+  const int2 it = wsp<int2>(ws, L.items)[item];
+  const int e = it.x, m0 = it.y;
+  const int rows = min(kGBM, wsp<int>(ws, L.cnt)[e] - m0);
+  const int rbase = wsp<int>(ws, L.off)[e] + m0;
+  const ExpertsDev X = e < kE ? routed : shared;
+  const size_t ee = e < kE ? (size_t)e : 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+
+  __shared__ __align__(16) __bf16 sA[2][kGBM * LR];
+  const uint16_t* hsrc = wsp<uint16_t>(ws, L.h);
+  const uint4* ap =
+      reinterpret_cast<const uint4*>(hsrc + (size_t)(rbase + min(tid / kW2TPR, rows - 1)) * kI) +
+      (tid % kW2TPR) * (kW2EA / 8);
+  __bf16* adst0 = sA[0] + (tid / kW2TPR) * LR + (tid % kW2TPR) * kW2EA;
+  const uint8_t* wrow[2];
+  const uint8_t* wsc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const size_t row = ee * kH + (size_t)kW2N * n + 64 * wave + 32 * j + (lane & 31);
+    wrow[j] = X.w2 + row * (kI / 2);
+    wsc[j] = X.w2s + row * (kI / 16);
+  }
+  W2Slot ring[kW2Ring];
+  W2Cur cur;
+  auto gload = [&](W2Slot& sl, int kt) {
+#pragma unroll
+    for (int i = 0; i < kW2EA / 8; ++i) sl.a[i] = ap[kt * (kW2BK / 8) + i];
+    w2_load_b(sl, wrow, wsc, kt, half);
+  };
+  auto sstore = [&](const W2Slot& sl, int buf) {
+    __bf16* d = adst0 + buf * (kGBM * LR);
+#pragma unroll
+    for (int i = 0; i < kW2EA / 8; ++i) st_lds16(d + 8 * i, sl.a[i]);
+    w2_take(sl, cur);
+  };
+  W2Acc acc;
+  acc.zero();
+  kpipeline<kW2Ring, kI / kW2BK>(ring, gload, sstore,
+                                 [&](int buf) { acc.mma<LR>(sA[buf], cur, lane); });
+  const float gl = X.glob[ee * 3 + 2];
+  __shared__ float s_wr[kGBM];                          // routing weight * global per row
+  if (tid < kGBM) s_wr[tid] = tid < rows ? wsp<float>(ws, L.wpos)[rbase + tid] * gl : 0.0f;
+  __syncthreads();
+  f16* part = wsp<f16>(ws, L.part);
+  const int col0 = kW2N * n + 64 * wave + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = W2Acc::row_of(lane, i, k);
+      if (r < rows) {
+        const float wr = s_wr[r];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          part[(size_t)(rbase + r) * kH + col0 + 32 * j] = (f16)(acc.c[i][j][k] * wr);
       }
     }
 }
@@ -746,8 +924,8 @@ hipError_t launch_prefill(int T, int fmt, const uint16_t* x, const uint16_t* rw,
   if (fmt == FMT_NVFP4) {
     hipLaunchKernelGGL(k_prefill_gateup<FMT_NVFP4>, dim3(items8 * kSlices1), dim3(kGThreads1), 0, st,
                        x, T, routed, shared, ws);
-    hipLaunchKernelGGL(k_prefill_down<FMT_NVFP4>, dim3(items8 * kSlices2), dim3(kGThreads2), 0, st,
-                       T, routed, shared, ws);
+    hipLaunchKernelGGL(k_prefill_down_w, dim3(items8 * kW2Slices2), dim3(kW2Threads), 0, st, T,
+                       routed, shared, ws);
   } else {
     hipLaunchKernelGGL(k_prefill_gateup<FMT_BF16>, dim3(items8 * kSlices1), dim3(kGThreads1), 0, st,
                        x, T, routed, shared, ws);
