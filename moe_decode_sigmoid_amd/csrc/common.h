@@ -164,6 +164,52 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// sum_k w_k v_k over one 32-element NVFP4 chunk of a weight row (16 code
+// bytes c, the two E4M3 block scales in the low bytes of s) against 32 bf16
+// values v given as 16 pairs, without the tensor scale: each 16-element
+// block is summed in fp32 and multiplied by its scale.  S is the type the
+// scales were loaded as (a 16-bit load kept at its width is not re-masked).
+template <typename S>
+__device__ __forceinline__ float nvfp4_dot32(uint4 c, S s, const uint32_t (&v)[16]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    b0 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), v[4 * d + 0], b0);
+    b0 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), v[4 * d + 1], b0);
+    b0 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), v[4 * d + 2], b0);
+    b0 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), v[4 * d + 3], b0);
+  }
+#pragma unroll
+  for (int d = 2; d < 4; ++d) {
+    b1 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), v[4 * d + 0], b1);
+    b1 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), v[4 * d + 1], b1);
+    b1 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), v[4 * d + 2], b1);
+    b1 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), v[4 * d + 3], b1);
+  }
+  return b0 * e4m3_to_f32<0>(s) + b1 * e4m3_to_f32<1>(s);
+}
+
+// The same for a 32-element bf16 chunk (w: four uint4 of 8 bf16 each).
+__device__ __forceinline__ float bf16_dot32(const uint4 (&w)[4], const uint32_t (&v)[16]) {
+  float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    b0 = dot2_bf16(w[i].x, v[4 * i + 0], b0);
+    b0 = dot2_bf16(w[i].y, v[4 * i + 1], b0);
+    b0 = dot2_bf16(w[i].z, v[4 * i + 2], b0);
+    b0 = dot2_bf16(w[i].w, v[4 * i + 3], b0);
+  }
+#pragma unroll
+  for (int i = 2; i < 4; ++i) {
+    b1 = dot2_bf16(w[i].x, v[4 * i + 0], b1);
+    b1 = dot2_bf16(w[i].y, v[4 * i + 1], b1);
+    b1 = dot2_bf16(w[i].z, v[4 * i + 2], b1);
+    b1 = dot2_bf16(w[i].w, v[4 * i + 3], b1);
+  }
+  return b0 + b1;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) {
   return __builtin_bit_cast(float, v & 0xFFFF0000u);

@@ -132,23 +132,7 @@ struct Chunk<FMT_NVFP4> {
   // sum_k w_k v_k over the chunk (v: 32 bf16 values in pairs), without the
   // tensor scale; v is x for gate/up rows and h for down rows
   __device__ __forceinline__ float dot_x(const uint32_t (&xw)[16]) const {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float b0 = 0.0f, b1 = 0.0f;
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      b0 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), xw[4 * d + 0], b0);
-      b0 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), xw[4 * d + 1], b0);
-      b0 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), xw[4 * d + 2], b0);
-      b0 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b0);
-    }
-#pragma unroll
-    for (int d = 2; d < 4; ++d) {
-      b1 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), xw[4 * d + 0], b1);
-      b1 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), xw[4 * d + 1], b1);
-      b1 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), xw[4 * d + 2], b1);
-      b1 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b1);
-    }
-    return b0 * e4m3_to_f32<0>(s) + b1 * e4m3_to_f32<1>(s);
+    return nvfp4_dot32(c, s, xw);
   }
   __device__ __forceinline__ static float gscale(const ExpertsDev& X, size_t ee, int m) {
     return gld<float>(X.glob + ee * 3 + m);
@@ -168,24 +152,7 @@ struct Chunk<FMT_BF16> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = gld<uint4>(p + 16 * i);
   }
-  __device__ __forceinline__ float dot_x(const uint32_t (&xw)[16]) const {
-    float b0 = 0.0f, b1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      b0 = dot2_bf16(w[i].x, xw[4 * i + 0], b0);
-      b0 = dot2_bf16(w[i].y, xw[4 * i + 1], b0);
-      b0 = dot2_bf16(w[i].z, xw[4 * i + 2], b0);
-      b0 = dot2_bf16(w[i].w, xw[4 * i + 3], b0);
-    }
-#pragma unroll
-    for (int i = 2; i < 4; ++i) {
-      b1 = dot2_bf16(w[i].x, xw[4 * i + 0], b1);
-      b1 = dot2_bf16(w[i].y, xw[4 * i + 1], b1);
-      b1 = dot2_bf16(w[i].z, xw[4 * i + 2], b1);
-      b1 = dot2_bf16(w[i].w, xw[4 * i + 3], b1);
-    }
-    return b0 + b1;
-  }
+  __device__ __forceinline__ float dot_x(const uint32_t (&xw)[16]) const { return bf16_dot32(w, xw); }
   __device__ __forceinline__ static float gscale(const ExpertsDev&, size_t, int) { return 1.0f; }
 };
 

@@ -21,27 +21,6 @@ namespace moe {
 constexpr int kGvThreads = 256;
 
 
-// sum over one 32-element chunk of w * x (x as 16 packed bf16 pairs), before
-// the tensor scale: two 16-element blocks, each times its E4M3 scale
-__device__ __forceinline__ float gv_dot(uint4 c, uint32_t s, const uint32_t (&xw)[16]) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float b0 = 0.0f, b1 = 0.0f;
-#pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    b0 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), xw[4 * d + 0], b0);
-    b0 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), xw[4 * d + 1], b0);
-    b0 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), xw[4 * d + 2], b0);
-    b0 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b0);
-  }
-#pragma unroll
-  for (int d = 2; d < 4; ++d) {
-    b1 = dot2_bf16(fp4x2_to_bf16<0>(w[d]), xw[4 * d + 0], b1);
-    b1 = dot2_bf16(fp4x2_to_bf16<1>(w[d]), xw[4 * d + 1], b1);
-    b1 = dot2_bf16(fp4x2_to_bf16<2>(w[d]), xw[4 * d + 2], b1);
-    b1 = dot2_bf16(fp4x2_to_bf16<3>(w[d]), xw[4 * d + 3], b1);
-  }
-  return b0 * e4m3_to_f32<0>(s) + b1 * e4m3_to_f32<1>(s);
-}
 
 // NC = chunk passes per lane (K / 32 chunks over 64 lanes, rounded up);
 // RW = output rows per wave (4 waves per workgroup)
@@ -104,7 +83,7 @@ __global__ __launch_bounds__(kGvThreads) void k_nvfp4_gemv(const uint16_t* __res
           xw[4 * j] = v.x; xw[4 * j + 1] = v.y; xw[4 * j + 2] = v.z; xw[4 * j + 3] = v.w;
         }
 #pragma unroll
-        for (int q = 0; q < RW; ++q) acc[q][t] += gv_dot(c[q][i], s[q][i], xw);
+        for (int q = 0; q < RW; ++q) acc[q][t] += nvfp4_dot32(c[q][i], s[q][i], xw);
       }
     }
   }
