@@ -215,12 +215,22 @@ __device__ __forceinline__ float bf16_hi(uint32_t v) {
   return __builtin_bit_cast(float, v & 0xFFFF0000u);
 }
 
-// fp32 -> bf16 bits, round to nearest even (inputs are finite here).
+// fp32 -> bf16 bits, round to nearest even (inputs are finite here), with
+// gfx950's v_cvt_pk_bf16_f32.  Checked on the GPU against the integer form
+// (u + 0x7FFF + ((u >> 16) & 1)) >> 16 over every non-NaN fp32 pattern: equal.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// Two at once, packed: lo in bits 0..15, hi in bits 16..31 (one instruction).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// s_waitcnt immediate that waits for this wave's vector memory operations
+// only (vmcnt 0; expcnt 7 and lgkmcnt 15 are "no wait" in gfx9's encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int kWaitVm0 = 0x0F70;
 
 // Device-coherent accesses for data one workgroup hands to others inside a
 // kernel: relaxed atomics at agent scope are issued with device-scope
@@ -287,21 +297,32 @@ struct FuseDev {
   uint16_t* xn_out;         // bf16 [T][H]: the normalised input, as used
 };
 
+// Sum of squares of the 8 bf16 elements of one 16-byte piece: a chain of
+// v_dot2_f32_bf16 over its four bf16 pairs in element order (one instruction
+// per pair, straight from the packed words).
+__device__ __forceinline__ float sumsq8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return dot2_bf16(d, d, dot2_bf16(c, c, dot2_bf16(b, b, dot2_bf16(a, a, 0.0f))));
+}
+
 // 1 / sqrt(mean square + eps) of a row of kH bf16 values held by one wave,
-// 32 per lane (lane l: elements 32 l .. 32 l + 31, as 16 bf16 pairs): each
-// lane sums its squares in element order, then the wave sums the lanes
-// (wave_sum's fixed order).  Every path that normalises a row uses this one
-// order.  Division and square root are the correctly rounded fp32 ones.
-__device__ __forceinline__ float row_rms_inv(const uint32_t (&v)[16], float eps) {
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float a = bf16_lo(v[i]), b = bf16_hi(v[i]);
-    s = __builtin_fmaf(a, a, s);
-    s = __builtin_fmaf(b, b, s);
-  }
-  const float ss = wave_sum(s);
+// 32 per lane (lane l: elements 32 l .. 32 l + 31, four 8-element pieces).
+// Each piece is summed in element order (sumsq8), a lane combines its four
+// piece sums as (p0 + p2) + (p1 + p3), and the wave sums the lanes in
+// wave_sum's fixed order.  Every path that normalises a row uses this one
+// order.  The lane combination is the same value whichever piece a lane
+// takes first (a rotation only swaps the two bracketed sums, and fp32
+// addition is commutative), so a lane may read its pieces starting anywhere.
+// Division and square root are the correctly rounded fp32 ones.
+__device__ __forceinline__ float rms_inv_from_pieces(float p0, float p1, float p2, float p3,
+                                                     float eps) {
+  const float ss = wave_sum((p0 + p2) + (p1 + p3));
   return 1.0f / sqrtf(ss * (1.0f / kH) + eps);
+}
+__device__ __forceinline__ float row_rms_inv(const uint32_t (&v)[16], float eps) {
+  float p[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) p[c] = sumsq8(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  return rms_inv_from_pieces(p[0], p[1], p[2], p[3], eps);
 }
 
 // bf16(x * r * w) for the 8 elements of one 16-byte piece: x * r and then
@@ -310,11 +331,19 @@ __device__ __forceinline__ uint4 rmsnorm8(uint4 x, uint4 w, float r) {
   const uint32_t xu[4] = {x.x, x.y, x.z, x.w}, wu[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = f32_to_bf16_rne((bf16_lo(xu[i]) * r) * bf16_lo(wu[i]));
-    const uint32_t hi = f32_to_bf16_rne((bf16_hi(xu[i]) * r) * bf16_hi(wu[i]));
-    o[i] = lo | (hi << 16);
-  }
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32x2_to_bf16x2_rne((bf16_lo(xu[i]) * r) * bf16_lo(wu[i]),
+                               (bf16_hi(xu[i]) * r) * bf16_hi(wu[i]));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+// The same with the weight piece already widened to fp32 (w[2 i], w[2 i + 1]
+// are the low and high element of word i), for a weight shared by B rows.
+__device__ __forceinline__ uint4 rmsnorm8w(uint4 x, const float (&w)[8], float r) {
+  const uint32_t xu[4] = {x.x, x.y, x.z, x.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32x2_to_bf16x2_rne((bf16_lo(xu[i]) * r) * w[2 * i], (bf16_hi(xu[i]) * r) * w[2 * i + 1]);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 

@@ -161,7 +161,8 @@ struct Chunk<FMT_BF16> {
 // written after the kernel's last step, so they add no stores to the
 // memory queue of the phases they time.
 #ifdef MOE_PHASE_TRACE
-__shared__ unsigned long long s_trace[16];
+constexpr int kTraceStamps = 24;
+__shared__ unsigned long long s_trace[kTraceStamps];
 #endif
 __device__ __forceinline__ void trace_stamp(uint8_t* ws, int k) {
 #ifdef MOE_PHASE_TRACE
@@ -174,9 +175,9 @@ __device__ __forceinline__ void trace_stamp(uint8_t* ws, int k) {
 __device__ __forceinline__ void trace_flush(uint8_t* ws) {
 #ifdef MOE_PHASE_TRACE
   __syncthreads();
-  if (threadIdx.x < 16)
-    reinterpret_cast<unsigned long long*>(ws + kDecodeWsBytes)[blockIdx.x * 16 + threadIdx.x] =
-        s_trace[threadIdx.x];
+  if (threadIdx.x < kTraceStamps)
+    reinterpret_cast<unsigned long long*>(ws + kDecodeWsBytes)[blockIdx.x * kTraceStamps +
+                                                               threadIdx.x] = s_trace[threadIdx.x];
 #else
   (void)ws;
 #endif
@@ -488,10 +489,14 @@ __device__ __forceinline__ void load_pre_down(StepAPre<FMT>& p, const ExpertsDev
 // entries (at most 6 B / 4 of them) all fit in the two down-row sets issued
 // before the h-ready wait.  Otherwise the prefetch goes out behind the last
 // down-row loads, so that none of them queues behind it.
-template <int FMT>
-constexpr int kDownDepth = FMT == FMT_NVFP4 ? 4 : 1;   // routed entries per down-row set
+// A set holds kDownDepth routed entries per wave: 4 for NVFP4, fewer when
+// two sets already cover a wave's at most ceil(6 B / 4) entries (the loads
+// are unconditional, so a slot past a wave's last entry is a wasted load).
 template <int B, int FMT>
-constexpr bool kPrefetchNext = kK * B <= 4 * 2 * kDownDepth<FMT>;
+constexpr int kDownDepth =
+    FMT == FMT_NVFP4 ? ((kK * B + 7) / 8 < 4 ? (kK * B + 7) / 8 : 4) : 1;
+template <int B, int FMT>
+constexpr bool kPrefetchNext = kK * B <= 4 * 2 * kDownDepth<B, FMT>;
 
 // ------------------------------------------------------------------ kernel
 // One layer, as one workgroup of the 256 runs it (the body of both kernels
@@ -525,7 +530,7 @@ __device__ __forceinline__ void decode_layer(
 #define MOE_GU_TB 3
 #endif
   constexpr int kTB = FMT == FMT_NVFP4 ? (B == 1 ? 3 : MOE_GU_TB) : 2;
-  constexpr int kDepthC = kDownDepth<FMT>;           // entries of down rows in flight
+  constexpr int kDepthC = kDownDepth<B, FMT>;           // entries of down rows in flight
   // batch 1 issues its routed down rows after publishing h instead of behind
   // the gate/up rows: the gate/up burst then carries only gate/up rows
   constexpr bool kLateDown = B == 1;
@@ -600,10 +605,12 @@ __device__ __forceinline__ void decode_layer(
     uint32_t xs[4 * B];
     wait_slots_u32<4 * B>(xslots + (g % kXReps) * (kSlotXRep / 8) + tid, kFusedThreads,
                           epoch_reg, xs, &ctl->err, kErrXReady);
+    if constexpr (B > 1) trace_stamp(ws, 15);   // (stamp 15 is the top-6 at B = 1)
     uint32_t* s_x32 = reinterpret_cast<uint32_t*>(s_x);
 #pragma unroll
     for (int k = 0; k < 4 * B; ++k) s_x32[tid + kFusedThreads * k] = xs[k];
     __syncthreads();
+    trace_stamp(ws, 16);
     if constexpr (B == 1) {
       xr[0] = s_x[tid];
 #pragma unroll
@@ -628,30 +635,50 @@ __device__ __forceinline__ void decode_layer(
       s_x[tid] = v;
       if (fz.xn_out && g == 0) reinterpret_cast<uint4*>(fz.xn_out)[tid] = v;
     } else {
-      for (int t = wave; t < B; t += 4) {
-        uint32_t v[16];
+      // the four piece sums of token t's row, lane l's pieces 4 l .. 4 l + 3
+      // (16-byte units).  From LDS, lane l starts at piece (l >> 1) & 3: the
+      // lanes of a 64-byte stride would otherwise share LDS banks, and the
+      // combined sum does not depend on the starting piece.
+      auto row_pieces = [&](int t, float (&p)[4]) __attribute__((always_inline)) {
         if constexpr (XIN == 1) {
+          const int r = (lane >> 1) & 3;
+          uint4 u[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 u = s_x[t * (kH / 8) + 4 * lane + i];
-            v[4 * i] = u.x; v[4 * i + 1] = u.y; v[4 * i + 2] = u.z; v[4 * i + 3] = u.w;
-          }
+          for (int k = 0; k < 4; ++k) u[k] = s_x[t * (kH / 8) + 4 * lane + ((k + r) & 3)];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) p[k] = sumsq8(u[k].x, u[k].y, u[k].z, u[k].w);
         } else {
           const uint4* q = reinterpret_cast<const uint4*>(x + t * kH + 32 * lane);
+          uint4 u[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 u = q[i];
-            v[4 * i] = u.x; v[4 * i + 1] = u.y; v[4 * i + 2] = u.z; v[4 * i + 3] = u.w;
-          }
+          for (int k = 0; k < 4; ++k) u[k] = q[k];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) p[k] = sumsq8(u[k].x, u[k].y, u[k].z, u[k].w);
         }
-        const float r = row_rms_inv(v, fz.eps);
-        if (lane == 0) s_rinv[t] = r;
+      };
+      // rows wave and wave + 4 side by side: independent sum chains
+      if (wave + 4 < B) {
+        float p0[4], p1[4];
+        row_pieces(wave, p0);
+        row_pieces(wave + 4, p1);
+        const float r0 = rms_inv_from_pieces(p0[0], p0[1], p0[2], p0[3], fz.eps);
+        const float r1 = rms_inv_from_pieces(p1[0], p1[1], p1[2], p1[3], fz.eps);
+        if (lane == 0) {
+          s_rinv[wave] = r0;
+          s_rinv[wave + 4] = r1;
+        }
+      } else if (wave < B) {
+        float p0[4];
+        row_pieces(wave, p0);
+        const float r0 = rms_inv_from_pieces(p0[0], p0[1], p0[2], p0[3], fz.eps);
+        if (lane == 0) s_rinv[wave] = r0;
       }
     }
   } else if constexpr (XIN == 0) {
 #pragma unroll
     for (int k = 0; k < B; ++k) s_x[k * (kH / 8) + tid] = xr[k];
   }
+  trace_stamp(ws, 17);
   if constexpr (B > 1) s_mask[tid] = 0u;
   // this call's epoch: the workgroup's counter + 1; layer l > 0 of a stacked
   // launch knows it already (the previous layer's + 1), which saves a memory
@@ -672,15 +699,37 @@ __device__ __forceinline__ void decode_layer(
       x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
     }
   }
+  trace_stamp(ws, 18);
   if constexpr (NORM && B > 1) {
+    // the weight piece is the same for every token: widened once
+    float nwf[8];
+    {
+      const uint32_t wu[4] = {nw.x, nw.y, nw.z, nw.w};
 #pragma unroll
-    for (int k = 0; k < B; ++k) {
-      // a chained layer's x is in LDS already: each thread normalises its own
-      // pieces in place (the row sums above read them before the barrier)
-      if constexpr (XIN == 1) xr[k] = s_x[k * (kH / 8) + tid];
-      const uint4 v = rmsnorm8(xr[k], nw, s_rinv[k]);
-      s_x[k * (kH / 8) + tid] = v;
-      if (fz.xn_out && g == 0) reinterpret_cast<uint4*>(fz.xn_out)[k * (kH / 8) + tid] = v;
+      for (int i = 0; i < 4; ++i) {
+        nwf[2 * i] = bf16_lo(wu[i]);
+        nwf[2 * i + 1] = bf16_hi(wu[i]);
+      }
+    }
+    // a chained layer's x is in LDS already: each thread normalises its own
+    // pieces in place (the row sums above read them before the barrier).
+    // All reads first, then the arithmetic, then the writes: a store through
+    // xn_out between them would keep the compiler from moving the next read
+    // ahead of it.
+    if constexpr (XIN == 1) {
+#pragma unroll
+      for (int k = 0; k < B; ++k) xr[k] = s_x[k * (kH / 8) + tid];
+    }
+    float rk[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) rk[k] = s_rinv[k];
+#pragma unroll
+    for (int k = 0; k < B; ++k) xr[k] = rmsnorm8w(xr[k], nwf, rk[k]);
+#pragma unroll
+    for (int k = 0; k < B; ++k) s_x[k * (kH / 8) + tid] = xr[k];
+    if (fz.xn_out && g == 0) {
+#pragma unroll
+      for (int k = 0; k < B; ++k) reinterpret_cast<uint4*>(fz.xn_out)[k * (kH / 8) + tid] = xr[k];
     }
     __syncthreads();
   }
@@ -877,12 +926,14 @@ __device__ __forceinline__ void decode_layer(
   // expert's tokens wave, wave + 4); the first kDepthC entries' down rows are
   // fetched behind the first gate/up batch
   const int wsel = (wave + 3) & 3;
+  // Unconditional, like the gate/up loads: an entry past the last (there are
+  // always at least kK) reads the last one's rows again and run_set drops
+  // it.  Under a branch these loads would make the compiler wait for every
+  // load in flight at the next barrier.
   auto load_entry = [&](Chunk<FMT> (&dst)[2], int a) {
-    if (a < nr) {
-      const size_t ee = (size_t)s_act[a];
+    const size_t ee = (size_t)s_act[a < nr ? a : nr - 1];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) dst[r].load_dn(routed, ee, g * kRowsPerWg + 2 * grp4 + r, c16);
-    }
+    for (int r = 0; r < 2; ++r) dst[r].load_dn(routed, ee, g * kRowsPerWg + 2 * grp4 + r, c16);
   };
   Chunk<FMT> dbuf[kDepthC][2];
   {
@@ -1008,6 +1059,12 @@ __device__ __forceinline__ void decode_layer(
   // threads on consecutive rows
   __syncthreads();
   trace_stamp(ws, 13);
+  // Every load of this wave has landed by now (the gate/up rows are used;
+  // the rest went out long ago), but the compiler cannot count the h stores
+  // below (a data-dependent loop): if a load were still outstanding on its
+  // books, reusing its register after the stores would wait for the stores'
+  // acknowledgements too.  Retire the loads here, before any store.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   // Once every 65536 epochs every h slot not written by this call is stamped
   // (workgroup g: slot g of each such pair), as the logit slots are, so that
   // no slot is ever 2^32 epochs old.
