@@ -364,6 +364,15 @@ __device__ __forceinline__ void wave_top6(const float (&v)[N][4], int lane, int 
 }
 
 
+// LDS position (16-byte units) of piece q (elements 8 q .. 8 q + 7) of token
+// t's x row.  The low two bits of q are XORed with bits 3..4: a lane's
+// 32-element chunk is pieces 4 l .. 4 l + 3, and with this swizzle the lanes
+// reading piece 4 l + i hit distinct banks in every group of 8 lanes
+// (unswizzled, their 64-byte stride puts four lanes on one bank), while 8
+// consecutive pieces stay in one 128-byte group, so piece-per-thread and
+// word-per-thread accesses stay conflict-free too.
+__device__ __forceinline__ int sx_pos(int t, int q) { return t * (kH / 8) + (q ^ ((q >> 3) & 3)); }
+
 // One gate/up row pair of an entry for the wave's tokens in `mask` (at most
 // four: the tokens of parity `par`, token t in slot t / 2); the wave's lanes
 // cover the 2048 columns.  The gate and up partial sums of every token are
@@ -389,7 +398,7 @@ __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 u4 = s_x[t * (kH / 8) + 4 * lane + i];
+        const uint4 u4 = s_x[sx_pos(t, 4 * lane + i)];
         xw[4 * i] = u4.x; xw[4 * i + 1] = u4.y; xw[4 * i + 2] = u4.z; xw[4 * i + 3] = u4.w;
       }
     }
@@ -608,14 +617,15 @@ __device__ __forceinline__ void decode_layer(
     if constexpr (B > 1) trace_stamp(ws, 15);   // (stamp 15 is the top-6 at B = 1)
     uint32_t* s_x32 = reinterpret_cast<uint32_t*>(s_x);
 #pragma unroll
-    for (int k = 0; k < 4 * B; ++k) s_x32[tid + kFusedThreads * k] = xs[k];
+    for (int k = 0; k < 4 * B; ++k)   // word tid + 256 k: token k / 4, piece 64 (k % 4) + tid / 4
+      s_x32[4 * sx_pos(k >> 2, 64 * (k & 3) + (tid >> 2)) + (tid & 3)] = xs[k];
     __syncthreads();
     trace_stamp(ws, 16);
     if constexpr (B == 1) {
-      xr[0] = s_x[tid];
+      xr[0] = s_x[sx_pos(0, tid)];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 v = s_x[4 * lane + i];
+        const uint4 v = s_x[sx_pos(0, 4 * lane + i)];
         x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
       }
     }
@@ -632,19 +642,16 @@ __device__ __forceinline__ void decode_layer(
       const float r = row_rms_inv(x0, fz.eps);
       const uint4 v = rmsnorm8(xr[0], nw, r);
       if constexpr (XIN == 1) __syncthreads();   // every wave has read its x0 from LDS
-      s_x[tid] = v;
+      s_x[sx_pos(0, tid)] = v;
       if (fz.xn_out && g == 0) reinterpret_cast<uint4*>(fz.xn_out)[tid] = v;
     } else {
       // the four piece sums of token t's row, lane l's pieces 4 l .. 4 l + 3
-      // (16-byte units).  From LDS, lane l starts at piece (l >> 1) & 3: the
-      // lanes of a 64-byte stride would otherwise share LDS banks, and the
-      // combined sum does not depend on the starting piece.
+      // (16-byte units; from LDS through the swizzle, conflict-free)
       auto row_pieces = [&](int t, float (&p)[4]) __attribute__((always_inline)) {
         if constexpr (XIN == 1) {
-          const int r = (lane >> 1) & 3;
           uint4 u[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) u[k] = s_x[t * (kH / 8) + 4 * lane + ((k + r) & 3)];
+          for (int k = 0; k < 4; ++k) u[k] = s_x[sx_pos(t, 4 * lane + k)];
 #pragma unroll
           for (int k = 0; k < 4; ++k) p[k] = sumsq8(u[k].x, u[k].y, u[k].z, u[k].w);
         } else {
@@ -676,7 +683,7 @@ __device__ __forceinline__ void decode_layer(
     }
   } else if constexpr (XIN == 0) {
 #pragma unroll
-    for (int k = 0; k < B; ++k) s_x[k * (kH / 8) + tid] = xr[k];
+    for (int k = 0; k < B; ++k) s_x[sx_pos(k, tid)] = xr[k];
   }
   trace_stamp(ws, 17);
   if constexpr (B > 1) s_mask[tid] = 0u;
@@ -695,7 +702,7 @@ __device__ __forceinline__ void decode_layer(
   if constexpr (NORM && B == 1) {          // x0 again, normalised
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 v = s_x[4 * lane + i];
+      const uint4 v = s_x[sx_pos(0, 4 * lane + i)];
       x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
     }
   }
@@ -718,7 +725,7 @@ __device__ __forceinline__ void decode_layer(
     // ahead of it.
     if constexpr (XIN == 1) {
 #pragma unroll
-      for (int k = 0; k < B; ++k) xr[k] = s_x[k * (kH / 8) + tid];
+      for (int k = 0; k < B; ++k) xr[k] = s_x[sx_pos(k, tid)];
     }
     float rk[B];
 #pragma unroll
@@ -726,7 +733,7 @@ __device__ __forceinline__ void decode_layer(
 #pragma unroll
     for (int k = 0; k < B; ++k) xr[k] = rmsnorm8w(xr[k], nwf, rk[k]);
 #pragma unroll
-    for (int k = 0; k < B; ++k) s_x[k * (kH / 8) + tid] = xr[k];
+    for (int k = 0; k < B; ++k) s_x[sx_pos(k, tid)] = xr[k];
     if (fz.xn_out && g == 0) {
 #pragma unroll
       for (int k = 0; k < B; ++k) reinterpret_cast<uint4*>(fz.xn_out)[k * (kH / 8) + tid] = xr[k];
@@ -738,7 +745,7 @@ __device__ __forceinline__ void decode_layer(
     float acc[B];
 #pragma unroll
     for (int t = 0; t < B; ++t) {
-      const uint4 xv = s_x[t * (kH / 8) + 64 * wave + lane];
+      const uint4 xv = s_x[sx_pos(t, 64 * wave + lane)];
       float a = dot2_bf16(pre.wr.x, xv.x, 0.0f);
       a = dot2_bf16(pre.wr.y, xv.y, a);
       a = dot2_bf16(pre.wr.z, xv.z, a);
@@ -992,7 +999,7 @@ __device__ __forceinline__ void decode_layer(
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const uint4 v = s_x[t * (kH / 8) + 4 * lane + i];
+            const uint4 v = s_x[sx_pos(t, 4 * lane + i)];
             xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
           }
         }
