@@ -88,17 +88,19 @@ double or_bf16(uint16_t h) {
   return (double)f;
 }
 
-/* Lookup tables filled from the closed forms above on first use. */
+/* Lookup tables filled from the closed forms above on first use.  The ready
+ * flag is read with acquire and set with release ordering (GCC's __atomic
+ * builtins), so a thread that sees it set also sees the filled tables. */
 static double g_e2m1[16], g_e4m3[256];
 static int g_tables_ready = 0;
 static void or_tables(void) {
-  if (g_tables_ready) return;
+  if (__atomic_load_n(&g_tables_ready, __ATOMIC_ACQUIRE)) return;
   #pragma omp critical(or_tables_init)
   {
-    if (!g_tables_ready) {
+    if (!__atomic_load_n(&g_tables_ready, __ATOMIC_RELAXED)) {
       for (int i = 0; i < 16; ++i) g_e2m1[i] = or_e2m1((uint8_t)i);
       for (int i = 0; i < 256; ++i) g_e4m3[i] = or_e4m3((uint8_t)i);
-      g_tables_ready = 1;
+      __atomic_store_n(&g_tables_ready, 1, __ATOMIC_RELEASE);
     }
   }
 }
