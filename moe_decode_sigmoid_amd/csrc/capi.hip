@@ -52,6 +52,15 @@ moe_status check_shape_decode(const moe_shape* s) {
   return MOE_ERR_UNSUPPORTED;
 }
 bool fast_path(const moe_shape* s) { return check_shape(s) == MOE_OK; }
+bool split_path_forced();
+// Flint's shape with two shared experts and NVFP4 weights (the Inkling
+// shape at Flint's widths): a general shape that the single-launch kernel
+// also serves, for the plain layer.
+bool ns2_path(const moe_shape* s) {
+  return s && s->wfmt == MOE_W_NVFP4 && s->hidden == moe::kH && s->inter == moe::kI &&
+         s->n_experts == moe::kE && s->top_k == moe::kK && s->n_shared == 2 &&
+         moe::fused_ns2_supported() && !split_path_forced();
+}
 
 // Workspace bytes of the decode entry points for a checked shape.
 size_t decode_ws_need(const moe_shape* s) {
@@ -264,6 +273,12 @@ moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
   if (st != MOE_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   moe::GenShape g;
+  if (ns2_path(shape)) {
+    const hipError_t e = moe::launch_decode_fused_ns2(
+        B, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), to_dev(routed),
+        to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out, static_cast<uint8_t*>(ws), s);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   if (!fast_path(shape) && general_shape(shape, &g)) {
     const hipError_t e = moe::launch_decode_general(
         B, shape->wfmt, g, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w),
@@ -327,7 +342,12 @@ moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32
   const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   hipError_t e;
   moe::GenShape g;
-  if (!fast_path(shape) && general_shape(shape, &g)) {
+  if (ns2_path(shape)) {
+    e = moe::launch_decode_fused_ns2(B, static_cast<const uint16_t*>(x),
+                                     static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                     to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                     static_cast<uint8_t*>(ws), s, e0, e1);
+  } else if (!fast_path(shape) && general_shape(shape, &g)) {
     e = hipEventRecord(e0, s);
     if (e == hipSuccess)
       e = moe::launch_decode_general(

@@ -16,6 +16,7 @@ constexpr int kE = 256;           // routed experts
 constexpr int kK = 6;             // experts per token
 constexpr int kMaxB = 8;          // low-latency decode batch limit
 constexpr int kMaxActive = kMaxB * kK + 1;   // distinct experts of one decode call + shared
+constexpr int kMaxShared = 2;   // shared experts the single-launch decode kernels serve (1 or 2)
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -100,11 +101,11 @@ constexpr size_t kSlotXOff = kFlagOff + (256 + 64 * kBankReps) * kFlagStride;
 // Everything below kDecodeWsBytes is the single-launch decode kernels'; the
 // epoch counters, h-ready counters and tagged slots keep their values from
 // call to call, so no other path writes below this offset.
-// h as tagged 8-byte slots {two bf16 values, epoch}: [kMaxB * (kK + 1) pairs]
-// [kI / 2 slots] (the small-batch hand-over between the GEMVs).
+// h as tagged 8-byte slots {two bf16 values, epoch}: [kMaxB * (kK + kMaxShared)
+// pairs][kI / 2 slots] (the small-batch hand-over between the GEMVs).
 constexpr size_t kHSlots = kI / 2;
 constexpr size_t kSlotHOff = kSlotXOff + kSlotXRep * kXReps;
-constexpr size_t kDecodeWsBytes = kSlotHOff + 8 * kMaxB * (kK + 1) * kHSlots;
+constexpr size_t kDecodeWsBytes = kSlotHOff + 8 * kMaxB * (kK + kMaxShared) * kHSlots;
 constexpr size_t kGenBase = kDecodeWsBytes;
 
 // Workspace of the general path: logits f32 [kMaxB][E], the dispatch, h

@@ -59,6 +59,21 @@ hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t
              : launch_fused_fmt<FMT_BF16>(B, x, rw, routed, shared, out, ids, w, ws, st, e0, e1, fz);
 }
 
+bool fused_ns2_supported() {
+  static int ok[64] = {0};
+  int dev = 0;
+  if (!fused_supported() || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (ok[dev] == 0) ok[dev] = occupancy_fused_ns2_fmt<FMT_NVFP4>() ? 1 : -1;
+  return ok[dev] == 1;
+}
+
+hipError_t launch_decode_fused_ns2(int B, const uint16_t* x, const uint16_t* rw,
+                                   const ExpertsDev& routed, const ExpertsDev& shared,
+                                   uint16_t* out, int32_t* ids, float* w, uint8_t* ws,
+                                   hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  return launch_fused_ns2_fmt<FMT_NVFP4>(B, x, rw, routed, shared, out, ids, w, ws, st, e0, e1);
+}
+
 hipError_t launch_decode_stack(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
                                uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st) {
   return fmt == FMT_NVFP4 ? launch_stack_fmt<FMT_NVFP4>(B, x, layers, L, out, ids, ws, st)

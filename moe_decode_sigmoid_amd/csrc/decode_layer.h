@@ -460,13 +460,15 @@ __device__ __forceinline__ uint32_t* hready_bank(uint8_t* ws, int r, int k) {
 }
 
 // The loads of a layer that depend on neither x nor the routing: router row
-// g (wave w covers columns [512 w, 512 w + 512), 8 per lane); the shared
+// g (wave w covers columns [512 w, 512 w + 512), 8 per lane); each shared
 // expert's gate/up row 2g + (w & 1) for the tokens of parity w >> 1 (at B = 1
-// waves 0 and 1 only); its down rows of this workgroup's 8 outputs.
-template <int FMT>
+// waves 0 and 1 only); its down rows of this workgroup's 8 outputs.  NS
+// shared experts (1 for Flint; 2 for the Inkling shape, which is Flint's with
+// two shared experts).
+template <int FMT, int NS = 1>
 struct StepAPre {
   uint4 wr;
-  Chunk<FMT> scg, scu, dsh[2];
+  Chunk<FMT> scg[NS], scu[NS], dsh[NS][2];
 };
 
 template <int B>
@@ -474,23 +476,28 @@ __device__ __forceinline__ unsigned shared_token_mask(int wave) {
   return ((1u << B) - 1u) & ((wave >> 1) ? 0xAAAAAAAAu : 0x55555555u);
 }
 
-template <int B, int FMT>
-__device__ __forceinline__ void load_pre_gateup(StepAPre<FMT>& p, const uint16_t* rw,
+template <int B, int FMT, int NS>
+__device__ __forceinline__ void load_pre_gateup(StepAPre<FMT, NS>& p, const uint16_t* rw,
                                                 const ExpertsDev& shared, int g, int wave,
                                                 int lane) {
   p.wr = gld<uint4>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
   if (shared_token_mask<B>(wave)) {
-    p.scg.load_gu(shared, 0, 0, 2 * g + (wave & 1), lane);
-    p.scu.load_gu(shared, 0, 1, 2 * g + (wave & 1), lane);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      p.scg[s].load_gu(shared, s, 0, 2 * g + (wave & 1), lane);
+      p.scu[s].load_gu(shared, s, 1, 2 * g + (wave & 1), lane);
+    }
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void load_pre_down(StepAPre<FMT>& p, const ExpertsDev& shared, int g,
-                                              int lane) {
+template <int FMT, int NS>
+__device__ __forceinline__ void load_pre_down(StepAPre<FMT, NS>& p, const ExpertsDev& shared,
+                                              int g, int lane) {
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
-    p.dsh[r].load_dn(shared, 0, g * kRowsPerWg + 2 * (lane >> 4) + r, lane & 15);
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      p.dsh[s][r].load_dn(shared, s, g * kRowsPerWg + 2 * (lane >> 4) + r, lane & 15);
 }
 
 // A stacked launch prefetches the next layer's step-A rows right after the
@@ -524,11 +531,11 @@ constexpr bool kPrefetchNext = kK * B <= 4 * 2 * kDownDepth<B, FMT>;
 // layer is the residual stream the previous layer wrote).  XOUT: publish the
 // output as tagged slots for the next layer, and keep this thread's output
 // element in resid_reg.
-template <int B, int FMT, bool NORM, int RES, int PF, bool EPREG, int XIN, bool XOUT>
+template <int B, int FMT, bool NORM, int RES, int PF, bool EPREG, int XIN, bool XOUT, int NS = 1>
 __device__ __forceinline__ void decode_layer(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, const ExpertsDev& routed,
     const ExpertsDev& shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz, StepAPre<FMT>& pre,
+    float* __restrict__ w_out, uint8_t* __restrict__ ws, const FuseDev& fz, StepAPre<FMT, NS>& pre,
     const LayerDev& next, uint32_t& epoch_reg, float& resid_reg) {
   // early: after the h copy (every routed down row is already in flight);
   // late: behind step C's last down-row loads
@@ -543,7 +550,8 @@ __device__ __forceinline__ void decode_layer(
   // batch 1 issues its routed down rows after publishing h instead of behind
   // the gate/up rows: the gate/up burst then carries only gate/up rows
   constexpr bool kLateDown = B == 1;
-  constexpr int kPairs = (kK + 1) * B;               // h pairs: 6 B routed + B shared
+  static_assert(NS >= 1 && NS <= kMaxShared, "one or two shared experts");
+  constexpr int kPairs = (kK + NS) * B;              // h pairs: 6 B routed + NS B shared
   const int g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp4 = lane >> 4, c16 = lane & 15;
@@ -568,13 +576,13 @@ __device__ __forceinline__ void decode_layer(
   __shared__ int s_nr;
   __shared__ int s_t01[2];                           // weighted gate/up range (B > 1)
   __shared__ uint32_t s_epoch;
-  __shared__ float s_hsh[2][kMaxB];                  // this workgroup's shared-expert h
+  __shared__ float s_hsh[NS][2][kMaxB];              // this workgroup's shared-expert h
   __shared__ float s_hout[kMaxRange][kMaxB];         // its routed h, by row of its range
 
   trace_stamp(ws, 0);
   // ---------------------------------------------------------------- step A
   const unsigned smask = shared_token_mask<B>(wave);
-  if constexpr (PF != 2) load_pre_gateup<B, FMT>(pre, rw, shared, g, wave, lane);
+  if constexpr (PF != 2) load_pre_gateup<B, FMT, NS>(pre, rw, shared, g, wave, lane);
   // Every load of step A goes out before any of them is used (loads return
   // in issue order, so a wait for one is a wait for all before it): x, piece
   // tid of each token; the norm weight and the residual of this workgroup's
@@ -602,9 +610,14 @@ __device__ __forceinline__ void decode_layer(
       x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
     }
   }
-  const float sh_sg = Chunk<FMT>::gscale(shared, 0, 0), sh_su = Chunk<FMT>::gscale(shared, 0, 1),
-              sh_sd = Chunk<FMT>::gscale(shared, 0, 2);
-  if constexpr (PF != 2) load_pre_down<FMT>(pre, shared, g, lane);
+  float sh_sg[NS], sh_su[NS], sh_sd[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    sh_sg[s] = Chunk<FMT>::gscale(shared, s, 0);
+    sh_su[s] = Chunk<FMT>::gscale(shared, s, 1);
+    sh_sd[s] = Chunk<FMT>::gscale(shared, s, 2);
+  }
+  if constexpr (PF != 2) load_pre_down<FMT, NS>(pre, shared, g, lane);
   const float resid = RES == 2 ? resid_reg : __builtin_bit_cast(float, (uint32_t)rv << 16);
   // A chained stack's x is the previous layer's output, which every
   // workgroup publishes as tagged slots of its rows (epoch of that layer):
@@ -770,9 +783,12 @@ __device__ __forceinline__ void decode_layer(
     }
   }
   trace_stamp(ws, 2);
-  if (smask)
-    gateup_compute<B, FMT>(pre.scg, pre.scu, sh_sg, sh_su, smask, wave >> 1, s_x, x0, lane,
-                           &s_hsh[wave & 1][0]);
+  if (smask) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      gateup_compute<B, FMT>(pre.scg[s], pre.scu[s], sh_sg[s], sh_su[s], smask, wave >> 1, s_x, x0,
+                             lane, &s_hsh[s][wave & 1][0]);
+  }
   trace_stamp(ws, 3);
 
   // ---------------------------------------------------------------- step B
@@ -1076,7 +1092,7 @@ __device__ __forceinline__ void decode_layer(
   // (workgroup g: slot g of each such pair), as the logit slots are, so that
   // no slot is ever 2^32 epochs old.
   if ((epoch & 0xFFFFu) == 0u) {
-    for (int p = (kTagH ? kPairs : 0) + tid; p < kMaxB * (kK + 1); p += kFusedThreads)
+    for (int p = (kTagH ? kPairs : 0) + tid; p < kMaxB * (kK + kMaxShared); p += kFusedThreads)
       put_slot_u32(hslots + (size_t)p * kHSlots + g, 0u, epoch);
   }
   if constexpr (kTagH) {
@@ -1085,9 +1101,11 @@ __device__ __forceinline__ void decode_layer(
     auto pack = [](float a, float b) {
       return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
     };
-    if (tid < B)
+    if (tid < NS * B) {   // shared expert s = tid / B, token t = tid % B: pair kK B + tid
+      const int s = tid / B, t = tid - s * B;
       put_slot_u32(hslots + (size_t)(kK * B + tid) * kHSlots + g,
-                   pack(s_hsh[0][tid], s_hsh[1][tid]), epoch);
+                   pack(s_hsh[s][0][t], s_hsh[s][1][t]), epoch);
+    }
     const int nloc2 = (T1 - T0) >> 1;
     for (int idx = tid; idx < nloc2 * B; idx += kFusedThreads) {
       const int t = idx / nloc2, j = idx - t * nloc2;
@@ -1108,9 +1126,10 @@ __device__ __forceinline__ void decode_layer(
       __hip_atomic_fetch_add(hready_bank(ws, tid, g % kHBanks), 1u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    if (tid < 2 * B) {
-      const int r = tid / B, t = tid % B;
-      store_coherent_u16(hbuf + (size_t)(kK * B + t) * kI + 2 * g + r, f32_to_bf16_rne(s_hsh[r][t]));
+    if (tid < 2 * NS * B) {   // shared expert s, row 2 g + r, token t: pair kK B + s B + t
+      const int s = tid / (2 * B), r = (tid / B) & 1, t = tid % B;
+      store_coherent_u16(hbuf + (size_t)(kK * B + s * B + t) * kI + 2 * g + r,
+                         f32_to_bf16_rne(s_hsh[s][r][t]));
     }
     {
       const int nloc = T1 - T0;
@@ -1211,7 +1230,7 @@ __device__ __forceinline__ void decode_layer(
   // since step A): no load of this layer is issued after this point when
   // every routed entry's down rows are already in flight, so these wait
   // behind nothing and arrive while this layer finishes.
-  if constexpr (kPfEarly) load_pre_gateup<B, FMT>(pre, next.rw, next.shared, g, wave, lane);
+  if constexpr (kPfEarly) load_pre_gateup<B, FMT, NS>(pre, next.rw, next.shared, g, wave, lane);
 
   float acc[2][B], accs[2][2];
 #pragma unroll
@@ -1220,20 +1239,22 @@ __device__ __forceinline__ void decode_layer(
     for (int t = 0; t < B; ++t) acc[r][t] = 0.0f;
     accs[r][0] = accs[r][1] = 0.0f;
   }
-  {                                                  // shared expert, tokens wave and wave + 4
-    const float gl = sh_sd;
+  // shared experts in order, tokens wave and wave + 4
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float gl = sh_sd[s];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int t = wave + 4 * j;
       if (t < B) {
         uint32_t h[16];
-        load_h(s_h, kK * B + t, c16, h);
-        accs[0][j] = __builtin_fmaf(gl, pre.dsh[0].dot_x(h), accs[0][j]);
-        accs[1][j] = __builtin_fmaf(gl, pre.dsh[1].dot_x(h), accs[1][j]);
+        load_h(s_h, kK * B + s * B + t, c16, h);
+        accs[0][j] = __builtin_fmaf(gl, pre.dsh[s][0].dot_x(h), accs[0][j]);
+        accs[1][j] = __builtin_fmaf(gl, pre.dsh[s][1].dot_x(h), accs[1][j]);
       }
     }
   }
-  if constexpr (kPfEarly) load_pre_down<FMT>(pre, next.shared, g, lane);  // the next layer's
+  if constexpr (kPfEarly) load_pre_down<FMT, NS>(pre, next.shared, g, lane);  // the next layer's
   // routed entries of this wave in order, two sets of kDepthC in flight
   const int n_mine = nr > wsel ? (nr - wsel + 3) >> 2 : 0;
   auto run_set = [&](const Chunk<FMT> (&buf)[kDepthC][2], int k0) {
@@ -1270,8 +1291,8 @@ __device__ __forceinline__ void decode_layer(
       load_set(dbuf2, k0 + 3 * kDepthC);
     }
     if constexpr (kPfLate) {     // the next layer's step-A rows, behind these
-      load_pre_gateup<B, FMT>(pre, next.rw, next.shared, g, wave, lane);
-      load_pre_down<FMT>(pre, next.shared, g, lane);
+      load_pre_gateup<B, FMT, NS>(pre, next.rw, next.shared, g, wave, lane);
+      load_pre_down<FMT, NS>(pre, next.shared, g, lane);
     }
     run_set(dbuf, k0);
     run_set(dbuf2, k0 + kDepthC);
@@ -1338,15 +1359,15 @@ __device__ __forceinline__ void decode_layer(
   trace_flush(ws);
 }
 
-template <int B, int FMT, bool NORM, bool RESID>
+template <int B, int FMT, bool NORM, bool RESID, int NS = 1>
 __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, ExpertsDev routed,
     ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, uint8_t* __restrict__ ws, FuseDev fz) {
-  StepAPre<FMT> pre;
+  StepAPre<FMT, NS> pre;
   uint32_t epoch = 0;
   float resid = 0.0f;
-  decode_layer<B, FMT, NORM, RESID ? 1 : 0, 0, false, 0, false>(
+  decode_layer<B, FMT, NORM, RESID ? 1 : 0, 0, false, 0, false, NS>(
       x, rw, routed, shared, out, ids_out, w_out, ws, fz, pre, LayerDev{}, epoch, resid);
 }
 
@@ -1474,6 +1495,32 @@ hipError_t launch_fused_fmt(int B, const uint16_t* x, const uint16_t* rw, const 
   }
 }
 
+// The plain layer (no fused neighbours) with two shared experts: Flint's
+// shape otherwise (the Inkling shape, served in one launch).
+template <int FMT>
+hipError_t launch_fused_ns2_fmt(int B, const uint16_t* x, const uint16_t* rw,
+                                const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                                int32_t* ids, float* w, uint8_t* ws, hipStream_t st, hipEvent_t e0,
+                                hipEvent_t e1) {
+  switch (B) {
+#define MOE_CASE(b)                                                                             \
+  case b:                                                                                       \
+    if (e0 && e1)                                                                               \
+      hipExtLaunchKernelGGL((k_decode_fused<b, FMT, false, false, 2>), dim3(kFusedGrid),        \
+                            dim3(kFusedThreads), 0, st, e0, e1, 0, x, rw, routed, shared, out,  \
+                            ids, w, ws, FuseDev{});                                             \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_decode_fused<b, FMT, false, false, 2>), dim3(kFusedGrid),           \
+                         dim3(kFusedThreads), 0, st, x, rw, routed, shared, out, ids, w, ws,    \
+                         FuseDev{});                                                            \
+    break;
+    MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
+#undef MOE_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Every instance of a kernel family can have one workgroup resident per CU.
 template <typename K>
 bool one_per_cu(K k) {
@@ -1503,6 +1550,12 @@ hipError_t launch_stack_fmt(int B, const uint16_t* x, const LayerDev* layers, in
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int FMT>
+bool occupancy_fused_ns2_fmt() {
+  return one_per_cu(k_decode_fused<8, FMT, false, false, 2>) &&
+         one_per_cu(k_decode_fused<1, FMT, false, false, 2>);
 }
 
 template <int FMT>
@@ -1554,6 +1607,11 @@ bool occupancy_chain_fmt() {
 #ifndef MOE_DECODE_INSTANTIATES
 MOE_EXTERN_FMT(FMT_NVFP4)
 MOE_EXTERN_FMT(FMT_BF16)
+extern template hipError_t launch_fused_ns2_fmt<FMT_NVFP4>(int, const uint16_t*, const uint16_t*,
+                                                           const ExpertsDev&, const ExpertsDev&,
+                                                           uint16_t*, int32_t*, float*, uint8_t*,
+                                                           hipStream_t, hipEvent_t, hipEvent_t);
+extern template bool occupancy_fused_ns2_fmt<FMT_NVFP4>();
 #endif
 #undef MOE_EXTERN_FMT
 

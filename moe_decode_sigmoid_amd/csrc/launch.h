@@ -25,6 +25,15 @@ hipError_t launch_decode_fused(int B, int fmt, const uint16_t* x, const uint16_t
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
                                const FuseDev& fuse = FuseDev{});
 
+// The same single-launch layer with two shared experts (NVFP4, Flint's shape
+// otherwise; no fused neighbours).
+bool fused_ns2_supported();
+hipError_t launch_decode_fused_ns2(int B, const uint16_t* x, const uint16_t* rw,
+                                   const ExpertsDev& routed, const ExpertsDev& shared,
+                                   uint16_t* out, int32_t* ids, float* w, uint8_t* ws,
+                                   hipStream_t st, hipEvent_t ev_start = nullptr,
+                                   hipEvent_t ev_stop = nullptr);
+
 // A stack of L layers (same x) in one launch of the fused kernel's body.
 hipError_t launch_decode_stack(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,
                                uint16_t* out, int32_t* ids, uint8_t* ws, hipStream_t st);

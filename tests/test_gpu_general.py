@@ -181,3 +181,78 @@ def test_one_workspace_serves_the_general_and_the_flint_path():
     torch.cuda.synchronize()
     for i, o in enumerate(outs):
         assert torch.equal(o, ref_f if i % 2 == 0 else ref_g), i
+
+
+# ---------------------------------------------------------------- two shared experts
+# Flint's shape with two shared experts (Inkling's) runs on the single-launch
+# kernel; MOE_DECODE_SPLIT=1 sends it to the four-launch general path instead.
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B", [2, 3, 4, 5, 6, 7])
+def test_inkling_single_launch_every_batch_size(B):
+    check("inkling_nvfp4", 6, B)
+
+
+@pytest.mark.gpu
+def test_inkling_single_launch_agrees_with_the_general_path(monkeypatch):
+    name = "inkling_nvfp4"
+    H = SHAPES[name][0]
+    host, dl = layers(name, 7)
+    S = S_of(name)
+    for B in (1, 8):
+        x = testgen.make_x(94 + B, B, H)
+        xd = moe.device.to_device_bf16(x)
+        ws = moe.alloc_workspace(moe.moe_workspace_bytes(B, S=S))
+        outs = {}
+        for split in ("0", "1"):
+            monkeypatch.setenv("MOE_DECODE_SPLIT", split)
+            o = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+            ids = torch.empty((B, 6), dtype=torch.int32, device="cuda")
+            moe.moe_decode_forward(xd, dl.router, dl.routed, dl.shared, o, ws, ids_out=ids, S=S)
+            torch.cuda.synchronize()
+            outs[split] = (parity.bf16_out_to_f64(o), ids.cpu().numpy())
+        y_or, ids_or, w_or, gap = oracle.forward_layer(x, host)
+        for split, (y, ids) in outs.items():
+            log = []
+            y_ref = parity.resolve_near_ties(x, host, ids, y_or, ids_or, w_or, gap, log)
+            parity.check_output(y, y_ref, f"{name} B {B} split {split}")
+        # the two paths sum in different orders: equal ids, outputs within the parity bar
+        confident = gap >= parity.NEAR_TIE
+        for t in np.nonzero(confident)[0]:
+            assert sorted(outs["0"][1][t]) == sorted(outs["1"][1][t]), t
+
+
+@pytest.mark.gpu
+def test_inkling_and_flint_single_launch_calls_share_a_workspace():
+    """The two-shared-expert kernel and Flint's one-shared-expert kernel keep
+    the same epoch counters and tagged slots: alternating calls on one
+    workspace give the results of separate workspaces, bit for bit."""
+    name = "inkling_nvfp4"
+    H = SHAPES[name][0]
+    _, dl = layers(name, 8)
+    S = S_of(name)
+    flint = moe.DeviceLayer.from_host(testgen.make_layer(2, 0, "nvfp4"))
+    for B in (1, 4):
+        x = moe.device.to_device_bf16(testgen.make_x(120 + B, B, H))
+        nbytes = max(moe.moe_workspace_bytes(B, S=S), moe.moe_workspace_bytes(B))
+        shared_ws = moe.alloc_workspace(nbytes)
+
+        def ink(ws):
+            o = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+            moe.moe_decode_forward(x, dl.router, dl.routed, dl.shared, o, ws, S=S)
+            return o
+
+        def fl(ws):
+            o = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+            moe.moe_decode_forward(x, flint.router, flint.routed, flint.shared, o, ws)
+            return o
+        ref_i = ink(moe.alloc_workspace(nbytes))
+        ref_f = fl(moe.alloc_workspace(nbytes))
+        outs = [ink(shared_ws), fl(shared_ws), ink(shared_ws), ink(shared_ws), fl(shared_ws)]
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            assert torch.equal(o, ref_f if i in (1, 4) else ref_i), (B, i)
+        st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        moe.moe_workspace_status(shared_ws, st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
