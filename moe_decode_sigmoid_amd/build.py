@@ -12,7 +12,7 @@ CSRC = HERE / "csrc"
 OBJ = HERE / "_build"
 LIB = HERE / "libmoe_decode.so"
 SOURCES = ["capi.hip", "decode.hip", "decode_fused.hip", "decode_fused_nv.hip",
-           "decode_fused_bf.hip", "decode_fused_ns2.hip", "decode_stack.hip", "decode_chain_nv.hip", "decode_chain_bf.hip",
+           "decode_fused_bf.hip", "decode_fused_ns2.hip", "decode_fused_a4.hip", "decode_stack.hip", "decode_chain_nv.hip", "decode_chain_bf.hip",
            "decode_general.hip", "prefill.hip", "gemv.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 

@@ -56,6 +56,14 @@ bool split_path_forced();
 // Flint's shape with two shared experts and NVFP4 weights (the Inkling
 // shape at Flint's widths): a general shape that the single-launch kernel
 // also serves, for the plain layer.
+// Flint's shape in W4A4 at batch 1: the single-launch kernel (larger
+// batches take the general path, where h is quantised once per pair rather
+// than by every workgroup).
+bool a4_path(const moe_shape* s, int B) {
+  return s && s->wfmt == MOE_W_NVFP4_A4 && B == 1 && s->hidden == moe::kH &&
+         s->inter == moe::kI && s->n_experts == moe::kE && s->top_k == moe::kK &&
+         s->n_shared == 1 && moe::fused_a4_supported() && !split_path_forced();
+}
 bool ns2_path(const moe_shape* s) {
   return s && s->wfmt == MOE_W_NVFP4 && s->hidden == moe::kH && s->inter == moe::kI &&
          s->n_experts == moe::kE && s->top_k == moe::kK && s->n_shared == 2 &&
@@ -273,6 +281,12 @@ moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
   if (st != MOE_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   moe::GenShape g;
+  if (a4_path(shape, B)) {
+    const hipError_t e = moe::launch_decode_fused_a4(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), to_dev(routed),
+        to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out, static_cast<uint8_t*>(ws), s);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   if (ns2_path(shape)) {
     const hipError_t e = moe::launch_decode_fused_ns2(
         B, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), to_dev(routed),
@@ -342,7 +356,12 @@ moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32
   const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   hipError_t e;
   moe::GenShape g;
-  if (ns2_path(shape)) {
+  if (a4_path(shape, B)) {
+    e = moe::launch_decode_fused_a4(static_cast<const uint16_t*>(x),
+                                    static_cast<const uint16_t*>(router_w), to_dev(routed),
+                                    to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
+                                    static_cast<uint8_t*>(ws), s, e0, e1);
+  } else if (ns2_path(shape)) {
     e = moe::launch_decode_fused_ns2(B, static_cast<const uint16_t*>(x),
                                      static_cast<const uint16_t*>(router_w), to_dev(routed),
                                      to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,

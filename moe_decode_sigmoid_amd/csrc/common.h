@@ -228,6 +228,45 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// ------------------------------------------------------------ Four Over Six
+// Scalar steps of the NVFP4 activation quantiser with the Four Over Six block
+// scale (the Inkling-2-Small article, 48-layer MoE section), shared by the
+// general path and the single-launch W4A4 layer so that both take the same
+// decisions.
+// nearest-even onto the E4M3FN grid of a finite s >= 0, saturating at 448.
+// Branch-free (both the subnormal and the normal rounding are computed and
+// one is selected): called by every lane of a wave with lane-dependent s.
+__device__ __forceinline__ uint32_t a4_e4m3_rne(float s) {
+  // subnormal: multiples of 2^-9 (s < 2^-6)
+  const float ms = __builtin_rintf(__builtin_ldexpf(s, 9));
+  const uint32_t sub = ms >= 8.0f ? 0x08u : (uint32_t)fmaxf(ms, 0.0f);
+  // normal: 3 mantissa bits, carry into the exponent; past 448 saturates
+  int e = (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFF) - 127;
+  float m = __builtin_rintf(__fmul_rn(__fsub_rn(__builtin_ldexpf(s, -e), 1.0f), 8.0f));
+  const bool carry = m >= 8.0f;
+  m = carry ? 0.0f : m;
+  e = carry ? e + 1 : e;
+  const bool big = e > 8 || (e == 8 && m > 6.0f);
+  const uint32_t nor = big ? 0x7Eu : (uint32_t)(((e + 7) << 3) | (int)m);
+  return !(s > 0.0f) ? 0u : s >= 448.0f ? 0x7Eu : s < 0.015625f ? sub : nor;
+}
+
+// nearest-even onto the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at
+// 6, as a signed value: midpoints go to the neighbour with the even mantissa
+// bit (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4).
+// The grid's step is 0.5 below 2, 1 below 4 and 2 above, so this is
+// round-to-nearest-even at that step (v_rndne_f32 on an exactly scaled
+// value); the result is the same as the chain of comparisons the definition
+// reads as, for every input including the infinities.
+__device__ __forceinline__ float a4_e2m1_rne(float v) {
+  const float a = fabsf(v);
+  const float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);   // selects of constants
+  const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+  return __builtin_copysignf(fminf(__builtin_rintf(a * inv) * step, 6.0f), v);
+}
+
+__device__ __forceinline__ float a4_e4m3_value(uint32_t b) { return e4m3_to_f32<0>(b); }
+
 // s_waitcnt immediate that waits for this wave's vector memory operations
 // only (vmcnt 0; expcnt 7 and lgkmcnt 15 are "no wait" in gfx9's encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).

@@ -130,33 +130,6 @@ __device__ __forceinline__ void load_x32(const uint16_t* x, int H, int t, int ch
 // summed in element order over |v - e2m1 * q|), so every workgroup, and any
 // other implementation of these steps, takes the same decisions.
 
-// nearest-even onto the E4M3FN grid of a finite s >= 0, saturating at 448
-__device__ __forceinline__ uint32_t a4_e4m3_rne(float s) {
-  if (!(s > 0.0f)) return 0u;
-  if (s >= 448.0f) return 0x7Eu;
-  if (s < 0.015625f) {                                  // subnormal: multiples of 2^-9
-    const float m = __builtin_rintf(__builtin_ldexpf(s, 9));
-    return m >= 8.0f ? 0x08u : (uint32_t)m;
-  }
-  int e = (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFF) - 127;   // s normal here
-  float m = __builtin_rintf(__fmul_rn(__fsub_rn(__builtin_ldexpf(s, -e), 1.0f), 8.0f));
-  if (m >= 8.0f) { m = 0.0f; e += 1; }
-  if (e > 8 || (e == 8 && m > 6.0f)) return 0x7Eu;
-  return (uint32_t)(((e + 7) << 3) | (int)m);
-}
-
-// nearest-even onto the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at
-// 6, as a signed value: midpoints go to the neighbour with the even mantissa
-// bit (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4)
-__device__ __forceinline__ float a4_e2m1_rne(float v) {
-  const float a = fabsf(v);
-  const float r = a <= 0.25f ? 0.0f : a < 0.75f ? 0.5f : a <= 1.25f ? 1.0f : a < 1.75f ? 1.5f
-                : a <= 2.5f ? 2.0f : a < 3.5f ? 3.0f : a <= 5.0f ? 4.0f : 6.0f;
-  return __builtin_copysignf(r, v);
-}
-
-__device__ __forceinline__ float a4_e4m3_value(uint32_t b) { return e4m3_to_f32<0>(b); }
-
 // max over each aligned group of 16 lanes (a DPP row)
 __device__ __forceinline__ float group16_max(float v) {
   v = fmaxf(v, dpp_f32<0x128>(v));
@@ -191,8 +164,9 @@ __device__ __forceinline__ float a4_quant_elem(float v, float g, int lane, float
   const uint32_t s4 = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bmax, 4.0f), g));
   const float v6 = a4_e4m3_value(s6), v4 = a4_e4m3_value(s4);
   const float q6 = __fmul_rn(v6, g), q4 = __fmul_rn(v4, g);
-  const float c6 = q6 > 0.0f ? a4_e2m1_rne(__fdiv_rn(v, q6)) : 0.0f;
-  const float c4 = q4 > 0.0f ? a4_e2m1_rne(__fdiv_rn(v, q4)) : 0.0f;
+  const float r6 = a4_e2m1_rne(__fdiv_rn(v, q6 > 0.0f ? q6 : 1.0f));   // no branch around the
+  const float r4 = a4_e2m1_rne(__fdiv_rn(v, q4 > 0.0f ? q4 : 1.0f));   // divisions
+  const float c6 = q6 > 0.0f ? r6 : 0.0f, c4 = q4 > 0.0f ? r4 : 0.0f;
   const float m6 = group16_sum_in_order(fabsf(__fsub_rn(v, __fmul_rn(c6, q6))), lane, lds);
   const float m4 = group16_sum_in_order(fabsf(__fsub_rn(v, __fmul_rn(c4, q4))), lane, lds + 64);
   return m4 < m6 ? c4 * v4 : c6 * v6;

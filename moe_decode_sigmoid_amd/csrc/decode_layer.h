@@ -364,6 +364,63 @@ __device__ __forceinline__ void wave_top6(const float (&v)[N][4], int lane, int 
 }
 
 
+// Four Over Six quantisation (W4A4) of 16-element blocks held by lane pairs:
+// lane 2b holds elements 0..7 of block b as one 16-byte piece, lane 2b + 1
+// elements 8..15; g is the vector's global scale (amax / 2688).  Returns this
+// lane's 8 quantised values e2m1 * e4m3 (the global apart), exact in bf16.
+// The decisions are the general path's and the oracle's: candidate scales
+// E4M3(bmax / M / g) for M = 6 and 4, codes E2M1(v / (e4m3 * g)), and the
+// block's absolute errors summed in element order (the even lane's eight
+// from 0, the odd lane continuing from that sum); 4 only if strictly better.
+__device__ __forceinline__ uint4 a4_quant_piece(uint4 piece, float g) {
+  const uint32_t u[4] = {piece.x, piece.y, piece.z, piece.w};
+  float v[8], m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(u[i]);
+    v[2 * i + 1] = bf16_hi(u[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  const float bmax = fmaxf(m, dpp_f32<0xB1>(m));           // quad_perm [1,0,3,2]: the partner
+  const bool zero = g == 0.0f || bmax == 0.0f;
+  const float gg = zero ? 1.0f : g, bb = zero ? 1.0f : bmax;  // (no division by 0 on the way)
+  const uint32_t s6 = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bb, 6.0f), gg));
+  const uint32_t s4 = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bb, 4.0f), gg));
+  const float v6 = a4_e4m3_value(s6), v4 = a4_e4m3_value(s4);
+  const float q6 = __fmul_rn(v6, gg), q4 = __fmul_rn(v4, gg);
+  // codes; a scale that rounded to 0 gives code 0 (the division by a
+  // stand-in divisor keeps the code free of branches)
+  const bool p6 = q6 > 0.0f, p4 = q4 > 0.0f;
+  const float d6 = p6 ? q6 : 1.0f, d4 = p4 ? q4 : 1.0f;
+  float c6[8], c4[8], own6 = 0.0f, own4 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float r6 = a4_e2m1_rne(__fdiv_rn(v[i], d6)), r4 = a4_e2m1_rne(__fdiv_rn(v[i], d4));
+    c6[i] = p6 ? r6 : 0.0f;
+    c4[i] = p4 ? r4 : 0.0f;
+    own6 = __fadd_rn(own6, fabsf(__fsub_rn(v[i], __fmul_rn(c6[i], q6))));
+    own4 = __fadd_rn(own4, fabsf(__fsub_rn(v[i], __fmul_rn(c4[i], q4))));
+  }
+  // odd lane: continue from the even lane's sum over the block's first half
+  float t6 = dpp_f32<0xA0>(own6), t4 = dpp_f32<0xA0>(own4);   // quad_perm [0,0,2,2]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    t6 = __fadd_rn(t6, fabsf(__fsub_rn(v[i], __fmul_rn(c6[i], q6))));
+    t4 = __fadd_rn(t4, fabsf(__fsub_rn(v[i], __fmul_rn(c4[i], q4))));
+  }
+  const float m6 = dpp_f32<0xF5>(t6), m4 = dpp_f32<0xF5>(t4);   // quad_perm [1,1,3,3]: the odd lane's
+  const bool four = m4 < m6;
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = zero ? 0.0f : (four ? c4[2 * i] * v4 : c6[2 * i] * v6);
+    const float b = zero ? 0.0f : (four ? c4[2 * i + 1] * v4 : c6[2 * i + 1] * v6);
+    o[i] = f32x2_to_bf16x2_rne(a, b);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // LDS position (16-byte units) of piece q (elements 8 q .. 8 q + 7) of token
 // t's x row.  The low two bits of q are XORed with bits 3..4: a lane's
 // 32-element chunk is pieces 4 l .. 4 l + 3, and with this swizzle the lanes
@@ -381,10 +438,11 @@ __device__ __forceinline__ int sx_pos(int t, int q) { return t * (kH / 8) + (q ^
 // lane 16 i puts h = SiLU(g) * u of slot i's token t in hdst[t] (LDS: the
 // workgroup writes its h to the workspace in one go, so that no store sits in
 // front of the next weight loads in the wave's memory queue).
-template <int B, int FMT>
+template <int B, int FMT, bool A4 = false>
 __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk<FMT>& cu, float sg,
                                                float su, unsigned mask, int par, const uint4* s_x,
-                                               const uint32_t (&x0)[16], int lane, float* hdst) {
+                                               const uint32_t (&x0)[16], int lane, float* hdst,
+                                               float gx = 1.0f) {
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = 0.0f;
@@ -408,7 +466,12 @@ __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk
   const float z = wave_sum8(v, lane);
   const float zu = dpp_f32<0x128>(z);
   const int t = 2 * (lane >> 4) + par;
-  if ((lane & 15) == 0 && t < B && ((mask >> t) & 1u)) hdst[t] = silu_mul(z * sg, zu * su);
+  if ((lane & 15) == 0 && t < B && ((mask >> t) & 1u)) {
+    if constexpr (A4)   // the dot products ran on e2m1 * e4m3: times x's global
+      hdst[t] = silu_mul(z * sg * gx, zu * su * gx);
+    else
+      hdst[t] = silu_mul(z * sg, zu * su);
+  }
 }
 
 // 32 consecutive bf16 h values (chunk c16, as 16 packed pairs) of pair p
@@ -426,15 +489,20 @@ __device__ __forceinline__ void load_h(const uint4* s_h, int p, int c16, uint32_
 // 16 j .. 16 j + 15 of a wave hold rows 2 j and 2 j + 1 (32 columns each);
 // acc[r][t] gathers the lane's unreduced partial sums, scaled by the routing
 // weight of token t and the tensor scale.  The entry's h pairs start at p0.
-template <int B, int FMT>
+template <int B, int FMT, bool A4 = false>
 __device__ __forceinline__ void down_entry(const Chunk<FMT> (&rows)[2], float gl, unsigned mask,
                                            const float* wt /* by token */, const uint4* s_h,
-                                           int p0, int c16, float (&acc)[2][B]) {
+                                           int p0, int c16, float (&acc)[2][B],
+                                           const float* gh = nullptr /* W4A4: h global by pair */) {
   auto token = [&](int t, int p) __attribute__((always_inline)) {
     uint32_t h[16];
     load_h(s_h, p, c16, h);
     const float sc = wt[t] * gl;
-    const float d0 = rows[0].dot_x(h), d1 = rows[1].dot_x(h);
+    float d0 = rows[0].dot_x(h), d1 = rows[1].dot_x(h);
+    if constexpr (A4) {   // the dot products ran on e2m1 * e4m3: times the pair's global
+      d0 *= gh[p];
+      d1 *= gh[p];
+    }
 #pragma unroll
     for (int tt = 0; tt < B; ++tt)       // static register index for any t
       if (tt == t) {
@@ -531,7 +599,8 @@ constexpr bool kPrefetchNext = kK * B <= 4 * 2 * kDownDepth<B, FMT>;
 // layer is the residual stream the previous layer wrote).  XOUT: publish the
 // output as tagged slots for the next layer, and keep this thread's output
 // element in resid_reg.
-template <int B, int FMT, bool NORM, int RES, int PF, bool EPREG, int XIN, bool XOUT, int NS = 1>
+template <int B, int FMT, bool NORM, int RES, int PF, bool EPREG, int XIN, bool XOUT, int NS = 1,
+          bool A4 = false>
 __device__ __forceinline__ void decode_layer(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, const ExpertsDev& routed,
     const ExpertsDev& shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
@@ -551,6 +620,11 @@ __device__ __forceinline__ void decode_layer(
   // the gate/up rows: the gate/up burst then carries only gate/up rows
   constexpr bool kLateDown = B == 1;
   static_assert(NS >= 1 && NS <= kMaxShared, "one or two shared experts");
+  // W4A4 (NVFP4 activations with the Four Over Six block scale, FMT_NVFP4
+  // weights): the plain batch-1 layer; x and h are quantised by every
+  // workgroup itself (all of x, and all of h after the h copy)
+  static_assert(!A4 || (B == 1 && FMT == FMT_NVFP4 && !NORM && RES == 0 && XIN == 0 && !XOUT &&
+                        NS == 1 && PF == 0), "W4A4: the plain batch-1 NVFP4 layer");
   constexpr int kPairs = (kK + NS) * B;              // h pairs: 6 B routed + NS B shared
   const int g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -754,6 +828,19 @@ __device__ __forceinline__ void decode_layer(
     __syncthreads();
   }
   trace_stamp(ws, 1);
+  // W4A4: this wave's maximum |x| (x's global scale is amax / 2688), visible
+  // to every wave after the barrier behind the router dot
+  float* s_a4max = nullptr;
+  if constexpr (A4) {
+    __shared__ float s_a4max_[4];
+    s_a4max = s_a4max_;
+    const uint32_t u[4] = {xr[0].x, xr[0].y, xr[0].z, xr[0].w};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[i])), fabsf(bf16_hi(u[i]))));
+    m = wave_max(m);
+    if (lane == 0) s_a4max[wave] = m;
+  }
   {
     float acc[B];
 #pragma unroll
@@ -783,11 +870,24 @@ __device__ __forceinline__ void decode_layer(
     }
   }
   trace_stamp(ws, 2);
+  // W4A4: x quantised in place (the router has read it; every workgroup
+  // quantises all of x, each thread its own piece), x0 reread
+  float gx = 1.0f;
+  if constexpr (A4) {
+    gx = __fdiv_rn(fmaxf(fmaxf(s_a4max[0], s_a4max[1]), fmaxf(s_a4max[2], s_a4max[3])), 2688.0f);
+    s_x[sx_pos(0, tid)] = a4_quant_piece(xr[0], gx);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = s_x[sx_pos(0, 4 * lane + i)];
+      x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
+    }
+  }
   if (smask) {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      gateup_compute<B, FMT>(pre.scg[s], pre.scu[s], sh_sg[s], sh_su[s], smask, wave >> 1, s_x, x0,
-                             lane, &s_hsh[s][wave & 1][0]);
+      gateup_compute<B, FMT, A4>(pre.scg[s], pre.scu[s], sh_sg[s], sh_su[s], smask, wave >> 1, s_x,
+                                 x0, lane, &s_hsh[s][wave & 1][0], gx);
   }
   trace_stamp(ws, 3);
 
@@ -1028,7 +1128,10 @@ __device__ __forceinline__ void decode_layer(
         const float z = wave_sum8(v, lane);
         const float zu = dpp_f32<0x128>(z);
         if ((lane & 15) == 0 && ((mme >> t) & 1u))
-          s_hout[ime][t] = silu_mul(z * sgme, zu * sume);
+          if constexpr (A4)
+            s_hout[ime][t] = silu_mul(z * sgme * gx, zu * sume * gx);
+          else
+            s_hout[ime][t] = silu_mul(z * sgme, zu * sume);
       }
     };
     // the routed entries' tensor scales: one thread each, fetched beside the
@@ -1226,6 +1329,31 @@ __device__ __forceinline__ void decode_layer(
   }
   __syncthreads();
   trace_stamp(ws, 10);
+  // W4A4: every h pair quantised in place with its own global (amax / 2688):
+  // wave w takes pairs w and w + 4, lane l its 16-byte chunk l (elements 8 l
+  // .. 8 l + 7, at LDS position 16 (l % 4) + l / 4 of the pair), so that the
+  // lanes of a 16-element block are a lane pair
+  float* s_gh = nullptr;
+  if constexpr (A4) {
+    __shared__ float s_gh_[kPairs];
+    s_gh = s_gh_;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int p = wave + 4 * r;
+      if (p < kPairs) {
+        uint4* c = s_xh + p * 64 + 16 * (lane & 3) + (lane >> 2);
+        const uint4 v = *c;
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[i])), fabsf(bf16_hi(u[i]))));
+        const float ghp = __fdiv_rn(wave_max(m), 2688.0f);
+        if (lane == 0) s_gh[p] = ghp;
+        *c = a4_quant_piece(v, ghp);
+      }
+    }
+    __syncthreads();
+  }
   // The next layer's router row and shared gate/up rows (registers free
   // since step A): no load of this layer is issued after this point when
   // every routed entry's down rows are already in flight, so these wait
@@ -1249,8 +1377,13 @@ __device__ __forceinline__ void decode_layer(
       if (t < B) {
         uint32_t h[16];
         load_h(s_h, kK * B + s * B + t, c16, h);
-        accs[0][j] = __builtin_fmaf(gl, pre.dsh[s][0].dot_x(h), accs[0][j]);
-        accs[1][j] = __builtin_fmaf(gl, pre.dsh[s][1].dot_x(h), accs[1][j]);
+        float d0 = pre.dsh[s][0].dot_x(h), d1 = pre.dsh[s][1].dot_x(h);
+        if constexpr (A4) {
+          d0 *= s_gh[kK * B + s * B + t];
+          d1 *= s_gh[kK * B + s * B + t];
+        }
+        accs[0][j] = __builtin_fmaf(gl, d0, accs[0][j]);
+        accs[1][j] = __builtin_fmaf(gl, d1, accs[1][j]);
       }
     }
   }
@@ -1263,8 +1396,8 @@ __device__ __forceinline__ void decode_layer(
       if (k0 + q < n_mine) {
         const int a = wsel + 4 * (k0 + q);
         const int e = s_act[a];
-        down_entry<B, FMT>(buf[q], s_gs[a][2], s_amask[a],
-                           &s_wfull[e][0], s_h, s_pair0[a], c16, acc);
+        down_entry<B, FMT, A4>(buf[q], s_gs[a][2], s_amask[a],
+                               &s_wfull[e][0], s_h, s_pair0[a], c16, acc, s_gh);
       }
     }
   };
@@ -1359,7 +1492,7 @@ __device__ __forceinline__ void decode_layer(
   trace_flush(ws);
 }
 
-template <int B, int FMT, bool NORM, bool RESID, int NS = 1>
+template <int B, int FMT, bool NORM, bool RESID, int NS = 1, bool A4 = false>
 __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ rw, ExpertsDev routed,
     ExpertsDev shared, uint16_t* __restrict__ out, int32_t* __restrict__ ids_out,
@@ -1367,7 +1500,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void k_decode_fused(
   StepAPre<FMT, NS> pre;
   uint32_t epoch = 0;
   float resid = 0.0f;
-  decode_layer<B, FMT, NORM, RESID ? 1 : 0, 0, false, 0, false, NS>(
+  decode_layer<B, FMT, NORM, RESID ? 1 : 0, 0, false, 0, false, NS, A4>(
       x, rw, routed, shared, out, ids_out, w_out, ws, fz, pre, LayerDev{}, epoch, resid);
 }
 

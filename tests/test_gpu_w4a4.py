@@ -13,6 +13,9 @@ h, at the usual tolerance (a decomposition).  End to end, the output is also
 compared with the oracle run from x alone (its own quantised x, h and
 quantised h) at the same tolerance, ids forced only for near-ties.  Inputs: seeded synthetic NVFP4 layers (weights
 N(0, 0.02) bf16 packed to NVFP4, x ~ N(0, 1) bf16)."""
+import contextlib
+import os
+
 import numpy as np
 import pytest
 
@@ -47,7 +50,24 @@ def bf16_f64(u16):
     return (np.asarray(u16, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def run(name, seed, B):
+@contextlib.contextmanager
+def general_path(on=True):
+    """Flint's shape at batch 1 runs on the single-launch kernel; with this
+    switch (the library's MOE_DECODE_SPLIT) it takes the four-launch general
+    path, whose workspace exposes x, h and their quantisations."""
+    old = os.environ.get("MOE_DECODE_SPLIT")
+    if on:
+        os.environ["MOE_DECODE_SPLIT"] = "1"
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("MOE_DECODE_SPLIT", None)
+        else:
+            os.environ["MOE_DECODE_SPLIT"] = old
+
+
+def run(name, seed, B, general=False):
     H, I, E, K, NS = SHAPES[name]
     host, dl = layer(name, seed)
     S = moe.shape(moe.MOE_W_NVFP4_A4, hidden=H, inter=I, n_experts=E, top_k=K, n_shared=NS)
@@ -56,9 +76,10 @@ def run(name, seed, B):
     ids = torch.empty((B, K), dtype=torch.int32, device="cuda")
     w = torch.empty((B, K), dtype=torch.float32, device="cuda")
     ws = moe.alloc_workspace(moe.moe_workspace_bytes(B, S=S))
-    moe.moe_decode_forward(moe.device.to_device_bf16(x), dl.router, dl.routed, dl.shared, out, ws,
-                           ids, w, S=S)
-    torch.cuda.synchronize()
+    with general_path(general):
+        moe.moe_decode_forward(moe.device.to_device_bf16(x), dl.router, dl.routed, dl.shared, out,
+                               ws, ids, w, S=S)
+        torch.cuda.synchronize()
     off = moe.general_workspace_layout(S)
     raw = ws.cpu().numpy()
 
@@ -88,7 +109,7 @@ def slots_of(ws_d, B):
 @pytest.mark.parametrize("name,B", [("flint", 1), ("flint", 8), ("inkling2small", 3),
                                     ("ragged", 5)])
 def test_w4a4_layer(name, B):
-    host, x, y, ids, w, ws_d = run(name, 3, B)
+    host, x, y, ids, w, ws_d = run(name, 3, B, general=True)
     # 1. x quantised bit for bit as the oracle quantises it
     for t in range(B):
         codes, scales, g, vals = oracle.quant_fp4_46(bf16_f64(x[t]).astype(np.float32))
@@ -117,17 +138,19 @@ def test_w4a4_layer(name, B):
 
 
 def test_w4a4_tokens_are_independent():
-    host, x, y, ids, w, _ = run("flint", 4, 4)
+    """On the general path a token's result does not depend on the batch."""
+    host, x, y, ids, w, _ = run("flint", 4, 4, general=True)
     H = SHAPES["flint"][0]
     host, dl = layer("flint", 4)
     S = moe.shape(moe.MOE_W_NVFP4_A4)
     ws = moe.alloc_workspace(moe.moe_workspace_bytes(1, S=S))
-    for t in range(4):
-        o = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
-        moe.moe_decode_forward(moe.device.to_device_bf16(x[t:t + 1].copy()), dl.router, dl.routed,
-                               dl.shared, o, ws, S=S)
-        torch.cuda.synchronize()
-        assert np.array_equal(parity.bf16_out_to_f64(o)[0], y[t]), t
+    with general_path():
+        for t in range(4):
+            o = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+            moe.moe_decode_forward(moe.device.to_device_bf16(x[t:t + 1].copy()), dl.router,
+                                   dl.routed, dl.shared, o, ws, S=S)
+            torch.cuda.synchronize()
+            assert np.array_equal(parity.bf16_out_to_f64(o)[0], y[t]), t
 
 
 @pytest.mark.parametrize("name,B,seed", [("flint", 1, 5), ("flint", 8, 5), ("flint", 4, 6),
@@ -147,3 +170,47 @@ def test_w4a4_end_to_end_against_the_oracles_own_h(name, B, seed):
                                           forced_ids=ids[t:t + 1].copy())[0][0]
     parity.check_weights(ids, w, ids_or, w_or, gap)
     print(parity.check_output(y, y_or, f"w4a4 e2e {name} B {B}"))
+
+
+# ---------------------------------------------------------------- single launch
+# Flint's shape at batch 1 runs on the single-launch kernel, every workgroup
+# quantising x and all h pairs itself with the same decisions.
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_w4a4_single_launch_end_to_end(seed):
+    test_w4a4_end_to_end_against_the_oracles_own_h("flint", 1, seed)
+
+
+def test_w4a4_single_launch_agrees_with_the_general_path():
+    for seed in (21, 22):
+        _, _, y1, ids1, w1, _ = run("flint", seed, 1)
+        _, _, y2, ids2, w2, _ = run("flint", seed, 1, general=True)
+        assert sorted(ids1[0].tolist()) == sorted(ids2[0].tolist())
+        np.testing.assert_allclose(np.sort(w1[0]), np.sort(w2[0]), rtol=2e-5, atol=1e-6)
+        parity.check_output(y1, y2, f"w4a4 single launch vs general, seed {seed}")
+
+
+def test_w4a4_single_launch_repeats_and_shares_a_workspace():
+    """Repeated calls give the same bits, and W4A4 and W4A16 single-launch
+    calls alternate on one workspace as on separate ones."""
+    H = SHAPES["flint"][0]
+    host, dl = layer("flint", 31)
+    S4 = moe.shape(moe.MOE_W_NVFP4_A4)
+    x = moe.device.to_device_bf16(testgen.make_x(131, 1, H))
+    nbytes = max(moe.moe_workspace_bytes(1, S=S4), moe.moe_workspace_bytes(1))
+    ws = moe.alloc_workspace(nbytes)
+
+    def call(S):
+        o = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+        moe.moe_decode_forward(x, dl.router, dl.routed, dl.shared, o, ws, S=S)
+        return o
+    ref4 = call(S4)
+    ref16 = call(None)
+    outs = [call(S4), call(None), call(S4), call(S4), call(None)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, ref16 if i in (1, 4) else ref4), i
+    st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    moe.moe_workspace_status(ws, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
