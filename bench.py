@@ -105,7 +105,7 @@ def write_traffic_record(dec_fetch: str, dec_write: str, copy_fetch: str, copy_w
     gib_kib = float(1 << 20)
     fs, wsc = gib_kib / f_cp, gib_kib / w_cp
     for kname, label, record, n in [
-            ("k_decode_fused<1, 0, false, false>", "k_decode_fused<1, nvfp4>",
+            ("k_decode_fused<1, 0, false, false, 1, false>", "k_decode_fused<1, nvfp4>",
              "k_decode_fused_b1_traffic", 1),
             ("k_decode_stack<1, 0>", f"k_decode_stack<1, nvfp4> ({layers} layers)",
              "k_decode_stack_b1_traffic", layers),
