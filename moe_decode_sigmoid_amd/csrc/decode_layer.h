@@ -446,22 +446,30 @@ __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-#pragma unroll
-  for (int t = 0; t < B; ++t) {
-    if (!((mask >> t) & 1u)) continue;
-    uint32_t xw[16];
-    if constexpr (B == 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xw[i] = x0[i];
-    } else {
+  if constexpr (B == 1) {
+    if (mask & 1u) {
+      v[0] = cg.dot_x(x0);
+      v[1] = cu.dot_x(x0);
+    }
+  } else {
+    // the tokens (a wave-uniform mask) in a rolled loop, for code size
+#pragma unroll 1
+    for (unsigned mm = __builtin_amdgcn_readfirstlane(mask); mm != 0u; mm &= mm - 1u) {
+      const int t = __builtin_ctz(mm);
+      uint32_t xw[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint4 u4 = s_x[sx_pos(t, 4 * lane + i)];
         xw[4 * i] = u4.x; xw[4 * i + 1] = u4.y; xw[4 * i + 2] = u4.z; xw[4 * i + 3] = u4.w;
       }
+      const float dg = cg.dot_x(xw), du = cu.dot_x(xw);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)           // static register index for any t
+        if (j == (t >> 1)) {
+          v[2 * j] = dg;
+          v[2 * j + 1] = du;
+        }
     }
-    v[2 * (t >> 1)] = cg.dot_x(xw);
-    v[2 * (t >> 1) + 1] = cu.dot_x(xw);
   }
   const float z = wave_sum8(v, lane);
   const float zu = dpp_f32<0x128>(z);
@@ -957,6 +965,7 @@ __device__ __forceinline__ void decode_layer(
     int my_id[2];
     float my_l[2];
     wave_top6<2>(v, lane, my_id, my_l);
+    trace_stamp(ws, 19);
     finish(wave, my_id[0], my_l[0]);
     finish(wave + 4, my_id[1], my_l[1]);
   } else if (wave < B) {
@@ -1105,20 +1114,7 @@ __device__ __forceinline__ void decode_layer(
           sume = suq[q];
         }
       const int ime = T0 + wave + 4 * (j0 + qme) - T0;
-#pragma unroll
-      for (int t = 0; t < B; ++t) {
-        if (!((um >> t) & 1u)) continue;
-        uint32_t xw[16];
-        if constexpr (B == 1) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xw[i] = x0[i];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 v = s_x[sx_pos(t, 4 * lane + i)];
-            xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
-          }
-        }
+      auto token = [&](int t, const uint32_t (&xw)[16]) __attribute__((always_inline)) {
         float v[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1127,11 +1123,30 @@ __device__ __forceinline__ void decode_layer(
         }
         const float z = wave_sum8(v, lane);
         const float zu = dpp_f32<0x128>(z);
-        if ((lane & 15) == 0 && ((mme >> t) & 1u))
+        if ((lane & 15) == 0 && ((mme >> t) & 1u)) {
           if constexpr (A4)
             s_hout[ime][t] = silu_mul(z * sgme * gx, zu * sume * gx);
           else
             s_hout[ime][t] = silu_mul(z * sgme, zu * sume);
+        }
+      };
+      if constexpr (B == 1) {
+        token(0, x0);
+      } else {
+        // the batch's tokens (a wave-uniform mask) in a rolled loop: unrolled
+        // over 8 tokens, the five batch bodies of this loop came to most of
+        // the kernel's code, more than the instruction cache holds
+#pragma unroll 1
+        for (unsigned mm = __builtin_amdgcn_readfirstlane(um); mm != 0u; mm &= mm - 1u) {
+          const int t = __builtin_ctz(mm);
+          uint32_t xw[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 v = s_x[sx_pos(t, 4 * lane + i)];
+            xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+          }
+          token(t, xw);
+        }
       }
     };
     // the routed entries' tensor scales: one thread each, fetched beside the
