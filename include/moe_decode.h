@@ -374,6 +374,20 @@ moe_status moe_general_workspace_layout(const moe_shape* shape, size_t offsets[8
 moe_status moe_nvfp4_dequant(const moe_shape* shape, const moe_experts* set, int32_t expert,
                              int32_t tensor, float* out, void* stream);
 
+/* Check of the hardware converts behind the W4A4 quantiser's roundings
+ * (Inkling-2-Small article, 48-layer MoE section: NVFP4 activations with
+ * the Four Over Six block scale).  The single-launch W4A4 kernel rounds
+ * block scales to E4M3 (nearest-even, saturating at 448) and scaled values
+ * to E2M1 (nearest-even, saturating at 6) with gfx950's fp32 -> FP8 / FP4
+ * converts; this runs them over every fp32 bit pattern against the
+ * roundings written out as arithmetic and writes the mismatch counts:
+ *   counts  device pointer to 2 uint64, overwritten: [0] E2M1 mismatches
+ *           over all finite fp32 values, [1] E4M3 mismatches over all
+ *           non-negative finite ones (both 0 on a conforming device).
+ * Asynchronous on `stream`; about 2^33 conversions.  MOE_ERR_INVALID_ARG for
+ * a null pointer, MOE_ERR_MISALIGNED for one not 8-byte aligned. */
+moe_status moe_a4_convert_check(uint64_t* counts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.moe_general_workspace_layout.argtypes = [P(Shape), P(sz)]
         L.moe_nvfp4_dequant.restype = ctypes.c_int
         L.moe_nvfp4_dequant.argtypes = [P(Shape), P(Experts), i32, i32, vp, vp]
+        L.moe_a4_convert_check.restype = ctypes.c_int
+        L.moe_a4_convert_check.argtypes = [vp, vp]
         _LIB = L
     return _LIB
 
@@ -331,6 +333,14 @@ def moe_workspace_status(ws, status, stream=None):
     st = lib().moe_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), _ptr(status),
                                     _stream(stream))
     _check(st, "moe_workspace_status")
+
+
+def moe_a4_convert_check(counts, stream=None):
+    """The W4A4 quantiser's hardware roundings against their definitions over
+    every fp32 bit pattern; counts: int64 [2] on the device, overwritten with
+    the E2M1 and E4M3 mismatch counts."""
+    st = lib().moe_a4_convert_check(_ptr(counts), _stream(stream))
+    _check(st, "moe_a4_convert_check")
 
 
 def moe_nvfp4_dequant(expert_set, expert: int, tensor: int, out, stream=None):

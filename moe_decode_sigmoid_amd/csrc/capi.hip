@@ -566,6 +566,14 @@ moe_status moe_nvfp4_dequant(const moe_shape* shape, const moe_experts* set, int
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+moe_status moe_a4_convert_check(uint64_t* counts, void* stream) {
+  moe_status st;
+  if ((st = check_ptr(counts, 8)) != MOE_OK) return st;
+  hipError_t e = moe::launch_a4_convert_check(reinterpret_cast<unsigned long long*>(counts),
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 moe_status moe_nvfp4_gemv(const void* x, int32_t B, int32_t K, int32_t N, const void* codes,
                           const void* scales, const float* global, void* y, void* stream) {
   moe_status st;

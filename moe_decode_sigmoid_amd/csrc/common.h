@@ -267,6 +267,48 @@ __device__ __forceinline__ float a4_e2m1_rne(float v) {
 
 __device__ __forceinline__ float a4_e4m3_value(uint32_t b) { return e4m3_to_f32<0>(b); }
 
+// The same two roundings by gfx950's converts, equal to the functions above
+// for every input (an exhaustive GPU check, moe_a4_convert_check: every fp32
+// bit pattern for E2M1, every non-negative finite fp32 for E4M3):
+//  - a4_e4m3_pk: E4M3 codes of two scales s >= 0 in bytes 0 and 1 (the fp32
+//    -> FP8 convert rounds to nearest-even; 448 is its largest finite value,
+//    and min(s, 448) makes it saturate there);
+//  - a4_e2m1_pk8 / a4_e2m1_unpk8: E2M1 codes of 8 values, two per byte
+//    (value 2 j in the low nibble of byte j), and their values (the fp32 ->
+//    FP4 convert rounds to nearest-even and saturates at 6; a scale operand
+//    of 1 leaves the values unscaled).
+__device__ __forceinline__ uint32_t a4_e4m3_pk(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(a, 448.0f), fminf(b, 448.0f), 0, false);
+}
+__device__ __forceinline__ uint32_t a4_e2m1_pk8(const float (&r)[8]) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[2], r[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[4], r[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[6], r[7], 1.0f, 3);
+}
+__device__ __forceinline__ void a4_e2m1_unpk8(uint32_t w, float (&c)[8]) {
+  const f32x2 c0 = fp4x2_to_f32<0>(w), c1 = fp4x2_to_f32<1>(w), c2 = fp4x2_to_f32<2>(w),
+              c3 = fp4x2_to_f32<3>(w);
+  c[0] = c0[0]; c[1] = c0[1]; c[2] = c1[0]; c[3] = c1[1];
+  c[4] = c2[0]; c[5] = c2[1]; c[6] = c3[0]; c[7] = c3[1];
+}
+
+// v / d rounded to nearest even, given y = RN(1 / d) (d > 0): the product
+// q = RN(v y) is within an ulp of v / d, and one residual step RN(q + (v - d q) y),
+// the residual exact by FMA, gives the correctly rounded quotient (Markstein's
+// theorem on division through a correctly rounded reciprocal).  Every step
+// scales exactly with the exponents of v and d while v, d, y, q and the
+// residual are normal numbers, so a host check of every bf16 significand of v
+// against every fp32 significand of d covers the normal range; callers keep d
+// in [2^-64, 2^64], where a quotient of 1/8 or more leaves every step normal
+// and a smaller one stays below the first E2M1 midpoint (1/4) either way.  A
+// zero quotient takes v's sign, as the division's does.
+__device__ __forceinline__ float div_by_recip(float v, float d, float y) {
+  const float q = __fmul_rn(v, y);
+  const float r = __builtin_fmaf(-d, q, v);
+  return __builtin_copysignf(__builtin_fmaf(r, y, q), v);
+}
+
 // s_waitcnt immediate that waits for this wave's vector memory operations
 // only (vmcnt 0; expcnt 7 and lgkmcnt 15 are "no wait" in gfx9's encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).

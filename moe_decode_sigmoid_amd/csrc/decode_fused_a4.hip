@@ -29,4 +29,46 @@ hipError_t launch_decode_fused_a4(const uint16_t* x, const uint16_t* rw, const E
   return hipGetLastError();
 }
 
+// Exhaustive check of the converts the quantiser takes its roundings from
+// (a4_e4m3_pk, a4_e2m1_pk8 / a4_e2m1_unpk8) against the roundings' own
+// definitions (a4_e4m3_rne, a4_e2m1_rne): thread i of part p takes the 256
+// fp32 bit patterns p 2^31 + 256 i + j.  counts[0]: E2M1 mismatches over all
+// finite fp32 values; counts[1]: E4M3 mismatches over all non-negative
+// finite ones.  A pattern's value is compared bit for bit.
+constexpr int kCvtPerThread = 256;
+__global__ __launch_bounds__(256) void k_a4_convert_check(unsigned long long* counts, uint32_t part) {
+  const uint64_t base = ((uint64_t)part << 31) +
+                        ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * kCvtPerThread;
+  unsigned long long b0 = 0, b1 = 0;
+  for (int j = 0; j < kCvtPerThread; j += 8) {
+    float r[8], c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = (uint32_t)(base + j + i);
+      r[i] = (u & 0x7F800000u) == 0x7F800000u ? 0.0f : __builtin_bit_cast(float, u);
+    }
+    a4_e2m1_unpk8(a4_e2m1_pk8(r), c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (__builtin_bit_cast(uint32_t, c[i]) != __builtin_bit_cast(uint32_t, a4_e2m1_rne(r[i]))) b0++;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const uint32_t sc = a4_e4m3_pk(fabsf(r[i]), fabsf(r[i + 1]));
+      if ((sc & 0xFFu) != a4_e4m3_rne(fabsf(r[i]))) b1++;
+      if (((sc >> 8) & 0xFFu) != a4_e4m3_rne(fabsf(r[i + 1]))) b1++;
+    }
+  }
+  if (b0) atomicAdd(counts + 0, b0);
+  if (b1) atomicAdd(counts + 1, b1);
+}
+
+hipError_t launch_a4_convert_check(unsigned long long* counts, hipStream_t st) {
+  hipError_t e = hipMemsetAsync(counts, 0, 2 * sizeof(unsigned long long), st);
+  if (e != hipSuccess) return e;
+  const unsigned blocks = (1u << 31) / kCvtPerThread / 256;
+  for (uint32_t part = 0; part < 2; ++part)
+    hipLaunchKernelGGL(k_a4_convert_check, dim3(blocks), dim3(256), 0, st, counts, part);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -385,29 +385,55 @@ __device__ __forceinline__ uint4 a4_quant_piece(uint4 piece, float g) {
   const float bmax = fmaxf(m, dpp_f32<0xB1>(m));           // quad_perm [1,0,3,2]: the partner
   const bool zero = g == 0.0f || bmax == 0.0f;
   const float gg = zero ? 1.0f : g, bb = zero ? 1.0f : bmax;  // (no division by 0 on the way)
-  const uint32_t s6 = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bb, 6.0f), gg));
-  const uint32_t s4 = a4_e4m3_rne(__fdiv_rn(__fdiv_rn(bb, 4.0f), gg));
-  const float v6 = a4_e4m3_value(s6), v4 = a4_e4m3_value(s4);
+  // bmax / 6 through the reciprocal (bmax is a bf16 value; see
+  // div_by_recip), bmax / 4 as a product (exact, or the same rounding when
+  // it underflows); the divisions by the global stay divisions
+  const float b6 = div_by_recip(bb, 6.0f, 0x1.555556p-3f), b4 = __fmul_rn(bb, 0.25f);
+  const uint32_t sc = a4_e4m3_pk(__fdiv_rn(b6, gg),     // byte 0: M = 6
+                                 __fdiv_rn(b4, gg));    // byte 1: M = 4
+  const float v6 = e4m3_to_f32<0>(sc), v4 = e4m3_to_f32<1>(sc);
   const float q6 = __fmul_rn(v6, gg), q4 = __fmul_rn(v4, gg);
   // codes; a scale that rounded to 0 gives code 0 (the division by a
   // stand-in divisor keeps the code free of branches)
   const bool p6 = q6 > 0.0f, p4 = q4 > 0.0f;
   const float d6 = p6 ? q6 : 1.0f, d4 = p4 ? q4 : 1.0f;
-  float c6[8], c4[8], own6 = 0.0f, own4 = 0.0f;
+  // the 16 quotients v / d, correctly rounded: from the reciprocal of each
+  // divisor when every block of the wave has divisors in [2^-64, 2^64] (see
+  // div_by_recip), else by division
+  float r6[8], r4[8];
+  const bool in_range = d6 >= 0x1p-64f && d6 <= 0x1p64f && d4 >= 0x1p-64f && d4 <= 0x1p64f;
+  if (__builtin_expect(__ballot(!in_range) == 0ull, 1)) {
+    const float y6 = __fdiv_rn(1.0f, d6), y4 = __fdiv_rn(1.0f, d4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      r6[i] = div_by_recip(v[i], d6, y6);
+      r4[i] = div_by_recip(v[i], d4, y4);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      r6[i] = __fdiv_rn(v[i], d6);
+      r4[i] = __fdiv_rn(v[i], d4);
+    }
+  }
+  float c6[8], c4[8], e6[8], e4[8], own6 = 0.0f, own4 = 0.0f;
+  a4_e2m1_unpk8(a4_e2m1_pk8(r6), c6);
+  a4_e2m1_unpk8(a4_e2m1_pk8(r4), c4);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float r6 = a4_e2m1_rne(__fdiv_rn(v[i], d6)), r4 = a4_e2m1_rne(__fdiv_rn(v[i], d4));
-    c6[i] = p6 ? r6 : 0.0f;
-    c4[i] = p4 ? r4 : 0.0f;
-    own6 = __fadd_rn(own6, fabsf(__fsub_rn(v[i], __fmul_rn(c6[i], q6))));
-    own4 = __fadd_rn(own4, fabsf(__fsub_rn(v[i], __fmul_rn(c4[i], q4))));
+    c6[i] = p6 ? c6[i] : 0.0f;
+    c4[i] = p4 ? c4[i] : 0.0f;
+    e6[i] = fabsf(__fsub_rn(v[i], __fmul_rn(c6[i], q6)));
+    e4[i] = fabsf(__fsub_rn(v[i], __fmul_rn(c4[i], q4)));
+    own6 = __fadd_rn(own6, e6[i]);
+    own4 = __fadd_rn(own4, e4[i]);
   }
   // odd lane: continue from the even lane's sum over the block's first half
   float t6 = dpp_f32<0xA0>(own6), t4 = dpp_f32<0xA0>(own4);   // quad_perm [0,0,2,2]
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    t6 = __fadd_rn(t6, fabsf(__fsub_rn(v[i], __fmul_rn(c6[i], q6))));
-    t4 = __fadd_rn(t4, fabsf(__fsub_rn(v[i], __fmul_rn(c4[i], q4))));
+    t6 = __fadd_rn(t6, e6[i]);
+    t4 = __fadd_rn(t4, e4[i]);
   }
   const float m6 = dpp_f32<0xF5>(t6), m4 = dpp_f32<0xF5>(t4);   // quad_perm [1,1,3,3]: the odd lane's
   const bool four = m4 < m6;
@@ -884,7 +910,9 @@ __device__ __forceinline__ void decode_layer(
   if constexpr (A4) {
     gx = __fdiv_rn(fmaxf(fmaxf(s_a4max[0], s_a4max[1]), fmaxf(s_a4max[2], s_a4max[3])), 2688.0f);
     s_x[sx_pos(0, tid)] = a4_quant_piece(xr[0], gx);
+    trace_stamp(ws, 22);
     __syncthreads();
+    trace_stamp(ws, 23);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 v = s_x[sx_pos(0, 4 * lane + i)];
@@ -1352,7 +1380,8 @@ __device__ __forceinline__ void decode_layer(
   if constexpr (A4) {
     __shared__ float s_gh_[kPairs];
     s_gh = s_gh_;
-#pragma unroll
+    // one copy of the quantiser's code serves both rounds
+#pragma unroll 1
     for (int r = 0; r < 2; ++r) {
       const int p = wave + 4 * r;
       if (p < kPairs) {
@@ -1367,7 +1396,9 @@ __device__ __forceinline__ void decode_layer(
         *c = a4_quant_piece(v, ghp);
       }
     }
+    trace_stamp(ws, 20);
     __syncthreads();
+    trace_stamp(ws, 21);
   }
   // The next layer's router row and shared gate/up rows (registers free
   // since step A): no load of this layer is issued after this point when

@@ -37,6 +37,7 @@ hipError_t launch_decode_fused_ns2(int B, const uint16_t* x, const uint16_t* rw,
 // The same single-launch layer in W4A4 (NVFP4 weights, NVFP4 activations
 // with the Four Over Six block scale), Flint's shape, batch 1.
 bool fused_a4_supported();
+hipError_t launch_a4_convert_check(unsigned long long* counts, hipStream_t st);
 hipError_t launch_decode_fused_a4(const uint16_t* x, const uint16_t* rw, const ExpertsDev& routed,
                                   const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
                                   uint8_t* ws, hipStream_t st, hipEvent_t ev_start = nullptr,

@@ -351,3 +351,9 @@ def test_dequant_argument_errors():
     Sb = moe.shape(moe.MOE_W_BF16)
     assert L.moe_nvfp4_dequant(ctypes.byref(Sb), ctypes.byref(X), 0, 0, A + 0x1000000, 0) == \
         moe.MOE_ERR_UNSUPPORTED
+
+
+def test_convert_check_argument_errors():
+    L = moe.lib()
+    assert L.moe_a4_convert_check(None, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_a4_convert_check(A + 4, 0) == moe.MOE_ERR_MISALIGNED

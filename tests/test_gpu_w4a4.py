@@ -214,3 +214,15 @@ def test_w4a4_single_launch_repeats_and_shares_a_workspace():
     moe.moe_workspace_status(ws, st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
+
+
+@pytest.mark.gpu
+def test_quantiser_converts_equal_the_rounding_definitions():
+    """The single-launch quantiser's E4M3 and E2M1 roundings come from
+    gfx950's fp32 -> FP8 / FP4 converts; over every fp32 bit pattern they
+    equal the roundings written out as arithmetic (nearest-even, saturating
+    at 448 and 6)."""
+    counts = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+    moe.moe_a4_convert_check(counts)
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [0, 0]
