@@ -994,8 +994,31 @@ __device__ __forceinline__ void decode_layer(
     float my_l[2];
     wave_top6<2>(v, lane, my_id, my_l);
     trace_stamp(ws, 19);
-    finish(wave, my_id[0], my_l[0]);
-    finish(wave + 4, my_id[1], my_l[1]);
+    // finish() for both tokens, the two chains side by side (same arithmetic)
+    const float s0 = 1.0f / (1.0f + expf(-my_l[0])), s1 = 1.0f / (1.0f + expf(-my_l[1]));
+    float sum0 = 0.0f, sum1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+      sum0 += readlane_f32(s0, j);
+      sum1 += readlane_f32(s1, j);
+    }
+    if (lane < kK) {
+      const float w0 = s0 / sum0, w1 = s1 / sum1;
+      atomicOr(&s_mask[my_id[0]], 1u << wave);
+      atomicOr(&s_mask[my_id[1]], 1u << (wave + 4));
+      s_wfull[my_id[0]][wave] = w0;
+      s_wfull[my_id[1]][wave + 4] = w1;
+      if (g == 0) {
+        if (ids_out) {
+          ids_out[wave * kK + lane] = my_id[0];
+          ids_out[(wave + 4) * kK + lane] = my_id[1];
+        }
+        if (w_out) {
+          w_out[wave * kK + lane] = w0;
+          w_out[(wave + 4) * kK + lane] = w1;
+        }
+      }
+    }
   } else if (wave < B) {
     float v[1][4];
     wait_slots<4>(lrep + wave * kE, 64, epoch, v[0], &ctl->err);
