@@ -1032,10 +1032,13 @@ __device__ __forceinline__ void decode_layer(
   __syncthreads();
   if (wave == 0) {            // entries: touched experts in ascending id, then the shared one
     int base = 0;
+    unsigned mq[4];             // the four reads first: one LDS round trip, not four
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mq[q] = s_mask[64 * q + lane];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 64 * q + lane;
-      const unsigned m = s_mask[e];
+      const unsigned m = mq[q];
       const uint64_t bal = __ballot(m != 0u);
       const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
