@@ -56,13 +56,13 @@ bool split_path_forced();
 // Flint's shape with two shared experts and NVFP4 weights (the Inkling
 // shape at Flint's widths): a general shape that the single-launch kernel
 // also serves, for the plain layer.
-// Flint's shape in W4A4 at batch 1: the single-launch kernel (larger
-// batches take the general path, where h is quantised once per pair rather
-// than by every workgroup).
+// Flint's shape in W4A4 at batch 1 to 8: the single-launch kernel, every
+// workgroup quantising all of x and all of h itself (the general path
+// quantises h once per pair, in a launch of its own).
 bool a4_path(const moe_shape* s, int B) {
-  return s && s->wfmt == MOE_W_NVFP4_A4 && B == 1 && s->hidden == moe::kH &&
+  return s && s->wfmt == MOE_W_NVFP4_A4 && B >= 1 && B <= moe::kMaxB && s->hidden == moe::kH &&
          s->inter == moe::kI && s->n_experts == moe::kE && s->top_k == moe::kK &&
-         s->n_shared == 1 && moe::fused_a4_supported() && !split_path_forced();
+         s->n_shared == 1 && moe::fused_a4_supported(B) && !split_path_forced();
 }
 bool ns2_path(const moe_shape* s) {
   return s && s->wfmt == MOE_W_NVFP4 && s->hidden == moe::kH && s->inter == moe::kI &&
@@ -283,7 +283,7 @@ moe_status moe_decode_forward(const moe_shape* shape, const void* x, int32_t B,
   moe::GenShape g;
   if (a4_path(shape, B)) {
     const hipError_t e = moe::launch_decode_fused_a4(
-        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), to_dev(routed),
+        B, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), to_dev(routed),
         to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out, static_cast<uint8_t*>(ws), s);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
@@ -357,7 +357,7 @@ moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32
   hipError_t e;
   moe::GenShape g;
   if (a4_path(shape, B)) {
-    e = moe::launch_decode_fused_a4(static_cast<const uint16_t*>(x),
+    e = moe::launch_decode_fused_a4(B, static_cast<const uint16_t*>(x),
                                     static_cast<const uint16_t*>(router_w), to_dev(routed),
                                     to_dev(shared), static_cast<uint16_t*>(out), ids_out, w_out,
                                     static_cast<uint8_t*>(ws), s, e0, e1);

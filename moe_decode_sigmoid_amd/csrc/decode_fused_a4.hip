@@ -1,25 +1,45 @@
 // The single-launch decode kernel in W4A4 (NVFP4 weights; NVFP4 activations
 // with the Four Over Six block scale: the Inkling-2-Small article, 48-layer
-// MoE section) for Flint's shape at batch 1: every workgroup quantises x
-// after the router has read it, and every h pair after the h copy.
+// MoE section) for Flint's shape at batch 1 to 8: every workgroup quantises
+// all of x after the router has read it, and every h pair after the h copy.
 // The kernel body is in decode_layer.h.
 #define MOE_DECODE_INSTANTIATES
 #include "decode_layer.h"
 
 namespace moe {
 
-bool fused_a4_supported() {
-  static int ok[64] = {0};
-  int dev = 0;
-  if (!fused_supported() || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  if (ok[dev] == 0) ok[dev] = one_per_cu(k_decode_fused<1, FMT_NVFP4, false, false, 1, true>) ? 1 : -1;
-  return ok[dev] == 1;
+template <int B>
+static bool a4_fits() {
+  return one_per_cu(k_decode_fused<B, FMT_NVFP4, false, false, 1, true>);
 }
 
-hipError_t launch_decode_fused_a4(const uint16_t* x, const uint16_t* rw, const ExpertsDev& routed,
-                                  const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
-                                  uint8_t* ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  auto k = k_decode_fused<1, FMT_NVFP4, false, false, 1, true>;
+bool fused_a4_supported(int B) {
+  static int ok[64][kMaxB + 1] = {};
+  int dev = 0;
+  if (B < 1 || B > kMaxB) return false;
+  if (!fused_supported() || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (ok[dev][B] == 0) {
+    bool fits = false;
+    switch (B) {
+      case 1: fits = a4_fits<1>(); break;
+      case 2: fits = a4_fits<2>(); break;
+      case 3: fits = a4_fits<3>(); break;
+      case 4: fits = a4_fits<4>(); break;
+      case 5: fits = a4_fits<5>(); break;
+      case 6: fits = a4_fits<6>(); break;
+      case 7: fits = a4_fits<7>(); break;
+      default: fits = a4_fits<8>(); break;
+    }
+    ok[dev][B] = fits ? 1 : -1;
+  }
+  return ok[dev][B] == 1;
+}
+
+template <int B>
+static hipError_t launch_a4_b(const uint16_t* x, const uint16_t* rw, const ExpertsDev& routed,
+                              const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
+                              uint8_t* ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  auto k = k_decode_fused<B, FMT_NVFP4, false, false, 1, true>;
   if (e0 && e1)
     hipExtLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, e0, e1, 0, x, rw, routed,
                           shared, out, ids, w, ws, FuseDev{});
@@ -27,6 +47,20 @@ hipError_t launch_decode_fused_a4(const uint16_t* x, const uint16_t* rw, const E
     hipLaunchKernelGGL(k, dim3(kFusedGrid), dim3(kFusedThreads), 0, st, x, rw, routed, shared, out,
                        ids, w, ws, FuseDev{});
   return hipGetLastError();
+}
+
+hipError_t launch_decode_fused_a4(int B, const uint16_t* x, const uint16_t* rw,
+                                  const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                                  int32_t* ids, float* w, uint8_t* ws, hipStream_t st, hipEvent_t e0,
+                                  hipEvent_t e1) {
+  switch (B) {
+#define MOE_A4_CASE(b) \
+  case b: return launch_a4_b<b>(x, rw, routed, shared, out, ids, w, ws, st, e0, e1);
+    MOE_A4_CASE(1) MOE_A4_CASE(2) MOE_A4_CASE(3) MOE_A4_CASE(4)
+    MOE_A4_CASE(5) MOE_A4_CASE(6) MOE_A4_CASE(7) MOE_A4_CASE(8)
+#undef MOE_A4_CASE
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Exhaustive check of the converts the quantiser takes its roundings from

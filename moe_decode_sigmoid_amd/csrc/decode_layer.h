@@ -468,7 +468,7 @@ template <int B, int FMT, bool A4 = false>
 __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk<FMT>& cu, float sg,
                                                float su, unsigned mask, int par, const uint4* s_x,
                                                const uint32_t (&x0)[16], int lane, float* hdst,
-                                               float gx = 1.0f) {
+                                               const float* gx = nullptr /* W4A4: x global by token */) {
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = 0.0f;
@@ -501,8 +501,8 @@ __device__ __forceinline__ void gateup_compute(const Chunk<FMT>& cg, const Chunk
   const float zu = dpp_f32<0x128>(z);
   const int t = 2 * (lane >> 4) + par;
   if ((lane & 15) == 0 && t < B && ((mask >> t) & 1u)) {
-    if constexpr (A4)   // the dot products ran on e2m1 * e4m3: times x's global
-      hdst[t] = silu_mul(z * sg * gx, zu * su * gx);
+    if constexpr (A4)   // the dot products ran on e2m1 * e4m3: times the token's x global
+      hdst[t] = silu_mul(z * sg * gx[t], zu * su * gx[t]);
     else
       hdst[t] = silu_mul(z * sg, zu * su);
   }
@@ -655,10 +655,10 @@ __device__ __forceinline__ void decode_layer(
   constexpr bool kLateDown = B == 1;
   static_assert(NS >= 1 && NS <= kMaxShared, "one or two shared experts");
   // W4A4 (NVFP4 activations with the Four Over Six block scale, FMT_NVFP4
-  // weights): the plain batch-1 layer; x and h are quantised by every
-  // workgroup itself (all of x, and all of h after the h copy)
-  static_assert(!A4 || (B == 1 && FMT == FMT_NVFP4 && !NORM && RES == 0 && XIN == 0 && !XOUT &&
-                        NS == 1 && PF == 0), "W4A4: the plain batch-1 NVFP4 layer");
+  // weights): the plain layer; x and h are quantised by every workgroup
+  // itself (all of x, and all of h after the h copy)
+  static_assert(!A4 || (FMT == FMT_NVFP4 && !NORM && RES == 0 && XIN == 0 && !XOUT && NS == 1 &&
+                        PF == 0), "W4A4: the plain NVFP4 layer");
   constexpr int kPairs = (kK + NS) * B;              // h pairs: 6 B routed + NS B shared
   const int g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -862,18 +862,22 @@ __device__ __forceinline__ void decode_layer(
     __syncthreads();
   }
   trace_stamp(ws, 1);
-  // W4A4: this wave's maximum |x| (x's global scale is amax / 2688), visible
-  // to every wave after the barrier behind the router dot
-  float* s_a4max = nullptr;
+  // W4A4: this wave's maximum |x| of each token (a token's global scale is
+  // its amax / 2688), visible to every wave after the barrier behind the
+  // router dot
+  float(*s_a4max)[4] = nullptr;
   if constexpr (A4) {
-    __shared__ float s_a4max_[4];
+    __shared__ float s_a4max_[kMaxB][4];
     s_a4max = s_a4max_;
-    const uint32_t u[4] = {xr[0].x, xr[0].y, xr[0].z, xr[0].w};
-    float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[i])), fabsf(bf16_hi(u[i]))));
-    m = wave_max(m);
-    if (lane == 0) s_a4max[wave] = m;
+    for (int t = 0; t < B; ++t) {
+      const uint32_t u[4] = {xr[t].x, xr[t].y, xr[t].z, xr[t].w};
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[i])), fabsf(bf16_hi(u[i]))));
+      m = wave_max(m);
+      if (lane == 0) s_a4max[t][wave] = m;
+    }
   }
   {
     float acc[B];
@@ -905,25 +909,37 @@ __device__ __forceinline__ void decode_layer(
   }
   trace_stamp(ws, 2);
   // W4A4: x quantised in place (the router has read it; every workgroup
-  // quantises all of x, each thread its own piece), x0 reread
-  float gx = 1.0f;
+  // quantises all of x, each thread its own piece of every token, read back
+  // from LDS so that one copy of the quantiser's code serves them all); at
+  // B = 1 x0 is reread
+  float* s_gx = nullptr;
   if constexpr (A4) {
-    gx = __fdiv_rn(fmaxf(fmaxf(s_a4max[0], s_a4max[1]), fmaxf(s_a4max[2], s_a4max[3])), 2688.0f);
-    s_x[sx_pos(0, tid)] = a4_quant_piece(xr[0], gx);
+    __shared__ float s_gx_[kMaxB];
+    s_gx = s_gx_;
+#pragma unroll 1
+    for (int t = 0; t < B; ++t) {
+      const float g = __fdiv_rn(fmaxf(fmaxf(s_a4max[t][0], s_a4max[t][1]),
+                                      fmaxf(s_a4max[t][2], s_a4max[t][3])), 2688.0f);
+      if (tid == 0) s_gx[t] = g;
+      const uint4 piece = s_x[sx_pos(t, tid)];
+      s_x[sx_pos(t, tid)] = a4_quant_piece(piece, g);
+    }
     trace_stamp(ws, 22);
     __syncthreads();
     trace_stamp(ws, 23);
+    if constexpr (B == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = s_x[sx_pos(0, 4 * lane + i)];
-      x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = s_x[sx_pos(0, 4 * lane + i)];
+        x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
+      }
     }
   }
   if (smask) {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       gateup_compute<B, FMT, A4>(pre.scg[s], pre.scu[s], sh_sg[s], sh_su[s], smask, wave >> 1, s_x,
-                                 x0, lane, &s_hsh[s][wave & 1][0], gx);
+                                 x0, lane, &s_hsh[s][wave & 1][0], s_gx);
   }
   trace_stamp(ws, 3);
 
@@ -1179,7 +1195,7 @@ __device__ __forceinline__ void decode_layer(
         const float zu = dpp_f32<0x128>(z);
         if ((lane & 15) == 0 && ((mme >> t) & 1u)) {
           if constexpr (A4)
-            s_hout[ime][t] = silu_mul(z * sgme * gx, zu * sume * gx);
+            s_hout[ime][t] = silu_mul(z * sgme * s_gx[t], zu * sume * s_gx[t]);
           else
             s_hout[ime][t] = silu_mul(z * sgme, zu * sume);
         }
@@ -1399,16 +1415,16 @@ __device__ __forceinline__ void decode_layer(
   __syncthreads();
   trace_stamp(ws, 10);
   // W4A4: every h pair quantised in place with its own global (amax / 2688):
-  // wave w takes pairs w and w + 4, lane l its 16-byte chunk l (elements 8 l
+  // wave w takes pairs w, w + 4, ..., lane l its 16-byte chunk l (elements 8 l
   // .. 8 l + 7, at LDS position 16 (l % 4) + l / 4 of the pair), so that the
   // lanes of a 16-element block are a lane pair
   float* s_gh = nullptr;
   if constexpr (A4) {
     __shared__ float s_gh_[kPairs];
     s_gh = s_gh_;
-    // one copy of the quantiser's code serves both rounds
+    // one copy of the quantiser's code serves every round
 #pragma unroll 1
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < (kPairs + 3) / 4; ++r) {
       const int p = wave + 4 * r;
       if (p < kPairs) {
         uint4* c = s_xh + p * 64 + 16 * (lane & 3) + (lane >> 2);

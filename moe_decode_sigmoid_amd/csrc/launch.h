@@ -35,13 +35,13 @@ hipError_t launch_decode_fused_ns2(int B, const uint16_t* x, const uint16_t* rw,
                                    hipEvent_t ev_stop = nullptr);
 
 // The same single-launch layer in W4A4 (NVFP4 weights, NVFP4 activations
-// with the Four Over Six block scale), Flint's shape, batch 1.
-bool fused_a4_supported();
+// with the Four Over Six block scale), Flint's shape, batch 1 to 8.
+bool fused_a4_supported(int B);
 hipError_t launch_a4_convert_check(unsigned long long* counts, hipStream_t st);
-hipError_t launch_decode_fused_a4(const uint16_t* x, const uint16_t* rw, const ExpertsDev& routed,
-                                  const ExpertsDev& shared, uint16_t* out, int32_t* ids, float* w,
-                                  uint8_t* ws, hipStream_t st, hipEvent_t ev_start = nullptr,
-                                  hipEvent_t ev_stop = nullptr);
+hipError_t launch_decode_fused_a4(int B, const uint16_t* x, const uint16_t* rw,
+                                  const ExpertsDev& routed, const ExpertsDev& shared, uint16_t* out,
+                                  int32_t* ids, float* w, uint8_t* ws, hipStream_t st,
+                                  hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // A stack of L layers (same x) in one launch of the fused kernel's body.
 hipError_t launch_decode_stack(int B, int fmt, const uint16_t* x, const LayerDev* layers, int L,

@@ -173,35 +173,38 @@ def test_w4a4_end_to_end_against_the_oracles_own_h(name, B, seed):
 
 
 # ---------------------------------------------------------------- single launch
-# Flint's shape at batch 1 runs on the single-launch kernel, every workgroup
-# quantising x and all h pairs itself with the same decisions.
+# Flint's shape at batch 1 to 8 runs on the single-launch kernel, every
+# workgroup quantising x and all h pairs itself with the same decisions.
 
-@pytest.mark.parametrize("seed", [11, 12, 13])
-def test_w4a4_single_launch_end_to_end(seed):
-    test_w4a4_end_to_end_against_the_oracles_own_h("flint", 1, seed)
+@pytest.mark.parametrize("B,seed", [(1, 11), (1, 12), (1, 13), (2, 14), (5, 15), (8, 16)])
+def test_w4a4_single_launch_end_to_end(B, seed):
+    test_w4a4_end_to_end_against_the_oracles_own_h("flint", B, seed)
 
 
-def test_w4a4_single_launch_agrees_with_the_general_path():
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_w4a4_single_launch_agrees_with_the_general_path(B):
     for seed in (21, 22):
-        _, _, y1, ids1, w1, _ = run("flint", seed, 1)
-        _, _, y2, ids2, w2, _ = run("flint", seed, 1, general=True)
-        assert sorted(ids1[0].tolist()) == sorted(ids2[0].tolist())
-        np.testing.assert_allclose(np.sort(w1[0]), np.sort(w2[0]), rtol=2e-5, atol=1e-6)
-        parity.check_output(y1, y2, f"w4a4 single launch vs general, seed {seed}")
+        _, _, y1, ids1, w1, _ = run("flint", seed, B)
+        _, _, y2, ids2, w2, _ = run("flint", seed, B, general=True)
+        for t in range(B):
+            assert sorted(ids1[t].tolist()) == sorted(ids2[t].tolist()), t
+            np.testing.assert_allclose(np.sort(w1[t]), np.sort(w2[t]), rtol=2e-5, atol=1e-6)
+        parity.check_output(y1, y2, f"w4a4 single launch vs general, B {B}, seed {seed}")
 
 
-def test_w4a4_single_launch_repeats_and_shares_a_workspace():
+@pytest.mark.parametrize("B", [1, 8])
+def test_w4a4_single_launch_repeats_and_shares_a_workspace(B):
     """Repeated calls give the same bits, and W4A4 and W4A16 single-launch
     calls alternate on one workspace as on separate ones."""
     H = SHAPES["flint"][0]
     host, dl = layer("flint", 31)
     S4 = moe.shape(moe.MOE_W_NVFP4_A4)
-    x = moe.device.to_device_bf16(testgen.make_x(131, 1, H))
-    nbytes = max(moe.moe_workspace_bytes(1, S=S4), moe.moe_workspace_bytes(1))
+    x = moe.device.to_device_bf16(testgen.make_x(131, B, H))
+    nbytes = max(moe.moe_workspace_bytes(B, S=S4), moe.moe_workspace_bytes(B))
     ws = moe.alloc_workspace(nbytes)
 
     def call(S):
-        o = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+        o = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
         moe.moe_decode_forward(x, dl.router, dl.routed, dl.shared, o, ws, S=S)
         return o
     ref4 = call(S4)
