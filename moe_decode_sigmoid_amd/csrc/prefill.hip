@@ -549,11 +549,37 @@ __global__ __launch_bounds__(kGThreads1, 1) void k_prefill_gateup(const uint16_t
   const uint8_t* bcodes = FMT == FMT_NVFP4 ? X.w13 + wrow * (kH / 2) + bcol / 2
                                            : X.w13 + (wrow * kH + bcol) * 2;
   const uint8_t* bscales = FMT == FMT_NVFP4 ? X.w13s + wrow * (kH / 16) + bcol / 16 : nullptr;
+  // NVFP4: the tile's block scales (256 rows x 128 bytes) go to LDS once, in
+  // full 16-byte loads (the two threads of a row take 64 bytes each); a
+  // stage then reads its 2 bytes per thread from LDS.  Loaded per stage from
+  // memory, each 2-byte load touched a cache line of its own and those loads
+  // cost about a fifth of the kernel.
+  // (row pitch 144 bytes: a wave's 32 rows spread over the banks)
+  constexpr int kSP = kH / 16 + 16;
+  __shared__ __align__(16) uint8_t sS[FMT == FMT_NVFP4 ? kGBN * kSP : 16];
+  if constexpr (FMT == FMT_NVFP4) {
+    const uint4* src = reinterpret_cast<const uint4*>(X.w13s + wrow * (kH / 16)) + (tid % G::TB) * 4;
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = src[i];
+    uint4* dst = reinterpret_cast<uint4*>(sS + brow * kSP) + (tid % G::TB) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    __syncthreads();
+  }
+  const uint8_t* sscales = sS + brow * kSP + bcol / 16;
   Slot ring[kRingDepth<FMT>];
   auto gload = [&](Slot& sl, int kt) {
 #pragma unroll
     for (int i = 0; i < G::EA / 8; ++i) sl.a[i] = ap[kt * (kGBK1 / 8) + i];
-    g_load_b<FMT, kGBK1>(sl, bcodes, bscales, kt);
+    if constexpr (FMT == FMT_NVFP4) {
+      const uint4* cp = reinterpret_cast<const uint4*>(bcodes + (size_t)kt * (kGBK1 / 2));
+#pragma unroll
+      for (int i = 0; i < G::EB / 32; ++i) sl.c[i] = cp[i];
+      sl.s = *reinterpret_cast<const decltype(sl.s)*>(sscales + kt * (kGBK1 / 16));
+    } else {
+      g_load_b<FMT, kGBK1>(sl, bcodes, bscales, kt);
+    }
   };
   auto sstore = [&](const Slot& sl, int buf) {
     g_store<FMT, kGBK1, kGThreads1>(sl, sA[buf], sB[buf], tid);
@@ -709,17 +735,6 @@ __device__ __forceinline__ void w2_take(const W2Slot& sl, W2Cur& cur) {
   }
 }
 
-// Stage kt of a lane's two weight rows (wrow[j]: the row's first code byte;
-// wsc[j]: its first scale byte).
-__device__ __forceinline__ void w2_load_b(W2Slot& sl, const uint8_t* const (&wrow)[2],
-                                          const uint8_t* const (&wsc)[2], int kt, int half) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    sl.c[j] = *reinterpret_cast<const uint4*>(wrow[j] + (size_t)kt * (kW2BK / 2) + 16 * half);
-    sl.s[j] = *reinterpret_cast<const uint32_t*>(wsc[j] + (size_t)kt * (kW2BK / 16));
-  }
-}
-
 // The wave's 128 x 64 accumulator (4 row blocks x 2 column blocks).
 struct W2Acc {
   f32x16 c[4][2];
@@ -784,19 +799,40 @@ __global__ __launch_bounds__(kW2Threads, 1) void k_prefill_down_w(int T, Experts
       (tid % kW2TPR) * (kW2EA / 8);
   __bf16* adst0 = sA[0] + (tid / kW2TPR) * LR + (tid % kW2TPR) * kW2EA;
   const uint8_t* wrow[2];
-  const uint8_t* wsc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const size_t row = ee * kH + (size_t)kW2N * n + 64 * wave + 32 * j + (lane & 31);
     wrow[j] = X.w2 + row * (kI / 2);
-    wsc[j] = X.w2s + row * (kI / 16);
   }
+  // the block scales of the workgroup's 512 weight rows (contiguous, 32 bytes
+  // a row) go to LDS once in 16-byte loads, and each stage reads its words
+  // there: loaded per stage from memory, every 4-byte scale load touched a
+  // cache line of its own (row pitch 48 bytes: at most two rows of a wave's
+  // 32 on a bank)
+  constexpr int kSP2 = kI / 16 + 16;
+  __shared__ __align__(16) uint8_t sS2[kW2N * kSP2];
+  {
+    const uint4* src =
+        reinterpret_cast<const uint4*>(X.w2s + (ee * kH + (size_t)kW2N * n) * (kI / 16)) + 2 * tid;
+    const uint4 v0 = src[0], v1 = src[1];
+    uint4* dst = reinterpret_cast<uint4*>(sS2 + tid * kSP2);
+    dst[0] = v0;
+    dst[1] = v1;
+    __syncthreads();
+  }
+  const uint8_t* ssc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) ssc[j] = sS2 + (64 * wave + 32 * j + (lane & 31)) * kSP2;
   W2Slot ring[kW2Ring];
   W2Cur cur;
   auto gload = [&](W2Slot& sl, int kt) {
 #pragma unroll
     for (int i = 0; i < kW2EA / 8; ++i) sl.a[i] = ap[kt * (kW2BK / 8) + i];
-    w2_load_b(sl, wrow, wsc, kt, half);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sl.c[j] = *reinterpret_cast<const uint4*>(wrow[j] + (size_t)kt * (kW2BK / 2) + 16 * half);
+      sl.s[j] = *reinterpret_cast<const uint32_t*>(ssc[j] + kt * (kW2BK / 16));
+    }
   };
   auto sstore = [&](const W2Slot& sl, int buf) {
     __bf16* d = adst0 + buf * (kGBM * LR);
