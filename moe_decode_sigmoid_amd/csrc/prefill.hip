@@ -907,19 +907,24 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_combine(int T, uint8_t* _
   const int* ids = wsp<int>(ws, L.ids);
   const int* pos = wsp<int>(ws, L.pos);
   const f16* part = wsp<f16>(ws, L.part);
-  int order[kK];
+  // the token's six (expert, partial row) pairs in registers, sorted by
+  // expert id (distinct within a token) with compare-exchanges on values
+  int eid[kK], prow[kK];
 #pragma unroll
-  for (int j = 0; j < kK; ++j) order[j] = j;
+  for (int j = 0; j < kK; ++j) {
+    eid[j] = ids[(size_t)t * kK + j];
+    prow[j] = pos[(size_t)t * kK + j];
+  }
 #pragma unroll
-  for (int a = 1; a < kK; ++a)                            // sort slots by expert id
+  for (int a = 1; a < kK; ++a)
 #pragma unroll
     for (int b = a; b > 0; --b) {
-      const int ea = ids[(size_t)t * kK + order[b]], eb = ids[(size_t)t * kK + order[b - 1]];
-      if (ea < eb) {
-        const int tmp = order[b];
-        order[b] = order[b - 1];
-        order[b - 1] = tmp;
-      }
+      const bool sw = eid[b] < eid[b - 1];
+      const int e0 = eid[b - 1], e1 = eid[b], p0 = prow[b - 1], p1 = prow[b];
+      eid[b - 1] = sw ? e1 : e0;
+      eid[b] = sw ? e0 : e1;
+      prow[b - 1] = sw ? p1 : p0;
+      prow[b] = sw ? p0 : p1;
     }
   float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   auto add_row = [&](int p) {
@@ -932,7 +937,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill_combine(int T, uint8_t* _
     }
   };
 #pragma unroll
-  for (int j = 0; j < kK; ++j) add_row(pos[(size_t)t * kK + order[j]]);
+  for (int j = 0; j < kK; ++j) add_row(prow[j]);
   add_row(T * kK + t);
   if (resid) {
     const uint4 v = *reinterpret_cast<const uint4*>(resid + (size_t)t * kH + c8);
