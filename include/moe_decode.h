@@ -96,9 +96,14 @@ typedef enum {
  * I values) a global amax / 2688, and per 16-block the E4M3 scale mapping
  * the block maximum to 6 or to 4, whichever reconstructs with the smaller
  * mean absolute error (a tie keeps 6), every step an fp32 operation in a
- * stated order (the library's general decode path).  The router
- * uses x itself.  Decode entry points only (general path); weights as
- * MOE_W_NVFP4. */
+ * stated order.  The router uses x itself.  Decode entry points only;
+ * weights as MOE_W_NVFP4.  Flint's shape at B <= 8 runs on the
+ * single-launch kernel, every workgroup quantising all of x and of h itself
+ * with the same decisions (its roundings by gfx950's converts, checked by
+ * moe_a4_convert_check); other shapes run on the general path, which
+ * quantises each vector once.  Setting the environment variable
+ * MOE_DECODE_SPLIT=1 sends every decode call to the multi-launch paths
+ * (a test switch: both compute the same layer). */
 typedef enum {
   MOE_W_NVFP4 = 0,
   MOE_W_BF16 = 1,
@@ -361,8 +366,9 @@ moe_status moe_prefill_forward_ex(const moe_shape* shape, const void* x, int32_t
  *   W4A4 only: [4] the quantised x as e2m1 * e4m3 (bf16 [8][hidden]),
  *   [5] the x globals (f32 [8]), [6] the quantised h as e2m1 * e4m3 (bf16
  *   [66][8][inter]), [7] the h globals (f32 [66][8]).
- * Valid after a decode call on that workspace; MOE_ERR_UNSUPPORTED for
- * shapes the general path does not serve. */
+ * Valid after a decode call that took the general path on that workspace
+ * (for Flint's shape in W4A4 that needs MOE_DECODE_SPLIT=1);
+ * MOE_ERR_UNSUPPORTED for shapes the general path does not serve. */
 moe_status moe_general_workspace_layout(const moe_shape* shape, size_t offsets[8]);
 
 /* Parity probe of the in-register NVFP4 decode: writes tensor `tensor`
