@@ -916,13 +916,30 @@ __device__ __forceinline__ void decode_layer(
   if constexpr (A4) {
     __shared__ float s_gx_[kMaxB];
     s_gx = s_gx_;
+    auto x_global = [&](int t) __attribute__((always_inline)) {
+      return __fdiv_rn(fmaxf(fmaxf(s_a4max[t][0], s_a4max[t][1]),
+                             fmaxf(s_a4max[t][2], s_a4max[t][3])), 2688.0f);
+    };
+    if constexpr (B == 1) {
+      const float g = x_global(0);
+      if (tid == 0) s_gx[0] = g;
+      s_x[sx_pos(0, tid)] = a4_quant_piece(s_x[sx_pos(0, tid)], g);
+    } else {
+      // two tokens per round, their serial chains side by side (an odd last
+      // token pairs with itself: the same value is written twice)
 #pragma unroll 1
-    for (int t = 0; t < B; ++t) {
-      const float g = __fdiv_rn(fmaxf(fmaxf(s_a4max[t][0], s_a4max[t][1]),
-                                      fmaxf(s_a4max[t][2], s_a4max[t][3])), 2688.0f);
-      if (tid == 0) s_gx[t] = g;
-      const uint4 piece = s_x[sx_pos(t, tid)];
-      s_x[sx_pos(t, tid)] = a4_quant_piece(piece, g);
+      for (int t = 0; t < B; t += 2) {
+        const int t1 = t + 1 < B ? t + 1 : t;
+        const float g0 = x_global(t), g1 = x_global(t1);
+        if (tid == 0) {
+          s_gx[t] = g0;
+          s_gx[t1] = g1;
+        }
+        const uint4 p0 = s_x[sx_pos(t, tid)], p1 = s_x[sx_pos(t1, tid)];
+        const uint4 q0 = a4_quant_piece(p0, g0), q1 = a4_quant_piece(p1, g1);
+        s_x[sx_pos(t, tid)] = q0;
+        s_x[sx_pos(t1, tid)] = q1;
+      }
     }
     trace_stamp(ws, 22);
     __syncthreads();
@@ -1422,20 +1439,32 @@ __device__ __forceinline__ void decode_layer(
   if constexpr (A4) {
     __shared__ float s_gh_[kPairs];
     s_gh = s_gh_;
-    // one copy of the quantiser's code serves every round
-#pragma unroll 1
-    for (int r = 0; r < (kPairs + 3) / 4; ++r) {
-      const int p = wave + 4 * r;
-      if (p < kPairs) {
-        uint4* c = s_xh + p * 64 + 16 * (lane & 3) + (lane >> 2);
-        const uint4 v = *c;
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-        float m = 0.0f;
+    // pairs w + 8 r and w + 8 r + 4 in one round, their serial chains side
+    // by side (without a second pair the first is taken twice: the same
+    // values are written twice)
+    auto h_global = [&](uint4 v) __attribute__((always_inline)) {
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[i])), fabsf(bf16_hi(u[i]))));
-        const float ghp = __fdiv_rn(wave_max(m), 2688.0f);
-        if (lane == 0) s_gh[p] = ghp;
-        *c = a4_quant_piece(v, ghp);
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[i])), fabsf(bf16_hi(u[i]))));
+      return __fdiv_rn(wave_max(m), 2688.0f);
+    };
+#pragma unroll 1
+    for (int r = 0; r < (kPairs + 7) / 8; ++r) {
+      const int pa = wave + 8 * r;
+      if (pa < kPairs) {
+        const int pb = pa + 4 < kPairs ? pa + 4 : pa;
+        uint4* ca = s_xh + pa * 64 + 16 * (lane & 3) + (lane >> 2);
+        uint4* cb = s_xh + pb * 64 + 16 * (lane & 3) + (lane >> 2);
+        const uint4 va = *ca, vb = *cb;
+        const float ga = h_global(va), gb = h_global(vb);
+        if (lane == 0) {
+          s_gh[pa] = ga;
+          s_gh[pb] = gb;
+        }
+        const uint4 qa = a4_quant_piece(va, ga), qb = a4_quant_piece(vb, gb);
+        *ca = qa;
+        *cb = qb;
       }
     }
     trace_stamp(ws, 20);
