@@ -207,7 +207,7 @@ moe_status moe_decode_forward_timed(const moe_shape* shape, const void* x, int32
  * 1..8; other shapes and B > 8 return MOE_ERR_UNSUPPORTED (they need more
  * than the library's own workspace holds).  The library keeps that
  * workspace in a static device array of the decode workspace's size (about
- * 1.3 MB; moe_workspace_bytes of Flint's decode shape), one per GPU, held
+ * 1.36 MB; moe_workspace_bytes of Flint's decode shape), one per GPU, held
  * until the process ends; the first call on a GPU looks its address up and
  * zero-fills it with a kernel on `stream`.  The call allocates nothing.
  * Every call on one GPU shares that array, which keeps the state of the last
@@ -261,7 +261,11 @@ typedef struct {
  * launch gap between layers (the pages hide that gap with programmatic
  * dependent launch: Optimization section, low-latency path and Fig. 3).
  * Each layer computes exactly what moe_decode_forward computes (the same
- * kernel code, bit for bit).
+ * arithmetic, bit for bit).  At B = 1 the stacked launches (this one and
+ * moe_decode_chain_forward) exchange the router logits inside each XCD,
+ * which relies on the hardware dealing a launch's workgroups out to the 8
+ * XCDs in turn; were the deal different, the logit wait gives up and the
+ * workspace status reports it (bit 0).
  *   layers   DEVICE array of n_layers moe_layer, 8-byte aligned; its
  *            contents cannot be checked on the host: every pointer in it
  *            must follow moe_decode_forward's rules for the shape.

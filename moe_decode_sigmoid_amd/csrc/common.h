@@ -105,7 +105,14 @@ constexpr size_t kSlotXOff = kFlagOff + (256 + 64 * kBankReps) * kFlagStride;
 // pairs][kI / 2 slots] (the small-batch hand-over between the GEMVs).
 constexpr size_t kHSlots = kI / 2;
 constexpr size_t kSlotHOff = kSlotXOff + kSlotXRep * kXReps;
-constexpr size_t kDecodeWsBytes = kSlotHOff + 8 * kMaxB * (kK + kMaxShared) * kHSlots;
+// Batch 1: the XCD-local logit slots, one copy per XCD ({fp32 value, epoch},
+// [kE] each, 2 KB apart): written and read only by the workgroups running on
+// that XCD.
+constexpr int kXcds = 8;
+constexpr size_t kSlotLXRep = 8 * kE;
+constexpr size_t kSlotLXOff = kSlotHOff + 8 * kMaxB * (kK + kMaxShared) * kHSlots;
+constexpr size_t kDecodeWsBytes = kSlotLXOff + kSlotLXRep * kXcds;
+static_assert(kSlotLXOff % 128 == 0 && kSlotLXRep % 128 == 0, "each XCD's slots on lines of their own");
 constexpr size_t kGenBase = kDecodeWsBytes;
 
 // Workspace of the general path: logits f32 [kMaxB][E], the dispatch, h

@@ -14,7 +14,9 @@
 // weight loads of a later step as soon as it knows their addresses:
 //
 //   A  router GEMV, one expert row per workgroup (the 4 waves split the 2048
-//      columns) -> logit slots; the shared expert's gate/up rows 2g, 2g+1
+//      columns) -> logit slots (batch 1 in a stacked launch: eight rows per
+//      workgroup, every XCD computing all 256; see kXcdLogits); the shared
+//      expert's gate/up rows 2g, 2g+1
 //      (routing-independent) -> h; the shared expert's down rows of the
 //      workgroup's 8 outputs are fetched.
 //   B  every workgroup waits for the 256 x B logits and repeats the sigmoid /
@@ -36,12 +38,14 @@
 // workgroup normalises the same x, so no exchange is needed), and the
 // residual add before the output rounding of step C.
 //
-// Hand-over between workgroups uses only device-coherent accesses (relaxed
-// agent-scope atomics: no cache write-back or invalidation):
+// Hand-over between workgroups uses relaxed agent-scope atomics (no cache
+// write-back or invalidation), and plain stores for the XCD-local logits:
 //  - call epoch: workgroup g keeps a private counter in the workspace; every
 //    call adds one, so all counters agree (the workspace starts zeroed).
 //  - logits: 8-byte slots {fp32 value, epoch} in kLogitReps copies; readers
-//    poll copy g % kLogitReps until the epochs match.
+//    poll copy g % kLogitReps until the epochs match.  Batch 1 in a stacked
+//    launch: one copy per XCD, written with plain stores and read by that
+//    XCD's workgroups only (the lines stay in its L2).
 //  - h: coherent stores; after waiting for them a workgroup adds 1 to
 //    h-ready counter g % 64 of each of kBankReps copies (one 128-byte line
 //    each); readers poll the 64 counters of copy g % kBankReps until each
@@ -90,6 +94,25 @@ constexpr bool kHDirect = MOE_H_DIRECT != 0;
 #define MOE_GU_WEIGHT 1
 #endif
 constexpr int kGuWeight = MOE_GU_WEIGHT;
+// Batch 1 in a stacked launch exchanges the router logits inside each XCD:
+// the 32 workgroups of an XCD compute all 256 router rows, 8 each (workgroup
+// g rows 8 (g / 8) + j), and hand the logits over through the XCD's own L2
+// (plain stores stay there; agent-scope loads read them), a round trip about
+// half as long as one through memory.  The next layer's eight router rows go
+// to LDS during the current layer's h exchange, when nothing waits for
+// memory; a one-layer launch would wait for them before its router dot,
+// which costs more than the exchange saves, so it keeps the device-wide
+// slots, as larger batches do.  The hardware deals a launch's workgroups out
+// to the 8 XCDs in turn, starting where the previous dispatch stopped, so
+// the workgroups of one XCD are g = c, c + 8, ... for some c: their g / 8
+// are 0 .. 31.  The slots are indexed by the XCD a workgroup reads from its
+// hardware register.  (Were the deal ever different, an XCD would miss some
+// rows and its logit wait would give up, which the status word reports.)
+#ifndef MOE_XCD_LOGITS
+#define MOE_XCD_LOGITS 1
+#endif
+template <int B, int PF>
+constexpr bool kXcdLogits = MOE_XCD_LOGITS != 0 && B == 1 && PF != 0;
 static_assert(kGuWeight >= 0 && kGuWeight + kMaxB < 16, "a row pair's weight fits 4 bits");
 
 // ------------------------------------------------------------------ row chunks
@@ -181,6 +204,18 @@ __device__ __forceinline__ void trace_flush(uint8_t* ws) {
 #else
   (void)ws;
 #endif
+}
+
+// A plain store: the line stays in this XCD's L2 (no write-through), where
+// the agent-scope loads of the XCD's other workgroups find it.
+__device__ __forceinline__ void put_slot_xcd(uint64_t* p, float v, uint32_t epoch) {
+  const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, v) | ((uint64_t)epoch << 32);
+  *(__attribute__((address_space(1))) uint64_t*)p = w;
+}
+
+// The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ int xcc_id() {
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u);
 }
 
 __device__ __forceinline__ void put_slot(uint64_t* p, float v, uint32_t epoch) {
@@ -562,7 +597,8 @@ __device__ __forceinline__ uint32_t* hready_bank(uint8_t* ws, int r, int k) {
 }
 
 // The loads of a layer that depend on neither x nor the routing: router row
-// g (wave w covers columns [512 w, 512 w + 512), 8 per lane); each shared
+// g at B > 1 (wave w covers columns [512 w, 512 w + 512), 8 per lane; batch 1
+// loads its eight rows at the start of the layer); each shared
 // expert's gate/up row 2g + (w & 1) for the tokens of parity w >> 1 (at B = 1
 // waves 0 and 1 only); its down rows of this workgroup's 8 outputs.  NS
 // shared experts (1 for Flint; 2 for the Inkling shape, which is Flint's with
@@ -578,11 +614,11 @@ __device__ __forceinline__ unsigned shared_token_mask(int wave) {
   return ((1u << B) - 1u) & ((wave >> 1) ? 0xAAAAAAAAu : 0x55555555u);
 }
 
-template <int B, int FMT, int NS>
+template <int B, int FMT, int NS, bool RW = true>
 __device__ __forceinline__ void load_pre_gateup(StepAPre<FMT, NS>& p, const uint16_t* rw,
                                                 const ExpertsDev& shared, int g, int wave,
                                                 int lane) {
-  p.wr = gld<uint4>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
+  if constexpr (RW) p.wr = gld<uint4>(rw + (size_t)g * kH + 512 * wave + 8 * lane);
   if (shared_token_mask<B>(wave)) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -590,6 +626,28 @@ __device__ __forceinline__ void load_pre_gateup(StepAPre<FMT, NS>& p, const uint
       p.scu[s].load_gu(shared, s, 1, 2 * g + (wave & 1), lane);
     }
   }
+}
+
+// The eight router rows of a batch-1 workgroup under the XCD-local logit
+// exchange, rows 8 (g / 8) + j, straight to LDS (16-byte loads that bypass
+// the registers: lane l of wave w lands at s_rw[64 (4 j + w) + l], its own
+// columns 512 w + 8 l .. + 7 of row j, which only it reads back).
+__device__ __forceinline__ void router_rows_to_lds(const uint16_t* rw, int g, int wave, int lane,
+                                                   uint4* s_rw) {
+  const uint16_t* rb = rw + (size_t)(8 * (g >> 3)) * kH + 512 * wave + 8 * lane;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(rb + (size_t)j * kH),
+        (__attribute__((address_space(3))) void*)(s_rw + 64 * (4 * j + wave)), 16, 0, 0);
+}
+
+// Their LDS: one array per kernel, declared outside the layer template, whose
+// instances (a stacked launch's first and later layers) would each get their
+// own and read rows the previous layer never loaded.
+__device__ __forceinline__ uint4* router_rows_lds() {
+  __shared__ uint4 s_rw[8 * 4 * 64];
+  return s_rw;
 }
 
 template <int FMT, int NS>
@@ -660,11 +718,13 @@ __device__ __forceinline__ void decode_layer(
   static_assert(!A4 || (FMT == FMT_NVFP4 && !NORM && RES == 0 && XIN == 0 && !XOUT && NS == 1 &&
                         PF == 0), "W4A4: the plain NVFP4 layer");
   constexpr int kPairs = (kK + NS) * B;              // h pairs: 6 B routed + NS B shared
+  constexpr bool kXL = kXcdLogits<B, PF>;
   const int g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp4 = lane >> 4, c16 = lane & 15;
   DecodeCtl* ctl = reinterpret_cast<DecodeCtl*>(ws);
   uint64_t* lslots = reinterpret_cast<uint64_t*>(ws + kSlotLogitOff);
+  uint64_t* lxslots = reinterpret_cast<uint64_t*>(ws + kSlotLXOff);
   uint64_t* xslots = reinterpret_cast<uint64_t*>(ws + kSlotXOff);
   uint64_t* hslots = reinterpret_cast<uint64_t*>(ws + kSlotHOff);
   constexpr bool kTagH = B <= kHTagMaxB;
@@ -690,7 +750,14 @@ __device__ __forceinline__ void decode_layer(
   trace_stamp(ws, 0);
   // ---------------------------------------------------------------- step A
   const unsigned smask = shared_token_mask<B>(wave);
-  if constexpr (PF != 2) load_pre_gateup<B, FMT, NS>(pre, rw, shared, g, wave, lane);
+  // batch 1 in a stacked launch: router rows 8 (g / 8) + j, j < 8 (the 32
+  // workgroups of an XCD cover all 256), in LDS; the first layer loads its
+  // own, a later one's came during the previous layer's h exchange
+  uint4* const s_rw = kXL ? router_rows_lds() : nullptr;
+  if constexpr (kXL && PF == 1) router_rows_to_lds(rw, g, wave, lane, s_rw);
+  // this XCD's copy of the XCD-local logit slots
+  uint64_t* const lxmine = lxslots + (xcc_id() & (kXcds - 1)) * kE;
+  if constexpr (PF != 2) load_pre_gateup<B, FMT, NS, !kXL>(pre, rw, shared, g, wave, lane);
   // Every load of step A goes out before any of them is used (loads return
   // in issue order, so a wait for one is a wait for all before it): x, piece
   // tid of each token; the norm weight and the residual of this workgroup's
@@ -879,7 +946,41 @@ __device__ __forceinline__ void decode_layer(
       if (lane == 0) s_a4max[t][wave] = m;
     }
   }
-  {
+  if constexpr (kXL) {
+    // eight rows: each row's wave total in wave_sum's order (the 16-lane
+    // group sums, groups 0 + 1 and 2 + 3, then the two pairs), so that every
+    // logit is bitwise the one a single-row workgroup computes.  Row j ends
+    // in s_part[wave][j].
+    const uint4 xv = s_x[sx_pos(0, 64 * wave + lane)];
+    uint4 wr8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wr8[j] = s_rw[64 * (4 * j + wave) + lane];
+    float a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float d = dot2_bf16(wr8[j].x, xv.x, 0.0f);
+      d = dot2_bf16(wr8[j].y, xv.y, d);
+      d = dot2_bf16(wr8[j].z, xv.z, d);
+      d = dot2_bf16(wr8[j].w, xv.w, d);
+      a[j] = group16_sum(d);
+    }
+    float u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {   // lanes 0-15, 32-47: row 2q; 16-31, 48-63: row 2q + 1
+      float lo = a[2 * q], hi = a[2 * q + 1];
+      swap16(lo, hi);
+      u[q] = lo + hi;
+    }
+    float r03 = u[0], r03b = u[1], r47 = u[2], r47b = u[3];
+    swap32(r03, r03b);   // rows 0-3 (4-7) in lane groups 0-3
+    swap32(r47, r47b);
+    r03 = r03 + r03b;
+    r47 = r47 + r47b;
+    if ((lane & 15) == 0) {
+      s_part[wave][lane >> 4] = r03;
+      s_part[wave][4 + (lane >> 4)] = r47;
+    }
+  } else {
     float acc[B];
 #pragma unroll
     for (int t = 0; t < B; ++t) {
@@ -898,12 +999,24 @@ __device__ __forceinline__ void decode_layer(
   __syncthreads();
   // the last wave stores (wave 0 polls first).  Once every 65536 calls the
   // slots of tokens t >= B are stamped too, so no slot is ever 2^32 calls old
-  // and a 32-bit tag cannot match a stale value.
+  // and a 32-bit tag cannot match a stale value; at that call batch 1 stamps
+  // the device-wide slots and larger batches the XCD-local ones.
   {
-    const int nt = (epoch & 0xFFFFu) == 0u ? kMaxB : B;
+    const bool wrap = (epoch & 0xFFFFu) == 0u;
+    if constexpr (kXL) {
+      const int j = tid - (kFusedThreads - 8);
+      if (j >= 0) {
+        const float v = s_part[0][j] + s_part[1][j] + s_part[2][j] + s_part[3][j];
+        put_slot_xcd(lxmine + 8 * (g >> 3) + j, v, epoch);
+      }
+    } else if (wrap && tid < 8) {
+      put_slot_xcd(lxmine + 8 * (g >> 3) + tid, 0.0f, epoch);
+    }
+    const int nt = wrap ? kMaxB : (kXL ? 0 : B);
     const int i = tid - (kFusedThreads - kMaxB * kLogitReps), t = i % kMaxB, r = i / kMaxB;
     if (i >= 0 && t < nt) {
-      const float v = t < B ? s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t] : 0.0f;
+      const float v =
+          !kXL && t < B ? s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t] : 0.0f;
       put_slot(lslots + r * (kSlotLogitRep / 8) + t * kE + g, v, epoch);
     }
   }
@@ -973,8 +1086,9 @@ __device__ __forceinline__ void decode_layer(
     // gone out (step C needs them, the loads do not).
     if (wave == 0) {
       float v[1][4];
-      wait_slots<4>(lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane, 64, epoch, v[0],
-                    &ctl->err);
+      wait_slots<4>(kXL ? lxmine + lane
+                        : lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane,
+                    64, epoch, v[0], &ctl->err);
       trace_stamp(ws, 4);
       int my_ids[1];
       float my_ls[1];
@@ -1390,7 +1504,13 @@ __device__ __forceinline__ void decode_layer(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     prefetch();
   }
-  __syncthreads();
+  // (with direct polling no wave waits for another here: every LDS use
+  // before the h copy ended at the barrier behind the gate/up rows)
+  if constexpr (kPollCounters) __syncthreads();
+  // The next layer's router rows (XCD-local logits) go to LDS behind the
+  // down rows and arrive while the h slots fill (the barrier behind the h
+  // copy waits for them).
+  if constexpr (kXL) router_rows_to_lds(next.rw, g, wave, lane, s_rw);
   trace_stamp(ws, 9);
 
   if constexpr (kTagH) {
@@ -1475,7 +1595,7 @@ __device__ __forceinline__ void decode_layer(
   // since step A): no load of this layer is issued after this point when
   // every routed entry's down rows are already in flight, so these wait
   // behind nothing and arrive while this layer finishes.
-  if constexpr (kPfEarly) load_pre_gateup<B, FMT, NS>(pre, next.rw, next.shared, g, wave, lane);
+  if constexpr (kPfEarly) load_pre_gateup<B, FMT, NS, !kXL>(pre, next.rw, next.shared, g, wave, lane);
 
   float acc[2][B], accs[2][2];
 #pragma unroll
@@ -1541,7 +1661,7 @@ __device__ __forceinline__ void decode_layer(
       load_set(dbuf2, k0 + 3 * kDepthC);
     }
     if constexpr (kPfLate) {     // the next layer's step-A rows, behind these
-      load_pre_gateup<B, FMT, NS>(pre, next.rw, next.shared, g, wave, lane);
+      load_pre_gateup<B, FMT, NS, !kXL>(pre, next.rw, next.shared, g, wave, lane);
       load_pre_down<FMT, NS>(pre, next.shared, g, lane);
     }
     run_set(dbuf, k0);

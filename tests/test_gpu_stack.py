@@ -69,6 +69,36 @@ def test_stack_layers_match_the_oracle(B):
         parity.check_output(parity.bf16_out_to_f64(out_s[l]), y_ref, f"stack layer {l}")
 
 
+def test_batch1_stack_after_launches_of_one_to_seven_workgroups():
+    """At batch 1 the stacked launch exchanges the router logits inside each
+    XCD.  The hardware deals a launch's workgroups out to the 8 XCDs in turn,
+    starting where the previous dispatch stopped, so 1 .. 7 one-workgroup
+    launches (the status kernel) before it change which workgroups share an
+    XCD.  Every such start gives the same bits, and no wait gives up."""
+    hosts, devs, table = stack("nvfp4")
+    B = 1
+    xd = moe.device.to_device_bf16(testgen.make_x(61, B))
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(B))
+    st = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    out = torch.empty((len(devs), B, 2048), dtype=torch.bfloat16, device="cuda")
+    moe.moe_decode_stack_forward(xd, table, out, ws)
+    moe.moe_workspace_status(ws, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref = out.clone()
+    for shift in range(1, 8):
+        print(f"batch-1 stack after {shift} one-workgroup launches", flush=True)
+        out.zero_()
+        torch.cuda.synchronize()
+        for _ in range(shift):
+            moe.moe_workspace_status(ws, st)
+        moe.moe_decode_stack_forward(xd, table, out, ws)
+        moe.moe_workspace_status(ws, st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, (shift, int(st.item()))
+        assert torch.equal(out, ref), shift
+
+
 def test_stack_in_a_hip_graph_replays_to_the_same_bits():
     hosts, devs, table = stack("nvfp4")
     B = 1
