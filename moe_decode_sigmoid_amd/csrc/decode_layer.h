@@ -213,6 +213,10 @@ __device__ __forceinline__ void put_slot_xcd(uint64_t* p, float v, uint32_t epoc
   *(__attribute__((address_space(1))) uint64_t*)p = w;
 }
 
+// Cache-policy operand of gfx950 memory instructions for a device-coherent
+// access: the SC1 bit (device scope; the data may come from another XCD).
+constexpr int kCpolDevice = 16;
+
 // The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
 __device__ __forceinline__ int xcc_id() {
   return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u);
@@ -1525,27 +1529,20 @@ __device__ __forceinline__ void decode_layer(
     for (int p = 0; p < kPairs; ++p) s_h32[4 * (p * 64 + 16 * (c & 3) + (c >> 2)) + wd] = hv[p];
   } else {
   // all 7 B h pairs of the call into LDS: 16-byte device-coherent loads
-  // (buffer loads with the device-scope bit), 8 in flight per thread
+  // (device-scope bit) straight to LDS, no registers, all in flight at once:
+  // wave w takes pairs w, w + 4, ...; lane i brings the piece that belongs
+  // at position i of the pair (uint4 c of a pair sits at 16 (c % 4) + c / 4,
+  // where load_h expects it).  The barrier below waits for them.
   {
-    constexpr int kN16 = kPairs * (kI * 2 / 16);
-    const __amdgpu_buffer_rsrc_t hr =
-        __builtin_amdgcn_make_buffer_rsrc(hbuf, 0, (int)(2 * kPairs * kI), 0x00020000);
-#pragma unroll 1
-    for (int i0 = 0; i0 < kN16; i0 += 8 * kFusedThreads) {
-      uint4 v[8];
+    const uint8_t* hb = reinterpret_cast<const uint8_t*>(hbuf);
+    const int c = 4 * (lane & 15) + (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = i0 + kFusedThreads * i + tid;
-        if (idx < kN16) v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hr, idx * 16, 0, 16));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = i0 + kFusedThreads * i + tid;
-        if (idx < kN16) {
-          const int c = idx & 63;
-          s_xh[(idx & ~63) + 16 * (c & 3) + (c >> 2)] = v[i];
-        }
-      }
+    for (int k = 0; k < (kPairs + 3) / 4; ++k) {
+      const int p = wave + 4 * k;
+      if (p < kPairs)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(hb + (size_t)p * (2 * kI) + 16 * c),
+            (__attribute__((address_space(3))) void*)(s_xh + 64 * p), 16, 0, kCpolDevice);
     }
   }
   }
