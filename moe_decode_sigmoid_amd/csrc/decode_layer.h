@@ -1686,7 +1686,6 @@ __device__ __forceinline__ void decode_layer(
     }
   }
   __syncthreads();
-  __shared__ uint16_t s_xo[kMaxB][kRowsPerWg];
   if (tid < kRowsPerWg * B) {
     const int r8 = tid / B, t = tid % B;
     float y = (s_red[0][r8][t] + s_red[1][r8][t]) + (s_red[2][r8][t] + s_red[3][r8][t]);
@@ -1695,24 +1694,32 @@ __device__ __forceinline__ void decode_layer(
     const uint16_t o = f32_to_bf16_rne(y);
     out[(size_t)t * kH + g * kRowsPerWg + r8] = o;
     if constexpr (XOUT) {
-      s_xo[t][r8] = o;
       resid_reg = __builtin_bit_cast(float, (uint32_t)o << 16);
+      // this workgroup's rows of the next layer's x, two rows to a slot, in
+      // every copy: rows 2 pp and 2 pp + 1 of token t are threads tid and
+      // tid + B of wave 0, so the even row's thread publishes both
+      const uint32_t o1 = __shfl_down((uint32_t)o, B);
+      if ((r8 & 1) == 0) {
+        const uint32_t v = (uint32_t)o | (o1 << 16);
+#pragma unroll
+        for (int rep = 0; rep < kXReps; ++rep)
+          put_slot_u32(xslots + rep * (kSlotXRep / 8) + t * (kH / 2) + g * (kRowsPerWg / 2) +
+                           (r8 >> 1),
+                       v, epoch);
+      }
     }
   }
-  if constexpr (XOUT) {
-    // this workgroup's rows of the next layer's x, two rows to a slot, in
-    // every copy; once every 65536 epochs the slots of the tokens t >= B are
-    // stamped too, as the logit slots are
-    __syncthreads();
-    const int nt = (epoch & 0xFFFFu) == 0u ? kMaxB : B;
-    const int n4 = nt * (kRowsPerWg / 2);
-    if (tid < n4 * kXReps) {
-      const int rep = tid / n4, j = tid - rep * n4, t = j / (kRowsPerWg / 2),
-                pp = j % (kRowsPerWg / 2);
-      const uint32_t v =
-          t < B ? (uint32_t)s_xo[t][2 * pp] | ((uint32_t)s_xo[t][2 * pp + 1] << 16) : 0u;
-      put_slot_u32(xslots + rep * (kSlotXRep / 8) + t * (kH / 2) + g * (kRowsPerWg / 2) + pp, v,
-                   epoch);
+  if constexpr (XOUT && B < kMaxB) {
+    // once every 65536 epochs the slots of the tokens t >= B are stamped too,
+    // as the logit slots are
+    if ((epoch & 0xFFFFu) == 0u) {
+      constexpr int n4 = (kMaxB - B) * (kRowsPerWg / 2);
+      for (int i = tid; i < n4 * kXReps; i += kFusedThreads) {
+        const int rep = i / n4, j = i - rep * n4;
+        put_slot_u32(xslots + rep * (kSlotXRep / 8) + (B + j / (kRowsPerWg / 2)) * (kH / 2) +
+                         g * (kRowsPerWg / 2) + j % (kRowsPerWg / 2),
+                     0u, epoch);
+      }
     }
   }
   if constexpr (B == 1) {
