@@ -833,8 +833,15 @@ __device__ __forceinline__ void decode_layer(
     if constexpr (B == 1) {
       const float r = row_rms_inv(x0, fz.eps);
       const uint4 v = rmsnorm8(xr[0], nw, r);
-      if constexpr (XIN == 1) __syncthreads();   // every wave has read its x0 from LDS
-      s_x[sx_pos(0, tid)] = v;
+      if constexpr (XIN == 1) {
+        // x in LDS is still being read (x0 of the other waves): the
+        // normalised x goes to a buffer of its own, which serves as x from here
+        __shared__ uint4 s_xn[kH / 8];
+        s_xn[sx_pos(0, tid)] = v;
+        s_x = s_xn;
+      } else {
+        s_x[sx_pos(0, tid)] = v;
+      }
       if (fz.xn_out && g == 0) reinterpret_cast<uint4*>(fz.xn_out)[tid] = v;
     } else {
       // the four piece sums of token t's row, lane l's pieces 4 l .. 4 l + 3
