@@ -1437,14 +1437,24 @@ __device__ __forceinline__ void decode_layer(
                    pack(s_hsh[s][0][t], s_hsh[s][1][t]), epoch);
     }
     const int nloc2 = (T1 - T0) >> 1;
-    for (int idx = tid; idx < nloc2 * B; idx += kFusedThreads) {
-      const int t = idx / nloc2, j = idx - t * nloc2;
-      const int s = T0 + 2 * j, a = s / kI;
-      const unsigned m = s_amask[a];
-      if ((m >> t) & 1u)
-        put_slot_u32(hslots + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kHSlots +
-                         (s % kI) / 2,
-                     pack(s_hout[2 * j][t], s_hout[2 * j + 1][t]), epoch);
+    if constexpr (B == 1) {
+      // one token: routed entry a is h pair a (every entry holds the token),
+      // so no table lookups stand between the values and their store
+      for (int j = tid; j < nloc2; j += kFusedThreads) {
+        const int s = T0 + 2 * j;
+        put_slot_u32(hslots + (size_t)(s / kI) * kHSlots + (s % kI) / 2,
+                     pack(s_hout[2 * j][0], s_hout[2 * j + 1][0]), epoch);
+      }
+    } else {
+      for (int idx = tid; idx < nloc2 * B; idx += kFusedThreads) {
+        const int t = idx / nloc2, j = idx - t * nloc2;
+        const int s = T0 + 2 * j, a = s / kI;
+        const unsigned m = s_amask[a];
+        if ((m >> t) & 1u)
+          put_slot_u32(hslots + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kHSlots +
+                           (s % kI) / 2,
+                       pack(s_hout[2 * j][t], s_hout[2 * j + 1][t]), epoch);
+      }
     }
     trace_stamp(ws, 14);
     // count in at once: the counters only tell the readers when to start
