@@ -27,7 +27,9 @@
 //      cut into 256 contiguous ranges, give SiLU(g) * u per token; the
 //      workgroup writes its h once, as bf16, then counts in on an h-ready
 //      counter.
-//   C  once all h is in: the 7 B h pairs are copied to LDS, then the down GEMV
+//   C  once all h is in: the 7 B h pairs are copied to LDS (batch 1: from
+//      epoch-tagged slots that every thread polls; larger batches: by
+//      global-to-LDS loads once the h-ready counters are full), then the down GEMV
 //      of the workgroup's 8 output rows over every entry (wave w takes routed
 //      entries a = w - 1 mod 4 and the shared expert's tokens w, w + 4),
 //      weighted by the routing, summed in a fixed order, rounded once to bf16.
@@ -49,7 +51,8 @@
 //  - h: coherent stores; after waiting for them a workgroup adds 1 to
 //    h-ready counter g % 64 of each of kBankReps copies (one 128-byte line
 //    each); readers poll the 64 counters of copy g % kBankReps until each
-//    holds 4 * epoch.
+//    holds 4 * epoch.  Batch 1 writes h as epoch-tagged slots instead, which
+//    readers poll directly (the counters still advance).
 // A wave's loads and stores complete in issue order, so the kernel keeps
 // stores out of the way of loads it waits for: h is staged in LDS and stored
 // in one go, and the polling wave issues its prefetches after its wait.
