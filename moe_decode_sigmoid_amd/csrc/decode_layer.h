@@ -302,6 +302,42 @@ __device__ __forceinline__ void wait_slots_u32(const uint64_t* p, int stride, ui
   }
 }
 
+// wait_slots_u32 with two poll rounds in flight: round r + 1 is issued
+// before round r is checked, so a slot that lands just after a round left is
+// seen half a round trip later rather than a whole one.  Four rounds in
+// straight-line code (so that the loads in flight are counted exactly), then
+// the plain loop; the rounds still in flight at an exit are discarded.  Only
+// where no global-to-LDS load is in flight: behind one the compiler waits
+// for every load before each check, which makes it slower than the loop.
+template <int N>
+__device__ __forceinline__ void wait_slots_u32_p2(const uint64_t* p, int stride, uint32_t epoch,
+                                                  uint32_t (&out)[N], unsigned* err,
+                                                  unsigned bit) {
+  uint64_t w0[N], w1[N], w2[N], w3[N];
+  auto issue = [&](uint64_t (&w)[N]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) w[k] = get_slot(p + k * stride);
+  };
+  auto done = [&](const uint64_t (&w)[N]) __attribute__((always_inline)) {
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) ok &= (uint32_t)(w[k] >> 32) == epoch;
+    if (__ballot(!ok) != 0) return false;
+#pragma unroll
+    for (int k = 0; k < N; ++k) out[k] = (uint32_t)w[k];
+    return true;
+  };
+  issue(w0);
+  issue(w1);
+  if (done(w0)) return;
+  issue(w2);
+  if (done(w1)) return;
+  issue(w3);
+  if (done(w2)) return;
+  if (done(w3)) return;
+  wait_slots_u32<N>(p, stride, epoch, out, err, bit);
+}
+
 __device__ __forceinline__ void put_slot_u32(uint64_t* p, uint32_t v, uint32_t epoch) {
   const uint64_t w = (uint64_t)v | ((uint64_t)epoch << 32);
   __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -807,8 +843,12 @@ __device__ __forceinline__ void decode_layer(
   // thread tid's slots tid + 256 k land in LDS as x's 32-bit words.
   if constexpr (XIN == 1) {
     uint32_t xs[4 * B];
-    wait_slots_u32<4 * B>(xslots + (g % kXReps) * (kSlotXRep / 8) + tid, kFusedThreads,
-                          epoch_reg, xs, &ctl->err, kErrXReady);
+    if constexpr (B <= 2)
+      wait_slots_u32_p2<4 * B>(xslots + (g % kXReps) * (kSlotXRep / 8) + tid, kFusedThreads,
+                               epoch_reg, xs, &ctl->err, kErrXReady);
+    else
+      wait_slots_u32<4 * B>(xslots + (g % kXReps) * (kSlotXRep / 8) + tid, kFusedThreads,
+                            epoch_reg, xs, &ctl->err, kErrXReady);
     if constexpr (B > 1) trace_stamp(ws, 15);   // (stamp 15 is the top-6 at B = 1)
     uint32_t* s_x32 = reinterpret_cast<uint32_t*>(s_x);
 #pragma unroll
@@ -1100,9 +1140,14 @@ __device__ __forceinline__ void decode_layer(
     // gone out (step C needs them, the loads do not).
     if (wave == 0) {
       float v[1][4];
-      wait_slots<4>(kXL ? lxmine + lane
-                        : lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane,
-                    64, epoch, v[0], &ctl->err);
+      {
+        uint32_t lw[4];
+        wait_slots_u32_p2<4>(kXL ? lxmine + lane
+                                 : lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane,
+                             64, epoch, lw, &ctl->err, kErrLogits);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[0][q] = __builtin_bit_cast(float, lw[q]);
+      }
       trace_stamp(ws, 4);
       int my_ids[1];
       float my_ls[1];
@@ -1542,7 +1587,10 @@ __device__ __forceinline__ void decode_layer(
     // polling until each carries this call's epoch, and puts its two values
     // where load_h expects them (uint4 c of a pair at 16 (c % 4) + c / 4)
     uint32_t hv[kPairs];
-    wait_slots_u32<kPairs>(hslots + tid, (int)kHSlots, epoch, hv, &ctl->err, kErrHReady);
+    if constexpr (kXL)   // the next layer's router rows are in flight to LDS
+      wait_slots_u32<kPairs>(hslots + tid, (int)kHSlots, epoch, hv, &ctl->err, kErrHReady);
+    else
+      wait_slots_u32_p2<kPairs>(hslots + tid, (int)kHSlots, epoch, hv, &ctl->err, kErrHReady);
     uint32_t* s_h32 = reinterpret_cast<uint32_t*>(s_xh);
     const int c = tid >> 2, wd = tid & 3;
 #pragma unroll
