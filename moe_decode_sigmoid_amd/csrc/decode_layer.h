@@ -309,11 +309,12 @@ __device__ __forceinline__ void wait_slots_u32(const uint64_t* p, int stride, ui
 // the plain loop; the rounds still in flight at an exit are discarded.  Only
 // where no global-to-LDS load is in flight: behind one the compiler waits
 // for every load before each check, which makes it slower than the loop.
-template <int N>
+template <int N, int R = 4>
 __device__ __forceinline__ void wait_slots_u32_p2(const uint64_t* p, int stride, uint32_t epoch,
                                                   uint32_t (&out)[N], unsigned* err,
                                                   unsigned bit) {
-  uint64_t w0[N], w1[N], w2[N], w3[N];
+  static_assert(R == 2 || R == 4, "two or four rounds");
+  uint64_t w0[N], w1[N], w2[N], w3[N];   // (w2, w3 unused with two rounds)
   auto issue = [&](uint64_t (&w)[N]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < N; ++k) w[k] = get_slot(p + k * stride);
@@ -330,12 +331,25 @@ __device__ __forceinline__ void wait_slots_u32_p2(const uint64_t* p, int stride,
   issue(w0);
   issue(w1);
   if (done(w0)) return;
-  issue(w2);
-  if (done(w1)) return;
-  issue(w3);
-  if (done(w2)) return;
-  if (done(w3)) return;
+  if constexpr (R == 4) {
+    issue(w2);
+    if (done(w1)) return;
+    issue(w3);
+    if (done(w2)) return;
+    if (done(w3)) return;
+  } else {
+    if (done(w1)) return;
+  }
   wait_slots_u32<N>(p, stride, epoch, out, err, bit);
+}
+
+// The same for one token's 256 logits (4 per lane, stride 64), as floats.
+__device__ __forceinline__ void wait_logits_p2(const uint64_t* p, uint32_t epoch, float (&v)[4],
+                                               unsigned* err) {
+  uint32_t w[4];
+  wait_slots_u32_p2<4>(p, 64, epoch, w, err, kErrLogits);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = __builtin_bit_cast(float, w[q]);
 }
 
 __device__ __forceinline__ void put_slot_u32(uint64_t* p, uint32_t v, uint32_t epoch) {
@@ -843,12 +857,9 @@ __device__ __forceinline__ void decode_layer(
   // thread tid's slots tid + 256 k land in LDS as x's 32-bit words.
   if constexpr (XIN == 1) {
     uint32_t xs[4 * B];
-    if constexpr (B <= 2)
-      wait_slots_u32_p2<4 * B>(xslots + (g % kXReps) * (kSlotXRep / 8) + tid, kFusedThreads,
-                               epoch_reg, xs, &ctl->err, kErrXReady);
-    else
-      wait_slots_u32<4 * B>(xslots + (g % kXReps) * (kSlotXRep / 8) + tid, kFusedThreads,
-                            epoch_reg, xs, &ctl->err, kErrXReady);
+    wait_slots_u32_p2<4 * B, (B <= 2 ? 4 : 2)>(xslots + (g % kXReps) * (kSlotXRep / 8) + tid,
+                                               kFusedThreads, epoch_reg, xs, &ctl->err,
+                                               kErrXReady);
     if constexpr (B > 1) trace_stamp(ws, 15);   // (stamp 15 is the top-6 at B = 1)
     uint32_t* s_x32 = reinterpret_cast<uint32_t*>(s_x);
 #pragma unroll
@@ -1193,8 +1204,8 @@ __device__ __forceinline__ void decode_layer(
   const uint64_t* lrep = lslots + (g % kLogitReps) * (kSlotLogitRep / 8) + lane;
   if (wave + 4 < B) {          // two tokens, wave and wave + 4: selected together
     float v[2][4];
-    wait_slots<4>(lrep + wave * kE, 64, epoch, v[0], &ctl->err);
-    wait_slots<4>(lrep + (wave + 4) * kE, 64, epoch, v[1], &ctl->err);
+    wait_logits_p2(lrep + wave * kE, epoch, v[0], &ctl->err);
+    wait_logits_p2(lrep + (wave + 4) * kE, epoch, v[1], &ctl->err);
     trace_stamp(ws, 4);
     int my_id[2];
     float my_l[2];
@@ -1227,7 +1238,7 @@ __device__ __forceinline__ void decode_layer(
     }
   } else if (wave < B) {
     float v[1][4];
-    wait_slots<4>(lrep + wave * kE, 64, epoch, v[0], &ctl->err);
+    wait_logits_p2(lrep + wave * kE, epoch, v[0], &ctl->err);
     trace_stamp(ws, 4);
     int my_id[1];
     float my_l[1];
@@ -1560,8 +1571,23 @@ __device__ __forceinline__ void decode_layer(
   if (!kPollCounters || wave != 3) prefetch();
   if (kPollCounters && wave == 3) {
     const uint32_t want = (uint32_t)(kFusedGrid / kHBanks) * epoch;
-    for (int spin = 0;; ++spin) {
-      const uint32_t v = load_flag(hready_bank(ws, g % kBankReps, lane));
+    const uint32_t* bank = hready_bank(ws, g % kBankReps, lane);
+    // first four polls with two in flight (as wait_slots_u32_p2), then the loop
+    bool ready;
+    {
+      const uint32_t c0 = load_flag(bank), c1 = load_flag(bank);
+      ready = __ballot(c0 != want) == 0;
+      if (!ready) {
+        const uint32_t c2 = load_flag(bank);
+        ready = __ballot(c1 != want) == 0;
+        if (!ready) {
+          const uint32_t c3 = load_flag(bank);
+          ready = __ballot(c2 != want) == 0 || __ballot(c3 != want) == 0;
+        }
+      }
+    }
+    for (int spin = 0; !ready; ++spin) {
+      const uint32_t v = load_flag(bank);
       if (__ballot(v != want) == 0) break;
       if (spin > kSpinLimit) {
         if (lane == 0)
