@@ -952,13 +952,6 @@ __device__ __forceinline__ void decode_layer(
   __syncthreads();
   const uint32_t epoch = s_epoch;
   epoch_reg = epoch;
-  if constexpr (NORM && B == 1) {          // x0 again, normalised
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = s_x[sx_pos(0, 4 * lane + i)];
-      x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
-    }
-  }
   trace_stamp(ws, 18);
   if constexpr (NORM && B > 1) {
     // the weight piece is the same for every token: widened once
@@ -1086,6 +1079,15 @@ __device__ __forceinline__ void decode_layer(
     }
   }
   trace_stamp(ws, 2);
+  // x0 again, normalised (for the gate/up products; read only now, so that
+  // these reads do not stand before the router's in LDS's in-order queue)
+  if constexpr (NORM && B == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = s_x[sx_pos(0, 4 * lane + i)];
+      x0[4 * i] = v.x; x0[4 * i + 1] = v.y; x0[4 * i + 2] = v.z; x0[4 * i + 3] = v.w;
+    }
+  }
   // W4A4: x quantised in place (the router has read it; every workgroup
   // quantises all of x, each thread its own piece of every token, read back
   // from LDS so that one copy of the quantiser's code serves them all); at
