@@ -1527,20 +1527,25 @@ __device__ __forceinline__ void decode_layer(
       __hip_atomic_fetch_add(hready_bank(ws, tid, g % kHBanks), 1u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    if (tid < 2 * NS * B) {   // shared expert s, row 2 g + r, token t: pair kK B + s B + t
-      const int s = tid / (2 * B), r = (tid / B) & 1, t = tid % B;
-      store_coherent_u16(hbuf + (size_t)(kK * B + s * B + t) * kI + 2 * g + r,
-                         f32_to_bf16_rne(s_hsh[s][r][t]));
+    if (tid < NS * B) {   // shared expert s, rows 2 g and 2 g + 1, token t: pair kK B + s B + t
+      const int s = tid / B, t = tid % B;
+      store_coherent_u32(
+          reinterpret_cast<uint32_t*>(hbuf + (size_t)(kK * B + s * B + t) * kI + 2 * g),
+          f32x2_to_bf16x2_rne(s_hsh[s][0][t], s_hsh[s][1][t]));
     }
     {
-      const int nloc = T1 - T0;
-      for (int idx = tid; idx < nloc * B; idx += kFusedThreads) {
-        const int t = idx / nloc, i = idx - t * nloc;
-        const int s = T0 + i, a = s / kI;
+      // rows in pairs (a workgroup's range starts and ends on even rows, and
+      // a pair never straddles two entries): one 4-byte store per pair
+      const int nloc2 = (T1 - T0) >> 1;
+      for (int idx = tid; idx < nloc2 * B; idx += kFusedThreads) {
+        const int t = idx / nloc2, j = idx - t * nloc2;
+        const int s = T0 + 2 * j, a = s / kI;
         const unsigned m = s_amask[a];
         if ((m >> t) & 1u)
-          store_coherent_u16(hbuf + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kI + (s % kI),
-                             f32_to_bf16_rne(s_hout[i][t]));
+          store_coherent_u32(
+              reinterpret_cast<uint32_t*>(hbuf + (size_t)(s_pair0[a] + __popc(m & ((1u << t) - 1u))) * kI +
+                                          (s % kI)),
+              f32x2_to_bf16x2_rne(s_hout[2 * j][t], s_hout[2 * j + 1][t]));
       }
     }
     // publish: wait for this workgroup's h stores, then count in on bank g % 64
